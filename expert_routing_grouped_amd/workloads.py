@@ -1,0 +1,146 @@
+"""Seeded synthetic workloads for the MoE expert layer.
+
+This module only draws inputs. It holds none of the layer's arithmetic (no
+routing, no sorting, no GEMM): both the HIP path and the CPU oracle take
+their inputs from here and from nowhere else.
+
+Draw recipe (the order of draws is part of the definition):
+
+* Grouped routing workloads follow the seeded simulation on the page
+  "大规模 EP 部署：分层 EPLB、DP 注意力的负载与双 batch 重叠"
+  (anrans.github.io, section "EPLB 与路由约束"): a generator
+  ``numpy.random.default_rng(seed)``; first a per-expert bias
+  ``b = normal(0, bias_std, E)`` (float64), then uniform scores
+  ``U = random((T, E))`` (float64), and the router input is
+  ``float32(U + 0.15 * b)``.
+* Then the activations ``x = standard_normal((T, d), float32)``.
+* Then, expert by expert in local order, the fused gate_up weight
+  ``0.02 * standard_normal((2I, d), float32)`` (rows [0, I) gate, rows
+  [I, 2I) up), and after all of them, expert by expert, the down weight
+  ``0.02 * standard_normal((d, I), float32)``.
+* bf16 workloads round x and the weights to bf16 (round to nearest even);
+  the toy workload keeps float32 and draws its router logits with
+  ``standard_normal((T, E), float32)`` before x.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+
+import numpy as np
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int                 # tokens
+    E: int                 # experts in the whole layer
+    top_k: int             # experts per token
+    num_groups: int        # expert groups (1 = no group stage)
+    topk_groups: int       # groups kept per token
+    score_mode: str        # "softmax" (router logits) or "raw" (scores used as given)
+    renormalize: bool      # selected weights divided by their sum
+    bias_std: float        # std of the per-expert bias b_e (raw mode)
+    hidden: int            # d; 0 = routing and permutation only
+    inter: int             # I (per-expert intermediate width)
+    expert_begin: int      # first expert owned by this GPU
+    num_local: int         # experts owned by this GPU
+    dtype: str             # "f32" or "bf16" for x, weights and outputs
+    seed: int = 0
+
+    @property
+    def has_ffn(self) -> bool:
+        return self.hidden > 0
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads, with the prefill share taken two ways: the expert
+# group that receives the most assignments (experts 32-63 at seed 0, the
+# busiest card that sets the layer time) and the literal experts 0-31.
+WORKLOADS = {
+    "toy_fp32": Workload("toy_fp32", T=128, E=8, top_k=2, num_groups=1, topk_groups=1,
+                         score_mode="softmax", renormalize=False, bias_std=0.0,
+                         hidden=256, inter=512, expert_begin=0, num_local=8, dtype="f32"),
+    "route_permute": Workload("route_permute", T=4096, E=256, top_k=8, num_groups=8, topk_groups=4,
+                              score_mode="raw", renormalize=True, bias_std=1.0,
+                              hidden=0, inter=0, expert_begin=0, num_local=256, dtype="f32"),
+    "decode_ep": Workload("decode_ep", T=512, E=256, top_k=8, num_groups=8, topk_groups=4,
+                          score_mode="raw", renormalize=True, bias_std=1.0,
+                          hidden=7168, inter=2048, expert_begin=0, num_local=8, dtype="bf16"),
+    "decode_tp": Workload("decode_tp", T=512, E=256, top_k=8, num_groups=8, topk_groups=4,
+                          score_mode="raw", renormalize=True, bias_std=1.0,
+                          hidden=7168, inter=64, expert_begin=0, num_local=256, dtype="bf16"),
+    "prefill_straggler": Workload("prefill_straggler", T=8192, E=256, top_k=8, num_groups=8, topk_groups=4,
+                                  score_mode="raw", renormalize=True, bias_std=2.0,
+                                  hidden=7168, inter=2048, expert_begin=32, num_local=32, dtype="bf16"),
+    "prefill_literal": Workload("prefill_literal", T=8192, E=256, top_k=8, num_groups=8, topk_groups=4,
+                                score_mode="raw", renormalize=True, bias_std=2.0,
+                                hidden=7168, inter=2048, expert_begin=0, num_local=32, dtype="bf16"),
+}
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); returns uint16 bit patterns.
+
+    Inputs are finite by construction, so no NaN handling is needed.
+    """
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+@dataclass
+class Inputs:
+    workload: Workload
+    scores: np.ndarray                 # [T, E] float32 (router logits or raw scores)
+    x: np.ndarray | None = None        # [T, d] float32, or uint16 bf16 bits
+    w_gate_up: np.ndarray | None = None  # [E_loc, 2I, d] float32 or uint16 bf16 bits
+    w_down: np.ndarray | None = None     # [E_loc, d, I]  float32 or uint16 bf16 bits
+
+
+def _weights(rng: np.random.Generator, n: int, shape: tuple, bf16: bool) -> np.ndarray:
+    out = np.empty((n,) + shape, dtype=np.uint16 if bf16 else np.float32)
+    for e in range(n):
+        w = rng.standard_normal(shape, dtype=np.float32)
+        w *= np.float32(0.02)
+        out[e] = f32_to_bf16_bits(w) if bf16 else w
+    return out
+
+
+def generate(w: Workload, with_ffn: bool = True) -> Inputs:
+    """Draw the seeded inputs of workload ``w`` (see the module docstring for the recipe)."""
+    rng = np.random.default_rng(w.seed)
+    if w.score_mode == "softmax":
+        scores = rng.standard_normal((w.T, w.E), dtype=np.float32)
+    else:
+        b = rng.normal(0.0, w.bias_std, w.E)
+        u = rng.random((w.T, w.E))
+        scores = (u + 0.15 * b).astype(np.float32)
+    inp = Inputs(w, np.ascontiguousarray(scores))
+    if not (w.has_ffn and with_ffn):
+        return inp
+    bf16 = w.dtype == "bf16"
+    x = rng.standard_normal((w.T, w.hidden), dtype=np.float32)
+    inp.x = f32_to_bf16_bits(x) if bf16 else x
+    inp.w_gate_up = _weights(rng, w.num_local, (2 * w.inter, w.hidden), bf16)
+    inp.w_down = _weights(rng, w.num_local, (w.hidden, w.inter), bf16)
+    return inp
+
+
+def page_simulation_scores(T: int = 20000, E: int = 256, seed: int = 0) -> np.ndarray:
+    """The router input of the page's seeded routing simulation (T = 20000, E = 256), as float32."""
+    return generate(Workload("page_sim", T=T, E=E, top_k=8, num_groups=8, topk_groups=4,
+                             score_mode="raw", renormalize=True, bias_std=1.0, hidden=0,
+                             inter=0, expert_begin=0, num_local=E, dtype="f32", seed=seed)).scores
+
+
+def tie_stress_scores(T: int, E: int, seed: int = 1, levels: int = 16) -> np.ndarray:
+    """Scores in [0, 1] quantised to multiples of 1/levels, so equal values are common (+0 and -0 both occur)."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(0, levels + 1, size=(T, E)).astype(np.float32) / np.float32(levels)
+    zero = q == 0
+    neg = rng.random((T, E)) < 0.5
+    q[zero & neg] = np.float32(-0.0)
+    return q

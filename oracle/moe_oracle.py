@@ -1,0 +1,266 @@
+"""CPU oracle of the MoE expert layer: route -> dispatch -> expert FFN -> combine.
+
+TEST INFRASTRUCTURE ONLY. This module is the slow, plain reference that the HIP
+path is checked against. Only the test suite, the package's smoke check and the
+CPU-baseline leg of the benchmark may import it; the product path never does,
+and it shares no code with the HIP kernels or their binding.
+
+Everything is numpy. Floating point work is done in float64 from exactly
+decoded inputs (float32 or bf16 bit patterns), with no intermediate rounding,
+except where a float decides an integer: routing compares the float32 scores
+and the float32 group scores, as the GPU does.
+
+Sources (web pages; section names as printed on them):
+
+* [EPLB] "大规模 EP 部署：分层 EPLB、DP 注意力的负载与双 batch 重叠"
+  (anrans.github.io, ai-infra-handbooks, serving/moe/ep-deploy), section
+  "EPLB 与路由约束": DeepSeek-V3 group-limited routing -- 256 experts in 8
+  groups, group score = sum of the group's two highest scores, keep 4
+  groups, then pick 8 experts inside them -- and its seeded simulation
+  (contiguous groups, bias b ~ N(0, 1), scores U(0,1) + 0.15 b, per-expert
+  load as a bincount of the routed table).
+* [CH15] "第十五章：多节点大模型推理——并行部署、解码优化与 MoE 路由"
+  (se7en.mintlify.app, ch15), section 3.4 "Expert Parallelism (EP)":
+  gating picks top-k experts per token, dispatch sends each token to its
+  experts, combine returns results to token order and merges them;
+  section 4.1: gating picks *logical* experts; section 4.3: the imbalance
+  metric max_e n_e / mean_e n_e.
+* [TRACE] "追踪一个 Token 在 MoE 推理中穿越 TP/CP/SP/EP/DP/PP 的路径"
+  (attain.fans), hop 4 "分发到两个专家": the combined output is the
+  router-weighted sum of the selected experts' outputs,
+  y = p5 E5(x) + p27 E27(x).
+* [L6] "Lecture 6 · 并行" (semidirectx.com, cs349d lecture06), section 2.2:
+  the MLP is W_gate, W_up (split along d_ff) and W_down.
+* [P2] "推理 INFRA 方法论（2）：分布式推理：TP、DP、EP、CP 与 PP"
+  (johneyzheng.top): the gate and up projections are fused into one GEMM
+  with N = 2 I.
+
+Readings where the pages leave a step open (each is also listed in the
+design notes of the repository):
+
+1. The gated MLP's activation is SiLU, silu(z) = z / (1 + exp(-z)),
+   h = silu(gate) * up (the pages name the three matrices but not the
+   activation).
+2. The fused weight is [gate; up] stacked along N: rows [0, I) are the
+   gate, rows [I, 2I) the up projection.
+3. Ties: the page's listing uses numpy's default argsort; here ties go
+   to the lower index (groups and experts), and -0 equals +0.
+4. Group scores are float32 sums of the two largest float32 scores (a
+   duplicated maximum counts twice); the page sums in float64 -- the two
+   readings route the page's 20000 tokens identically.
+5. "Plain softmax top-2" (toy workload): selection on the logits,
+   weights are the softmax probabilities over all experts, not
+   renormalised unless asked.
+6. Within one expert, rows keep assignment order a = t * k + j (a stable
+   counting sort); any order gives the same combined output.
+7. On one GPU's share of experts, tokens with no local expert get a zero
+   output row; y is this GPU's partial sum.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64", "route_softmax_topk", "route_grouped", "route",
+    "dispatch", "gather_rows", "expert_ffn", "expert_ffn_rows", "combine",
+    "layer",
+]
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact decode of bf16 bit patterns (uint16) to float64."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def _decode(a: np.ndarray) -> np.ndarray:
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f64(a)
+    return a.astype(np.float64)
+
+
+def route_softmax_topk(logits: np.ndarray, top_k: int, renormalize: bool = False):
+    """Plain top-k gating on router logits [CH15 section 4.1].
+
+    Selection: descending logit, ties to the lower expert index (on the
+    float32 logits; softmax is monotone so the set is the same as on the
+    probabilities). Weights: softmax over all E experts in float64, taken
+    at the selected experts; divided by their sum if ``renormalize``.
+    Returns (topk_ids int32 [T, k], topk_weights float64 [T, k]).
+    """
+    logits = np.asarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    if not 1 <= top_k <= E:
+        raise ValueError("top_k out of range")
+    # A stable sort of the negated values orders by descending value and
+    # keeps lower indices first among equal values.
+    ids = np.argsort(-logits, axis=1, kind="stable")[:, :top_k]
+    l64 = logits.astype(np.float64)
+    ex = np.exp(l64 - l64.max(axis=1, keepdims=True))
+    p = ex / ex.sum(axis=1, keepdims=True)
+    w = np.take_along_axis(p, ids, axis=1)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return ids.astype(np.int32), w
+
+
+def route_grouped(scores: np.ndarray, top_k: int, num_groups: int, topk_groups: int,
+                  renormalize: bool = True):
+    """Group-limited top-k routing [EPLB, section "EPLB 与路由约束"].
+
+    1. The E experts form ``num_groups`` contiguous groups of G = E / num_groups.
+    2. Group score = float32 sum of the group's two highest scores.
+    3. Keep the ``topk_groups`` groups with the highest group score
+       (ties: lower group index).
+    4. Among the experts of the kept groups, pick ``top_k`` by descending
+       score (ties: lower expert index); output slots are in that order.
+    5. Weights are the selected raw scores, divided by their sum when
+       ``renormalize`` (float64).
+    With ``num_groups == 1`` steps 2-3 are skipped (plain top-k on scores).
+    Returns (topk_ids int32 [T, k], topk_weights float64 [T, k]).
+    """
+    s = np.asarray(scores, dtype=np.float32)
+    T, E = s.shape
+    if num_groups < 1 or E % num_groups:
+        raise ValueError("E must be a multiple of num_groups")
+    G = E // num_groups
+    if not 1 <= topk_groups <= num_groups or not 1 <= top_k <= topk_groups * G:
+        raise ValueError("top_k / topk_groups out of range")
+    if num_groups > 1:
+        if G < 2:
+            raise ValueError("groups need at least two experts for a top-2 group score")
+        by_group = np.sort(s.reshape(T, num_groups, G), axis=-1)          # ascending
+        group_score = by_group[..., -1] + by_group[..., -2]                # float32 + float32 -> float32
+        kept_groups = np.argsort(-group_score, axis=1, kind="stable")[:, :topk_groups]
+        kept = np.zeros((T, num_groups), dtype=bool)
+        np.put_along_axis(kept, kept_groups, True, axis=1)
+        expert_kept = np.repeat(kept, G, axis=1)
+    else:
+        expert_kept = np.ones((T, E), dtype=bool)
+    # Sort key: kept experts first, then descending score; lexsort is stable,
+    # so equal keys stay in expert-index order.
+    order = np.lexsort((-s, ~expert_kept), axis=1)
+    ids = order[:, :top_k]
+    w = np.take_along_axis(s, ids, axis=1).astype(np.float64)
+    if renormalize:
+        w = w / w.sum(axis=1, keepdims=True)
+    return ids.astype(np.int32), w
+
+
+def route(scores, top_k, num_groups, topk_groups, score_mode, renormalize):
+    if score_mode == "softmax":
+        if num_groups != 1:
+            raise ValueError("softmax gating is used without groups")
+        return route_softmax_topk(scores, top_k, renormalize)
+    return route_grouped(scores, top_k, num_groups, topk_groups, renormalize)
+
+
+def dispatch(topk_ids: np.ndarray, expert_begin: int, num_local: int):
+    """Counting-sort permutation of assignments to this GPU's experts [CH15 section 3.4, dispatch].
+
+    Assignment a = t * k + j (token t, slot j) is local when its expert lies
+    in [expert_begin, expert_begin + num_local). Local assignments are
+    ordered by (local expert, a).
+    Returns (counts [E_loc], offsets [E_loc + 1], sorted_assign [M],
+    assign_pos [T * k] with -1 for non-local assignments), all int32.
+    """
+    flat = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    local = (flat >= expert_begin) & (flat < expert_begin + num_local)
+    a_local = np.nonzero(local)[0]
+    e_local = flat[a_local] - expert_begin
+    sorted_assign = a_local[np.argsort(e_local, kind="stable")]
+    counts = np.bincount(e_local, minlength=num_local)
+    offsets = np.zeros(num_local + 1, dtype=np.int64)
+    np.cumsum(counts, out=offsets[1:])
+    assign_pos = np.full(flat.shape[0], -1, dtype=np.int64)
+    assign_pos[sorted_assign] = np.arange(sorted_assign.shape[0])
+    return (counts.astype(np.int32), offsets.astype(np.int32),
+            sorted_assign.astype(np.int32), assign_pos.astype(np.int32))
+
+
+def gather_rows(x: np.ndarray, sorted_assign: np.ndarray, top_k: int) -> np.ndarray:
+    """Row i of the permuted activations is the row of token sorted_assign[i] // k (exact copy)."""
+    return np.asarray(x)[np.asarray(sorted_assign, dtype=np.int64) // top_k]
+
+
+def _silu(z: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(x_sorted: np.ndarray, offsets: np.ndarray, w_gate_up: np.ndarray,
+               w_down: np.ndarray) -> np.ndarray:
+    """Grouped SwiGLU expert FFN over the permuted rows [L6 section 2.2; P2 fused gate_up].
+
+    For each local expert e with rows [offsets[e], offsets[e+1]):
+    g = X Wg^T, u = X Wu^T with [Wg; Wu] = w_gate_up[e] ([2I, d]),
+    h = silu(g) * u, o = h Wd^T with Wd = w_down[e] ([d, I]).
+    Experts without rows are skipped. float64 throughout; returns o [M, d].
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    E_loc = offsets.shape[0] - 1
+    I = w_gate_up.shape[1] // 2
+    d = w_gate_up.shape[2]
+    out = np.zeros((int(offsets[-1]), d), dtype=np.float64)
+    for e in range(E_loc):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        out[lo:hi] = _one_expert(_decode(x_sorted[lo:hi]), w_gate_up[e], w_down[e], I)
+    return out
+
+
+def _one_expert(xr: np.ndarray, wgu: np.ndarray, wd: np.ndarray, I: int) -> np.ndarray:
+    wgu = _decode(wgu)
+    g = xr @ wgu[:I].T
+    u = xr @ wgu[I:].T
+    h = _silu(g) * u
+    return h @ _decode(wd).T
+
+
+def expert_ffn_rows(x_rows: np.ndarray, local_expert: np.ndarray, w_gate_up: np.ndarray,
+                    w_down: np.ndarray) -> np.ndarray:
+    """The same FFN for an arbitrary set of rows: row r goes through local expert local_expert[r].
+
+    Used to check sampled rows of large workloads one by one.
+    """
+    local_expert = np.asarray(local_expert, dtype=np.int64)
+    I = w_gate_up.shape[1] // 2
+    out = np.zeros((local_expert.shape[0], w_gate_up.shape[2]), dtype=np.float64)
+    for e in np.unique(local_expert):
+        sel = np.nonzero(local_expert == e)[0]
+        out[sel] = _one_expert(_decode(np.asarray(x_rows)[sel]), w_gate_up[e], w_down[e], I)
+    return out
+
+
+def combine(o_sorted: np.ndarray, assign_pos: np.ndarray, topk_weights: np.ndarray) -> np.ndarray:
+    """Gate-weighted combine back to token order [TRACE hop 4; CH15 section 3.4, combine].
+
+    y[t] = sum over slots j (in order) with a local expert of
+    topk_weights[t, j] * o_sorted[assign_pos[t * k + j]]; tokens with no
+    local slot get zeros. float64.
+    """
+    w = np.asarray(topk_weights, dtype=np.float64)
+    T, k = w.shape
+    o = _decode(o_sorted) if np.asarray(o_sorted).dtype == np.uint16 else np.asarray(o_sorted, np.float64)
+    pos = np.asarray(assign_pos, dtype=np.int64).reshape(T, k)
+    y = np.zeros((T, o.shape[1] if o.ndim == 2 else 0), dtype=np.float64)
+    for j in range(k):
+        has = pos[:, j] >= 0
+        y[has] += w[has, j, None] * o[pos[has, j]]
+    return y
+
+
+def layer(scores, x, w_gate_up, w_down, *, top_k, num_groups, topk_groups, score_mode,
+          renormalize, expert_begin, num_local):
+    """All four steps for one GPU's share; returns a dict of every intermediate."""
+    ids, w = route(scores, top_k, num_groups, topk_groups, score_mode, renormalize)
+    counts, offsets, sorted_assign, assign_pos = dispatch(ids, expert_begin, num_local)
+    out = dict(topk_ids=ids, topk_weights=w, counts=counts, offsets=offsets,
+               sorted_assign=sorted_assign, assign_pos=assign_pos)
+    if x is not None:
+        xs = gather_rows(x, sorted_assign, top_k)
+        o = expert_ffn(xs, offsets, w_gate_up, w_down)
+        out.update(x_sorted=xs, o_sorted=o, y=combine(o, assign_pos, w))
+    return out
