@@ -1,0 +1,232 @@
+"""Benchmark of one GPU's share of the MoE expert layer.
+
+A step is one pass of the whole path over one batch of seeded synthetic input:
+moe_route -> moe_dispatch (count, scan, permute, row gather) -> moe_expert_ffn
+(gate_up GEMM + SiLU*up, down GEMM) -> moe_combine. Inputs are resident in HBM
+before the timed region. Decode weight sets (0.35-0.7 GB) are comparable to
+the 256 MB last-level cache, so the timed steps rotate over several copies of
+the weights and every step reads its weights from HBM.
+
+Prints one JSON line (rank 0, N = 1). Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from expert_routing_grouped_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+F32_PEAK_TFLOPS = 157.3      # MI355X fp32 vector, published
+METRIC = "MoE layer tokens/s + grouped-GEMM %HBM-BW (decode) / %MFMA peak (prefill)"
+HEADLINE = "decode_ep"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=HEADLINE, choices=sorted(W.WORKLOADS))
+    p.add_argument("--all", action="store_true", help="also time every other workload")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copies", type=int, default=0,
+                   help="weight copies rotated over the timed steps (0 = enough to exceed the cache)")
+    return p.parse_args()
+
+
+def ffn_accounting(wl, counts):
+    """Algorithmic FLOPs and HBM bytes of moe_expert_ffn for the measured routing."""
+    counts = np.asarray(counts, dtype=np.int64)
+    M = int(counts.sum())
+    hit = int((counts > 0).sum())
+    es = 2 if wl.dtype == "bf16" else 4
+    d, I = wl.hidden, wl.inter
+    flops = 6.0 * M * I * d
+    weight_bytes = hit * 3.0 * I * d * es
+    act_bytes = 2.0 * M * d * es            # permuted rows in, expert outputs out
+    return dict(M=M, hit=hit, flops=flops, bytes=weight_bytes + act_bytes,
+                weight_bytes=weight_bytes, act_bytes=act_bytes)
+
+
+def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host):
+    dev = "cuda:0"
+    t0 = time.time()
+    inp = W.generate(wl)
+    gen_s = time.time() - t0
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    mode = moe.MOE_SCORE_SOFTMAX if wl.score_mode == "softmax" else moe.MOE_SCORE_RAW
+    layer = moe.MoELayer(num_tokens=wl.T, num_experts=wl.E, top_k=wl.top_k,
+                         num_groups=wl.num_groups, topk_groups=wl.topk_groups, score_mode=mode,
+                         renormalize=wl.renormalize, expert_begin=wl.expert_begin,
+                         num_local_experts=wl.num_local, hidden=wl.hidden, inter=wl.inter,
+                         dtype=dt, device=dev)
+    scores = to_device(inp.scores, dev)
+    x = to_device(inp.x, dev) if wl.has_ffn else None
+    weights = []
+    if wl.has_ffn:
+        wbytes = (inp.w_gate_up.nbytes + inp.w_down.nbytes)
+        n = copies or max(1, min(8, int(np.ceil(768e6 / wbytes)) + 1))
+        for _ in range(n):
+            weights.append((to_device(inp.w_gate_up, dev), to_device(inp.w_down, dev)))
+    else:
+        weights.append((None, None))
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        wgu, wd = weights[i % len(weights)]
+        if ev is not None:
+            ev[0].record(stream)
+        layer.route(scores)
+        if ev is not None:
+            ev[1].record(stream)
+        layer.dispatch(x)
+        if ev is not None:
+            ev[2].record(stream)
+        if x is not None:
+            layer.ffn(wgu, wd)
+            if ev is not None:
+                ev[3].record(stream)
+            layer.combine()
+        if ev is not None:
+            ev[4].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # whole-step timing: no events inside
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        step(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = start.elapsed_time(end) / steps
+    # per-call timing on the same stream (separate pass, events between the calls)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    parts = np.zeros(4)
+    for ev in evs:
+        parts += [ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]),
+                  ev[2].elapsed_time(ev[3]) if x is not None else 0.0,
+                  ev[3].elapsed_time(ev[4]) if x is not None else 0.0]
+    parts_us = parts / steps * 1e3
+    counts = to_host(layer.buf["counts"])
+    res = dict(workload=wl.name, T=wl.T, ms_per_step=ms_per_step, wall_ms_per_step=wall / steps * 1e3,
+               tokens_per_s=wl.T / (ms_per_step * 1e-3), gen_s=gen_s, weight_copies=len(weights),
+               breakdown_us=dict(route=parts_us[0], dispatch=parts_us[1], ffn=parts_us[2],
+                                 combine=parts_us[3]))
+    if wl.has_ffn:
+        acc = ffn_accounting(wl, counts)
+        t_ffn = parts_us[2] * 1e-6
+        res.update(M=acc["M"], hit_experts=acc["hit"], ffn_gflop=acc["flops"] / 1e9,
+                   ffn_bytes_mb=acc["bytes"] / 1e6,
+                   ffn_tflops=acc["flops"] / t_ffn / 1e12, ffn_gbs=acc["bytes"] / t_ffn / 1e9,
+                   layer_tflops=acc["flops"] / (ms_per_step * 1e-3) / 1e12)
+        ai = acc["flops"] / acc["bytes"]
+        res["ffn_bound"] = "mfma" if ai > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+    else:
+        M = int(counts.sum())
+        route_bytes = wl.T * wl.E * 4 + wl.T * wl.top_k * 8
+        res.update(M=M, route_gbs=route_bytes / (parts_us[0] * 1e-6) / 1e9)
+    res["_inputs"] = inp
+    return res
+
+
+def cpu_baseline(inp, wl):
+    """The oracle as it stands, on the host cores, over the whole headline workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = 1
+    t0 = time.perf_counter()
+    oracle.layer(inp.scores, inp.x, inp.w_gate_up, inp.w_down, top_k=wl.top_k,
+                 num_groups=wl.num_groups, topk_groups=wl.topk_groups, score_mode=wl.score_mode,
+                 renormalize=wl.renormalize, expert_begin=wl.expert_begin, num_local=wl.num_local)
+    t = time.perf_counter() - t0
+    return {"value": wl.T / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"the whole {wl.name} layer ({wl.T} tokens): numpy float64 oracle, "
+                      f"{t:.2f} s", "seconds": t}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU's share of the layer; run it with --gpus 1 "
+              "(no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from expert_routing_grouped_amd import moe
+    from expert_routing_grouped_amd.tensors import to_device, to_host
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    moe.lib()
+
+    wl = W.WORKLOADS[args.workload]
+    print(f"bench: workload {wl.name}, steps {args.steps}, warmup {args.warmup}", file=sys.stderr,
+          flush=True)
+    head = run_workload(wl, args.steps, args.warmup, args.copies, torch, moe, to_device, to_host)
+    inp = head.pop("_inputs")
+    out = {
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": wl.T, "experts": wl.E, "top_k": wl.top_k,
+                   "groups": f"{wl.num_groups} keep {wl.topk_groups}", "hidden": wl.hidden,
+                   "inter": wl.inter, "local_experts": f"[{wl.expert_begin}, {wl.expert_begin + wl.num_local})",
+                   "parallelism": "one GPU's expert share"},
+    }
+    if wl.has_ffn:
+        bound = head["ffn_bound"]
+        if bound == "hbm":
+            ach, peak, unit = head["ffn_gbs"], HBM_PEAK_GBS, "GB/s"
+        else:
+            ach, peak, unit = head["ffn_tflops"], BF16_PEAK_TFLOPS, "TFLOP/s"
+        out["roofline"] = {"bound": bound, "achieved": ach, "peak": peak, "unit": unit,
+                           "frac": ach / peak, "traffic": None,
+                           "kernel": "moe_expert_ffn (plan, gate_up GEMM + SiLU*up, down GEMM)",
+                           "us_per_launch": head["breakdown_us"]["ffn"],
+                           "algorithmic_bytes": head["ffn_bytes_mb"] * 1e6,
+                           "algorithmic_flops": head["ffn_gflop"] * 1e9}
+    out["detail"] = {k: v for k, v in head.items() if k not in ("tokens_per_s",)}
+    print(f"bench: {wl.name} {head['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline and wl.has_ffn:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, wl)
+    del inp
+    if args.all:
+        others = {}
+        for name in W.WORKLOADS:
+            if name == wl.name:
+                continue
+            print(f"bench: workload {name}", file=sys.stderr, flush=True)
+            r = run_workload(W.WORKLOADS[name], max(5, args.steps // 2), max(2, args.warmup // 2),
+                             args.copies, torch, moe, to_device, to_host)
+            r.pop("_inputs")
+            others[name] = r
+            torch.cuda.empty_cache()
+        out["workloads"] = others
+    print(json.dumps(out, default=float))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,143 @@
+// Public C entry points (include/moe.h): host-side argument validation, then
+// the kernel launchers. Nothing is enqueued when validation fails, and no C++
+// exception crosses the ABI.
+#include "../../include/moe.h"
+
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+moe_status_t from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return kAbiVersion; }
+
+const char* moe_status_string(moe_status_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+moe_status_t moe_route(const float* scores, int32_t num_tokens, int32_t num_experts,
+                       int32_t top_k, int32_t num_groups, int32_t topk_groups,
+                       int32_t score_mode, int32_t renormalize, int32_t* topk_ids,
+                       float* topk_weights, hipStream_t stream) {
+  if (num_tokens < 0 || num_experts < 1 || top_k < 1 || num_groups < 1 || topk_groups < 1)
+    return MOE_ERR_INVALID;
+  if (score_mode != MOE_SCORE_SOFTMAX && score_mode != MOE_SCORE_RAW) return MOE_ERR_INVALID;
+  if (num_experts % num_groups != 0 || topk_groups > num_groups) return MOE_ERR_INVALID;
+  const int G = num_experts / num_groups;
+  if (num_groups > 1 && G < 2) return MOE_ERR_INVALID;
+  if ((int64_t)top_k > (int64_t)topk_groups * G) return MOE_ERR_INVALID;
+  if (score_mode == MOE_SCORE_SOFTMAX && num_groups != 1) return MOE_ERR_INVALID;
+  if (num_experts > 1024 || top_k > 64 || num_groups > 64) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)num_tokens * num_experts >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MOE_OK;
+  if (!scores || !topk_ids || !topk_weights) return MOE_ERR_INVALID;
+  moe::RouteArgs a{scores,      num_tokens,  num_experts, top_k,   num_groups, topk_groups,
+                   score_mode == MOE_SCORE_SOFTMAX ? 1 : 0, renormalize ? 1 : 0, topk_ids,
+                   topk_weights};
+  return from_hip(moe::launch_route(a, stream));
+}
+
+moe_status_t moe_dispatch(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
+                          int32_t expert_begin, int32_t num_local_experts, const void* x,
+                          int32_t hidden, int32_t dtype, int32_t* expert_counts,
+                          int32_t* expert_offsets, int32_t* sorted_assign, int32_t* assign_pos,
+                          void* x_sorted, hipStream_t stream) {
+  if (num_tokens < 0 || top_k < 1 || expert_begin < 0 || num_local_experts < 1)
+    return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (num_local_experts > moe::kDispatchMaxLocal) return MOE_ERR_UNSUPPORTED;
+  const int64_t n = (int64_t)num_tokens * top_k;
+  if (n >= ((int64_t)1 << 31) - 65536) return MOE_ERR_UNSUPPORTED;
+  if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID;
+  if (n > 0 && (!topk_ids || !sorted_assign || !assign_pos)) return MOE_ERR_INVALID;
+  if ((x == nullptr) != (x_sorted == nullptr)) return MOE_ERR_INVALID;
+  int row_bytes = 0;
+  if (x) {
+    if (hidden < 8 || hidden % 8 != 0) return MOE_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(x_sorted)) return MOE_ERR_INVALID;
+    const int64_t rb = (int64_t)hidden * (dtype == MOE_BF16 ? 2 : 4);
+    if (rb > (1 << 30)) return MOE_ERR_UNSUPPORTED;
+    row_bytes = (int)rb;
+  }
+  moe::DispatchArgs a{topk_ids, (int)n, top_k, expert_begin, num_local_experts, expert_counts,
+                      expert_offsets, sorted_assign, assign_pos, x, x_sorted, row_bytes};
+  return from_hip(moe::launch_dispatch(a, stream));
+}
+
+static moe_status_t check_ffn_sizes(int32_t num_local_experts, int32_t hidden, int32_t inter,
+                                    int32_t row_capacity, int32_t dtype) {
+  if (num_local_experts < 1 || hidden < 1 || inter < 1 || row_capacity < 0) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (num_local_experts > 1024) return MOE_ERR_UNSUPPORTED;
+  if (dtype == MOE_BF16) {
+    if (hidden % 256 != 0 || inter % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  } else {
+    if (hidden % 4 != 0 || inter % 4 != 0) return MOE_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)2 * inter * hidden >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)row_capacity * (hidden > inter ? hidden : inter) >= ((int64_t)1 << 40))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_expert_ffn_workspace_size(int32_t num_local_experts, int32_t hidden, int32_t inter,
+                                     int32_t row_capacity, int32_t dtype) {
+  if (check_ffn_sizes(num_local_experts, hidden, inter, row_capacity, dtype) != MOE_OK) return 0;
+  return moe::ffn_workspace_size(num_local_experts, hidden, inter, row_capacity,
+                                 dtype == MOE_BF16);
+}
+
+moe_status_t moe_expert_ffn(const void* x_sorted, const int32_t* expert_offsets,
+                            const void* w_gate_up, const void* w_down,
+                            int32_t num_local_experts, int32_t hidden, int32_t inter,
+                            int32_t row_capacity, int32_t dtype, void* o_sorted, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  const moe_status_t st = check_ffn_sizes(num_local_experts, hidden, inter, row_capacity, dtype);
+  if (st != MOE_OK) return st;
+  if (!expert_offsets || !w_gate_up || !w_down) return MOE_ERR_INVALID;
+  if (row_capacity > 0 && (!x_sorted || !o_sorted)) return MOE_ERR_INVALID;
+  if (!aligned16(x_sorted) || !aligned16(o_sorted) || !aligned16(w_gate_up) ||
+      !aligned16(w_down))
+    return MOE_ERR_INVALID;
+  const size_t need = moe::ffn_workspace_size(num_local_experts, hidden, inter, row_capacity,
+                                              dtype == MOE_BF16);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
+  moe::FfnArgs a{x_sorted, expert_offsets, w_gate_up, w_down, num_local_experts, hidden, inter,
+                 row_capacity, dtype == MOE_BF16, o_sorted, workspace};
+  return from_hip(moe::launch_ffn(a, stream));
+}
+
+moe_status_t moe_combine(const void* o_sorted, const int32_t* assign_pos,
+                         const float* topk_weights, int32_t num_tokens, int32_t top_k,
+                         int32_t hidden, int32_t dtype, int32_t out_dtype, void* y,
+                         hipStream_t stream) {
+  if (num_tokens < 0 || top_k < 1 || hidden < 8 || hidden % 8 != 0) return MOE_ERR_INVALID;
+  if ((dtype != MOE_F32 && dtype != MOE_BF16) || (out_dtype != MOE_F32 && out_dtype != MOE_BF16))
+    return MOE_ERR_INVALID;
+  if (top_k > 64) return MOE_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MOE_OK;
+  if (!o_sorted || !assign_pos || !topk_weights || !y) return MOE_ERR_INVALID;
+  if (!aligned16(o_sorted) || !aligned16(y)) return MOE_ERR_INVALID;
+  moe::CombineArgs a{o_sorted, assign_pos, topk_weights, num_tokens, top_k, hidden,
+                     dtype == MOE_BF16, out_dtype == MOE_BF16, y};
+  return from_hip(moe::launch_combine(a, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Internal launchers of the HIP kernels; the public entry points in api.hip
+// validate arguments and then call these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouteArgs {
+  const float* scores;
+  int T, E, k, num_groups, topk_groups, softmax, renormalize;
+  int* ids;
+  float* weights;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+struct DispatchArgs {
+  const int* ids;
+  int n;  // T * k assignments
+  int k, expert_begin, num_local;
+  int* counts;
+  int* offsets;
+  int* sorted_assign;
+  int* assign_pos;
+  const void* x;
+  void* x_sorted;
+  int row_bytes;  // hidden * element size; 0 = no gather
+};
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+constexpr int kDispatchMaxLocal = 1000;  // per-(wave, expert) counters fit in 64 KiB of LDS
+
+struct FfnArgs {
+  const void* x_sorted;
+  const int* offsets;
+  const void* w_gate_up;
+  const void* w_down;
+  int num_local, hidden, inter, capacity;
+  bool bf16;
+  void* o_sorted;
+  void* workspace;
+};
+size_t ffn_workspace_size(int num_local, int hidden, int inter, int capacity, bool bf16);
+hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  const void* o_sorted;
+  const int* assign_pos;
+  const float* weights;
+  int T, k, hidden;
+  bool o_bf16, y_bf16;
+  void* y;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,254 @@
+"""Python binding of libmoe_mi355x.so (the C ABI declared in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. torch supplies device memory and the current stream; the functions
+allocate missing outputs with torch and pass raw device pointers.
+
+There is no fallback: if the library is not built, or a call returns an
+error status, a MoeError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_RAW = 0, 1
+
+# Every symbol include/moe.h declares: (name, restype, argtypes).
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIGNATURES = {
+    "moe_abi_version": (ctypes.c_int32, []),
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_route": (ctypes.c_int, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_dispatch": (ctypes.c_int, [_P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "moe_expert_ffn": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P,
+                                      ctypes.c_size_t, _P]),
+    "moe_combine": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+}
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (once). Raises MoeError if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m expert_routing_grouped_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().moe_status_string(code).decode()
+
+
+def _check(code: int, name: str) -> None:
+    if code != 0:
+        raise MoeError(f"{name} failed: {status_string(code)} (status {code})")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise MoeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise MoeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise MoeError(f"{name} must be contiguous")
+    return t
+
+
+def _code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return MOE_BF16
+    if dtype == torch.float32:
+        return MOE_F32
+    raise MoeError(f"unsupported dtype {dtype}")
+
+
+def moe_route(scores, top_k, num_groups=1, topk_groups=1, score_mode=MOE_SCORE_RAW,
+              renormalize=True, topk_ids=None, topk_weights=None, stream=None):
+    """topk_ids [T, k] int32, topk_weights [T, k] float32 (see moe_route in include/moe.h)."""
+    _dev(scores, torch.float32, "scores")
+    T, E = scores.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=scores.device)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, top_k), dtype=torch.float32, device=scores.device)
+    _dev(topk_ids, torch.int32, "topk_ids")
+    _dev(topk_weights, torch.float32, "topk_weights")
+    _check(lib().moe_route(_ptr(scores), T, E, top_k, num_groups, topk_groups, score_mode,
+                           int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_weights),
+                           _stream(stream)), "moe_route")
+    return topk_ids, topk_weights
+
+
+def moe_dispatch(topk_ids, expert_begin, num_local_experts, x=None, out=None, stream=None):
+    """Counting-sort dispatch. Returns dict(counts, offsets, sorted_assign, assign_pos, x_sorted)."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    o = dict(out or {})
+    n = T * k
+    o.setdefault("counts", torch.empty(num_local_experts, dtype=torch.int32, device=dev))
+    o.setdefault("offsets", torch.empty(num_local_experts + 1, dtype=torch.int32, device=dev))
+    o.setdefault("sorted_assign", torch.empty(max(n, 1), dtype=torch.int32, device=dev))
+    o.setdefault("assign_pos", torch.empty(max(n, 1), dtype=torch.int32, device=dev))
+    hidden, dtype = 0, MOE_BF16
+    if x is not None:
+        dtype = _code(x.dtype)
+        _dev(x, x.dtype, "x")
+        hidden = x.shape[1]
+        o.setdefault("x_sorted", torch.empty((max(n, 1), hidden), dtype=x.dtype, device=dev))
+        _dev(o["x_sorted"], x.dtype, "x_sorted")
+    else:
+        o["x_sorted"] = None
+    for name in ("counts", "offsets", "sorted_assign", "assign_pos"):
+        _dev(o[name], torch.int32, name)
+    _check(lib().moe_dispatch(_ptr(topk_ids), T, k, expert_begin, num_local_experts, _ptr(x),
+                              hidden, dtype, _ptr(o["counts"]), _ptr(o["offsets"]),
+                              _ptr(o["sorted_assign"]), _ptr(o["assign_pos"]),
+                              _ptr(o["x_sorted"]), _stream(stream)), "moe_dispatch")
+    return o
+
+
+def ffn_workspace_size(num_local_experts, hidden, inter, row_capacity, dtype) -> int:
+    code = _code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(lib().moe_expert_ffn_workspace_size(num_local_experts, hidden, inter,
+                                                   row_capacity, code))
+
+
+def moe_expert_ffn(x_sorted, expert_offsets, w_gate_up, w_down, o_sorted=None, workspace=None,
+                   stream=None):
+    """Grouped SwiGLU FFN over the permuted rows; returns o_sorted [row_capacity, d]."""
+    dt = x_sorted.dtype
+    _dev(x_sorted, dt, "x_sorted")
+    _dev(expert_offsets, torch.int32, "expert_offsets")
+    _dev(w_gate_up, dt, "w_gate_up")
+    _dev(w_down, dt, "w_down")
+    cap, hidden = x_sorted.shape
+    E_loc, two_i, d2 = w_gate_up.shape
+    inter = two_i // 2
+    if d2 != hidden or tuple(w_down.shape) != (E_loc, hidden, inter):
+        raise MoeError("weight shapes do not match x_sorted")
+    if o_sorted is None:
+        o_sorted = torch.empty((cap, hidden), dtype=dt, device=x_sorted.device)
+    _dev(o_sorted, dt, "o_sorted")
+    need = ffn_workspace_size(E_loc, hidden, inter, cap, dt)
+    if need == 0:
+        raise MoeError("moe_expert_ffn: unsupported sizes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x_sorted.device)
+    _check(lib().moe_expert_ffn(_ptr(x_sorted), _ptr(expert_offsets), _ptr(w_gate_up),
+                                _ptr(w_down), E_loc, hidden, inter, cap, _code(dt),
+                                _ptr(o_sorted), _ptr(workspace), workspace.numel(),
+                                _stream(stream)), "moe_expert_ffn")
+    return o_sorted
+
+
+def moe_combine(o_sorted, assign_pos, topk_weights, out_dtype=None, y=None, stream=None):
+    """y [T, d] = router-weighted sum of each token's local expert outputs."""
+    _dev(o_sorted, o_sorted.dtype, "o_sorted")
+    _dev(assign_pos, torch.int32, "assign_pos")
+    _dev(topk_weights, torch.float32, "topk_weights")
+    T, k = topk_weights.shape
+    hidden = o_sorted.shape[1]
+    out_dtype = out_dtype or o_sorted.dtype
+    if y is None:
+        y = torch.empty((T, hidden), dtype=out_dtype, device=o_sorted.device)
+    _dev(y, out_dtype, "y")
+    _check(lib().moe_combine(_ptr(o_sorted), _ptr(assign_pos), _ptr(topk_weights), T, k, hidden,
+                             _code(o_sorted.dtype), _code(out_dtype), _ptr(y), _stream(stream)),
+           "moe_combine")
+    return y
+
+
+class MoELayer:
+    """One GPU's share of the MoE layer with its buffers allocated once.
+
+    forward() enqueues the four calls on the current stream and returns y;
+    intermediates stay in self.buf.
+    """
+
+    def __init__(self, *, num_tokens, num_experts, top_k, num_groups, topk_groups, score_mode,
+                 renormalize, expert_begin, num_local_experts, hidden, inter, dtype, device):
+        self.T, self.E, self.k = num_tokens, num_experts, top_k
+        self.num_groups, self.topk_groups = num_groups, topk_groups
+        self.score_mode, self.renormalize = score_mode, renormalize
+        self.expert_begin, self.num_local = expert_begin, num_local_experts
+        self.hidden, self.inter, self.dtype = hidden, inter, dtype
+        cap = num_tokens * top_k
+        dev = torch.device(device)
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.buf = dict(
+            topk_ids=torch.empty((num_tokens, top_k), **i32),
+            topk_weights=torch.empty((num_tokens, top_k), dtype=torch.float32, device=dev),
+            counts=torch.empty(num_local_experts, **i32),
+            offsets=torch.empty(num_local_experts + 1, **i32),
+            sorted_assign=torch.empty(max(cap, 1), **i32),
+            assign_pos=torch.empty(max(cap, 1), **i32),
+        )
+        if hidden:
+            self.buf["x_sorted"] = torch.empty((max(cap, 1), hidden), dtype=dtype, device=dev)
+            self.buf["o_sorted"] = torch.empty((max(cap, 1), hidden), dtype=dtype, device=dev)
+            self.buf["y"] = torch.empty((num_tokens, hidden), dtype=dtype, device=dev)
+            need = ffn_workspace_size(num_local_experts, hidden, inter, max(cap, 1), dtype)
+            if need == 0:
+                raise MoeError("unsupported FFN sizes")
+            self.buf["workspace"] = torch.empty(need, dtype=torch.uint8, device=dev)
+
+    def route(self, scores, stream=None):
+        return moe_route(scores, self.k, self.num_groups, self.topk_groups, self.score_mode,
+                         self.renormalize, self.buf["topk_ids"], self.buf["topk_weights"], stream)
+
+    def dispatch(self, x=None, stream=None):
+        b = self.buf
+        out = {n: b[n] for n in ("counts", "offsets", "sorted_assign", "assign_pos")}
+        if x is not None:
+            out["x_sorted"] = b["x_sorted"]
+        return moe_dispatch(b["topk_ids"], self.expert_begin, self.num_local, x, out, stream)
+
+    def ffn(self, w_gate_up, w_down, stream=None):
+        b = self.buf
+        return moe_expert_ffn(b["x_sorted"], b["offsets"], w_gate_up, w_down, b["o_sorted"],
+                              b["workspace"], stream)
+
+    def combine(self, stream=None):
+        b = self.buf
+        return moe_combine(b["o_sorted"], b["assign_pos"], b["topk_weights"], self.dtype, b["y"],
+                           stream)
+
+    def forward(self, scores, x=None, w_gate_up=None, w_down=None, stream=None):
+        self.route(scores, stream)
+        self.dispatch(x, stream)
+        if x is None:
+            return None
+        self.ffn(w_gate_up, w_down, stream)
+        return self.combine(stream)

@@ -1,0 +1,181 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE expert layer: one GPU's share of
+ * a DeepSeek-V3-style mixture-of-experts layer, in four calls:
+ *
+ *   moe_route       group-limited top-k routing of each token
+ *   moe_dispatch    counting-sort permutation of token rows to local experts
+ *   moe_expert_ffn  grouped SwiGLU expert FFN (fused gate_up GEMM, SiLU*up, down GEMM)
+ *   moe_combine     router-weighted sum of the expert outputs, back in token order
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every array argument is a DEVICE pointer owned by the caller; the library
+ *   keeps no pointer after a call returns and allocates no memory.
+ * - Calls are asynchronous on `stream` (0 = the default stream). They do not
+ *   synchronise with the host, so a sequence of calls can be captured in a
+ *   HIP graph.
+ * - Every argument is validated on the host before anything is enqueued; a
+ *   call that returns an error status has enqueued nothing, except
+ *   MOE_ERR_LAUNCH, which reports a failed kernel launch (hipGetLastError).
+ * - Layouts are row-major and dense. bf16 buffers hold bf16 bit patterns.
+ *   Activations and weights are 16-byte aligned.
+ * - Preconditions not checked on the device: scores are finite; with
+ *   renormalisation the selected scores have a positive sum; outputs do not
+ *   alias inputs; topk_ids hold values in [0, num_experts).
+ *
+ * Sources (web pages; sections as printed on them):
+ * - "大规模 EP 部署：分层 EPLB、DP 注意力的负载与双 batch 重叠" (anrans.github.io,
+ *   ai-infra-handbooks serving/moe/ep-deploy), section "EPLB 与路由约束":
+ *   group-limited routing and its seeded simulation.
+ * - "第十五章：多节点大模型推理——并行部署、解码优化与 MoE 路由"
+ *   (se7en.mintlify.app ch15), sections 3.4 and 4.1: gating, dispatch, combine.
+ * - "追踪一个 Token 在 MoE 推理中穿越 TP/CP/SP/EP/DP/PP 的路径" (attain.fans),
+ *   hop 4: y = p5 E5(x) + p27 E27(x).
+ * - "Lecture 6 · 并行" (semidirectx.com cs349d lecture06), section 2.2: the
+ *   gated MLP with W_gate, W_up, W_down.
+ * - "推理 INFRA 方法论（2）：分布式推理：TP、DP、EP、CP 与 PP" (johneyzheng.top):
+ *   gate and up fused into one GEMM with N = 2I; experts that no token hits
+ *   are skipped.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,      /* an argument is out of range or a required pointer is NULL */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid, but a shape this library does not implement */
+  MOE_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than the *_workspace_size query */
+  MOE_ERR_LAUNCH = 4        /* a kernel launch failed */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+typedef enum {
+  MOE_SCORE_SOFTMAX = 0,  /* scores are router logits: select on them, weight = softmax over all experts */
+  MOE_SCORE_RAW = 1       /* scores are used as given: weight = the selected score */
+} moe_score_mode_t;
+
+/* Version of this ABI (incremented on any incompatible change). */
+int32_t moe_abi_version(void);
+
+/* Static, NUL-terminated description of a status; host only, never NULL. */
+const char* moe_status_string(moe_status_t status);
+
+/*
+ * moe_route -- top-k gating per token (ch15 section 4.1), group-limited as on
+ * the EPLB page (section "EPLB 与路由约束").
+ *
+ * scores        [T, E] float32. RAW: used as given. SOFTMAX: router logits.
+ * topk_ids      [T, k] int32 out: selected experts, in selection order.
+ * topk_weights  [T, k] float32 out.
+ *
+ * Per token:
+ * 1. With num_groups > 1 the E experts form num_groups contiguous groups of
+ *    G = E / num_groups. A group's score is the float32 sum of its two highest
+ *    scores (a duplicated maximum counts twice). The topk_groups groups with
+ *    the highest group score are kept (ties: lower group index).
+ * 2. Among the experts of the kept groups (all experts if num_groups == 1),
+ *    the top_k highest scores are selected, in descending order; ties go to
+ *    the lower expert index, and -0 ties with +0.
+ * 3. RAW: weight = selected score. SOFTMAX: weight = softmax over all E
+ *    logits, at the selected expert. With renormalize != 0 the k weights are
+ *    divided by their sum.
+ * Limits: 1 <= E <= 1024; 1 <= top_k <= min(64, topk_groups * G);
+ * num_groups divides E; G >= 2 when num_groups > 1; SOFTMAX needs
+ * num_groups == 1. T = 0 is a valid no-op.
+ */
+moe_status_t moe_route(const float* scores, int32_t num_tokens, int32_t num_experts,
+                       int32_t top_k, int32_t num_groups, int32_t topk_groups,
+                       int32_t score_mode, int32_t renormalize,
+                       int32_t* topk_ids, float* topk_weights, hipStream_t stream);
+
+/*
+ * moe_dispatch -- the dispatch step of ch15 section 3.4 on one GPU: a stable
+ * counting sort of the assignments a = t * k + j (token t, slot j) whose
+ * expert lies in [expert_begin, expert_begin + num_local_experts), followed by
+ * a gather of the token rows into expert order.
+ *
+ * topk_ids        [T, k] int32 (from moe_route).
+ * expert_counts   [E_loc] int32 out: rows per local expert.
+ * expert_offsets  [E_loc + 1] int32 out: exclusive prefix sum; offsets[E_loc] = M.
+ * sorted_assign   [T * k] int32 out: entries [0, M) hold the local assignments
+ *                 ordered by (local expert, a); entries >= M are not written.
+ * assign_pos      [T * k] int32 out: position of assignment a in sorted_assign,
+ *                 or -1 when its expert is not local.
+ * x               [T, hidden] (dtype) or NULL: token rows to gather.
+ * x_sorted        [T * k, hidden] (dtype) out, or NULL (only with x == NULL):
+ *                 row i = x[sorted_assign[i] / k] for i < M (exact copy).
+ * Limits: 1 <= num_local_experts <= 1000; T * k < 2^31; hidden % 8 == 0
+ * when x is given. T = 0 writes zero counts and offsets.
+ */
+moe_status_t moe_dispatch(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
+                          int32_t expert_begin, int32_t num_local_experts,
+                          const void* x, int32_t hidden, int32_t dtype,
+                          int32_t* expert_counts, int32_t* expert_offsets,
+                          int32_t* sorted_assign, int32_t* assign_pos, void* x_sorted,
+                          hipStream_t stream);
+
+/*
+ * Bytes of device workspace moe_expert_ffn needs for these sizes; 0 when the
+ * sizes are invalid.
+ */
+size_t moe_expert_ffn_workspace_size(int32_t num_local_experts, int32_t hidden, int32_t inter,
+                                     int32_t row_capacity, int32_t dtype);
+
+/*
+ * moe_expert_ffn -- the gated MLP of lecture 6 section 2.2 per local expert,
+ * with gate and up fused into one GEMM of N = 2I (the INFRA page), over the
+ * permuted rows: for each local expert e with rows [off[e], off[e+1]):
+ *   [g | u] = X_e * W_gate_up[e]^T,  h = silu(g) * u,  o = h * W_down[e]^T,
+ * silu(z) = z / (1 + exp(-z)). Experts without rows read no weights.
+ *
+ * x_sorted        [row_capacity, hidden] (dtype): permuted rows (moe_dispatch).
+ * expert_offsets  [E_loc + 1] int32 (moe_dispatch); read on the device only.
+ * w_gate_up       [E_loc, 2 * inter, hidden] (dtype): rows [0, I) gate, [I, 2I) up.
+ * w_down          [E_loc, hidden, inter] (dtype).
+ * o_sorted        [row_capacity, hidden] (dtype) out: rows [0, M) written.
+ * workspace       device buffer of at least moe_expert_ffn_workspace_size bytes;
+ *                 holds h and the tile schedule; contents need not be initialised.
+ * bf16: float32 accumulation; h and o are rounded to bf16.
+ * Limits (bf16): hidden % 256 == 0, inter % 64 == 0. f32: hidden % 4 == 0,
+ * inter % 4 == 0. M = offsets[E_loc] must not exceed row_capacity (rows past
+ * row_capacity are ignored on the device).
+ */
+moe_status_t moe_expert_ffn(const void* x_sorted, const int32_t* expert_offsets,
+                            const void* w_gate_up, const void* w_down,
+                            int32_t num_local_experts, int32_t hidden, int32_t inter,
+                            int32_t row_capacity, int32_t dtype, void* o_sorted,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_combine -- the combine step (ch15 section 3.4; attain.fans hop 4):
+ *   y[t] = sum over slots j = 0..k-1 with assign_pos[t*k+j] >= 0 of
+ *          topk_weights[t, j] * o_sorted[assign_pos[t*k+j]],
+ * summed in slot order in float32. Tokens with no local slot get a zero row
+ * (y is this GPU's partial sum of the layer output).
+ *
+ * o_sorted      [>= M, hidden] (dtype).
+ * assign_pos    [T * k] int32 (moe_dispatch).
+ * topk_weights  [T, k] float32 (moe_route).
+ * y             [T, hidden] (out_dtype) out.
+ * Limits: hidden % 8 == 0; 1 <= top_k <= 64.
+ */
+moe_status_t moe_combine(const void* o_sorted, const int32_t* assign_pos,
+                         const float* topk_weights, int32_t num_tokens, int32_t top_k,
+                         int32_t hidden, int32_t dtype, int32_t out_dtype, void* y,
+                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every declared symbol and validates arguments on the host.
+
+No test here touches a GPU: every call below fails validation before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from expert_routing_grouped_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH),
+                                reason="library not built (python -m expert_routing_grouped_amd.build)")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert sorted(moe._SIGNATURES) == _declared()
+
+
+def test_version_and_status_strings():
+    lib = moe.lib()
+    assert lib.moe_abi_version() == 1
+    assert moe.status_string(0) == "ok"
+    assert moe.status_string(1) == "invalid argument"
+    assert moe.status_string(3).startswith("workspace")
+    assert moe.status_string(99) == "unknown status"
+
+
+def test_route_validation():
+    l = moe.lib()
+    R = moe.MOE_SCORE_RAW
+    assert l.moe_route(None, 4, 256, 0, 8, 4, R, 1, None, None, None) == 1       # k = 0
+    assert l.moe_route(None, 4, 250, 8, 8, 4, R, 1, None, None, None) == 1       # 8 does not divide 250
+    assert l.moe_route(None, 4, 16, 9, 4, 2, R, 1, None, None, None) == 1        # 9 > 2 groups * 4
+    assert l.moe_route(None, 4, 16, 2, 4, 5, R, 1, None, None, None) == 1        # 5 > 4 groups
+    assert l.moe_route(None, 4, 16, 2, 4, 2, moe.MOE_SCORE_SOFTMAX, 0, None, None, None) == 1
+    assert l.moe_route(None, 4, 16, 2, 16, 2, R, 1, None, None, None) == 1       # groups of one
+    assert l.moe_route(None, 4, 2048, 8, 1, 1, R, 1, None, None, None) == 2      # E > 1024
+    assert l.moe_route(None, 4, 256, 8, 8, 4, 7, 1, None, None, None) == 1       # bad score mode
+    assert l.moe_route(None, 4, 256, 8, 8, 4, R, 1, None, None, None) == 1       # NULL pointers
+    assert l.moe_route(None, 0, 256, 8, 8, 4, R, 1, None, None, None) == 0       # T = 0: no-op
+
+
+def test_dispatch_validation():
+    l = moe.lib()
+    p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    assert l.moe_dispatch(None, 4, 0, 0, 8, None, 0, 1, p, p, p, p, None, None) == 1
+    assert l.moe_dispatch(p, 4, 8, 0, 0, None, 0, 1, p, p, p, p, None, None) == 1
+    assert l.moe_dispatch(p, 4, 8, 0, 2000, None, 0, 1, p, p, p, p, None, None) == 2
+    assert l.moe_dispatch(p, 4, 8, 0, 8, p, 0, 1, p, p, p, p, None, None) == 1      # x without x_sorted
+    assert l.moe_dispatch(p, 4, 8, 0, 8, p, 12, 1, p, p, p, p, p, None) == 1         # hidden % 8
+    assert l.moe_dispatch(p, 4, 8, 0, 8, ctypes.c_void_p(8), 16, 1, p, p, p, p, p, None) == 1  # unaligned
+    assert l.moe_dispatch(p, 4, 8, 0, 8, None, 0, 5, p, p, p, p, None, None) == 1    # bad dtype
+    assert l.moe_dispatch(None, 4, 8, 0, 8, None, 0, 1, p, p, p, p, None, None) == 1 # NULL ids
+
+
+def test_ffn_validation_and_workspace():
+    l = moe.lib()
+    p = ctypes.c_void_p(256)
+    assert l.moe_expert_ffn_workspace_size(8, 7168, 2048, 4096, 1) > 4096 * 2048 * 2
+    assert l.moe_expert_ffn_workspace_size(8, 7000, 2048, 4096, 1) == 0     # hidden % 256
+    assert l.moe_expert_ffn_workspace_size(8, 7168, 100, 4096, 1) == 0      # inter % 64
+    assert l.moe_expert_ffn_workspace_size(0, 7168, 2048, 4096, 1) == 0
+    assert l.moe_expert_ffn(p, p, p, p, 8, 7000, 2048, 64, 1, p, p, 1 << 30, None) == 2
+    assert l.moe_expert_ffn(p, None, p, p, 8, 7168, 2048, 64, 1, p, p, 1 << 30, None) == 1
+    assert l.moe_expert_ffn(p, p, p, p, 8, 7168, 2048, 64, 1, p, p, 16, None) == 3   # workspace small
+    assert l.moe_expert_ffn(p, p, p, p, 8, 7168, 2048, 64, 1, p, None, 1 << 30, None) == 3
+
+
+def test_combine_validation():
+    l = moe.lib()
+    p = ctypes.c_void_p(256)
+    assert l.moe_combine(p, p, p, 4, 0, 7168, 1, 1, p, None) == 1
+    assert l.moe_combine(p, p, p, 4, 8, 7164, 1, 1, p, None) == 1
+    assert l.moe_combine(p, p, p, 4, 100, 7168, 1, 1, p, None) == 2
+    assert l.moe_combine(None, p, p, 4, 8, 7168, 1, 1, p, None) == 1
+    assert l.moe_combine(p, p, p, 0, 8, 7168, 1, 1, p, None) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(moe.MoeError):
+        moe.lib()
