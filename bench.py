@@ -94,7 +94,7 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host):
         if ev is not None:
             ev[2].record(stream)
         if x is not None:
-            layer.ffn(wgu, wd)
+            layer.ffn(wgu, wd, x)
             if ev is not None:
                 ev[3].record(stream)
             layer.combine()

@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -90,6 +90,8 @@ static moe_status_t check_ffn_sizes(int32_t num_local_experts, int32_t hidden, i
     if (hidden % 256 != 0 || inter % 64 != 0) return MOE_ERR_UNSUPPORTED;
   } else {
     if (hidden % 4 != 0 || inter % 4 != 0) return MOE_ERR_UNSUPPORTED;
+    // the float32 kernels index (expert, 16-row tile) along one grid dimension
+    if ((int64_t)num_local_experts * ((row_capacity + 15) / 16) > 65535) return MOE_ERR_UNSUPPORTED;
   }
   if ((int64_t)2 * inter * hidden >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)row_capacity * (hidden > inter ? hidden : inter) >= ((int64_t)1 << 40))
@@ -104,23 +106,24 @@ size_t moe_expert_ffn_workspace_size(int32_t num_local_experts, int32_t hidden, 
                                  dtype == MOE_BF16);
 }
 
-moe_status_t moe_expert_ffn(const void* x_sorted, const int32_t* expert_offsets,
-                            const void* w_gate_up, const void* w_down,
-                            int32_t num_local_experts, int32_t hidden, int32_t inter,
-                            int32_t row_capacity, int32_t dtype, void* o_sorted, void* workspace,
-                            size_t workspace_bytes, hipStream_t stream) {
+moe_status_t moe_expert_ffn(const void* x, const int32_t* row_index, int32_t row_index_div,
+                            const int32_t* expert_offsets, const void* w_gate_up,
+                            const void* w_down, int32_t num_local_experts, int32_t hidden,
+                            int32_t inter, int32_t row_capacity, int32_t dtype, void* o_sorted,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const moe_status_t st = check_ffn_sizes(num_local_experts, hidden, inter, row_capacity, dtype);
   if (st != MOE_OK) return st;
   if (!expert_offsets || !w_gate_up || !w_down) return MOE_ERR_INVALID;
-  if (row_capacity > 0 && (!x_sorted || !o_sorted)) return MOE_ERR_INVALID;
-  if (!aligned16(x_sorted) || !aligned16(o_sorted) || !aligned16(w_gate_up) ||
-      !aligned16(w_down))
+  if (row_index && row_index_div < 1) return MOE_ERR_INVALID;
+  if (row_capacity > 0 && (!x || !o_sorted)) return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(o_sorted) || !aligned16(w_gate_up) || !aligned16(w_down))
     return MOE_ERR_INVALID;
   const size_t need = moe::ffn_workspace_size(num_local_experts, hidden, inter, row_capacity,
                                               dtype == MOE_BF16);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
-  moe::FfnArgs a{x_sorted, expert_offsets, w_gate_up, w_down, num_local_experts, hidden, inter,
-                 row_capacity, dtype == MOE_BF16, o_sorted, workspace};
+  moe::FfnArgs a{x, row_index, row_index ? row_index_div : 1, expert_offsets, w_gate_up, w_down,
+                 num_local_experts, hidden, inter, row_capacity, dtype == MOE_BF16, o_sorted,
+                 workspace};
   return from_hip(moe::launch_ffn(a, stream));
 }
 

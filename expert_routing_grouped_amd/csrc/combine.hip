@@ -42,36 +42,40 @@ __device__ __forceinline__ void store8(void* base, size_t elem, const float (&v)
   }
 }
 
+// Workgroup = 4 wavefronts on one token; wavefront = 512 consecutive
+// elements (8 per lane). The k slot positions and weights are read once per
+// wavefront (lane j holds slot j) and broadcast; the k row loads are
+// independent, so all of them are in flight together.
 template <bool O_BF16, bool Y_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o,
                                                       const int* __restrict__ assign_pos,
                                                       const float* __restrict__ weights, int T,
                                                       int k, int hidden, void* __restrict__ y) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // uniform per wave
-  const int* pos = assign_pos + (size_t)t * k;
-  const float* w = weights + (size_t)t * k;
-  for (int c = lane * 8; c < hidden; c += 64 * 8) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int p = pos[j];
-      if (p < 0) continue;
-      const float wj = w[j];
-      float v[8];
-      load8<O_BF16>(o, (size_t)p * hidden + c, v);
+  const int t = blockIdx.x;
+  const int c0 = (blockIdx.y * 4 + (threadIdx.x >> 6)) * 512;
+  if (c0 >= hidden) return;  // uniform per wave
+  const int c = c0 + lane * 8;
+  const bool active = c < hidden;
+  const int mypos = lane < k ? assign_pos[(size_t)t * k + lane] : -1;
+  const float myw = lane < k ? weights[(size_t)t * k + lane] : 0.0f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int p = __shfl(mypos, j, MOE_WAVE);
+    const float wj = __shfl(myw, j, MOE_WAVE);
+    float v[8];
+    load8<O_BF16>(o, (size_t)(p >= 0 ? p : 0) * hidden + (active ? c : 0), v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += wj * v[i];
-    }
-    store8<Y_BF16>(y, (size_t)t * hidden + c, acc);
+    for (int i = 0; i < 8; ++i) acc[i] += p >= 0 ? wj * v[i] : 0.0f;
   }
+  if (active) store8<Y_BF16>(y, (size_t)t * hidden + c, acc);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const dim3 grid((a.T + 3) / 4), block(256);
+  const dim3 grid(a.T, (a.hidden + 2047) / 2048), block(256);
 #define MOE_COMBINE(OB, YB)                                                                  \
   hipLaunchKernelGGL((combine_kernel<OB, YB>), grid, block, 0, s, a.o_sorted, a.assign_pos, \
                      a.weights, a.T, a.k, a.hidden, a.y)

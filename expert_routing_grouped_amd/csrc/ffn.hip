@@ -1,6 +1,6 @@
 // Grouped SwiGLU expert FFN over the permuted rows.
 //
-// Per local expert e (rows [off[e], off[e+1]) of x_sorted):
+// Per local expert e (rows [off[e], off[e+1]) of the permuted activations):
 //   [g | u] = X_e W_gate_up[e]^T      fused gate_up GEMM, N = 2I
 //   h       = silu(g) * u             fused into the GEMM-1 epilogue
 //   o       = h W_down[e]^T           GEMM-2
@@ -9,17 +9,20 @@
 // N = 2I and the skipping of experts that no token reaches come from the page
 // "推理 INFRA 方法论（2）：分布式推理：TP、DP、EP、CP 与 PP" (johneyzheng.top).
 //
-// Scheduling: a one-workgroup plan kernel turns expert_offsets into a list of
-// row tiles (expert, first row), so the number of rows never returns to the
-// host; GEMM workgroups whose tile index is past the list end exit at once,
-// and experts with no rows have no tiles, so their weights are never read.
+// The permuted activations are either a materialised x_sorted or, fused with
+// the dispatch gather, the token rows x read through sorted_assign
+// (row i = x[sorted_assign[i] / k]).
 //
-// bf16 GEMMs use v_mfma_f32_16x16x32_bf16 (fp32 accumulate) on LDS tiles that
-// are double-buffered through registers. Both operands are K-contiguous
-// (activations [rows, K], weights [N, K]), so A and B fragments are the same
-// kind of 16-byte LDS read. For GEMM-1 a workgroup's weight tile takes BN/2
-// gate rows and the matching BN/2 up rows, arranged so that one lane holds
-// g and u of the same output element; SiLU*up is applied before h is stored.
+// Each GEMM is two persistent kernels that read expert_offsets on the device
+// (the row counts never return to the host) and build their work lists in LDS:
+// * streaming kernel -- experts with at most 64 rows (decode). Bound by the
+//   weight read: every weight byte goes from HBM straight into MFMA registers
+//   once, with the next K step's loads in flight during the current MFMAs.
+// * tiled kernel -- experts with more rows (prefill): LDS-staged 16x16x32 bf16
+//   MFMA tiles that reuse each weight tile across 64 rows.
+// Experts with no rows appear in neither list, so their weights are not read.
+#include <hip/hip_runtime.h>
+
 #include <algorithm>
 
 #include "device_common.h"
@@ -29,166 +32,413 @@ namespace moe {
 
 namespace {
 
-constexpr int kBfBM = 64;   // rows per tile, bf16 path
-constexpr int kF32BM = 16;  // rows per tile, f32 path
+constexpr int kStreamMT = 4;                  // row tiles of 16 per streamed row chunk
+constexpr int kChunkRows = kStreamMT * 16;    // rows per streamed chunk
+constexpr int kStreamRows = 4 * kChunkRows;   // experts with more rows are tiled
+constexpr int kTileBM = 64;                   // rows per tile in the tiled kernel
+constexpr int kMaxLocal = 1024;
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
-// ---------------------------------------------------------------- plan
+struct GemmArgs {
+  const uint16_t* A;      // activations: permuted rows, or token rows when row_index != null
+  const int* row_index;   // null, or sorted_assign: permuted row i is A row row_index[i] / row_div
+  int row_div;
+  const int* offsets;     // [nloc + 1]
+  int nloc, capacity;
+  const uint16_t* W;      // [nloc, N, K], K contiguous
+  int N, K, inter;        // gated GEMMs pair weight row n with row inter + n
+  uint16_t* C;            // [capacity, ldc]
+  int ldc;
+};
 
-__global__ __launch_bounds__(1024) void plan_kernel(const int* __restrict__ offsets, int nloc,
-                                                    int capacity, int bm,
-                                                    int* __restrict__ num_tiles,
-                                                    int* __restrict__ tile_expert,
-                                                    int* __restrict__ tile_row0) {
-  __shared__ int wsum[16];
-  const int e = threadIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int lo = 0, n = 0;
-  if (e < nloc) {
-    lo = min(offsets[e], capacity);
-    const int hi = min(offsets[e + 1], capacity);
-    n = hi > lo ? (hi - lo + bm - 1) / bm : 0;
-  }
-  int incl = n;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, MOE_WAVE);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) wsum[w] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int i = 0; i < w; ++i) base += wsum[i];
-  const int start = base + incl - n;
-  for (int i = 0; i < n; ++i) {
-    tile_expert[start + i] = e;
-    tile_row0[start + i] = lo + i * bm;
-  }
-  if (e == blockDim.x - 1) num_tiles[0] = base + incl;
+__device__ __forceinline__ const uint16_t* a_row_ptr(const GemmArgs& a, int row) {
+  const int src = a.row_index ? a.row_index[row] / a.row_div : row;
+  return a.A + (size_t)src * a.K;
 }
 
-// ---------------------------------------------------------------- bf16 MFMA GEMM
+// ---------------------------------------------------------------- expert lists
 
+// Splits the local experts by row count m, in expert order:
+//   1 <= m <= kStreamRows: streamed, in ceil(m / kChunkRows) row chunks;
+//                          s_first[e] = first chunk of expert e, s_first[nloc] = chunks
+//   m > kStreamRows:       tiled, in ceil(m / bm) row tiles;
+//                          t_first[e] = first tile of expert e, t_first[nloc] = tiles
+// Every thread of the 256-thread workgroup calls this; 4 experts per thread.
+__device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_first, int* wsum,
+                            int& n_chunks, int& n_tiles) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int cc[4], tc[4], cs = 0, ct = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    int m = 0;
+    if (e < a.nloc) {
+      const int lo = min(a.offsets[e], a.capacity);
+      m = max(0, min(a.offsets[e + 1], a.capacity) - lo);
+    }
+    cc[q] = (m > 0 && m <= kStreamRows) ? (m + kChunkRows - 1) / kChunkRows : 0;
+    tc[q] = (m > kStreamRows) ? (m + bm - 1) / bm : 0;
+    cs += cc[q];
+    ct += tc[q];
+  }
+  int is = cs, it = ct;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int os = __shfl_up(is, d, MOE_WAVE), ot = __shfl_up(it, d, MOE_WAVE);
+    if (lane >= d) { is += os; it += ot; }
+  }
+  if (lane == 63) { wsum[w] = is; wsum[4 + w] = it; }
+  __syncthreads();
+  int bs = 0, bt = 0, ts = 0, tt = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < w) { bs += wsum[i]; bt += wsum[4 + i]; }
+    ts += wsum[i];
+    tt += wsum[4 + i];
+  }
+  int ps = bs + is - cs, pt = bt + it - ct;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    if (e < a.nloc) {
+      s_first[e] = ps;
+      t_first[e] = pt;
+      ps += cc[q];
+      pt += tc[q];
+    }
+  }
+  if (tid == 0) {
+    s_first[a.nloc] = ts;
+    t_first[a.nloc] = tt;
+  }
+  n_chunks = ts;
+  n_tiles = tt;
+  __syncthreads();
+}
+
+// The expert e with first[e] <= idx < first[e + 1] (first is non-decreasing).
+__device__ __forceinline__ int find_expert(const int* first, int nloc, int idx) {
+  int lo = 0, hi = nloc - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (first[mid] <= idx) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------- streaming kernel
+
+// A workgroup owns a slab of weight rows of one expert; its 4 wavefronts split
+// K into KS slices and (4 / KS) groups of NTW 16-row weight tiles. In a K step
+// of 32*U, load u of lane (r, g) = (lane % 16, lane / 16) reads 8 bf16 of
+// weight row r at k = kk + 32u + 8g, so one load instruction covers 64
+// contiguous bytes of each of 16 rows, and MFMA u consumes exactly the 32 k of
+// load u for both operands. Weight loads for step s+1 are issued before the
+// MFMAs of step s (two weight register sets used alternately, so no copy waits
+// on a load). K slices are summed through LDS in slice order, then SiLU*up
+// (gated) or the plain bf16 store.
+template <int NTW, int KS, int U, bool GATED>
+struct Stream {
+  static constexpr int MT = kStreamMT;
+  static constexpr int NWN = 4 / KS;
+  static constexpr int HT = GATED ? NTW / 2 : NTW;  // output tiles per wavefront
+  static constexpr int COLS = NWN * HT * 16;        // output columns per slab
+  static constexpr int KSTEP = 32 * U;
+  static_assert(!GATED || NTW % 2 == 0, "gated slabs pair gate and up tiles");
+
+  // MTA = active row tiles of this expert (1..MT): the K loop has no
+  // branches, so the only waits are on the registers an MFMA reads.
+  template <int MTA>
+  __device__ static void run_mt(const GemmArgs& a, int e, int lo, int m, int slab, f32x4_t* red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ks = wave % KS, wn = wave / KS;
+    const int fr = lane & 15, g = lane >> 4;
+
+    int col[HT];
+    const uint16_t* wp[NTW];
+#pragma unroll
+    for (int t = 0; t < HT; ++t) col[t] = (slab * NWN + wn) * HT * 16 + t * 16 + fr;
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      const int wrow = GATED ? (t < HT ? col[t] : a.inter + col[t - HT]) : col[t];
+      wp[t] = a.W + ((size_t)e * a.N + wrow) * a.K + g * 8;
+    }
+    // Rows past the expert's end read its first row instead: an MFMA output row
+    // depends only on its own input row, and those output rows are not stored.
+    const uint16_t* ap[MTA];
+#pragma unroll
+    for (int i = 0; i < MTA; ++i) {
+      const int r = i * 16 + fr;
+      ap[i] = a_row_ptr(a, lo + (r < m ? r : 0)) + g * 8;
+    }
+
+    f32x4_t acc[MTA][NTW];
+#pragma unroll
+    for (int i = 0; i < MTA; ++i)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    bf16x8_t w0[NTW][U], w1[NTW][U], w2[NTW][U], a0[MTA][U], a1[MTA][U];
+    auto load_w = [&](bf16x8_t (&w)[NTW][U], int kk) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) w[t][u] = *(const bf16x8_t*)(wp[t] + kk + u * 32);
+    };
+    auto load_a = [&](bf16x8_t (&av)[MTA][U], int kk) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < MTA; ++i) av[i][u] = *(const bf16x8_t*)(ap[i] + kk + u * 32);
+    };
+    auto mma = [&](const bf16x8_t (&w)[NTW][U], const bf16x8_t (&av)[MTA][U]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < MTA; ++i)
+#pragma unroll
+          for (int t = 0; t < NTW; ++t)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][u], w[t][u], acc[i][t], 0, 0, 0);
+    };
+
+    // Software pipeline over K steps of KSTEP: weights two steps ahead (three
+    // register sets), activations one step ahead (two sets). In step s the
+    // loads for A(s+1) and then W(s+2) are issued before the MFMAs of step s.
+    // Loads complete in issue order, so the oldest outstanding loads are
+    // exactly W(s) and A(s): the MFMAs wait for those while W(s+1), A(s+1) and
+    // W(s+2) stay in flight. Steps past the end reload the last chunk instead
+    // of branching. The scheduling barriers keep this issue order.
+    const int kw = a.K / KS, kbeg = ks * kw, klast = kbeg + kw - KSTEP;
+    const int steps = kw / KSTEP;
+    int kk = kbeg;
+    load_w(w0, kk);
+    load_a(a0, kk);
+    load_w(w1, min(kk + KSTEP, klast));
+#define MOE_STEP(WC, WN, AC, AN)                    \
+  load_a(AN, min(kk + KSTEP, klast));              \
+  load_w(WN, min(kk + 2 * KSTEP, klast));          \
+  __builtin_amdgcn_sched_barrier(0);               \
+  mma(WC, AC);                                     \
+  __builtin_amdgcn_sched_barrier(0);               \
+  kk += KSTEP;
+    for (int s = 0; s < steps; s += 6) {
+      MOE_STEP(w0, w2, a0, a1)
+      if (s + 1 >= steps) break;
+      MOE_STEP(w1, w0, a1, a0)
+      if (s + 2 >= steps) break;
+      MOE_STEP(w2, w1, a0, a1)
+      if (s + 3 >= steps) break;
+      MOE_STEP(w0, w2, a1, a0)
+      if (s + 4 >= steps) break;
+      MOE_STEP(w1, w0, a0, a1)
+      if (s + 5 >= steps) break;
+      MOE_STEP(w2, w1, a1, a0)
+    }
+#undef MOE_STEP
+
+    if (KS > 1) {
+      // red: [KS][NWN][MT][NTW][64] float4; slice ks finishes row tiles i with i % KS == ks
+#pragma unroll
+      for (int i = 0; i < MTA; ++i)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) red[(((ks * NWN + wn) * MT + i) * NTW + t) * 64 + lane] = acc[i][t];
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < MTA; ++i) {
+        if (i % KS != ks) continue;
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          f32x4_t sum = red[(((0 * NWN + wn) * MT + i) * NTW + t) * 64 + lane];
+#pragma unroll
+          for (int q = 1; q < KS; ++q) sum += red[(((q * NWN + wn) * MT + i) * NTW + t) * 64 + lane];
+          acc[i][t] = sum;
+        }
+      }
+    }
+    // Lane holds rows 4*(lane/16) + r and column lane % 16 of every 16x16 fragment.
+#pragma unroll
+    for (int i = 0; i < MTA; ++i) {
+      if (KS > 1 && i % KS != ks) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = i * 16 + g * 4 + r;
+        if (row >= m) continue;
+        uint16_t* crow = a.C + (size_t)(lo + row) * a.ldc;
+#pragma unroll
+        for (int t = 0; t < HT; ++t) {
+          const float v = GATED ? silu(acc[i][t][r]) * acc[i][t + HT][r] : acc[i][t][r];
+          crow[col[t]] = (uint16_t)f32_to_bf16_bits(v);
+        }
+      }
+    }
+    if (KS > 1) __syncthreads();  // red is reused by the next work item
+  }
+
+  // Row chunk `chunk` (kChunkRows rows) of expert e, output slab `slab`.
+  __device__ static void run(const GemmArgs& a, int e, int chunk, int slab, f32x4_t* red) {
+    const int lo = min(a.offsets[e], a.capacity) + chunk * kChunkRows;
+    const int m = min(kChunkRows, min(a.offsets[e + 1], a.capacity) - lo);
+    switch ((m + 15) >> 4) {
+      case 1: run_mt<1>(a, e, lo, m, slab, red); break;
+      case 2: run_mt<2>(a, e, lo, m, slab, red); break;
+      case 3: run_mt<3>(a, e, lo, m, slab, red); break;
+      default: run_mt<4>(a, e, lo, m, slab, red); break;
+    }
+  }
+};
+
+template <int NTW, int KS, int U, bool GATED>
+__global__ __launch_bounds__(256) void stream_gemm_kernel(GemmArgs a) {
+  using S = Stream<NTW, KS, U, GATED>;
+  __shared__ int s_first[kMaxLocal + 1];
+  __shared__ int t_first[kMaxLocal + 1];
+  __shared__ int wsum[8];
+  __shared__ f32x4_t red[KS > 1 ? KS * S::NWN * S::MT * NTW * 64 : 1];
+  int n_chunks, n_tiles;
+  build_lists(a, kTileBM, s_first, t_first, wsum, n_chunks, n_tiles);
+  const int slabs = (GATED ? a.inter : a.N) / S::COLS;
+  const int total = n_chunks * slabs;
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int c = w / slabs;
+    const int e = find_expert(s_first, a.nloc, c);
+    S::run(a, e, c - s_first[e], w % slabs, red);
+  }
+}
+
+// ---------------------------------------------------------------- tiled kernel
+
+// BM x BN output tile (GEMM-1: BN/2 gate + the matching BN/2 up columns, so one
+// lane holds g and u of the same element), BK = 64, 4 wavefronts in WM x WN,
+// LDS double-buffered through registers. Persistent over (row tile, column block).
 template <int BM, int BN, int BK, int WM, int WN, bool GATED>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
-    const uint16_t* __restrict__ A, const int* __restrict__ offsets, int capacity,
-    const int* __restrict__ num_tiles, const int* __restrict__ tile_expert,
-    const int* __restrict__ tile_row0, const uint16_t* __restrict__ W, int N, int K, int inter,
-    uint16_t* __restrict__ C, int ldc) {
+__global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(GemmArgs a) {
   constexpr int NT = WM * WN * 64;
   constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
   constexpr int LDK = BK + 8;  // padded LDS row (elements): spreads rows over banks
   constexpr int CPR = BK / 8;  // 16-byte chunks per tile row
   constexpr int A_CH = BM * CPR / NT, B_CH = BN * CPR / NT;
+  constexpr int HALF = TN * 8;  // gate (or up) columns per wavefront in a gated tile
   static_assert(A_CH * NT == BM * CPR && B_CH * NT == BN * CPR, "tile/thread mismatch");
   static_assert(!GATED || TN % 2 == 0, "gated tiles pair gate and up fragments");
+  static_assert(BM == kTileBM, "tile lists are built for kTileBM rows");
   __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDK];
-
-  const int tile = blockIdx.y;
-  if (tile >= num_tiles[0]) return;
-  const int e = tile_expert[tile];
-  const int row0 = tile_row0[tile];
-  const int rows = min(BM, min(offsets[e + 1], capacity) - row0);
-  const uint16_t* We = W + (size_t)e * N * K;
+  __shared__ int s_first[kMaxLocal + 1];
+  __shared__ int t_first[kMaxLocal + 1];
+  __shared__ int wsum[8];
+  int n_chunks, n_tiles;
+  build_lists(a, BM, s_first, t_first, wsum, n_chunks, n_tiles);
+  const int nblk = (GATED ? a.inter : a.N) / (GATED ? BN / 2 : BN);
+  const int total = n_tiles * nblk;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  constexpr int HALF = TN * 8;  // gate (or up) columns per wave in a gated tile
-
-  // Weight row held by LDS tile row r. Gated tiles: wave column ww owns HALF
-  // gate rows followed by the HALF up rows of the same output columns.
-  const int gate0 = blockIdx.x * (BN / 2);
-  int b_row[B_CH], b_kc[B_CH], a_row[A_CH], a_kc[A_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + i * NT;
-    a_row[i] = c / CPR;
-    a_kc[i] = (c % CPR) * 8;
-  }
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + i * NT, r = c / CPR;
-    b_kc[i] = (c % CPR) * 8;
-    if (GATED) {
-      const int ww = r / (TN * 16), rem = r % (TN * 16);
-      b_row[i] = rem < HALF ? gate0 + ww * HALF + rem : inter + gate0 + ww * HALF + rem - HALF;
-    } else {
-      b_row[i] = blockIdx.x * BN + r;
-    }
-  }
-
-  u32x4_t ra[A_CH], rb[B_CH];
-#define MOE_GLOAD(k0)                                                                         \
-  do {                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) ra[i] =                                  \
-        a_row[i] < rows ? *(const u32x4_t*)(A + (size_t)(row0 + a_row[i]) * K + (k0) + a_kc[i]) \
-                        : u32x4_t{0u, 0u, 0u, 0u};                                         \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) rb[i] =                                  \
-        *(const u32x4_t*)(We + (size_t)b_row[i] * K + (k0) + b_kc[i]);                          \
-  } while (0)
-#define MOE_SSTORE(buf)                                                                                  \
-  do {                                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) *(u32x4_t*)&As[buf][(tid + i * NT) / CPR * LDK + a_kc[i]] = ra[i]; \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) *(u32x4_t*)&Bs[buf][(tid + i * NT) / CPR * LDK + b_kc[i]] = rb[i]; \
-  } while (0)
-
-  f32x4_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nk = K / BK;
-  MOE_GLOAD(0);
-  MOE_SSTORE(0);
-  __syncthreads();
   const int fr = lane & 15, fk = (lane >> 4) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) MOE_GLOAD((kt + 1) * BK);
+  const int K = a.K;
+
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int tile = w / nblk, nb = w % nblk;
+    const int e = find_expert(t_first, a.nloc, tile);
+    const int base = min(a.offsets[e], a.capacity);
+    const int row0 = base + (tile - t_first[e]) * BM;
+    const int rows = min(BM, min(a.offsets[e + 1], a.capacity) - row0);
+    const uint16_t* We = a.W + (size_t)e * a.N * K;
+
+    const uint16_t* aptr[A_CH];
+    int a_kc[A_CH], b_kc[B_CH];
+    const uint16_t* bptr[B_CH];
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      bf16x8_t a[TM], b[TN];
+    for (int i = 0; i < A_CH; ++i) {
+      const int c = tid + i * NT, r = c / CPR;
+      a_kc[i] = (c % CPR) * 8;
+      aptr[i] = r < rows ? a_row_ptr(a, row0 + r) : nullptr;
+    }
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        a[i] = *(const bf16x8_t*)&As[buf][(wm * TM * 16 + i * 16 + fr) * LDK + ks * 32 + fk];
+    for (int i = 0; i < B_CH; ++i) {
+      const int c = tid + i * NT, r = c / CPR;
+      b_kc[i] = (c % CPR) * 8;
+      int wrow;
+      if (GATED) {
+        const int ww = r / (TN * 16), rem = r % (TN * 16), n0 = nb * (BN / 2);
+        wrow = rem < HALF ? n0 + ww * HALF + rem : a.inter + n0 + ww * HALF + rem - HALF;
+      } else {
+        wrow = nb * BN + r;
+      }
+      bptr[i] = We + (size_t)wrow * K;
+    }
+
+    u32x4_t ra[A_CH], rb[B_CH];
+#define MOE_GLOAD(k0)                                                                   \
+  do {                                                                                  \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) ra[i] =                            \
+        aptr[i] ? *(const u32x4_t*)(aptr[i] + (k0) + a_kc[i]) : u32x4_t{0u, 0u, 0u, 0u}; \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) rb[i] =                            \
+        *(const u32x4_t*)(bptr[i] + (k0) + b_kc[i]);                                    \
+  } while (0)
+#define MOE_SSTORE(buf)                                                                           \
+  do {                                                                                            \
+    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                              \
+        *(u32x4_t*)&As[buf][(tid + i * NT) / CPR * LDK + a_kc[i]] = ra[i];                        \
+    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                              \
+        *(u32x4_t*)&Bs[buf][(tid + i * NT) / CPR * LDK + b_kc[i]] = rb[i];                        \
+  } while (0)
+
+    f32x4_t acc[TM][TN];
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        b[j] = *(const bf16x8_t*)&Bs[buf][(wn * TN * 16 + j * 16 + fr) * LDK + ks * 32 + fk];
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int nk = K / BK;
+    MOE_GLOAD(0);
+    MOE_SSTORE(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) MOE_GLOAD((kt + 1) * BK);
+#pragma unroll
+      for (int ks = 0; ks < BK / 32; ++ks) {
+        bf16x8_t av[TM], bv[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          av[i] = *(const bf16x8_t*)&As[buf][(wm * TM * 16 + i * 16 + fr) * LDK + ks * 32 + fk];
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          bv[j] = *(const bf16x8_t*)&Bs[buf][(wn * TN * 16 + j * 16 + fr) * LDK + ks * 32 + fk];
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      }
+      if (kt + 1 < nk) MOE_SSTORE(buf ^ 1);
+      __syncthreads();
     }
-    if (kt + 1 < nk) MOE_SSTORE(buf ^ 1);
-    __syncthreads();
-  }
-
 #undef MOE_GLOAD
 #undef MOE_SSTORE
 
-  // Epilogue. Lane holds rows 4*(lane/16) + r, column lane % 16 of each 16x16 fragment.
-  const int rq = (lane >> 4) * 4;
+    const int rq = (lane >> 4) * 4;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+    for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = wm * TM * 16 + i * 16 + rq + r;
-      if (row >= rows) continue;
-      uint16_t* crow = C + (size_t)(row0 + row) * ldc;
-      if (GATED) {
-        const int n0 = blockIdx.x * (BN / 2) + wn * HALF;
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * TM * 16 + i * 16 + rq + r;
+        if (row >= rows) continue;
+        uint16_t* crow = a.C + (size_t)(row0 + row) * a.ldc;
+        if (GATED) {
+          const int n0 = nb * (BN / 2) + wn * HALF;
 #pragma unroll
-        for (int j = 0; j < TN / 2; ++j) {
-          const float g = acc[i][j][r], u = acc[i][j + TN / 2][r];
-          crow[n0 + j * 16 + fr] = (uint16_t)f32_to_bf16_bits(silu(g) * u);
+          for (int j = 0; j < TN / 2; ++j) {
+            const float gv = acc[i][j][r], uv = acc[i][j + TN / 2][r];
+            crow[n0 + j * 16 + fr] = (uint16_t)f32_to_bf16_bits(silu(gv) * uv);
+          }
+        } else {
+          const int n0 = nb * BN + wn * TN * 16;
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            crow[n0 + j * 16 + fr] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
         }
-      } else {
-        const int n0 = blockIdx.x * BN + wn * TN * 16;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) crow[n0 + j * 16 + fr] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
       }
     }
   }
@@ -196,106 +446,167 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(
 
 // ---------------------------------------------------------------- f32 GEMM (small shapes)
 
-// 16 rows x 16 output columns per workgroup, plain FMA; bounds-checked in N and K.
+struct GemmArgsF32 {
+  const float* A;
+  const int* row_index;
+  int row_div;
+  const int* offsets;
+  int nloc, capacity, max_row_tiles;
+  const float* W;
+  int N, K, inter;
+  float* C;
+  int ldc;
+};
+
+// 16 rows x 16 output columns per workgroup, plain FMA, bounds-checked in N and K.
+// blockIdx.y = expert * max_row_tiles + row tile; blockIdx.x = column block.
 template <bool GATED>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(
-    const float* __restrict__ A, const int* __restrict__ offsets, int capacity,
-    const int* __restrict__ num_tiles, const int* __restrict__ tile_expert,
-    const int* __restrict__ tile_row0, const float* __restrict__ W, int N, int K, int inter,
-    float* __restrict__ C, int ldc) {
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF32 a) {
   __shared__ float As[16][17], Bg[16][17], Bu[16][17];
-  const int tile = blockIdx.y;
-  if (tile >= num_tiles[0]) return;
-  const int e = tile_expert[tile];
-  const int row0 = tile_row0[tile];
-  const int rows = min(16, min(offsets[e + 1], capacity) - row0);
-  const int n_out = GATED ? inter : N;
-  const float* We = W + (size_t)e * N * K;
+  const int e = blockIdx.y / a.max_row_tiles, tile = blockIdx.y % a.max_row_tiles;
+  const int lo = min(a.offsets[e], a.capacity), hi = min(a.offsets[e + 1], a.capacity);
+  const int row0 = lo + tile * 16;
+  if (row0 >= hi) return;
+  const int rows = min(16, hi - row0);
+  const int n_out = GATED ? a.inter : a.N;
+  const int K = a.K;
+  const float* We = a.W + (size_t)e * a.N * K;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int col0 = blockIdx.x * 16;
-  float g = 0.f, u = 0.f;
+  const float* arow = nullptr;
+  if (ty < rows) {
+    const int r = row0 + ty;
+    arow = a.A + (size_t)(a.row_index ? a.row_index[r] / a.row_div : r) * K;
+  }
+  float gs = 0.f, us = 0.f;
   for (int k0 = 0; k0 < K; k0 += 16) {
     const int kk = k0 + tx;
-    As[ty][tx] = (ty < rows && kk < K) ? A[(size_t)(row0 + ty) * K + kk] : 0.f;
+    As[ty][tx] = (arow && kk < K) ? arow[kk] : 0.f;
     const int n = col0 + ty;
     Bg[ty][tx] = (n < n_out && kk < K) ? We[(size_t)n * K + kk] : 0.f;
-    if (GATED) Bu[ty][tx] = (n < n_out && kk < K) ? We[(size_t)(inter + n) * K + kk] : 0.f;
+    if (GATED) Bu[ty][tx] = (n < n_out && kk < K) ? We[(size_t)(a.inter + n) * K + kk] : 0.f;
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      g += As[ty][q] * Bg[tx][q];
-      if (GATED) u += As[ty][q] * Bu[tx][q];
+      gs += As[ty][q] * Bg[tx][q];
+      if (GATED) us += As[ty][q] * Bu[tx][q];
     }
     __syncthreads();
   }
   const int col = col0 + tx;
-  if (ty < rows && col < n_out) C[(size_t)(row0 + ty) * ldc + col] = GATED ? silu(g) * u : g;
+  if (ty < rows && col < n_out) a.C[(size_t)(row0 + ty) * a.ldc + col] = GATED ? silu(gs) * us : gs;
 }
 
-// ---------------------------------------------------------------- workspace
-
-struct Workspace {
-  int* num_tiles;
-  int* tile_expert;
-  int* tile_row0;
-  void* h;
-  size_t bytes;
-};
+// ---------------------------------------------------------------- host side
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-Workspace carve(void* base, int num_local, int inter, int capacity, bool bf16) {
-  const int bm = bf16 ? kBfBM : kF32BM;
-  const size_t max_tiles = (size_t)(capacity + bm - 1) / bm + num_local;
-  char* p = (char*)base;
-  Workspace w;
-  size_t off = 0;
-  w.num_tiles = (int*)(p + off);
-  off += 256;
-  w.tile_expert = (int*)(p + off);
-  off += align256(max_tiles * sizeof(int));
-  w.tile_row0 = (int*)(p + off);
-  off += align256(max_tiles * sizeof(int));
-  w.h = p + off;
-  off += align256((size_t)capacity * inter * (bf16 ? 2 : 4));
-  w.bytes = off;
-  return w;
+int cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Resident workgroups per CU of a kernel (queried once per kernel).
+template <typename F>
+int occupancy(F kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n <= 0)
+    n = 1;
+  return n;
+}
+
+// K split across the 4 wavefronts (KS) and K step unroll (U) of the streaming
+// kernel: at least 8 K steps per wavefront when K allows, K a multiple of KS * 32 * U.
+struct StreamShape {
+  int ks, u;
+};
+StreamShape stream_shape(int K) {
+  for (int ks : {4, 2, 1})
+    for (int u : {2, 1})
+      if (K % (ks * 32 * u) == 0 && (K / ks >= 256 || ks == 1)) return {ks, u};
+  return {0, 0};
+}
+
+template <bool GATED, int KS, int U>
+void launch_stream_t(const GemmArgs& g, hipStream_t s) {
+  constexpr int NTW = 2;
+  using S = Stream<NTW, KS, U, GATED>;
+  static const int occ = occupancy(stream_gemm_kernel<NTW, KS, U, GATED>, 256);
+  const int slabs = (GATED ? g.inter : g.N) / S::COLS;
+  const long max_chunks = std::min<long>((long)g.nloc * (kStreamRows / kChunkRows),
+                                         (long)(g.capacity + kChunkRows - 1) / kChunkRows + g.nloc);
+  const long max_work = max_chunks * slabs;
+  const int grid = (int)std::max<long>(1, std::min<long>(max_work, (long)cu_count() * occ));
+  hipLaunchKernelGGL((stream_gemm_kernel<NTW, KS, U, GATED>), dim3(grid), dim3(256), 0, s, g);
+}
+
+template <bool GATED>
+hipError_t launch_stream(const GemmArgs& g, hipStream_t s) {
+  const StreamShape sh = stream_shape(g.K);
+#define MOE_STREAM(KS_, U_)                        \
+  if (sh.ks == KS_ && sh.u == U_) {                \
+    launch_stream_t<GATED, KS_, U_>(g, s);         \
+    return hipGetLastError();                      \
+  }
+  MOE_STREAM(4, 4) MOE_STREAM(4, 2) MOE_STREAM(4, 1)
+  MOE_STREAM(2, 4) MOE_STREAM(2, 2) MOE_STREAM(2, 1)
+  MOE_STREAM(1, 4) MOE_STREAM(1, 2) MOE_STREAM(1, 1)
+#undef MOE_STREAM
+  return hipErrorInvalidValue;
+}
+
+template <bool GATED>
+hipError_t launch_tiled(const GemmArgs& g, hipStream_t s) {
+  constexpr int BM = kTileBM, BN = 128, BK = 64;
+  auto kernel = tiled_gemm_kernel<BM, BN, BK, 2, 2, GATED>;
+  static const int occ = occupancy(kernel, 256);
+  const int nblk = (GATED ? g.inter : g.N) / (GATED ? BN / 2 : BN);
+  const long max_work = ((long)(g.capacity + BM - 1) / BM + g.nloc) * nblk;
+  const int grid = (int)std::max<long>(1, std::min<long>(max_work, (long)cu_count() * occ));
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, g);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 size_t ffn_workspace_size(int num_local, int hidden, int inter, int capacity, bool bf16) {
+  (void)num_local;
   (void)hidden;
-  return carve(nullptr, num_local, inter, capacity, bf16).bytes;
+  return align256((size_t)capacity * inter * (bf16 ? 2 : 4));  // h
 }
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
-  const Workspace ws = carve(a.workspace, a.num_local, a.inter, a.capacity, a.bf16);
-  const int bm = a.bf16 ? kBfBM : kF32BM;
-  const int max_tiles = (a.capacity + bm - 1) / bm + a.num_local;
   if (a.capacity == 0) return hipSuccess;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.num_local, a.capacity,
-                     bm, ws.num_tiles, ws.tile_expert, ws.tile_row0);
   const int I = a.inter, d = a.hidden;
   if (a.bf16) {
-    constexpr int BM = kBfBM, BN = 128, BK = 64;
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, 2, 2, true>), dim3(I / (BN / 2), max_tiles),
-                       dim3(256), 0, s, (const uint16_t*)a.x_sorted, a.offsets, a.capacity,
-                       ws.num_tiles, ws.tile_expert, ws.tile_row0, (const uint16_t*)a.w_gate_up,
-                       2 * I, d, I, (uint16_t*)ws.h, I);
-    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, BK, 2, 2, false>), dim3(d / BN, max_tiles),
-                       dim3(256), 0, s, (const uint16_t*)ws.h, a.offsets, a.capacity,
-                       ws.num_tiles, ws.tile_expert, ws.tile_row0, (const uint16_t*)a.w_down, d,
-                       I, I, (uint16_t*)a.o_sorted, d);
-  } else {
-    hipLaunchKernelGGL((gemm_f32_kernel<true>), dim3((I + 15) / 16, max_tiles), dim3(256), 0, s,
-                       (const float*)a.x_sorted, a.offsets, a.capacity, ws.num_tiles,
-                       ws.tile_expert, ws.tile_row0, (const float*)a.w_gate_up, 2 * I, d, I,
-                       (float*)ws.h, I);
-    hipLaunchKernelGGL((gemm_f32_kernel<false>), dim3((d + 15) / 16, max_tiles), dim3(256), 0, s,
-                       (const float*)ws.h, a.offsets, a.capacity, ws.num_tiles, ws.tile_expert,
-                       ws.tile_row0, (const float*)a.w_down, d, I, I, (float*)a.o_sorted, d);
+    GemmArgs g1{(const uint16_t*)a.x, a.row_index, a.row_div, a.offsets, a.num_local,
+                a.capacity, (const uint16_t*)a.w_gate_up, 2 * I, d, I,
+                (uint16_t*)a.workspace, I};
+    GemmArgs g2{(const uint16_t*)a.workspace, nullptr, 1, a.offsets, a.num_local, a.capacity,
+                (const uint16_t*)a.w_down, d, I, I, (uint16_t*)a.o_sorted, d};
+    hipError_t err;
+    if ((err = launch_stream<true>(g1, s)) != hipSuccess) return err;
+    if ((err = launch_tiled<true>(g1, s)) != hipSuccess) return err;
+    if ((err = launch_stream<false>(g2, s)) != hipSuccess) return err;
+    return launch_tiled<false>(g2, s);
   }
+  const int mrt = (a.capacity + 15) / 16;
+  GemmArgsF32 g1{(const float*)a.x, a.row_index, a.row_div, a.offsets, a.num_local, a.capacity,
+                 mrt, (const float*)a.w_gate_up, 2 * I, d, I, (float*)a.workspace, I};
+  GemmArgsF32 g2{(const float*)a.workspace, nullptr, 1, a.offsets, a.num_local, a.capacity, mrt,
+                 (const float*)a.w_down, d, I, I, (float*)a.o_sorted, d};
+  hipLaunchKernelGGL((gemm_f32_kernel<true>), dim3((I + 15) / 16, a.num_local * mrt), dim3(256),
+                     0, s, g1);
+  hipLaunchKernelGGL((gemm_f32_kernel<false>), dim3((d + 15) / 16, a.num_local * mrt), dim3(256),
+                     0, s, g2);
   return hipGetLastError();
 }
 

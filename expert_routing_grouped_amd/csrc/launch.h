@@ -32,7 +32,9 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 constexpr int kDispatchMaxLocal = 1000;  // per-(wave, expert) counters fit in 64 KiB of LDS
 
 struct FfnArgs {
-  const void* x_sorted;
+  const void* x;         // permuted rows, or token rows read through row_index
+  const int* row_index;  // null, or sorted_assign (row i = x[row_index[i] / row_div])
+  int row_div;
   const int* offsets;
   const void* w_gate_up;
   const void* w_down;

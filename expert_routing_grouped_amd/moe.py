@@ -29,7 +29,7 @@ _SIGNATURES = {
     "moe_route": (ctypes.c_int, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moe_dispatch": (ctypes.c_int, [_P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
-    "moe_expert_ffn": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P,
+    "moe_expert_ffn": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P,
                                       ctypes.c_size_t, _P]),
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
 }
@@ -145,29 +145,40 @@ def ffn_workspace_size(num_local_experts, hidden, inter, row_capacity, dtype) ->
                                                    row_capacity, code))
 
 
-def moe_expert_ffn(x_sorted, expert_offsets, w_gate_up, w_down, o_sorted=None, workspace=None,
-                   stream=None):
-    """Grouped SwiGLU FFN over the permuted rows; returns o_sorted [row_capacity, d]."""
-    dt = x_sorted.dtype
-    _dev(x_sorted, dt, "x_sorted")
+def moe_expert_ffn(x, expert_offsets, w_gate_up, w_down, row_index=None, row_index_div=1,
+                   row_capacity=None, o_sorted=None, workspace=None, stream=None):
+    """Grouped SwiGLU FFN over the permuted rows; returns o_sorted [row_capacity, d].
+
+    x is x_sorted (row_index None) or the token rows, read through row_index
+    (sorted_assign) and row_index_div (top_k): the dispatch gather fused into the GEMM.
+    """
+    dt = x.dtype
+    _dev(x, dt, "x")
     _dev(expert_offsets, torch.int32, "expert_offsets")
     _dev(w_gate_up, dt, "w_gate_up")
     _dev(w_down, dt, "w_down")
-    cap, hidden = x_sorted.shape
+    if row_index is not None:
+        _dev(row_index, torch.int32, "row_index")
+        cap = row_index.numel() if row_capacity is None else row_capacity
+    else:
+        cap = x.shape[0] if row_capacity is None else row_capacity
+    hidden = x.shape[1]
     E_loc, two_i, d2 = w_gate_up.shape
     inter = two_i // 2
     if d2 != hidden or tuple(w_down.shape) != (E_loc, hidden, inter):
-        raise MoeError("weight shapes do not match x_sorted")
+        raise MoeError("weight shapes do not match x")
     if o_sorted is None:
-        o_sorted = torch.empty((cap, hidden), dtype=dt, device=x_sorted.device)
+        o_sorted = torch.empty((max(cap, 1), hidden), dtype=dt, device=x.device)
     _dev(o_sorted, dt, "o_sorted")
+    if o_sorted.shape[0] < cap or (row_index is None and x.shape[0] < cap):
+        raise MoeError("row buffers are smaller than row_capacity")
     need = ffn_workspace_size(E_loc, hidden, inter, cap, dt)
     if need == 0:
         raise MoeError("moe_expert_ffn: unsupported sizes")
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x_sorted.device)
-    _check(lib().moe_expert_ffn(_ptr(x_sorted), _ptr(expert_offsets), _ptr(w_gate_up),
-                                _ptr(w_down), E_loc, hidden, inter, cap, _code(dt),
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check(lib().moe_expert_ffn(_ptr(x), _ptr(row_index), int(row_index_div), _ptr(expert_offsets),
+                                _ptr(w_gate_up), _ptr(w_down), E_loc, hidden, inter, cap, _code(dt),
                                 _ptr(o_sorted), _ptr(workspace), workspace.numel(),
                                 _stream(stream)), "moe_expert_ffn")
     return o_sorted
@@ -198,13 +209,16 @@ class MoELayer:
     """
 
     def __init__(self, *, num_tokens, num_experts, top_k, num_groups, topk_groups, score_mode,
-                 renormalize, expert_begin, num_local_experts, hidden, inter, dtype, device):
+                 renormalize, expert_begin, num_local_experts, hidden, inter, dtype, device,
+                 fuse_gather=True):
         self.T, self.E, self.k = num_tokens, num_experts, top_k
         self.num_groups, self.topk_groups = num_groups, topk_groups
         self.score_mode, self.renormalize = score_mode, renormalize
         self.expert_begin, self.num_local = expert_begin, num_local_experts
         self.hidden, self.inter, self.dtype = hidden, inter, dtype
+        self.fuse_gather = fuse_gather
         cap = num_tokens * top_k
+        self.cap = cap
         dev = torch.device(device)
         i32 = dict(dtype=torch.int32, device=dev)
         self.buf = dict(
@@ -216,7 +230,8 @@ class MoELayer:
             assign_pos=torch.empty(max(cap, 1), **i32),
         )
         if hidden:
-            self.buf["x_sorted"] = torch.empty((max(cap, 1), hidden), dtype=dtype, device=dev)
+            if not fuse_gather:
+                self.buf["x_sorted"] = torch.empty((max(cap, 1), hidden), dtype=dtype, device=dev)
             self.buf["o_sorted"] = torch.empty((max(cap, 1), hidden), dtype=dtype, device=dev)
             self.buf["y"] = torch.empty((num_tokens, hidden), dtype=dtype, device=dev)
             need = ffn_workspace_size(num_local_experts, hidden, inter, max(cap, 1), dtype)
@@ -229,16 +244,23 @@ class MoELayer:
                          self.renormalize, self.buf["topk_ids"], self.buf["topk_weights"], stream)
 
     def dispatch(self, x=None, stream=None):
+        """Counting sort; also gathers x into x_sorted unless the gather is fused into the FFN."""
         b = self.buf
         out = {n: b[n] for n in ("counts", "offsets", "sorted_assign", "assign_pos")}
-        if x is not None:
+        if x is not None and not self.fuse_gather:
             out["x_sorted"] = b["x_sorted"]
-        return moe_dispatch(b["topk_ids"], self.expert_begin, self.num_local, x, out, stream)
+            return moe_dispatch(b["topk_ids"], self.expert_begin, self.num_local, x, out, stream)
+        return moe_dispatch(b["topk_ids"], self.expert_begin, self.num_local, None, out, stream)
 
-    def ffn(self, w_gate_up, w_down, stream=None):
+    def ffn(self, w_gate_up, w_down, x=None, stream=None):
         b = self.buf
-        return moe_expert_ffn(b["x_sorted"], b["offsets"], w_gate_up, w_down, b["o_sorted"],
-                              b["workspace"], stream)
+        if self.fuse_gather:
+            return moe_expert_ffn(x, b["offsets"], w_gate_up, w_down, row_index=b["sorted_assign"],
+                                  row_index_div=self.k, row_capacity=self.cap,
+                                  o_sorted=b["o_sorted"], workspace=b["workspace"], stream=stream)
+        return moe_expert_ffn(b["x_sorted"], b["offsets"], w_gate_up, w_down,
+                              row_capacity=self.cap, o_sorted=b["o_sorted"],
+                              workspace=b["workspace"], stream=stream)
 
     def combine(self, stream=None):
         b = self.buf
@@ -250,5 +272,5 @@ class MoELayer:
         self.dispatch(x, stream)
         if x is None:
             return None
-        self.ffn(w_gate_up, w_down, stream)
+        self.ffn(w_gate_up, w_down, x, stream)
         return self.combine(stream)

@@ -138,22 +138,26 @@ size_t moe_expert_ffn_workspace_size(int32_t num_local_experts, int32_t hidden, 
  *   [g | u] = X_e * W_gate_up[e]^T,  h = silu(g) * u,  o = h * W_down[e]^T,
  * silu(z) = z / (1 + exp(-z)). Experts without rows read no weights.
  *
- * x_sorted        [row_capacity, hidden] (dtype): permuted rows (moe_dispatch).
+ * x               the permuted activations, in one of two forms:
+ *                 row_index == NULL: x_sorted [row_capacity, hidden] (moe_dispatch);
+ *                 row_index != NULL: token rows [T, hidden], and permuted row i is
+ *                 x[row_index[i] / row_index_div] -- pass sorted_assign and top_k to
+ *                 fuse the dispatch gather into the first GEMM's loads.
  * expert_offsets  [E_loc + 1] int32 (moe_dispatch); read on the device only.
  * w_gate_up       [E_loc, 2 * inter, hidden] (dtype): rows [0, I) gate, [I, 2I) up.
  * w_down          [E_loc, hidden, inter] (dtype).
  * o_sorted        [row_capacity, hidden] (dtype) out: rows [0, M) written.
- * workspace       device buffer of at least moe_expert_ffn_workspace_size bytes;
- *                 holds h and the tile schedule; contents need not be initialised.
+ * workspace       device buffer of at least moe_expert_ffn_workspace_size bytes
+ *                 (holds h); contents need not be initialised.
  * bf16: float32 accumulation; h and o are rounded to bf16.
  * Limits (bf16): hidden % 256 == 0, inter % 64 == 0. f32: hidden % 4 == 0,
- * inter % 4 == 0. M = offsets[E_loc] must not exceed row_capacity (rows past
- * row_capacity are ignored on the device).
+ * inter % 4 == 0, E_loc * ceil(row_capacity / 16) <= 65535. M = offsets[E_loc]
+ * must not exceed row_capacity (rows past row_capacity are ignored on the device).
  */
-moe_status_t moe_expert_ffn(const void* x_sorted, const int32_t* expert_offsets,
-                            const void* w_gate_up, const void* w_down,
-                            int32_t num_local_experts, int32_t hidden, int32_t inter,
-                            int32_t row_capacity, int32_t dtype, void* o_sorted,
+moe_status_t moe_expert_ffn(const void* x, const int32_t* row_index, int32_t row_index_div,
+                            const int32_t* expert_offsets, const void* w_gate_up,
+                            const void* w_down, int32_t num_local_experts, int32_t hidden,
+                            int32_t inter, int32_t row_capacity, int32_t dtype, void* o_sorted,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = moe.lib()
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     assert moe.status_string(0) == "ok"
     assert moe.status_string(1) == "invalid argument"
     assert moe.status_string(3).startswith("workspace")
@@ -76,14 +76,16 @@ def test_dispatch_validation():
 def test_ffn_validation_and_workspace():
     l = moe.lib()
     p = ctypes.c_void_p(256)
-    assert l.moe_expert_ffn_workspace_size(8, 7168, 2048, 4096, 1) > 4096 * 2048 * 2
+    assert l.moe_expert_ffn_workspace_size(8, 7168, 2048, 4096, 1) >= 4096 * 2048 * 2
     assert l.moe_expert_ffn_workspace_size(8, 7000, 2048, 4096, 1) == 0     # hidden % 256
     assert l.moe_expert_ffn_workspace_size(8, 7168, 100, 4096, 1) == 0      # inter % 64
     assert l.moe_expert_ffn_workspace_size(0, 7168, 2048, 4096, 1) == 0
-    assert l.moe_expert_ffn(p, p, p, p, 8, 7000, 2048, 64, 1, p, p, 1 << 30, None) == 2
-    assert l.moe_expert_ffn(p, None, p, p, 8, 7168, 2048, 64, 1, p, p, 1 << 30, None) == 1
-    assert l.moe_expert_ffn(p, p, p, p, 8, 7168, 2048, 64, 1, p, p, 16, None) == 3   # workspace small
-    assert l.moe_expert_ffn(p, p, p, p, 8, 7168, 2048, 64, 1, p, None, 1 << 30, None) == 3
+    assert l.moe_expert_ffn(p, None, 1, p, p, p, 8, 7000, 2048, 64, 1, p, p, 1 << 30, None) == 2
+    assert l.moe_expert_ffn(p, None, 1, None, p, p, 8, 7168, 2048, 64, 1, p, p, 1 << 30, None) == 1
+    assert l.moe_expert_ffn(p, p, 0, p, p, p, 8, 7168, 2048, 64, 1, p, p, 1 << 30, None) == 1  # div 0
+    assert l.moe_expert_ffn(p, None, 1, p, p, p, 8, 7168, 2048, 64, 1, p, p, 16, None) == 3   # small ws
+    assert l.moe_expert_ffn(p, None, 1, p, p, p, 8, 7168, 2048, 64, 1, p, None, 1 << 30, None) == 3
+    assert l.moe_expert_ffn(p, None, 1, p, p, p, 8000, 256, 64, 64, 0, p, p, 1 << 30, None) == 2
 
 
 def test_combine_validation():

@@ -200,18 +200,22 @@ def test_dispatch_gathers_bf16_rows():
 
 # ------------------------------------------------------------------ full layer
 
-def run_layer(inp, wl):
-    """The four calls on the GPU; returns host copies of every output."""
+def run_layer(inp, wl, fuse=True):
+    """The four calls on the GPU; returns host copies of every output.
+
+    fuse: the FFN reads token rows through sorted_assign (gather fused into GEMM-1);
+    otherwise moe_dispatch materialises x_sorted and the FFN reads that."""
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     layer = moe.MoELayer(num_tokens=wl.T, num_experts=wl.E, top_k=wl.top_k,
                          num_groups=wl.num_groups, topk_groups=wl.topk_groups,
                          score_mode=moe.MOE_SCORE_SOFTMAX if wl.score_mode == "softmax" else moe.MOE_SCORE_RAW,
                          renormalize=wl.renormalize, expert_begin=wl.expert_begin,
                          num_local_experts=wl.num_local, hidden=wl.hidden, inter=wl.inter,
-                         dtype=dt, device=DEV)
+                         dtype=dt, device=DEV, fuse_gather=fuse)
     s, x = to_device(inp.scores, DEV), to_device(inp.x, DEV)
     wgu, wd = to_device(inp.w_gate_up, DEV), to_device(inp.w_down, DEV)
-    print(f"layer {wl.name} T={wl.T} d={wl.hidden} I={wl.inter} local={wl.num_local}", flush=True)
+    print(f"layer {wl.name} T={wl.T} d={wl.hidden} I={wl.inter} local={wl.num_local} fuse={fuse}",
+          flush=True)
     layer.forward(s, x, wgu, wd)
     torch.cuda.synchronize()
     return {k: to_host(v) for k, v in layer.buf.items() if k != "workspace"}
@@ -241,13 +245,14 @@ def small_bf16_workload(T, E, k, ng, tg, d, I, begin, nloc, seed):
                       expert_begin=begin, num_local=nloc, dtype="bf16", seed=seed)
 
 
-def check_full(wl, inp, tol):
-    g = run_layer(inp, wl)
+def check_full(wl, inp, tol, fuse=True):
+    g = run_layer(inp, wl, fuse)
     ref = oracle_front(inp, wl)
     M = check_front(g, ref)
     ids, w, counts, offsets, sa, pos = ref
     xs = oracle.gather_rows(inp.x, sa, wl.top_k)
-    assert np.array_equal(g["x_sorted"][:M], xs)
+    if not fuse:
+        assert np.array_equal(g["x_sorted"][:M], xs)
     o_ref = oracle.expert_ffn(xs, offsets, inp.w_gate_up, inp.w_down)
     e_o = rel_err(as_f64(g["o_sorted"][:M]), o_ref)
     y_ref = oracle.combine(o_ref, pos, w)
@@ -260,9 +265,10 @@ def check_full(wl, inp, tol):
     return g
 
 
-def test_layer_toy_fp32():
+@pytest.mark.parametrize("fuse", [True, False])
+def test_layer_toy_fp32(fuse):
     wl = W.WORKLOADS["toy_fp32"]
-    check_full(wl, inputs("toy_fp32"), TOL_F32)
+    check_full(wl, inputs("toy_fp32"), TOL_F32, fuse)
 
 
 @pytest.mark.parametrize("T,E,k,ng,tg,d,I,begin,nloc", [
@@ -271,14 +277,16 @@ def test_layer_toy_fp32():
     (40, 64, 6, 8, 4, 1024, 192, 0, 64),    # many experts with 0-9 rows
     (700, 8, 2, 1, 1, 256, 256, 0, 8),      # > 64 rows per expert
 ])
-def test_layer_bf16_small(T, E, k, ng, tg, d, I, begin, nloc):
+@pytest.mark.parametrize("fuse", [True, False])
+def test_layer_bf16_small(T, E, k, ng, tg, d, I, begin, nloc, fuse):
     wl = small_bf16_workload(T, E, k, ng, tg, d, I, begin, nloc, seed=T + d)
-    check_full(wl, W.generate(wl), TOL_BF16)
+    check_full(wl, W.generate(wl), TOL_BF16, fuse)
 
 
-def test_layer_decode_ep_full():
+@pytest.mark.parametrize("fuse", [True, False])
+def test_layer_decode_ep_full(fuse):
     wl = W.WORKLOADS["decode_ep"]
-    check_full(wl, inputs("decode_ep"), TOL_BF16)
+    check_full(wl, inputs("decode_ep"), TOL_BF16, fuse)
 
 
 def test_layer_decode_tp_full_and_deterministic():
