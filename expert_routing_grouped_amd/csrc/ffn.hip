@@ -13,12 +13,13 @@
 // the dispatch gather, the token rows x read through sorted_assign
 // (row i = x[sorted_assign[i] / k]).
 //
-// Each GEMM is two persistent kernels that read expert_offsets on the device
-// (the row counts never return to the host) and build their work lists in LDS:
-// * streaming kernel -- experts with at most 64 rows (decode). Bound by the
-//   weight read: every weight byte goes from HBM straight into MFMA registers
-//   once, with the next K step's loads in flight during the current MFMAs.
-// * tiled kernel -- experts with more rows (prefill): LDS-staged 16x16x32 bf16
+// Each GEMM is one persistent kernel that reads expert_offsets on the device
+// (the row counts never return to the host) and builds its work lists in LDS:
+// * streaming path -- experts with at most 256 rows (decode), in 64-row
+//   chunks. Bound by the weight read: weight bytes go from HBM straight into
+//   MFMA registers, with the next two K steps' loads in flight during the
+//   current MFMAs.
+// * tiled path -- experts with more rows (prefill): LDS-staged 16x16x32 bf16
 //   MFMA tiles that reuse each weight tile across 64 rows.
 // Experts with no rows appear in neither list, so their weights are not read.
 #include <hip/hip_runtime.h>
@@ -35,7 +36,7 @@ namespace {
 constexpr int kStreamMT = 4;                  // row tiles of 16 per streamed row chunk
 constexpr int kChunkRows = kStreamMT * 16;    // rows per streamed chunk
 constexpr int kStreamRows = 4 * kChunkRows;   // experts with more rows are tiled
-constexpr int kTileBM = 64;                   // rows per tile in the tiled kernel
+constexpr int kTileBM = 64;                   // rows per tile in the tiled path
 constexpr int kMaxLocal = 1024;
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
@@ -127,17 +128,19 @@ __device__ __forceinline__ int find_expert(const int* first, int nloc, int idx) 
   return lo;
 }
 
-// ---------------------------------------------------------------- streaming kernel
+// ---------------------------------------------------------------- streaming path
 
-// A workgroup owns a slab of weight rows of one expert; its 4 wavefronts split
-// K into KS slices and (4 / KS) groups of NTW 16-row weight tiles. In a K step
-// of 32*U, load u of lane (r, g) = (lane % 16, lane / 16) reads 8 bf16 of
-// weight row r at k = kk + 32u + 8g, so one load instruction covers 64
-// contiguous bytes of each of 16 rows, and MFMA u consumes exactly the 32 k of
-// load u for both operands. Weight loads for step s+1 are issued before the
-// MFMAs of step s (two weight register sets used alternately, so no copy waits
-// on a load). K slices are summed through LDS in slice order, then SiLU*up
-// (gated) or the plain bf16 store.
+// A work item is a row chunk (up to 64 rows) of one expert and a slab of
+// output columns. The workgroup's 4 wavefronts split K into KS slices and
+// (4 / KS) groups of NTW 16-row weight tiles. The weight tile is the MFMA A
+// operand and the activations the B operand, so a lane ends up holding 4
+// consecutive output columns of one row (one 8-byte store).
+//
+// In a K step of 32*U, load u of lane (r, g) = (lane % 16, lane / 16) reads 8
+// bf16 of weight row r (or activation row r) at k = kk + 32u + 8g: one load
+// instruction covers 64 contiguous bytes of each of 16 rows, and MFMA u
+// consumes exactly the 32 k of load u for both operands. K slices are summed
+// through LDS in slice order; then SiLU*up (gated) or the plain bf16 store.
 template <int NTW, int KS, int U, bool GATED>
 struct Stream {
   static constexpr int MT = kStreamMT;
@@ -145,27 +148,27 @@ struct Stream {
   static constexpr int HT = GATED ? NTW / 2 : NTW;  // output tiles per wavefront
   static constexpr int COLS = NWN * HT * 16;        // output columns per slab
   static constexpr int KSTEP = 32 * U;
+  static constexpr int RED_BYTES = KS > 1 ? KS * NWN * MT * NTW * 64 * 16 : 0;
   static_assert(!GATED || NTW % 2 == 0, "gated slabs pair gate and up tiles");
 
-  // MTA = active row tiles of this expert (1..MT): the K loop has no
-  // branches, so the only waits are on the registers an MFMA reads.
+  // MTA = active row tiles of the chunk (1..MT): the K loop has no branches,
+  // so the only waits are on the registers an MFMA reads.
   template <int MTA>
   __device__ static void run_mt(const GemmArgs& a, int e, int lo, int m, int slab, f32x4_t* red) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ks = wave % KS, wn = wave / KS;
     const int fr = lane & 15, g = lane >> 4;
+    const int col0 = (slab * NWN + wn) * HT * 16;  // first output column of this wavefront
 
-    int col[HT];
     const uint16_t* wp[NTW];
 #pragma unroll
-    for (int t = 0; t < HT; ++t) col[t] = (slab * NWN + wn) * HT * 16 + t * 16 + fr;
-#pragma unroll
     for (int t = 0; t < NTW; ++t) {
-      const int wrow = GATED ? (t < HT ? col[t] : a.inter + col[t - HT]) : col[t];
+      const int c = col0 + (t % HT) * 16 + fr;
+      const int wrow = (GATED && t >= HT) ? a.inter + c : c;
       wp[t] = a.W + ((size_t)e * a.N + wrow) * a.K + g * 8;
     }
-    // Rows past the expert's end read its first row instead: an MFMA output row
-    // depends only on its own input row, and those output rows are not stored.
+    // Rows past the chunk's end read its first row instead: an MFMA output
+    // column depends only on its own activation row, and it is not stored.
     const uint16_t* ap[MTA];
 #pragma unroll
     for (int i = 0; i < MTA; ++i) {
@@ -199,28 +202,28 @@ struct Stream {
         for (int i = 0; i < MTA; ++i)
 #pragma unroll
           for (int t = 0; t < NTW; ++t)
-            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][u], w[t][u], acc[i][t], 0, 0, 0);
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[t][u], av[i][u], acc[i][t], 0, 0, 0);
     };
 
-    // Software pipeline over K steps of KSTEP: weights two steps ahead (three
-    // register sets), activations one step ahead (two sets). In step s the
-    // loads for A(s+1) and then W(s+2) are issued before the MFMAs of step s.
-    // Loads complete in issue order, so the oldest outstanding loads are
-    // exactly W(s) and A(s): the MFMAs wait for those while W(s+1), A(s+1) and
-    // W(s+2) stay in flight. Steps past the end reload the last chunk instead
-    // of branching. The scheduling barriers keep this issue order.
+    // Software pipeline over K steps: weights two steps ahead (three register
+    // sets), activations one step ahead (two sets). In step s the loads for
+    // A(s+1) and then W(s+2) are issued before the MFMAs of step s. Loads
+    // complete in issue order, so the oldest outstanding loads are exactly
+    // W(s) and A(s): the MFMAs wait for those while W(s+1), A(s+1) and W(s+2)
+    // stay in flight. Steps past the end reload the last chunk instead of
+    // branching. The scheduling barriers keep this issue order.
     const int kw = a.K / KS, kbeg = ks * kw, klast = kbeg + kw - KSTEP;
     const int steps = kw / KSTEP;
     int kk = kbeg;
     load_w(w0, kk);
     load_a(a0, kk);
     load_w(w1, min(kk + KSTEP, klast));
-#define MOE_STEP(WC, WN, AC, AN)                    \
-  load_a(AN, min(kk + KSTEP, klast));              \
-  load_w(WN, min(kk + 2 * KSTEP, klast));          \
-  __builtin_amdgcn_sched_barrier(0);               \
-  mma(WC, AC);                                     \
-  __builtin_amdgcn_sched_barrier(0);               \
+#define MOE_STEP(WC, WN, AC, AN)           \
+  load_a(AN, min(kk + KSTEP, klast));     \
+  load_w(WN, min(kk + 2 * KSTEP, klast)); \
+  __builtin_amdgcn_sched_barrier(0);      \
+  mma(WC, AC);                            \
+  __builtin_amdgcn_sched_barrier(0);      \
   kk += KSTEP;
     for (int s = 0; s < steps; s += 6) {
       MOE_STEP(w0, w2, a0, a1)
@@ -256,20 +259,20 @@ struct Stream {
         }
       }
     }
-    // Lane holds rows 4*(lane/16) + r and column lane % 16 of every 16x16 fragment.
+    // Lane holds output row i*16 + lane % 16, columns col0 + t*16 + 4*(lane/16) + (0..3).
 #pragma unroll
     for (int i = 0; i < MTA; ++i) {
       if (KS > 1 && i % KS != ks) continue;
+      const int row = i * 16 + fr;
+      if (row >= m) continue;
+      uint16_t* crow = a.C + (size_t)(lo + row) * a.ldc + col0 + g * 4;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = i * 16 + g * 4 + r;
-        if (row >= m) continue;
-        uint16_t* crow = a.C + (size_t)(lo + row) * a.ldc;
+      for (int t = 0; t < HT; ++t) {
+        float v[4];
 #pragma unroll
-        for (int t = 0; t < HT; ++t) {
-          const float v = GATED ? silu(acc[i][t][r]) * acc[i][t + HT][r] : acc[i][t][r];
-          crow[col[t]] = (uint16_t)f32_to_bf16_bits(v);
-        }
+        for (int r = 0; r < 4; ++r)
+          v[r] = GATED ? silu(acc[i][t][r]) * acc[i][t + HT][r] : acc[i][t][r];
+        *(uint2*)(crow + t * 16) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     }
     if (KS > 1) __syncthreads();  // red is reused by the next work item
@@ -288,63 +291,35 @@ struct Stream {
   }
 };
 
-template <int NTW, int KS, int U, bool GATED>
-__global__ __launch_bounds__(256) void stream_gemm_kernel(GemmArgs a) {
-  using S = Stream<NTW, KS, U, GATED>;
-  __shared__ int s_first[kMaxLocal + 1];
-  __shared__ int t_first[kMaxLocal + 1];
-  __shared__ int wsum[8];
-  __shared__ f32x4_t red[KS > 1 ? KS * S::NWN * S::MT * NTW * 64 : 1];
-  int n_chunks, n_tiles;
-  build_lists(a, kTileBM, s_first, t_first, wsum, n_chunks, n_tiles);
-  const int slabs = (GATED ? a.inter : a.N) / S::COLS;
-  const int total = n_chunks * slabs;
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const int c = w / slabs;
-    const int e = find_expert(s_first, a.nloc, c);
-    S::run(a, e, c - s_first[e], w % slabs, red);
-  }
-}
+// ---------------------------------------------------------------- tiled path
 
-// ---------------------------------------------------------------- tiled kernel
-
-// BM x BN output tile (GEMM-1: BN/2 gate + the matching BN/2 up columns, so one
-// lane holds g and u of the same element), BK = 64, 4 wavefronts in WM x WN,
-// LDS double-buffered through registers. Persistent over (row tile, column block).
+// Experts with more than kStreamRows rows (prefill). BM x BN output tile
+// (GEMM-1: BN/2 gate + the matching BN/2 up columns, so one lane holds g and u
+// of the same element), BK = 64, 4 wavefronts in WM x WN, LDS double-buffered
+// through registers.
 template <int BM, int BN, int BK, int WM, int WN, bool GATED>
-__global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(GemmArgs a) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
-  constexpr int LDK = BK + 8;  // padded LDS row (elements): spreads rows over banks
-  constexpr int CPR = BK / 8;  // 16-byte chunks per tile row
-  constexpr int A_CH = BM * CPR / NT, B_CH = BN * CPR / NT;
-  constexpr int HALF = TN * 8;  // gate (or up) columns per wavefront in a gated tile
+struct Tiled {
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
+  static constexpr int LDK = BK + 8;  // padded LDS row (elements): spreads rows over banks
+  static constexpr int CPR = BK / 8;  // 16-byte chunks per tile row
+  static constexpr int A_CH = BM * CPR / NT, B_CH = BN * CPR / NT;
+  static constexpr int HALF = TN * 8;  // gate (or up) columns per wavefront in a gated tile
+  static constexpr int COLS = GATED ? BN / 2 : BN;  // output columns per tile
+  static constexpr int LDS_BYTES = 2 * (BM + BN) * LDK * 2;
   static_assert(A_CH * NT == BM * CPR && B_CH * NT == BN * CPR, "tile/thread mismatch");
   static_assert(!GATED || TN % 2 == 0, "gated tiles pair gate and up fragments");
-  static_assert(BM == kTileBM, "tile lists are built for kTileBM rows");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDK];
-  __shared__ int s_first[kMaxLocal + 1];
-  __shared__ int t_first[kMaxLocal + 1];
-  __shared__ int wsum[8];
-  int n_chunks, n_tiles;
-  build_lists(a, BM, s_first, t_first, wsum, n_chunks, n_tiles);
-  const int nblk = (GATED ? a.inter : a.N) / (GATED ? BN / 2 : BN);
-  const int total = n_tiles * nblk;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int fr = lane & 15, fk = (lane >> 4) * 8;
-  const int K = a.K;
-
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const int tile = w / nblk, nb = w % nblk;
-    const int e = find_expert(t_first, a.nloc, tile);
-    const int base = min(a.offsets[e], a.capacity);
-    const int row0 = base + (tile - t_first[e]) * BM;
-    const int rows = min(BM, min(a.offsets[e + 1], a.capacity) - row0);
+  __device__ static void run(const GemmArgs& a, int e, int row0, int rows, int nb, uint16_t* lds) {
+    uint16_t* As[2] = {lds, lds + BM * LDK};
+    uint16_t* Bs[2] = {lds + 2 * BM * LDK, lds + 2 * BM * LDK + BN * LDK};
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int fr = lane & 15, fk = (lane >> 4) * 8;
+    const int K = a.K;
     const uint16_t* We = a.W + (size_t)e * a.N * K;
 
+    // Rows past the tile's end read its first row (their outputs are not stored).
     const uint16_t* aptr[A_CH];
     int a_kc[A_CH], b_kc[B_CH];
     const uint16_t* bptr[B_CH];
@@ -352,7 +327,7 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(GemmArgs a) {
     for (int i = 0; i < A_CH; ++i) {
       const int c = tid + i * NT, r = c / CPR;
       a_kc[i] = (c % CPR) * 8;
-      aptr[i] = r < rows ? a_row_ptr(a, row0 + r) : nullptr;
+      aptr[i] = a_row_ptr(a, row0 + (r < rows ? r : 0));
     }
 #pragma unroll
     for (int i = 0; i < B_CH; ++i) {
@@ -369,20 +344,18 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(GemmArgs a) {
     }
 
     u32x4_t ra[A_CH], rb[B_CH];
-#define MOE_GLOAD(k0)                                                                   \
-  do {                                                                                  \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) ra[i] =                            \
-        aptr[i] ? *(const u32x4_t*)(aptr[i] + (k0) + a_kc[i]) : u32x4_t{0u, 0u, 0u, 0u}; \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) rb[i] =                            \
-        *(const u32x4_t*)(bptr[i] + (k0) + b_kc[i]);                                    \
-  } while (0)
-#define MOE_SSTORE(buf)                                                                           \
-  do {                                                                                            \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i)                                              \
-        *(u32x4_t*)&As[buf][(tid + i * NT) / CPR * LDK + a_kc[i]] = ra[i];                        \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i)                                              \
-        *(u32x4_t*)&Bs[buf][(tid + i * NT) / CPR * LDK + b_kc[i]] = rb[i];                        \
-  } while (0)
+    auto gload = [&](int k0) {
+#pragma unroll
+      for (int i = 0; i < A_CH; ++i) ra[i] = *(const u32x4_t*)(aptr[i] + k0 + a_kc[i]);
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) rb[i] = *(const u32x4_t*)(bptr[i] + k0 + b_kc[i]);
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < A_CH; ++i) *(u32x4_t*)&As[buf][(tid + i * NT) / CPR * LDK + a_kc[i]] = ra[i];
+#pragma unroll
+      for (int i = 0; i < B_CH; ++i) *(u32x4_t*)&Bs[buf][(tid + i * NT) / CPR * LDK + b_kc[i]] = rb[i];
+    };
 
     f32x4_t acc[TM][TN];
 #pragma unroll
@@ -391,33 +364,32 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(GemmArgs a) {
       for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     const int nk = K / BK;
-    MOE_GLOAD(0);
-    MOE_SSTORE(0);
+    gload(0);
+    sstore(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       const int buf = kt & 1;
-      if (kt + 1 < nk) MOE_GLOAD((kt + 1) * BK);
+      if (kt + 1 < nk) gload((kt + 1) * BK);
 #pragma unroll
-      for (int ks = 0; ks < BK / 32; ++ks) {
+      for (int kq = 0; kq < BK / 32; ++kq) {
         bf16x8_t av[TM], bv[TN];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          av[i] = *(const bf16x8_t*)&As[buf][(wm * TM * 16 + i * 16 + fr) * LDK + ks * 32 + fk];
+          av[i] = *(const bf16x8_t*)&As[buf][(wm * TM * 16 + i * 16 + fr) * LDK + kq * 32 + fk];
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          bv[j] = *(const bf16x8_t*)&Bs[buf][(wn * TN * 16 + j * 16 + fr) * LDK + ks * 32 + fk];
+          bv[j] = *(const bf16x8_t*)&Bs[buf][(wn * TN * 16 + j * 16 + fr) * LDK + kq * 32 + fk];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
       }
-      if (kt + 1 < nk) MOE_SSTORE(buf ^ 1);
+      if (kt + 1 < nk) sstore(buf ^ 1);
       __syncthreads();
     }
-#undef MOE_GLOAD
-#undef MOE_SSTORE
 
+    // Lane holds rows 4*(lane/16) + r, column lane % 16 of each 16x16 fragment.
     const int rq = (lane >> 4) * 4;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -440,6 +412,41 @@ __global__ __launch_bounds__(WM * WN * 64) void tiled_gemm_kernel(GemmArgs a) {
             crow[n0 + j * 16 + fr] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
         }
       }
+    }
+  }
+};
+
+// ---------------------------------------------------------------- the GEMM kernel
+
+// One persistent kernel per GEMM: first the streamed row chunks, then the row
+// tiles of larger experts. The two paths share the LDS buffer.
+template <int NTW, int KS, int U, bool GATED>
+__global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(GemmArgs a) {
+  using S = Stream<NTW, KS, U, GATED>;
+  using T = Tiled<kTileBM, 128, 64, 2, 2, GATED>;
+  constexpr int SMEM = S::RED_BYTES > T::LDS_BYTES ? S::RED_BYTES : T::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  __shared__ int s_first[kMaxLocal + 1];
+  __shared__ int t_first[kMaxLocal + 1];
+  __shared__ int wsum[8];
+  int n_chunks, n_tiles;
+  build_lists(a, kTileBM, s_first, t_first, wsum, n_chunks, n_tiles);
+  const int ncols = GATED ? a.inter : a.N;
+  const int slabs = ncols / S::COLS, nblk = ncols / T::COLS;
+  const int n_stream = n_chunks * slabs;
+  const int total = n_stream + n_tiles * nblk;
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    if (w < n_stream) {
+      const int c = w / slabs;
+      const int e = find_expert(s_first, a.nloc, c);
+      S::run(a, e, c - s_first[e], w % slabs, (f32x4_t*)smem);
+    } else {
+      const int tile = (w - n_stream) / nblk, nb = (w - n_stream) % nblk;
+      const int e = find_expert(t_first, a.nloc, tile);
+      const int row0 = min(a.offsets[e], a.capacity) + (tile - t_first[e]) * kTileBM;
+      const int rows = min(kTileBM, min(a.offsets[e + 1], a.capacity) - row0);
+      T::run(a, e, row0, rows, nb, (uint16_t*)smem);
+      __syncthreads();  // the LDS buffer is reused by the next work item
     }
   }
 }
@@ -523,56 +530,43 @@ int occupancy(F kernel, int threads) {
   return n;
 }
 
-// K split across the 4 wavefronts (KS) and K step unroll (U) of the streaming
-// kernel: at least 8 K steps per wavefront when K allows, K a multiple of KS * 32 * U.
-struct StreamShape {
-  int ks, u;
-};
-StreamShape stream_shape(int K) {
-  for (int ks : {4, 2, 1})
-    for (int u : {2, 1})
-      if (K % (ks * 32 * u) == 0 && (K / ks >= 256 || ks == 1)) return {ks, u};
-  return {0, 0};
+// Shape of the streaming path per GEMM:
+//   gate_up (gated): NTW = 2 (a gate and the matching up tile), U = 2
+//   down (plain):    NTW = 4, U = 1
+// and KS, the K slices of a workgroup: 4 when every slice still has at least
+// 8 K steps, else 2 (gated: K = hidden is a multiple of 256), else 1.
+template <bool GATED>
+int stream_ks(int K) {
+  constexpr int U = GATED ? 2 : 1;
+  if (K % (4 * 32 * U) == 0 && K / 4 >= 8 * 32 * U) return 4;
+  if (GATED || (K % (2 * 32 * U) == 0 && K / 2 >= 4 * 32 * U)) return 2;
+  return 1;
 }
 
-template <bool GATED, int KS, int U>
-void launch_stream_t(const GemmArgs& g, hipStream_t s) {
-  constexpr int NTW = 2;
+template <bool GATED, int KS>
+hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s) {
+  constexpr int NTW = GATED ? 2 : 4, U = GATED ? 2 : 1;
   using S = Stream<NTW, KS, U, GATED>;
-  static const int occ = occupancy(stream_gemm_kernel<NTW, KS, U, GATED>, 256);
-  const int slabs = (GATED ? g.inter : g.N) / S::COLS;
+  using T = Tiled<kTileBM, 128, 64, 2, 2, GATED>;
+  auto kernel = ffn_gemm_kernel<NTW, KS, U, GATED>;
+  static const int occ = occupancy(kernel, 256);
+  const int ncols = GATED ? g.inter : g.N;
   const long max_chunks = std::min<long>((long)g.nloc * (kStreamRows / kChunkRows),
                                          (long)(g.capacity + kChunkRows - 1) / kChunkRows + g.nloc);
-  const long max_work = max_chunks * slabs;
-  const int grid = (int)std::max<long>(1, std::min<long>(max_work, (long)cu_count() * occ));
-  hipLaunchKernelGGL((stream_gemm_kernel<NTW, KS, U, GATED>), dim3(grid), dim3(256), 0, s, g);
-}
-
-template <bool GATED>
-hipError_t launch_stream(const GemmArgs& g, hipStream_t s) {
-  const StreamShape sh = stream_shape(g.K);
-#define MOE_STREAM(KS_, U_)                        \
-  if (sh.ks == KS_ && sh.u == U_) {                \
-    launch_stream_t<GATED, KS_, U_>(g, s);         \
-    return hipGetLastError();                      \
-  }
-  MOE_STREAM(4, 4) MOE_STREAM(4, 2) MOE_STREAM(4, 1)
-  MOE_STREAM(2, 4) MOE_STREAM(2, 2) MOE_STREAM(2, 1)
-  MOE_STREAM(1, 4) MOE_STREAM(1, 2) MOE_STREAM(1, 1)
-#undef MOE_STREAM
-  return hipErrorInvalidValue;
-}
-
-template <bool GATED>
-hipError_t launch_tiled(const GemmArgs& g, hipStream_t s) {
-  constexpr int BM = kTileBM, BN = 128, BK = 64;
-  auto kernel = tiled_gemm_kernel<BM, BN, BK, 2, 2, GATED>;
-  static const int occ = occupancy(kernel, 256);
-  const int nblk = (GATED ? g.inter : g.N) / (GATED ? BN / 2 : BN);
-  const long max_work = ((long)(g.capacity + BM - 1) / BM + g.nloc) * nblk;
+  const long max_tiles = (long)(g.capacity + kTileBM - 1) / kTileBM + g.nloc;
+  const long max_work = max_chunks * (ncols / S::COLS) + max_tiles * (ncols / T::COLS);
   const int grid = (int)std::max<long>(1, std::min<long>(max_work, (long)cu_count() * occ));
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, g);
   return hipGetLastError();
+}
+
+template <bool GATED>
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  switch (stream_ks<GATED>(g.K)) {
+    case 4: return launch_gemm_t<GATED, 4>(g, s);
+    case 2: return launch_gemm_t<GATED, 2>(g, s);
+    default: return GATED ? hipErrorInvalidValue : launch_gemm_t<false, 1>(g, s);
+  }
 }
 
 }  // namespace
@@ -592,11 +586,9 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
                 (uint16_t*)a.workspace, I};
     GemmArgs g2{(const uint16_t*)a.workspace, nullptr, 1, a.offsets, a.num_local, a.capacity,
                 (const uint16_t*)a.w_down, d, I, I, (uint16_t*)a.o_sorted, d};
-    hipError_t err;
-    if ((err = launch_stream<true>(g1, s)) != hipSuccess) return err;
-    if ((err = launch_tiled<true>(g1, s)) != hipSuccess) return err;
-    if ((err = launch_stream<false>(g2, s)) != hipSuccess) return err;
-    return launch_tiled<false>(g2, s);
+    const hipError_t err = launch_gemm<true>(g1, s);
+    if (err != hipSuccess) return err;
+    return launch_gemm<false>(g2, s);
   }
   const int mrt = (a.capacity + 15) / 16;
   GemmArgsF32 g1{(const float*)a.x, a.row_index, a.row_div, a.offsets, a.num_local, a.capacity,
