@@ -42,7 +42,21 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copies", type=int, default=0,
                    help="weight copies rotated over the timed steps (0 = enough to exceed the cache)")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                   help="only run a plain device-to-device copy of MB megabytes, 5 times "
+                        "(the known-size reference for hardware byte counters)")
     return p.parse_args()
+
+
+def calibrate_copy(mb, torch):
+    n = mb * 1000 * 1000
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
 
 
 def ffn_accounting(wl, counts):
@@ -178,6 +192,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, torch)
+        return
     moe.lib()
 
     wl = W.WORKLOADS[args.workload]

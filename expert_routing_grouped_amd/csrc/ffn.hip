@@ -19,8 +19,8 @@
 //   chunks. Bound by the weight read: weight bytes go from HBM straight into
 //   MFMA registers, with the next two K steps' loads in flight during the
 //   current MFMAs.
-// * tiled path -- experts with more rows (prefill): LDS-staged 16x16x32 bf16
-//   MFMA tiles that reuse each weight tile across 64 rows.
+// * tiled path -- experts with more rows (prefill): 128 x 128 tiles staged
+//   through LDS on 32x32x16 bf16 MFMA.
 // Experts with no rows appear in neither list, so their weights are not read.
 #include <hip/hip_runtime.h>
 
@@ -36,7 +36,7 @@ namespace {
 constexpr int kStreamMT = 4;                  // row tiles of 16 per streamed row chunk
 constexpr int kChunkRows = kStreamMT * 16;    // rows per streamed chunk
 constexpr int kStreamRows = 4 * kChunkRows;   // experts with more rows are tiled
-constexpr int kTileBM = 64;                   // rows per tile in the tiled path
+constexpr int kTileBM = 128;                  // tokens per tile in the tiled path
 constexpr int kMaxLocal = 1024;
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
@@ -293,124 +293,142 @@ struct Stream {
 
 // ---------------------------------------------------------------- tiled path
 
-// Experts with more than kStreamRows rows (prefill). BM x BN output tile
-// (GEMM-1: BN/2 gate + the matching BN/2 up columns, so one lane holds g and u
-// of the same element), BK = 64, 4 wavefronts in WM x WN, LDS double-buffered
-// through registers.
-template <int BM, int BN, int BK, int WM, int WN, bool GATED>
+// Experts with more than kStreamRows rows (prefill): 128 weight rows x 128
+// tokens per tile, K staged through LDS 64 at a time (double-buffered through
+// registers), 4 wavefronts of 64 x 64 on v_mfma_f32_32x32x16_bf16 with
+// float32 accumulators.
+//
+// The weight tile is the MFMA A operand (rows = output columns) and the token
+// tile the B operand; a lane's 16 accumulators of a fragment are 4 runs of 4
+// consecutive output columns of one token row (8-byte stores). A gated tile
+// holds 64 gate rows and the 64 matching up rows, arranged so that fragment 0
+// (gate) and fragment 1 (up) of a wavefront cover the same output columns.
+//
+// LDS rows are 64 bf16 (eight 16-byte chunks); chunk c of row r is stored at
+// c ^ (r & 7), so the 32 rows one fragment read touches at one k are spread
+// over the banks.
+constexpr int kTileBN = 128;  // weight rows per tile
+constexpr int kTileBK = 64;
+
+template <bool GATED>
 struct Tiled {
-  static constexpr int NT = WM * WN * 64;
-  static constexpr int TM = BM / WM / 16, TN = BN / WN / 16;
-  static constexpr int LDK = BK + 8;  // padded LDS row (elements): spreads rows over banks
-  static constexpr int CPR = BK / 8;  // 16-byte chunks per tile row
-  static constexpr int A_CH = BM * CPR / NT, B_CH = BN * CPR / NT;
-  static constexpr int HALF = TN * 8;  // gate (or up) columns per wavefront in a gated tile
-  static constexpr int COLS = GATED ? BN / 2 : BN;  // output columns per tile
-  static constexpr int LDS_BYTES = 2 * (BM + BN) * LDK * 2;
-  static_assert(A_CH * NT == BM * CPR && B_CH * NT == BN * CPR, "tile/thread mismatch");
-  static_assert(!GATED || TN % 2 == 0, "gated tiles pair gate and up fragments");
+  static constexpr int COLS = GATED ? kTileBN / 2 : kTileBN;  // output columns per tile
+  static constexpr int TILE = kTileBN * kTileBK;               // elements per operand tile
+  static constexpr int LDS_BYTES = 2 * 2 * TILE * 2;           // [buffer][W | X], bf16
+  static_assert(kTileBM == 128, "the tile holds 128 tokens");
+
+  __device__ static __forceinline__ int swz(int row, int chunk) {
+    return row * kTileBK + ((chunk ^ (row & 7)) << 3);
+  }
 
   __device__ static void run(const GemmArgs& a, int e, int row0, int rows, int nb, uint16_t* lds) {
-    uint16_t* As[2] = {lds, lds + BM * LDK};
-    uint16_t* Bs[2] = {lds + 2 * BM * LDK, lds + 2 * BM * LDK + BN * LDK};
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WN, wn = wave % WN;
-    const int fr = lane & 15, fk = (lane >> 4) * 8;
+    const int wm = wave >> 1, wn = wave & 1;  // wavefront: weight rows wm*64.., tokens wn*64..
     const int K = a.K;
-    const uint16_t* We = a.W + (size_t)e * a.N * K;
+    const int kc = tid & 7;                   // 16-byte chunk this thread loads in every row
+    const int rbase = tid >> 3;               // tile rows rbase + 32 i, i = 0..3
 
-    // Rows past the tile's end read its first row (their outputs are not stored).
-    const uint16_t* aptr[A_CH];
-    int a_kc[A_CH], b_kc[B_CH];
-    const uint16_t* bptr[B_CH];
+    // This thread's weight rows are wrow0 + woff[i]; its token rows are tok[i]
+    // (rows past the tile's end read its first row; their outputs are not stored).
+    int wrow0, woff[4];
+    if (GATED) {
+      // tile rows: [gate 32 | up 32] for wavefront row group 0, then for group 1
+      wrow0 = nb * COLS + rbase;
+      woff[0] = 0;
+      woff[1] = a.inter;
+      woff[2] = 32;
+      woff[3] = a.inter + 32;
+    } else {
+      wrow0 = nb * kTileBN + rbase;
 #pragma unroll
-    for (int i = 0; i < A_CH; ++i) {
-      const int c = tid + i * NT, r = c / CPR;
-      a_kc[i] = (c % CPR) * 8;
-      aptr[i] = a_row_ptr(a, row0 + (r < rows ? r : 0));
+      for (int i = 0; i < 4; ++i) woff[i] = 32 * i;
     }
+    const uint16_t* wsrc = a.W + ((size_t)e * a.N + wrow0) * K + kc * 8;
+    int tok[4];
 #pragma unroll
-    for (int i = 0; i < B_CH; ++i) {
-      const int c = tid + i * NT, r = c / CPR;
-      b_kc[i] = (c % CPR) * 8;
-      int wrow;
-      if (GATED) {
-        const int ww = r / (TN * 16), rem = r % (TN * 16), n0 = nb * (BN / 2);
-        wrow = rem < HALF ? n0 + ww * HALF + rem : a.inter + n0 + ww * HALF + rem - HALF;
-      } else {
-        wrow = nb * BN + r;
-      }
-      bptr[i] = We + (size_t)wrow * K;
+    for (int i = 0; i < 4; ++i) {
+      const int r = rbase + 32 * i;
+      const int row = row0 + (r < rows ? r : 0);
+      tok[i] = a.row_index ? a.row_index[row] / a.row_div : row;
     }
+    const uint16_t* xsrc = a.A + kc * 8;
 
-    u32x4_t ra[A_CH], rb[B_CH];
+    u32x4_t sw[4], sx[4];
     auto gload = [&](int k0) {
 #pragma unroll
-      for (int i = 0; i < A_CH; ++i) ra[i] = *(const u32x4_t*)(aptr[i] + k0 + a_kc[i]);
+      for (int i = 0; i < 4; ++i) sw[i] = *(const u32x4_t*)(wsrc + (size_t)woff[i] * K + k0);
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) rb[i] = *(const u32x4_t*)(bptr[i] + k0 + b_kc[i]);
+      for (int i = 0; i < 4; ++i) sx[i] = *(const u32x4_t*)(xsrc + (size_t)tok[i] * K + k0);
     };
     auto sstore = [&](int buf) {
+      uint16_t* lw = lds + buf * 2 * TILE;
+      uint16_t* lx = lw + TILE;
 #pragma unroll
-      for (int i = 0; i < A_CH; ++i) *(u32x4_t*)&As[buf][(tid + i * NT) / CPR * LDK + a_kc[i]] = ra[i];
+      for (int i = 0; i < 4; ++i) *(u32x4_t*)(lw + swz(rbase + 32 * i, kc)) = sw[i];
 #pragma unroll
-      for (int i = 0; i < B_CH; ++i) *(u32x4_t*)&Bs[buf][(tid + i * NT) / CPR * LDK + b_kc[i]] = rb[i];
+      for (int i = 0; i < 4; ++i) *(u32x4_t*)(lx + swz(rbase + 32 * i, kc)) = sx[i];
     };
 
-    f32x4_t acc[TM][TN];
+    f32x16_t acc[2][2];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
-    const int nk = K / BK;
+    const int fr = lane & 31, fh = lane >> 5;  // fragment row, k half (8 of 16)
+    const int nk = K / kTileBK;
     gload(0);
     sstore(0);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       const int buf = kt & 1;
-      if (kt + 1 < nk) gload((kt + 1) * BK);
+      if (kt + 1 < nk) gload((kt + 1) * kTileBK);
+      const uint16_t* lw = lds + buf * 2 * TILE;
+      const uint16_t* lx = lw + TILE;
 #pragma unroll
-      for (int kq = 0; kq < BK / 32; ++kq) {
-        bf16x8_t av[TM], bv[TN];
+      for (int kq = 0; kq < kTileBK / 16; ++kq) {
+        const int chunk = kq * 2 + fh;
+        bf16x8_t av[2], bv[2];
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
-          av[i] = *(const bf16x8_t*)&As[buf][(wm * TM * 16 + i * 16 + fr) * LDK + kq * 32 + fk];
+        for (int i = 0; i < 2; ++i) av[i] = *(const bf16x8_t*)(lw + swz(wm * 64 + i * 32 + fr, chunk));
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-          bv[j] = *(const bf16x8_t*)&Bs[buf][(wn * TN * 16 + j * 16 + fr) * LDK + kq * 32 + fk];
+        for (int j = 0; j < 2; ++j) bv[j] = *(const bf16x8_t*)(lx + swz(wn * 64 + j * 32 + fr, chunk));
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
       }
       if (kt + 1 < nk) sstore(buf ^ 1);
       __syncthreads();
     }
 
-    // Lane holds rows 4*(lane/16) + r, column lane % 16 of each 16x16 fragment.
-    const int rq = (lane >> 4) * 4;
+    // acc[i][j][r]: token wn*64 + j*32 + lane%32; weight tile row
+    // wm*64 + i*32 + (r/4)*8 + (lane/32)*4 + r%4.
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int j = 0; j < 2; ++j) {
+      const int t = wn * 64 + j * 32 + fr;
+      if (t >= rows) continue;
+      uint16_t* crow = a.C + (size_t)(row0 + t) * a.ldc;
+      if (GATED) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wm * TM * 16 + i * 16 + rq + r;
-        if (row >= rows) continue;
-        uint16_t* crow = a.C + (size_t)(row0 + row) * a.ldc;
-        if (GATED) {
-          const int n0 = nb * (BN / 2) + wn * HALF;
+        for (int q = 0; q < 4; ++q) {
+          const int col = nb * COLS + wm * 32 + q * 8 + fh * 4;
+          float v[4];
 #pragma unroll
-          for (int j = 0; j < TN / 2; ++j) {
-            const float gv = acc[i][j][r], uv = acc[i][j + TN / 2][r];
-            crow[n0 + j * 16 + fr] = (uint16_t)f32_to_bf16_bits(silu(gv) * uv);
-          }
-        } else {
-          const int n0 = nb * BN + wn * TN * 16;
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            crow[n0 + j * 16 + fr] = (uint16_t)f32_to_bf16_bits(acc[i][j][r]);
+          for (int r = 0; r < 4; ++r) v[r] = silu(acc[0][j][q * 4 + r]) * acc[1][j][q * 4 + r];
+          *(uint2*)(crow + col) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = nb * COLS + wm * 64 + i * 32 + q * 8 + fh * 4;
+            const f32x16_t& c = acc[i][j];
+            *(uint2*)(crow + col) = make_uint2(pack_bf16x2(c[q * 4], c[q * 4 + 1]),
+                                               pack_bf16x2(c[q * 4 + 2], c[q * 4 + 3]));
+          }
       }
     }
   }
@@ -423,7 +441,7 @@ struct Tiled {
 template <int NTW, int KS, int U, bool GATED>
 __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(GemmArgs a) {
   using S = Stream<NTW, KS, U, GATED>;
-  using T = Tiled<kTileBM, 128, 64, 2, 2, GATED>;
+  using T = Tiled<GATED>;
   constexpr int SMEM = S::RED_BYTES > T::LDS_BYTES ? S::RED_BYTES : T::LDS_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ int s_first[kMaxLocal + 1];
@@ -547,7 +565,7 @@ template <bool GATED, int KS>
 hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s) {
   constexpr int NTW = GATED ? 2 : 4, U = GATED ? 2 : 1;
   using S = Stream<NTW, KS, U, GATED>;
-  using T = Tiled<kTileBM, 128, 64, 2, 2, GATED>;
+  using T = Tiled<GATED>;
   auto kernel = ffn_gemm_kernel<NTW, KS, U, GATED>;
   static const int occ = occupancy(kernel, 256);
   const int ncols = GATED ? g.inter : g.N;
