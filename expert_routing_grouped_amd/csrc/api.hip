@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -54,11 +54,19 @@ moe_status_t moe_route(const float* scores, int32_t num_tokens, int32_t num_expe
   return from_hip(moe::launch_route(a, stream));
 }
 
+size_t moe_dispatch_workspace_size(int32_t num_tokens, int32_t top_k, int32_t num_local_experts) {
+  if (num_tokens < 0 || top_k < 1 || num_local_experts < 1) return 0;
+  const int64_t n = (int64_t)num_tokens * top_k;
+  if (n >= ((int64_t)1 << 31) - 65536) return 0;
+  return moe::dispatch_workspace_size((int)n, num_local_experts);
+}
+
 moe_status_t moe_dispatch(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
                           int32_t expert_begin, int32_t num_local_experts, const void* x,
                           int32_t hidden, int32_t dtype, int32_t* expert_counts,
                           int32_t* expert_offsets, int32_t* sorted_assign, int32_t* assign_pos,
-                          void* x_sorted, hipStream_t stream) {
+                          void* x_sorted, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
   if (num_tokens < 0 || top_k < 1 || expert_begin < 0 || num_local_experts < 1)
     return MOE_ERR_INVALID;
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
@@ -76,8 +84,12 @@ moe_status_t moe_dispatch(const int32_t* topk_ids, int32_t num_tokens, int32_t t
     if (rb > (1 << 30)) return MOE_ERR_UNSUPPORTED;
     row_bytes = (int)rb;
   }
+  const size_t need = moe::dispatch_workspace_size((int)n, num_local_experts);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return MOE_ERR_WORKSPACE;
   moe::DispatchArgs a{topk_ids, (int)n, top_k, expert_begin, num_local_experts, expert_counts,
-                      expert_offsets, sorted_assign, assign_pos, x, x_sorted, row_bytes};
+                      expert_offsets, sorted_assign, assign_pos, x, x_sorted, row_bytes,
+                      workspace};
   return from_hip(moe::launch_dispatch(a, stream));
 }
 

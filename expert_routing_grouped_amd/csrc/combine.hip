@@ -43,9 +43,10 @@ __device__ __forceinline__ void store8(void* base, size_t elem, const float (&v)
 }
 
 // Workgroup = 4 wavefronts on one token; wavefront = 512 consecutive
-// elements (8 per lane). The k slot positions and weights are read once per
-// wavefront (lane j holds slot j) and broadcast; the k row loads are
-// independent, so all of them are in flight together.
+// elements (8 per lane). The token's slot positions and weights are read once
+// (lane j holds slot j); a ballot lists the slots whose expert is local, and
+// their rows are loaded four at a time (all four in flight) and added in slot
+// order. Non-local slots cost nothing.
 template <bool O_BF16, bool Y_BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o,
                                                       const int* __restrict__ assign_pos,
@@ -57,16 +58,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o
   if (c0 >= hidden) return;  // uniform per wave
   const int c = c0 + lane * 8;
   const bool active = c < hidden;
+  const int cc = active ? c : 0;
   const int mypos = lane < k ? assign_pos[(size_t)t * k + lane] : -1;
   const float myw = lane < k ? weights[(size_t)t * k + lane] : 0.0f;
+  uint64_t local = __ballot(mypos >= 0);  // slot j's bit is bit j
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const int p = __shfl(mypos, j, MOE_WAVE);
-    const float wj = __shfl(myw, j, MOE_WAVE);
-    float v[8];
-    load8<O_BF16>(o, (size_t)(p >= 0 ? p : 0) * hidden + (active ? c : 0), v);
+  while (local) {
+    int p[4];
+    float w[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += p >= 0 ? wj * v[i] : 0.0f;
+    for (int q = 0; q < 4; ++q) {
+      p[q] = -1;
+      w[q] = 0.0f;
+      if (local) {
+        const int j = __ffsll((unsigned long long)local) - 1;
+        local &= local - 1;
+        p[q] = __builtin_amdgcn_readlane(mypos, j);
+        w[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(myw), j));
+      }
+    }
+    float v[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load8<O_BF16>(o, (size_t)(p[q] >= 0 ? p[q] : p[0]) * hidden + cc, v[q]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (p[q] >= 0)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += w[q] * v[q][i];
   }
   if (active) store8<Y_BF16>(y, (size_t)t * hidden + c, acc);
 }

@@ -23,6 +23,7 @@ namespace moe {
 namespace {
 
 constexpr int kSortWaves = 16;
+constexpr int kSingleBlockMax = 8192;  // larger T*k uses the multi-workgroup sort
 
 // Bitmask of the lanes whose key equals this lane's key (only among active lanes).
 __device__ __forceinline__ uint64_t match_key(int key, bool active, int nbits) {
@@ -45,6 +46,162 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// Counts one wavefront's assignments [lo, hi) per local expert into my_cnt
+// (this wavefront's LDS row). The lowest lane of each group of equal keys adds
+// the group's size, so no two lanes write the same counter.
+__device__ __forceinline__ void wave_count(const int* __restrict__ ids, int lo, int hi, int begin,
+                                           int nloc, int nbits, int* my_cnt) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  for (int base = lo; base < hi; base += 64) {
+    const int a = base + lane;
+    int e = -1;
+    if (a < hi) {
+      const int x = ids[a] - begin;
+      if ((unsigned)x < (unsigned)nloc) e = x;
+    }
+    const uint64_t peers = match_key(e, e >= 0, nbits);
+    if (e >= 0 && (peers & lt_mask) == 0ull) my_cnt[e] += __popcll(peers);
+  }
+}
+
+// Writes one wavefront's assignments [lo, hi) in order: assignment a with
+// local expert e goes to my_base[e] + (earlier assignments of e in this
+// wavefront's range). Non-local assignments get assign_pos = -1.
+__device__ __forceinline__ void wave_scatter(const int* __restrict__ ids, int lo, int hi, int begin,
+                                             int nloc, int nbits, int* my_base,
+                                             int* __restrict__ sorted_assign,
+                                             int* __restrict__ assign_pos) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  for (int base = lo; base < hi; base += 64) {
+    const int a = base + lane;
+    int e = -1;
+    if (a < hi) {
+      const int x = ids[a] - begin;
+      if ((unsigned)x < (unsigned)nloc) e = x;
+    }
+    const uint64_t peers = match_key(e, e >= 0, nbits);
+    if (a < hi) {
+      if (e >= 0) {
+        const int p = my_base[e] + __popcll(peers & lt_mask);
+        sorted_assign[p] = a;
+        assign_pos[a] = p;
+      } else {
+        assign_pos[a] = -1;
+      }
+    }
+    // LDS operations of one wave execute in order: every lane has read the
+    // running base above before the leader advances it here.
+    if (e >= 0 && (peers & lt_mask) == 0ull) my_base[e] += __popcll(peers);
+  }
+}
+
+// ---- multi-workgroup sort (large T*k): block b owns assignments
+// [b*per_block, (b+1)*per_block), wavefront w a quarter of that. per_block is
+// 2048 until the block count reaches kMaxBlocks, then grows, so every block's
+// pass over the per-block counts stays short.
+constexpr int kBlkWaves = 4;
+constexpr int kBlkElems = kBlkWaves * 512;
+constexpr int kMaxBlocks = 256;
+
+__host__ __device__ inline int sort_blocks(int n) {
+  const int b = (n + kBlkElems - 1) / kBlkElems;
+  return b < kMaxBlocks ? b : kMaxBlocks;
+}
+// Assignments per block: a multiple of 256 so each wavefront's quarter is a
+// whole number of 64-lane steps.
+__host__ __device__ inline int sort_per_block(int n) {
+  const int b = sort_blocks(n);
+  const long per = ((long)n + b - 1) / b;
+  return (int)((per + 255) & ~255L);
+}
+
+// Pass 1: per-block counts per local expert -> ws[b * nloc + e].
+__global__ __launch_bounds__(256) void block_count_kernel(const int* __restrict__ ids, int n,
+                                                          int per_block, int begin, int nloc,
+                                                          int nbits, int* __restrict__ ws) {
+  extern __shared__ int lds[];
+  int* cnt = lds;  // [kBlkWaves][nloc]
+  const int w = threadIdx.x >> 6, b = blockIdx.x;
+  for (int i = threadIdx.x; i < kBlkWaves * nloc; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  const int per_wave = per_block / kBlkWaves;
+  const int lo = (int)min((long)n, (long)b * per_block + (long)w * per_wave);
+  const int hi = (int)min((long)n, (long)lo + per_wave);
+  wave_count(ids, lo, hi, begin, nloc, nbits, cnt + w * nloc);
+  __syncthreads();
+  for (int e = threadIdx.x; e < nloc; e += blockDim.x) {
+    int c = 0;
+    for (int ww = 0; ww < kBlkWaves; ++ww) c += cnt[ww * nloc + e];
+    ws[b * nloc + e] = c;
+  }
+}
+
+// Pass 2: every block derives the expert offsets and its own start per expert
+// from the per-block counts (same sums in every block), recounts its
+// wavefronts, then scatters. Block 0 also writes counts and offsets.
+__global__ __launch_bounds__(256) void block_scatter_kernel(
+    const int* __restrict__ ids, int n, int per_block, int begin, int nloc, int nbits,
+    const int* __restrict__ ws, int nblocks, int* __restrict__ counts, int* __restrict__ offsets,
+    int* __restrict__ sorted_assign, int* __restrict__ assign_pos) {
+  extern __shared__ int lds[];
+  int* cnt = lds;                          // [kBlkWaves][nloc]
+  int* wsum = lds + kBlkWaves * nloc;      // [4]
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, b = blockIdx.x;
+  for (int i = tid; i < kBlkWaves * nloc; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  const int per_wave = per_block / kBlkWaves;
+  const int lo = (int)min((long)n, (long)b * per_block + (long)w * per_wave);
+  const int hi = (int)min((long)n, (long)lo + per_wave);
+  wave_count(ids, lo, hi, begin, nloc, nbits, cnt + w * nloc);
+
+  // totals and this block's preceding counts for experts tid*4 .. tid*4+3
+  int tot[4], before[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    tot[q] = 0;
+    before[q] = 0;
+    if (e < nloc) {
+      for (int bb = 0; bb < nblocks; ++bb) {
+        const int c = ws[bb * nloc + e];
+        tot[q] += c;
+        if (bb < b) before[q] += c;
+      }
+    }
+    sum += tot[q];
+  }
+  const int incl = wave_inclusive_scan(sum);
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();  // also orders the recount above before the reads below
+  int run = incl - sum;
+  for (int i = 0; i < w; ++i) run += wsum[i];
+  int total = 0;
+  for (int i = 0; i < 4; ++i) total += wsum[i];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    if (e < nloc) {
+      if (b == 0) {
+        counts[e] = tot[q];
+        offsets[e] = run;
+      }
+      // wave bases: block start + counts of the block's earlier wavefronts
+      int s = run + before[q];
+      for (int ww = 0; ww < kBlkWaves; ++ww) {
+        const int c = cnt[ww * nloc + e];
+        cnt[ww * nloc + e] = s;
+        s += c;
+      }
+    }
+    run += tot[q];
+  }
+  if (b == 0 && tid == 0) offsets[nloc] = total;
+  __syncthreads();
+  wave_scatter(ids, lo, hi, begin, nloc, nbits, cnt + w * nloc, sorted_assign, assign_pos);
+}
+
 __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids, int n, int begin,
                                                     int nloc, int nbits, int* __restrict__ counts,
                                                     int* __restrict__ offsets,
@@ -59,20 +216,10 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids,
 
   const int per_wave = (((n + kSortWaves - 1) / kSortWaves) + 63) & ~63;
   const int lo = min(n, w * per_wave), hi = min(n, lo + per_wave);
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
   int* my_cnt = cnt + w * nloc;
 
   // pass 1: counts per (wave, expert)
-  for (int base = lo; base < hi; base += 64) {
-    const int a = base + lane;
-    int e = -1;
-    if (a < hi) {
-      const int x = ids[a] - begin;
-      if ((unsigned)x < (unsigned)nloc) e = x;
-    }
-    const uint64_t peers = match_key(e, e >= 0, nbits);
-    if (e >= 0 && (peers & lt_mask) == 0ull) my_cnt[e] += __popcll(peers);
-  }
+  wave_count(ids, lo, hi, begin, nloc, nbits, my_cnt);
   __syncthreads();
 
   // scan: per-expert column prefix over waves, then exclusive scan over experts
@@ -106,27 +253,7 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids,
   __syncthreads();
 
   // pass 2: scatter in chunk order
-  for (int base = lo; base < hi; base += 64) {
-    const int a = base + lane;
-    int e = -1;
-    if (a < hi) {
-      const int x = ids[a] - begin;
-      if ((unsigned)x < (unsigned)nloc) e = x;
-    }
-    const uint64_t peers = match_key(e, e >= 0, nbits);
-    if (a < hi) {
-      if (e >= 0) {
-        const int p = my_cnt[e] + __popcll(peers & lt_mask);
-        sorted_assign[p] = a;
-        assign_pos[a] = p;
-      } else {
-        assign_pos[a] = -1;
-      }
-    }
-    // LDS operations of one wave execute in order: every lane has read the
-    // running count above before the leader advances it here.
-    if (e >= 0 && (peers & lt_mask) == 0ull) my_cnt[e] += __popcll(peers);
-  }
+  wave_scatter(ids, lo, hi, begin, nloc, nbits, my_cnt, sorted_assign, assign_pos);
 }
 
 __global__ void zero_counts_kernel(int nloc, int* counts, int* offsets) {
@@ -154,6 +281,11 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
 
 }  // namespace
 
+size_t dispatch_workspace_size(int n, int num_local) {
+  if (n <= kSingleBlockMax) return 0;
+  return (size_t)sort_blocks(n) * num_local * sizeof(int);
+}
+
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   if (a.n == 0) {
     hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(256), 0, s, a.num_local, a.counts,
@@ -162,10 +294,21 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   }
   int nbits = 1;
   while ((1 << nbits) < a.num_local) ++nbits;
-  const size_t lds = (size_t)(kSortWaves * a.num_local + kSortWaves) * sizeof(int);
-  hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(kSortWaves * 64), lds, s, a.ids, a.n,
-                     a.expert_begin, a.num_local, nbits, a.counts, a.offsets, a.sorted_assign,
-                     a.assign_pos);
+  if (a.n <= kSingleBlockMax) {
+    const size_t lds = (size_t)(kSortWaves * a.num_local + kSortWaves) * sizeof(int);
+    hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(kSortWaves * 64), lds, s, a.ids, a.n,
+                       a.expert_begin, a.num_local, nbits, a.counts, a.offsets, a.sorted_assign,
+                       a.assign_pos);
+  } else {
+    const int blocks = sort_blocks(a.n), per_block = sort_per_block(a.n);
+    const size_t lds = (size_t)(kBlkWaves * a.num_local + 4) * sizeof(int);
+    hipLaunchKernelGGL(block_count_kernel, dim3(blocks), dim3(256), lds, s, a.ids, a.n, per_block,
+                       a.expert_begin, a.num_local, nbits, (int*)a.workspace);
+    hipLaunchKernelGGL(block_scatter_kernel, dim3(blocks), dim3(256), lds, s, a.ids, a.n,
+                       per_block, a.expert_begin, a.num_local, nbits, (const int*)a.workspace,
+                       blocks,
+                       a.counts, a.offsets, a.sorted_assign, a.assign_pos);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.row_bytes == 0) return err;
   const int row_vec = a.row_bytes / 16;

@@ -27,7 +27,9 @@ struct DispatchArgs {
   const void* x;
   void* x_sorted;
   int row_bytes;  // hidden * element size; 0 = no gather
+  void* workspace;
 };
+size_t dispatch_workspace_size(int n, int num_local);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 constexpr int kDispatchMaxLocal = 1000;  // per-(wave, expert) counters fit in 64 KiB of LDS
 

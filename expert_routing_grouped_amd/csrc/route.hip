@@ -8,10 +8,10 @@
 //
 // Layout: lane l holds experts [l*V, l*V + V) of its token in registers
 // (V = values per lane, a power of two, 64*V >= E). Selection runs k rounds
-// of a wave-wide maximum over 64-bit keys (order-preserving float bits in the
-// high word, the complemented expert index in the low word), so equal scores
-// resolve to the lower expert index and the result does not depend on the
-// reduction order.
+// of a wave-wide maximum over order-preserving float keys (DPP within rows of
+// 16 lanes, scalar reads across rows); among lanes holding the maximum the
+// lowest one wins, so equal scores resolve to the lower expert index and the
+// result does not depend on the reduction order.
 #include "device_common.h"
 #include "launch.h"
 
@@ -68,28 +68,40 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ sc
     lsum = wave_sum_f32(s);
   }
 
-  // ---- group stage: which groups stay candidates
-  uint64_t kept = ~0ull;
-  int G = E;
+  // ---- group stage: which experts stay candidates
+  bool cand[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) cand[v] = valid[v];
   if (num_groups > 1) {
-    G = E / num_groups;
-    float gs = -INFINITY;  // lane g < num_groups ends up holding group g's score
+    const int G = E / num_groups;
     if (ALIGNED) {
-      // Each lane's V experts lie in one group; a group spans G / V lanes.
+      // Each lane's V experts lie in one group; a group spans lpg = G / V lanes
+      // (a power of two): merge the (first, second) pairs across the group's
+      // lanes with DPP inside rows of 16 and shuffles across rows.
       const int lpg = G / V;
       float a1 = -INFINITY, a2 = -INFINITY;
 #pragma unroll
       for (int v = 0; v < V; ++v)
         if (valid[v]) top2_insert(val[v], a1, a2);
-      for (int m = 1; m < lpg; m <<= 1) {
-        const float b1 = __shfl_xor(a1, m, MOE_WAVE);
-        const float b2 = __shfl_xor(a2, m, MOE_WAVE);
-        top2_merge(a1, a2, b1, b2);
+      if (lpg >= 2) top2_merge(a1, a2, dpp_f32<kDppQuadXor1>(a1), dpp_f32<kDppQuadXor1>(a2));
+      if (lpg >= 4) top2_merge(a1, a2, dpp_f32<kDppQuadXor2>(a1), dpp_f32<kDppQuadXor2>(a2));
+      if (lpg >= 8) top2_merge(a1, a2, dpp_f32<kDppHalfMirror>(a1), dpp_f32<kDppHalfMirror>(a2));
+      if (lpg >= 16) top2_merge(a1, a2, dpp_f32<kDppRowMirror>(a1), dpp_f32<kDppRowMirror>(a2));
+      for (int m = 16; m < lpg; m <<= 1)
+        top2_merge(a1, a2, __shfl_xor(a1, m, MOE_WAVE), __shfl_xor(a2, m, MOE_WAVE));
+      const float mine = a1 + a2;  // every lane of the group holds its group score
+      const int gl = lane / lpg;
+      // rank of this lane's group: groups ahead of it (higher score, or equal and lower index)
+      int rank = 0;
+      for (int g2 = 0; g2 < num_groups; ++g2) {
+        const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), g2 * lpg));
+        rank += (o > mine) || (o == mine && g2 < gl);
       }
-      const float mine = a1 + a2;
-      const int src = (lane < num_groups ? lane : 0) * lpg;
-      gs = __shfl(mine, src, MOE_WAVE);
+      const bool keep = rank < topk_groups;
+#pragma unroll
+      for (int v = 0; v < V; ++v) cand[v] = cand[v] && keep;
     } else {
+      float gs = -INFINITY;  // lane g < num_groups ends up holding group g's score
       for (int g = 0; g < num_groups; ++g) {
         float a1 = -INFINITY, a2 = -INFINITY;
 #pragma unroll
@@ -105,44 +117,47 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ sc
         }
         if (lane == g) gs = a1 + a2;
       }
-    }
-    // rank of group `lane` = number of groups ahead of it (higher score, or equal and lower index)
-    int rank = 0;
-    for (int g2 = 0; g2 < num_groups; ++g2) {
-      const float o = __shfl(gs, g2, MOE_WAVE);
-      rank += (o > gs) || (o == gs && g2 < lane);
-    }
-    kept = __ballot(lane < num_groups && rank < topk_groups);
-  }
-
-  // ---- candidate keys
-  uint64_t key[V];
+      int rank = 0;
+      for (int g2 = 0; g2 < num_groups; ++g2) {
+        const float o = __shfl(gs, g2, MOE_WAVE);
+        rank += (o > gs) || (o == gs && g2 < lane);
+      }
+      const uint64_t kept = __ballot(lane < num_groups && rank < topk_groups);
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const uint32_t idx = (uint32_t)(lane * V + v);
-    const bool cand = valid[v] && ((kept >> (idx / (uint32_t)G)) & 1ull);
-    key[v] = cand ? (((uint64_t)ordered_key(val[v]) << 32) | (uint32_t)(~idx)) : 0ull;
+      for (int v = 0; v < V; ++v) {
+        const int idx = lane * V + v;
+        cand[v] = cand[v] && ((kept >> (idx / G)) & 1ull);
+      }
+    }
   }
 
-  // ---- k rounds of wave argmax
+  // ---- k rounds of wave argmax. Keys are order-preserving float bits (0 =
+  // not a candidate). The round's maximum comes from a DPP reduction; the
+  // lowest lane holding it (a ballot) has the lowest expert index among equal
+  // scores, and inside a lane the first v wins.
+  uint32_t key[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) key[v] = cand[v] ? ordered_key(val[v]) : 0u;
   int my_id = 0;
   float my_val = 0.0f;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = 0ull;
-    float bestv = 0.0f;
+    uint32_t best = 0u;
+    int bv = 0;
+    float bval = 0.0f;
 #pragma unroll
     for (int v = 0; v < V; ++v)
-      if (key[v] > best) { best = key[v]; bestv = val[v]; }
-    const uint64_t win = wave_max_u64(best);
-    const int idx = (int)(~(uint32_t)win);
-    const int owner = idx / V;
-    const float sv = __shfl(bestv, owner, MOE_WAVE);
+      if (key[v] > best) { best = key[v]; bv = v; bval = val[v]; }
+    const uint32_t win = wave_max_u32_dpp(best);
+    const uint64_t holders = __ballot(best == win);
+    const int owner = __ffsll((unsigned long long)holders) - 1;
+    const int vsel = __builtin_amdgcn_readlane(bv, owner);
+    const float sv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(bval), owner));
     if (lane == owner) {
 #pragma unroll
       for (int v = 0; v < V; ++v)
-        if (key[v] == win) key[v] = 0ull;
+        if (v == vsel) key[v] = 0u;
     }
-    if (lane == r) { my_id = idx; my_val = sv; }
+    if (lane == r) { my_id = owner * V + vsel; my_val = sv; }
   }
 
   float w = softmax ? expf(my_val - lmax) / lsum : my_val;

@@ -27,7 +27,9 @@ _SIGNATURES = {
     "moe_abi_version": (ctypes.c_int32, []),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_route": (ctypes.c_int, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
-    "moe_dispatch": (ctypes.c_int, [_P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P]),
+    "moe_dispatch_workspace_size": (ctypes.c_size_t, [_I, _I, _I]),
+    "moe_dispatch": (ctypes.c_int, [_P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P,
+                                    ctypes.c_size_t, _P]),
     "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "moe_expert_ffn": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P,
                                       ctypes.c_size_t, _P]),
@@ -132,10 +134,16 @@ def moe_dispatch(topk_ids, expert_begin, num_local_experts, x=None, out=None, st
         o["x_sorted"] = None
     for name in ("counts", "offsets", "sorted_assign", "assign_pos"):
         _dev(o[name], torch.int32, name)
+    need = int(lib().moe_dispatch_workspace_size(T, k, num_local_experts))
+    ws = o.get("workspace")
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
     _check(lib().moe_dispatch(_ptr(topk_ids), T, k, expert_begin, num_local_experts, _ptr(x),
                               hidden, dtype, _ptr(o["counts"]), _ptr(o["offsets"]),
                               _ptr(o["sorted_assign"]), _ptr(o["assign_pos"]),
-                              _ptr(o["x_sorted"]), _stream(stream)), "moe_dispatch")
+                              _ptr(o["x_sorted"]), _ptr(ws if need else None),
+                              ws.numel() if (need and ws is not None) else 0, _stream(stream)),
+           "moe_dispatch")
     return o
 
 
@@ -229,6 +237,9 @@ class MoELayer:
             sorted_assign=torch.empty(max(cap, 1), **i32),
             assign_pos=torch.empty(max(cap, 1), **i32),
         )
+        dneed = int(lib().moe_dispatch_workspace_size(num_tokens, top_k, num_local_experts))
+        if dneed:
+            self.buf["dispatch_ws"] = torch.empty(dneed, dtype=torch.uint8, device=dev)
         if hidden:
             if not fuse_gather:
                 self.buf["x_sorted"] = torch.empty((max(cap, 1), hidden), dtype=dtype, device=dev)
@@ -247,6 +258,8 @@ class MoELayer:
         """Counting sort; also gathers x into x_sorted unless the gather is fused into the FFN."""
         b = self.buf
         out = {n: b[n] for n in ("counts", "offsets", "sorted_assign", "assign_pos")}
+        if "dispatch_ws" in b:
+            out["workspace"] = b["dispatch_ws"]
         if x is not None and not self.fuse_gather:
             out["x_sorted"] = b["x_sorted"]
             return moe_dispatch(b["topk_ids"], self.expert_begin, self.num_local, x, out, stream)

@@ -99,10 +99,16 @@ moe_status_t moe_route(const float* scores, int32_t num_tokens, int32_t num_expe
                        int32_t* topk_ids, float* topk_weights, hipStream_t stream);
 
 /*
+ * Bytes of device workspace moe_dispatch needs for T * k assignments and
+ * num_local_experts experts (0 when T * k <= 8192: then workspace may be NULL).
+ */
+size_t moe_dispatch_workspace_size(int32_t num_tokens, int32_t top_k, int32_t num_local_experts);
+
+/*
  * moe_dispatch -- the dispatch step of ch15 section 3.4 on one GPU: a stable
  * counting sort of the assignments a = t * k + j (token t, slot j) whose
  * expert lies in [expert_begin, expert_begin + num_local_experts), followed by
- * a gather of the token rows into expert order.
+ * an optional gather of the token rows into expert order.
  *
  * topk_ids        [T, k] int32 (from moe_route).
  * expert_counts   [E_loc] int32 out: rows per local expert.
@@ -114,6 +120,8 @@ moe_status_t moe_route(const float* scores, int32_t num_tokens, int32_t num_expe
  * x               [T, hidden] (dtype) or NULL: token rows to gather.
  * x_sorted        [T * k, hidden] (dtype) out, or NULL (only with x == NULL):
  *                 row i = x[sorted_assign[i] / k] for i < M (exact copy).
+ * workspace       device buffer of moe_dispatch_workspace_size bytes (per-block
+ *                 counts of the multi-workgroup sort); contents need not be set.
  * Limits: 1 <= num_local_experts <= 1000; T * k < 2^31; hidden % 8 == 0
  * when x is given. T = 0 writes zero counts and offsets.
  */
@@ -122,7 +130,7 @@ moe_status_t moe_dispatch(const int32_t* topk_ids, int32_t num_tokens, int32_t t
                           const void* x, int32_t hidden, int32_t dtype,
                           int32_t* expert_counts, int32_t* expert_offsets,
                           int32_t* sorted_assign, int32_t* assign_pos, void* x_sorted,
-                          hipStream_t stream);
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Bytes of device workspace moe_expert_ffn needs for these sizes; 0 when the

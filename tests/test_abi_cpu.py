@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = moe.lib()
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     assert moe.status_string(0) == "ok"
     assert moe.status_string(1) == "invalid argument"
     assert moe.status_string(3).startswith("workspace")
@@ -63,14 +63,20 @@ def test_route_validation():
 def test_dispatch_validation():
     l = moe.lib()
     p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
-    assert l.moe_dispatch(None, 4, 0, 0, 8, None, 0, 1, p, p, p, p, None, None) == 1
-    assert l.moe_dispatch(p, 4, 8, 0, 0, None, 0, 1, p, p, p, p, None, None) == 1
-    assert l.moe_dispatch(p, 4, 8, 0, 2000, None, 0, 1, p, p, p, p, None, None) == 2
-    assert l.moe_dispatch(p, 4, 8, 0, 8, p, 0, 1, p, p, p, p, None, None) == 1      # x without x_sorted
-    assert l.moe_dispatch(p, 4, 8, 0, 8, p, 12, 1, p, p, p, p, p, None) == 1         # hidden % 8
-    assert l.moe_dispatch(p, 4, 8, 0, 8, ctypes.c_void_p(8), 16, 1, p, p, p, p, p, None) == 1  # unaligned
-    assert l.moe_dispatch(p, 4, 8, 0, 8, None, 0, 5, p, p, p, p, None, None) == 1    # bad dtype
-    assert l.moe_dispatch(None, 4, 8, 0, 8, None, 0, 1, p, p, p, p, None, None) == 1 # NULL ids
+    W = (None, 0, None)       # no workspace, default stream
+    assert l.moe_dispatch(None, 4, 0, 0, 8, None, 0, 1, p, p, p, p, None, *W) == 1
+    assert l.moe_dispatch(p, 4, 8, 0, 0, None, 0, 1, p, p, p, p, None, *W) == 1
+    assert l.moe_dispatch(p, 4, 8, 0, 2000, None, 0, 1, p, p, p, p, None, *W) == 2
+    assert l.moe_dispatch(p, 4, 8, 0, 8, p, 0, 1, p, p, p, p, None, *W) == 1      # x without x_sorted
+    assert l.moe_dispatch(p, 4, 8, 0, 8, p, 12, 1, p, p, p, p, p, *W) == 1         # hidden % 8
+    assert l.moe_dispatch(p, 4, 8, 0, 8, ctypes.c_void_p(8), 16, 1, p, p, p, p, p, *W) == 1  # unaligned
+    assert l.moe_dispatch(p, 4, 8, 0, 8, None, 0, 5, p, p, p, p, None, *W) == 1    # bad dtype
+    assert l.moe_dispatch(None, 4, 8, 0, 8, None, 0, 1, p, p, p, p, None, *W) == 1 # NULL ids
+    # large T*k needs a workspace of one int per (2048-assignment block, local expert)
+    assert l.moe_dispatch_workspace_size(1024, 8, 32) == 0
+    assert l.moe_dispatch_workspace_size(8192, 8, 32) == 32 * 32 * 4
+    assert l.moe_dispatch(p, 8192, 8, 0, 32, None, 0, 1, p, p, p, p, None, None, 0, None) == 3
+    assert l.moe_dispatch(p, 8192, 8, 0, 32, None, 0, 1, p, p, p, p, None, p, 100, None) == 3
 
 
 def test_ffn_validation_and_workspace():

@@ -172,7 +172,10 @@ def test_dispatch_workloads(name, begin, nloc):
 
 @pytest.mark.parametrize("T,k,E,begin,nloc", [
     (1, 1, 4, 0, 4), (37, 3, 16, 3, 5), (1000, 8, 64, 0, 64), (513, 8, 1000, 0, 1000),
-    (5, 2, 8, 6, 2), (4096, 2, 2, 0, 1)])
+    (5, 2, 8, 6, 2), (4096, 2, 2, 0, 1),
+    # above 8192 assignments: the multi-workgroup sort, ragged last block, and
+    # beyond 256 blocks of 2048 where each block's share grows
+    (1100, 8, 1000, 0, 1000), (8193, 1, 3, 0, 3), (70001, 8, 256, 5, 200)])
 def test_dispatch_ragged(T, k, E, begin, nloc):
     rng = np.random.default_rng(T * 7 + k)
     ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
