@@ -106,7 +106,9 @@ static moe_status_t check_ffn_sizes(int32_t num_local_experts, int32_t hidden, i
     if ((int64_t)num_local_experts * ((row_capacity + 15) / 16) > 65535) return MOE_ERR_UNSUPPORTED;
   }
   if ((int64_t)2 * inter * hidden >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
-  if ((int64_t)row_capacity * (hidden > inter ? hidden : inter) >= ((int64_t)1 << 40))
+  // the bf16 kernels address an expert's weights and the activation rows with
+  // 32-bit byte offsets
+  if ((int64_t)row_capacity * (hidden > inter ? hidden : inter) >= ((int64_t)1 << 31))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }

@@ -37,7 +37,11 @@ constexpr int kStreamMT = 4;                  // row tiles of 16 per streamed ro
 constexpr int kChunkRows = kStreamMT * 16;    // rows per streamed chunk
 constexpr int kStreamRows = 4 * kChunkRows;   // experts with more rows are tiled
 constexpr int kTileBM = 128;                  // tokens per tile in the tiled path
+constexpr int kStreamDW = 3;                  // weight register sets of the streaming path
+constexpr int kStreamDA = 3;                  // activation register sets
 constexpr int kMaxLocal = 1024;
+
+constexpr int gcd_c(int x, int y) { return y == 0 ? x : gcd_c(y, x % y); }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
@@ -53,21 +57,35 @@ struct GemmArgs {
   int ldc;
 };
 
-__device__ __forceinline__ const uint16_t* a_row_ptr(const GemmArgs& a, int row) {
-  const int src = a.row_index ? a.row_index[row] / a.row_div : row;
-  return a.A + (size_t)src * a.K;
+// Replaces each permuted row number by the row of A that holds it. All index
+// loads are issued before the first is used, so they cost one memory latency.
+template <int N>
+__device__ __forceinline__ void a_rows(const GemmArgs& a, uint32_t* rows) {
+  if (a.row_index) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) rows[j] = (uint32_t)a.row_index[rows[j]];
+    const uint32_t div = (uint32_t)a.row_div;
+#pragma unroll
+    for (int j = 0; j < N; ++j) rows[j] /= div;
+  }
 }
+
+// Buffer resource word 3 for raw (unformatted, unswizzled) buffer loads on gfx9.
+constexpr int kBufferConfig = 0x00020000;
+// Cache-policy operand of a buffer load: non-temporal (streamed once).
+constexpr int kNonTemporal = 2;
 
 // ---------------------------------------------------------------- expert lists
 
-// Splits the local experts by row count m, in expert order:
+// Splits the local experts by row count m, in expert order (and leaves the
+// clamped row bounds in s_lo: rows of expert e are [s_lo[e], s_lo[e] + m)):
 //   1 <= m <= kStreamRows: streamed, in ceil(m / kChunkRows) row chunks;
 //                          s_first[e] = first chunk of expert e, s_first[nloc] = chunks
 //   m > kStreamRows:       tiled, in ceil(m / bm) row tiles;
 //                          t_first[e] = first tile of expert e, t_first[nloc] = tiles
 // Every thread of the 256-thread workgroup calls this; 4 experts per thread.
-__device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_first, int* wsum,
-                            int& n_chunks, int& n_tiles) {
+__device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_first, int* s_lo,
+                            int* wsum, int& n_chunks, int& n_tiles) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int cc[4], tc[4], cs = 0, ct = 0;
 #pragma unroll
@@ -76,7 +94,10 @@ __device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_firs
     int m = 0;
     if (e < a.nloc) {
       const int lo = min(a.offsets[e], a.capacity);
-      m = max(0, min(a.offsets[e + 1], a.capacity) - lo);
+      const int hi = min(a.offsets[e + 1], a.capacity);
+      m = max(0, hi - lo);
+      s_lo[e] = lo;
+      if (e == a.nloc - 1) s_lo[a.nloc] = max(lo, hi);
     }
     cc[q] = (m > 0 && m <= kStreamRows) ? (m + kChunkRows - 1) / kChunkRows : 0;
     tc[q] = (m > kStreamRows) ? (m + bm - 1) / bm : 0;
@@ -136,45 +157,78 @@ __device__ __forceinline__ int find_expert(const int* first, int nloc, int idx) 
 // operand and the activations the B operand, so a lane ends up holding 4
 // consecutive output columns of one row (one 8-byte store).
 //
-// In a K step of 32*U, load u of lane (r, g) = (lane % 16, lane / 16) reads 8
-// bf16 of weight row r (or activation row r) at k = kk + 32u + 8g: one load
-// instruction covers 64 contiguous bytes of each of 16 rows, and MFMA u
-// consumes exactly the 32 k of load u for both operands. K slices are summed
-// through LDS in slice order; then SiLU*up (gated) or the plain bf16 store.
-template <int NTW, int KS, int U, bool GATED>
+// A K step is 64 k: 128 bytes, one full cache line, of each row. Global loads
+// are coalesced: load h of a 16-row tile gives lane l the 16-byte chunk l % 8
+// of row 8h + l / 8, so each instruction reads 8 whole lines. (Loading
+// directly in MFMA layout would touch 16 lines per instruction, 64 bytes each;
+// the load pipeline then moves about a quarter of the bytes per clock.) The
+// lane writes its chunk into its wavefront's LDS tile at row * 128 +
+// ((chunk ^ row % 8) * 16), and MFMA fragments are read back with lane
+// (r = l % 16, g = l / 16) taking chunk 4u + g of row r for MFMA u = 0, 1 --
+// the same k order for weights and activations. The XOR keeps both the writes
+// and the reads free of bank conflicts. Each wavefront has its own LDS tiles,
+// so no barrier is needed inside the K loop.
+//
+// K slices are summed through LDS in slice order; then SiLU*up (gated) or the
+// plain bf16 store.
+template <int NTW, int KS, bool GATED, int DW, int DA>
 struct Stream {
+  static constexpr int PERIOD = DW * DA / gcd_c(DW, DA);  // register sets repeat every PERIOD steps
   static constexpr int MT = kStreamMT;
   static constexpr int NWN = 4 / KS;
   static constexpr int HT = GATED ? NTW / 2 : NTW;  // output tiles per wavefront
   static constexpr int COLS = NWN * HT * 16;        // output columns per slab
-  static constexpr int KSTEP = 32 * U;
-  static constexpr int RED_BYTES = KS > 1 ? KS * NWN * MT * NTW * 64 * 16 : 0;
+  static constexpr int KSTEP = 64;
+  static constexpr int TILE_BYTES = 16 * 128;       // one 16-row tile of a K step
+  static constexpr int WAVE_LDS = (NTW + MT) * TILE_BYTES;
+  static constexpr int LDS_BYTES = 4 * WAVE_LDS;
   static_assert(!GATED || NTW % 2 == 0, "gated slabs pair gate and up tiles");
+  static_assert(MT * NTW * 1024 <= WAVE_LDS, "K-slice partial sums fit in the wavefront's tiles");
 
   // MTA = active row tiles of the chunk (1..MT): the K loop has no branches,
   // so the only waits are on the registers an MFMA reads.
-  template <int MTA>
-  __device__ static void run_mt(const GemmArgs& a, int e, int lo, int m, int slab, f32x4_t* red) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  template <int MTA, bool NT>
+  __device__ static void run_mt(const GemmArgs& a, int e, int lo, int m, int slab, char* smem) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ks = wave % KS, wn = wave / KS;
     const int fr = lane & 15, g = lane >> 4;
+    const int lr = lane >> 3, lc = lane & 7;       // load mapping: row lr (+8), chunk lc
     const int col0 = (slab * NWN + wn) * HT * 16;  // first output column of this wavefront
+    const uint32_t pitch = (uint32_t)a.K * 2;      // row pitch in bytes
 
-    const uint16_t* wp[NTW];
+    // Weights: one buffer per expert; the lane's byte offset is fixed and the
+    // tile/half/K-step offsets are wavefront-uniform.
+    const __amdgpu_buffer_rsrc_t wbuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.W + (size_t)e * a.N * a.K), 0, (int)(a.N * pitch), kBufferConfig);
+    const uint32_t wv = (uint32_t)(col0 + lr) * pitch + lc * 16;
+    int wso[NTW][2];
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-      const int c = col0 + (t % HT) * 16 + fr;
-      const int wrow = (GATED && t >= HT) ? a.inter + c : c;
-      wp[t] = a.W + ((size_t)e * a.N + wrow) * a.K + g * 8;
-    }
-    // Rows past the chunk's end read its first row instead: an MFMA output
-    // column depends only on its own activation row, and it is not stored.
-    const uint16_t* ap[MTA];
+    for (int t = 0; t < NTW; ++t)
 #pragma unroll
-    for (int i = 0; i < MTA; ++i) {
-      const int r = i * 16 + fr;
-      ap[i] = a_row_ptr(a, lo + (r < m ? r : 0)) + g * 8;
-    }
+      for (int h = 0; h < 2; ++h)
+        wso[t][h] = ((t % HT) * 16 + h * 8 + ((GATED && t >= HT) ? a.inter : 0)) * (int)pitch;
+    // Activations: rows past the chunk's end read its first row instead: an
+    // MFMA output column depends only on its own activation row, and it is not
+    // stored.
+    const __amdgpu_buffer_rsrc_t abuf = __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, -1, kBufferConfig);
+    uint32_t av[MTA][2];
+#pragma unroll
+    for (int i = 0; i < MTA; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = i * 16 + h * 8 + lr;
+        av[i][h] = lo + (r < m ? r : 0);
+      }
+    a_rows<MTA * 2>(a, &av[0][0]);
+#pragma unroll
+    for (int i = 0; i < MTA; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) av[i][h] = av[i][h] * pitch + lc * 16;
+
+    char* xs = smem + wave * WAVE_LDS;  // NTW weight tiles, then MT activation tiles
+    const int woff[2] = {lr * 128 + ((lc ^ lr) << 4), (8 + lr) * 128 + ((lc ^ lr) << 4)};
+    const int roff[2] = {fr * 128 + ((g ^ (fr & 7)) << 4), fr * 128 + (((4 + g) ^ (fr & 7)) << 4)};
 
     f32x4_t acc[MTA][NTW];
 #pragma unroll
@@ -182,79 +236,97 @@ struct Stream {
 #pragma unroll
       for (int t = 0; t < NTW; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    bf16x8_t w0[NTW][U], w1[NTW][U], w2[NTW][U], a0[MTA][U], a1[MTA][U];
-    auto load_w = [&](bf16x8_t (&w)[NTW][U], int kk) {
+    u32x4_t wr[DW][NTW][2], ar[DA][MTA][2];
+    auto load_w = [&](u32x4_t (&w)[NTW][2], int kk) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int t = 0; t < NTW; ++t)
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) w[t][u] = *(const bf16x8_t*)(wp[t] + kk + u * 32);
+        for (int h = 0; h < 2; ++h)
+          w[t][h] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, wv, wso[t][h] + kk * 2, NT ? kNonTemporal : 0);
     };
-    auto load_a = [&](bf16x8_t (&av)[MTA][U], int kk) {
+    auto load_a = [&](u32x4_t (&x)[MTA][2], int kk) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int i = 0; i < MTA; ++i)
 #pragma unroll
-        for (int i = 0; i < MTA; ++i) av[i][u] = *(const bf16x8_t*)(ap[i] + kk + u * 32);
+        for (int h = 0; h < 2; ++h) x[i][h] = __builtin_amdgcn_raw_buffer_load_b128(abuf, av[i][h], kk * 2, 0);
     };
-    auto mma = [&](const bf16x8_t (&w)[NTW][U], const bf16x8_t (&av)[MTA][U]) {
+    auto mma = [&](const u32x4_t (&w)[NTW][2], const u32x4_t (&av)[MTA][2]) {
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) *(u32x4_t*)(xs + t * TILE_BYTES + woff[h]) = w[t][h];
+#pragma unroll
+      for (int i = 0; i < MTA; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) *(u32x4_t*)(xs + (NTW + i) * TILE_BYTES + woff[h]) = av[i][h];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8_t wf[NTW], af[MTA];
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) wf[t] = *(const bf16x8_t*)(xs + t * TILE_BYTES + roff[u]);
+#pragma unroll
+        for (int i = 0; i < MTA; ++i) af[i] = *(const bf16x8_t*)(xs + (NTW + i) * TILE_BYTES + roff[u]);
 #pragma unroll
         for (int i = 0; i < MTA; ++i)
 #pragma unroll
           for (int t = 0; t < NTW; ++t)
-            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[t][u], av[i][u], acc[i][t], 0, 0, 0);
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[t], af[i], acc[i][t], 0, 0, 0);
+      }
     };
 
-    // Software pipeline over K steps: weights two steps ahead (three register
-    // sets), activations one step ahead (two sets). In step s the loads for
-    // A(s+1) and then W(s+2) are issued before the MFMAs of step s. Loads
-    // complete in issue order, so the oldest outstanding loads are exactly
-    // W(s) and A(s): the MFMAs wait for those while W(s+1), A(s+1) and W(s+2)
-    // stay in flight. Steps past the end reload the last chunk instead of
-    // branching. The scheduling barriers keep this issue order.
+    // Software pipeline over K steps: weights DW - 1 steps ahead (DW register
+    // sets), activations DA - 1 steps ahead (DA sets). Step s first issues the
+    // loads of W(s + DW - 1) and A(s + DA - 1), then consumes W(s) and A(s).
+    // Loads complete in issue order, so step s waits only for its own data
+    // while the later steps stay in flight. Steps past the end reload the last
+    // step instead of branching. The scheduling barriers keep this issue order.
     const int kw = a.K / KS, kbeg = ks * kw, klast = kbeg + kw - KSTEP;
     const int steps = kw / KSTEP;
-    int kk = kbeg;
-    load_w(w0, kk);
-    load_a(a0, kk);
-    load_w(w1, min(kk + KSTEP, klast));
-#define MOE_STEP(WC, WN, AC, AN)           \
-  load_a(AN, min(kk + KSTEP, klast));     \
-  load_w(WN, min(kk + 2 * KSTEP, klast)); \
-  __builtin_amdgcn_sched_barrier(0);      \
-  mma(WC, AC);                            \
-  __builtin_amdgcn_sched_barrier(0);      \
+#pragma unroll
+    for (int j = 0; j < (DW > DA ? DW : DA) - 1; ++j) {
+      if (j < DW - 1) load_w(wr[j], min(kbeg + j * KSTEP, klast));
+      if (j < DA - 1) load_a(ar[j], min(kbeg + j * KSTEP, klast));
+    }
+    // The main loop runs whole periods with no exit inside, so the compiler's
+    // wait counts stay exact across the back edge (an exit in the body makes
+    // it drain every load at the loop head); the remainder runs after it.
+    int kk = kbeg, s = 0;
+#define MOE_STEP(q)                                                        \
+  load_w(wr[((q) + DW - 1) % DW], min(kk + (DW - 1) * KSTEP, klast));      \
+  load_a(ar[((q) + DA - 1) % DA], min(kk + (DA - 1) * KSTEP, klast));      \
+  __builtin_amdgcn_sched_barrier(0);                                       \
+  mma(wr[(q) % DW], ar[(q) % DA]);                                         \
+  __builtin_amdgcn_sched_barrier(0);                                       \
   kk += KSTEP;
-    for (int s = 0; s < steps; s += 6) {
-      MOE_STEP(w0, w2, a0, a1)
-      if (s + 1 >= steps) break;
-      MOE_STEP(w1, w0, a1, a0)
-      if (s + 2 >= steps) break;
-      MOE_STEP(w2, w1, a0, a1)
-      if (s + 3 >= steps) break;
-      MOE_STEP(w0, w2, a1, a0)
-      if (s + 4 >= steps) break;
-      MOE_STEP(w1, w0, a0, a1)
-      if (s + 5 >= steps) break;
-      MOE_STEP(w2, w1, a1, a0)
+    for (; s + PERIOD <= steps; s += PERIOD) {
+#pragma unroll
+      for (int q = 0; q < PERIOD; ++q) { MOE_STEP(q) }
+    }
+#pragma unroll
+    for (int q = 0; q < PERIOD - 1; ++q) {
+      if (s + q >= steps) break;
+      MOE_STEP(q)
     }
 #undef MOE_STEP
 
     if (KS > 1) {
-      // red: [KS][NWN][MT][NTW][64] float4; slice ks finishes row tiles i with i % KS == ks
+      // Each wavefront parks its partial sums in its own tiles ([MT][NTW][64]
+      // float4); slice ks then finishes the row tiles i with i % KS == ks.
+      f32x4_t* red = (f32x4_t*)xs;
 #pragma unroll
       for (int i = 0; i < MTA; ++i)
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) red[(((ks * NWN + wn) * MT + i) * NTW + t) * 64 + lane] = acc[i][t];
+        for (int t = 0; t < NTW; ++t) red[(i * NTW + t) * 64 + lane] = acc[i][t];
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < MTA; ++i) {
         if (i % KS != ks) continue;
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
-          f32x4_t sum = red[(((0 * NWN + wn) * MT + i) * NTW + t) * 64 + lane];
+          f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int q = 1; q < KS; ++q) sum += red[(((q * NWN + wn) * MT + i) * NTW + t) * 64 + lane];
+          for (int q = 0; q < KS; ++q)
+            sum += ((const f32x4_t*)(smem + (wn * KS + q) * WAVE_LDS))[(i * NTW + t) * 64 + lane];
           acc[i][t] = sum;
         }
       }
@@ -275,18 +347,27 @@ struct Stream {
         *(uint2*)(crow + t * 16) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
       }
     }
-    if (KS > 1) __syncthreads();  // red is reused by the next work item
   }
 
-  // Row chunk `chunk` (kChunkRows rows) of expert e, output slab `slab`.
-  __device__ static void run(const GemmArgs& a, int e, int chunk, int slab, f32x4_t* red) {
-    const int lo = min(a.offsets[e], a.capacity) + chunk * kChunkRows;
-    const int m = min(kChunkRows, min(a.offsets[e + 1], a.capacity) - lo);
-    switch ((m + 15) >> 4) {
-      case 1: run_mt<1>(a, e, lo, m, slab, red); break;
-      case 2: run_mt<2>(a, e, lo, m, slab, red); break;
-      case 3: run_mt<3>(a, e, lo, m, slab, red); break;
-      default: run_mt<4>(a, e, lo, m, slab, red); break;
+  // Row chunk `chunk` (kChunkRows rows) of expert e, output slab `slab`. The
+  // weights of an expert with a single chunk are read once per GEMM: with a
+  // long K they are loaded non-temporally, which keeps the activation rows
+  // that every slab re-reads in the caches.
+  __device__ static void run(const GemmArgs& a, const int* s_lo, int e, int chunk, int slab, char* smem) {
+    e = __builtin_amdgcn_readfirstlane(e);
+    const int lo = __builtin_amdgcn_readfirstlane(s_lo[e] + chunk * kChunkRows);
+    const int m = __builtin_amdgcn_readfirstlane(min(kChunkRows, s_lo[e + 1] - lo));
+    const bool nt = __builtin_amdgcn_readfirstlane(s_lo[e + 1] - s_lo[e]) <= kChunkRows && a.K >= 512;
+    slab = __builtin_amdgcn_readfirstlane(slab);
+    switch (((m + 15) >> 4) * 2 + (nt ? 1 : 0)) {
+      case 2: run_mt<1, false>(a, e, lo, m, slab, smem); break;
+      case 3: run_mt<1, true>(a, e, lo, m, slab, smem); break;
+      case 4: run_mt<2, false>(a, e, lo, m, slab, smem); break;
+      case 5: run_mt<2, true>(a, e, lo, m, slab, smem); break;
+      case 6: run_mt<3, false>(a, e, lo, m, slab, smem); break;
+      case 7: run_mt<3, true>(a, e, lo, m, slab, smem); break;
+      case 9: run_mt<4, true>(a, e, lo, m, slab, smem); break;
+      default: run_mt<4, false>(a, e, lo, m, slab, smem); break;
     }
   }
 };
@@ -344,13 +425,13 @@ struct Tiled {
       for (int i = 0; i < 4; ++i) woff[i] = 32 * i;
     }
     const uint16_t* wsrc = a.W + ((size_t)e * a.N + wrow0) * K + kc * 8;
-    int tok[4];
+    uint32_t tok[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = rbase + 32 * i;
-      const int row = row0 + (r < rows ? r : 0);
-      tok[i] = a.row_index ? a.row_index[row] / a.row_div : row;
+      tok[i] = row0 + (r < rows ? r : 0);
     }
+    a_rows<4>(a, tok);
     const uint16_t* xsrc = a.A + kc * 8;
 
     u32x4_t sw[4], sx[4];
@@ -438,17 +519,18 @@ struct Tiled {
 
 // One persistent kernel per GEMM: first the streamed row chunks, then the row
 // tiles of larger experts. The two paths share the LDS buffer.
-template <int NTW, int KS, int U, bool GATED>
+template <int NTW, int KS, bool GATED>
 __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(GemmArgs a) {
-  using S = Stream<NTW, KS, U, GATED>;
+  using S = Stream<NTW, KS, GATED, kStreamDW, kStreamDA>;
   using T = Tiled<GATED>;
-  constexpr int SMEM = S::RED_BYTES > T::LDS_BYTES ? S::RED_BYTES : T::LDS_BYTES;
+  constexpr int SMEM = S::LDS_BYTES > T::LDS_BYTES ? S::LDS_BYTES : T::LDS_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ int s_first[kMaxLocal + 1];
   __shared__ int t_first[kMaxLocal + 1];
+  __shared__ int s_lo[kMaxLocal + 1];
   __shared__ int wsum[8];
   int n_chunks, n_tiles;
-  build_lists(a, kTileBM, s_first, t_first, wsum, n_chunks, n_tiles);
+  build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles);
   const int ncols = GATED ? a.inter : a.N;
   const int slabs = ncols / S::COLS, nblk = ncols / T::COLS;
   const int n_stream = n_chunks * slabs;
@@ -457,12 +539,13 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(GemmArgs a) {
     if (w < n_stream) {
       const int c = w / slabs;
       const int e = find_expert(s_first, a.nloc, c);
-      S::run(a, e, c - s_first[e], w % slabs, (f32x4_t*)smem);
+      S::run(a, s_lo, e, c - s_first[e], w % slabs, smem);
+      __syncthreads();  // the LDS buffer is reused by the next work item
     } else {
       const int tile = (w - n_stream) / nblk, nb = (w - n_stream) % nblk;
       const int e = find_expert(t_first, a.nloc, tile);
-      const int row0 = min(a.offsets[e], a.capacity) + (tile - t_first[e]) * kTileBM;
-      const int rows = min(kTileBM, min(a.offsets[e + 1], a.capacity) - row0);
+      const int row0 = s_lo[e] + (tile - t_first[e]) * kTileBM;
+      const int rows = min(kTileBM, s_lo[e + 1] - row0);
       T::run(a, e, row0, rows, nb, (uint16_t*)smem);
       __syncthreads();  // the LDS buffer is reused by the next work item
     }
@@ -548,25 +631,25 @@ int occupancy(F kernel, int threads) {
   return n;
 }
 
-// Shape of the streaming path per GEMM:
-//   gate_up (gated): NTW = 2 (a gate and the matching up tile), U = 2
-//   down (plain):    NTW = 4, U = 1
-// and KS, the K slices of a workgroup: 4 when every slice still has at least
-// 8 K steps, else 2 (gated: K = hidden is a multiple of 256), else 1.
+// Shape of the streaming path: NTW = 2 weight tiles per wavefront (gated: a
+// gate tile and the matching up tile) and KS, the K slices of a workgroup.
+// Gated GEMMs (K = hidden, a multiple of 256) take KS = 4 from K = 1024 on,
+// else 2. Plain GEMMs take the largest KS that still leaves every slice at
+// least 16 K steps, else 2 when K allows it, else 1.
 template <bool GATED>
 int stream_ks(int K) {
-  constexpr int U = GATED ? 2 : 1;
-  if (K % (4 * 32 * U) == 0 && K / 4 >= 8 * 32 * U) return 4;
-  if (GATED || (K % (2 * 32 * U) == 0 && K / 2 >= 4 * 32 * U)) return 2;
+  if (GATED) return K >= 1024 ? 4 : 2;
+  if (K % 256 == 0 && K / 4 >= 1024) return 4;
+  if (K % 128 == 0) return 2;
   return 1;
 }
 
 template <bool GATED, int KS>
 hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s) {
-  constexpr int NTW = GATED ? 2 : 4, U = GATED ? 2 : 1;
-  using S = Stream<NTW, KS, U, GATED>;
+  constexpr int NTW = 2;
+  using S = Stream<NTW, KS, GATED, kStreamDW, kStreamDA>;
   using T = Tiled<GATED>;
-  auto kernel = ffn_gemm_kernel<NTW, KS, U, GATED>;
+  auto kernel = ffn_gemm_kernel<NTW, KS, GATED>;
   static const int occ = occupancy(kernel, 256);
   const int ncols = GATED ? g.inter : g.N;
   const long max_chunks = std::min<long>((long)g.nloc * (kStreamRows / kChunkRows),

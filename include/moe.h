@@ -158,9 +158,11 @@ size_t moe_expert_ffn_workspace_size(int32_t num_local_experts, int32_t hidden, 
  * workspace       device buffer of at least moe_expert_ffn_workspace_size bytes
  *                 (holds h); contents need not be initialised.
  * bf16: float32 accumulation; h and o are rounded to bf16.
- * Limits (bf16): hidden % 256 == 0, inter % 64 == 0. f32: hidden % 4 == 0,
- * inter % 4 == 0, E_loc * ceil(row_capacity / 16) <= 65535. M = offsets[E_loc]
- * must not exceed row_capacity (rows past row_capacity are ignored on the device).
+ * Limits (bf16): hidden % 256 == 0, inter % 64 == 0; row_capacity * max(hidden,
+ * inter) < 2^31, and the caller keeps x below 2^32 bytes (the kernels address
+ * rows with 32-bit byte offsets). f32: hidden % 4 == 0, inter % 4 == 0,
+ * E_loc * ceil(row_capacity / 16) <= 65535. M = offsets[E_loc] must not exceed
+ * row_capacity (rows past row_capacity are ignored on the device).
  */
 moe_status_t moe_expert_ffn(const void* x, const int32_t* row_index, int32_t row_index_div,
                             const int32_t* expert_offsets, const void* w_gate_up,
