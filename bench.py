@@ -59,6 +59,31 @@ def calibrate_copy(mb, torch):
     print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
 
 
+FFN_SOURCES = ["expert_routing_grouped_amd/csrc/ffn.hip", "expert_routing_grouped_amd/csrc/device_common.h",
+               "expert_routing_grouped_amd/csrc/launch.h"]
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_ep_ffn_traffic.md")
+
+
+def measured_traffic(workload):
+    """HBM bytes per moe_expert_ffn call from the committed rocprofv3 counter summary,
+    or None when the GEMM sources changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = None
+        for line in open(TRAFFIC_RECORD):
+            if line.startswith("traffic-record: "):
+                rec = json.loads(line[len("traffic-record: "):])
+        h = hashlib.sha256()
+        for f in FFN_SOURCES:
+            with open(os.path.join(ROOT, f), "rb") as fh:
+                h.update(fh.read())
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("workload") != workload or rec.get("source_sha256_16") != h.hexdigest()[:16]:
+        return None
+    return int(rec["traffic_bytes_per_call"])
+
+
 def ffn_accounting(wl, counts):
     """Algorithmic FLOPs and HBM bytes of moe_expert_ffn for the measured routing."""
     counts = np.asarray(counts, dtype=np.int64)
@@ -140,6 +165,20 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host):
                   ev[2].elapsed_time(ev[3]) if x is not None else 0.0,
                   ev[3].elapsed_time(ev[4]) if x is not None else 0.0]
     parts_us = parts / steps * 1e3
+    ffn_us = None
+    if x is not None:
+        # moe_expert_ffn alone, back to back on the launch stream (the routing of
+        # the last step stays in place): the per-launch duration of the roofline
+        n_ffn = max(steps, 10)
+        for i in range(2):
+            layer.ffn(*weights[i % len(weights)], x)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n_ffn):
+            layer.ffn(*weights[i % len(weights)], x)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ffn_us = e0.elapsed_time(e1) / n_ffn * 1e3
     counts = to_host(layer.buf["counts"])
     res = dict(workload=wl.name, T=wl.T, ms_per_step=ms_per_step, wall_ms_per_step=wall / steps * 1e3,
                tokens_per_s=wl.T / (ms_per_step * 1e-3), gen_s=gen_s, weight_copies=len(weights),
@@ -147,7 +186,8 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host):
                                  combine=parts_us[3]))
     if wl.has_ffn:
         acc = ffn_accounting(wl, counts)
-        t_ffn = parts_us[2] * 1e-6
+        res["ffn_us_per_launch"] = ffn_us
+        t_ffn = ffn_us * 1e-6
         res.update(M=acc["M"], hit_experts=acc["hit"], ffn_gflop=acc["flops"] / 1e9,
                    ffn_bytes_mb=acc["bytes"] / 1e6,
                    ffn_tflops=acc["flops"] / t_ffn / 1e12, ffn_gbs=acc["bytes"] / t_ffn / 1e9,
@@ -162,22 +202,26 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host):
     return res
 
 
-def cpu_baseline(inp, wl):
-    """The oracle as it stands, on the host cores, over the whole headline workload."""
+def cpu_baseline(inp, wl, min_seconds=10.0):
+    """The oracle as it stands, on the host cores: whole layer passes over the
+    workload, repeated until about min_seconds of CPU work."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = 1
-    t0 = time.perf_counter()
-    oracle.layer(inp.scores, inp.x, inp.w_gate_up, inp.w_down, top_k=wl.top_k,
-                 num_groups=wl.num_groups, topk_groups=wl.topk_groups, score_mode=wl.score_mode,
-                 renormalize=wl.renormalize, expert_begin=wl.expert_begin, num_local=wl.num_local)
-    t = time.perf_counter() - t0
-    return {"value": wl.T / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"the whole {wl.name} layer ({wl.T} tokens): numpy float64 oracle, "
-                      f"{t:.2f} s", "seconds": t}
+    runs, t = 0, 0.0
+    while runs == 0 or t < min_seconds:
+        t0 = time.perf_counter()
+        oracle.layer(inp.scores, inp.x, inp.w_gate_up, inp.w_down, top_k=wl.top_k,
+                     num_groups=wl.num_groups, topk_groups=wl.topk_groups, score_mode=wl.score_mode,
+                     renormalize=wl.renormalize, expert_begin=wl.expert_begin, num_local=wl.num_local)
+        t += time.perf_counter() - t0
+        runs += 1
+    return {"value": wl.T * runs / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{runs} passes of the whole {wl.name} layer ({wl.T} tokens each) through the "
+                      f"numpy float64 oracle, {t:.1f} s", "seconds": t}
 
 
 def main():
@@ -219,9 +263,10 @@ def main():
         else:
             ach, peak, unit = head["ffn_tflops"], BF16_PEAK_TFLOPS, "TFLOP/s"
         out["roofline"] = {"bound": bound, "achieved": ach, "peak": peak, "unit": unit,
-                           "frac": ach / peak, "traffic": None,
-                           "kernel": "moe_expert_ffn (plan, gate_up GEMM + SiLU*up, down GEMM)",
-                           "us_per_launch": head["breakdown_us"]["ffn"],
+                           "frac": ach / peak, "traffic": measured_traffic(wl.name),
+                           "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                           "kernel": "moe_expert_ffn (gate_up GEMM + SiLU*up, down GEMM)",
+                           "us_per_launch": head["ffn_us_per_launch"],
                            "algorithmic_bytes": head["ffn_bytes_mb"] * 1e6,
                            "algorithmic_flops": head["ffn_gflop"] * 1e9}
     out["detail"] = {k: v for k, v in head.items() if k not in ("tokens_per_s",)}
