@@ -59,6 +59,12 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, MOE_WAVE);
+  return v;
+}
+
 __device__ __forceinline__ float wave_max_f32(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, MOE_WAVE));

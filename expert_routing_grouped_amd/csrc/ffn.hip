@@ -37,8 +37,11 @@ constexpr int kStreamMT = 4;                  // row tiles of 16 per streamed ro
 constexpr int kChunkRows = kStreamMT * 16;    // rows per streamed chunk
 constexpr int kStreamRows = 4 * kChunkRows;   // experts with more rows are tiled
 constexpr int kTileBM = 128;                  // tokens per tile in the tiled path
+constexpr int kBigBM = 256;                   // tokens per tile in the large-tile path
 constexpr int kStreamDW = 3;                  // weight register sets of the streaming path
 constexpr int kStreamDA = 3;                  // activation register sets
+constexpr bool kUseBigTiles = true;           // 256 x 256 tiles for large experts
+constexpr int kBigMinCapacity = 16384;        // row capacity from which they are used
 constexpr int kMaxLocal = 1024;
 
 constexpr int gcd_c(int x, int y) { return y == 0 ? x : gcd_c(y, x % y); }
@@ -55,18 +58,28 @@ struct GemmArgs {
   int N, K, inter;        // gated GEMMs pair weight row n with row inter + n
   uint16_t* C;            // [capacity, ldc]
   int ldc;
+  int big_ok;             // the large-tile kernel is launched too
+  int big_min_items;      // ... and takes the tiled experts when it has at least this many tiles
 };
 
 // Replaces each permuted row number by the row of A that holds it. All index
 // loads are issued before the first is used, so they cost one memory latency.
+// The division by row_div is floor((v + 0.5) * (1 / row_div)) in float64: for
+// v < 2^31 the rounding error stays below 2^-21 / row_div while (v + 0.5) /
+// row_div is at least 0.5 / row_div away from any integer, so the truncation
+// is exact; the reciprocal is a scalar, so nothing per lane outlives the call.
 template <int N>
 __device__ __forceinline__ void a_rows(const GemmArgs& a, uint32_t* rows) {
   if (a.row_index) {
 #pragma unroll
     for (int j = 0; j < N; ++j) rows[j] = (uint32_t)a.row_index[rows[j]];
-    const uint32_t div = (uint32_t)a.row_div;
+    int div = a.row_div;
+    asm volatile("" : "+s"(div));  // computed here, not hoisted out of a caller's loop
+    if (div != 1) {
+      const double inv = 1.0 / (double)div;
 #pragma unroll
-    for (int j = 0; j < N; ++j) rows[j] /= div;
+      for (int j = 0; j < N; ++j) rows[j] = (uint32_t)(((double)rows[j] + 0.5) * inv);
+    }
   }
 }
 
@@ -78,16 +91,17 @@ constexpr int kNonTemporal = 2;
 // ---------------------------------------------------------------- expert lists
 
 // Splits the local experts by row count m, in expert order (and leaves the
-// clamped row bounds in s_lo: rows of expert e are [s_lo[e], s_lo[e] + m)):
+// clamped row bounds in s_lo: rows of expert e are [s_lo[e], s_lo[e] + m);
+// n_big = the tiles of kBigBM rows the tiled experts need):
 //   1 <= m <= kStreamRows: streamed, in ceil(m / kChunkRows) row chunks;
 //                          s_first[e] = first chunk of expert e, s_first[nloc] = chunks
 //   m > kStreamRows:       tiled, in ceil(m / bm) row tiles;
 //                          t_first[e] = first tile of expert e, t_first[nloc] = tiles
 // Every thread of the 256-thread workgroup calls this; 4 experts per thread.
 __device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_first, int* s_lo,
-                            int* wsum, int& n_chunks, int& n_tiles) {
+                            int* wsum, int& n_chunks, int& n_tiles, int& n_big) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int cc[4], tc[4], cs = 0, ct = 0;
+  int cc[4], tc[4], cs = 0, ct = 0, cb = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = tid * 4 + q;
@@ -103,21 +117,24 @@ __device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_firs
     tc[q] = (m > kStreamRows) ? (m + bm - 1) / bm : 0;
     cs += cc[q];
     ct += tc[q];
+    cb += (m > kStreamRows) ? (m + kBigBM - 1) / kBigBM : 0;
   }
+  cb = wave_sum_i32(cb);
   int is = cs, it = ct;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int os = __shfl_up(is, d, MOE_WAVE), ot = __shfl_up(it, d, MOE_WAVE);
     if (lane >= d) { is += os; it += ot; }
   }
-  if (lane == 63) { wsum[w] = is; wsum[4 + w] = it; }
+  if (lane == 63) { wsum[w] = is; wsum[4 + w] = it; wsum[8 + w] = cb; }
   __syncthreads();
-  int bs = 0, bt = 0, ts = 0, tt = 0;
+  int bs = 0, bt = 0, ts = 0, tt = 0, tb = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i < w) { bs += wsum[i]; bt += wsum[4 + i]; }
     ts += wsum[i];
     tt += wsum[4 + i];
+    tb += wsum[8 + i];
   }
   int ps = bs + is - cs, pt = bt + it - ct;
 #pragma unroll
@@ -134,8 +151,11 @@ __device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_firs
     s_first[a.nloc] = ts;
     t_first[a.nloc] = tt;
   }
-  n_chunks = ts;
-  n_tiles = tt;
+  // the totals are the same in every lane; say so, so that values derived
+  // from them can live in scalar registers
+  n_chunks = __builtin_amdgcn_readfirstlane(ts);
+  n_tiles = __builtin_amdgcn_readfirstlane(tt);
+  n_big = __builtin_amdgcn_readfirstlane(tb);
   __syncthreads();
 }
 
@@ -515,6 +535,214 @@ struct Tiled {
   }
 };
 
+// ---------------------------------------------------------------- large-tile path
+
+// Experts with more than kStreamRows rows (prefill), as an alternative to the
+// 128 x 128 tiles above: 256 weight rows x 256 tokens per tile, one workgroup
+// of 4 wavefronts per CU, each wavefront 128 x 128 on v_mfma_f32_32x32x16_bf16
+// (4 x 4 fragments, 256 float32 accumulators per lane). Per 64-k stage a
+// wavefront reads 32 KB of fragments from LDS for 64 MFMAs, so the LDS traffic
+// (reads plus the stage writes) stays at about three quarters of its
+// bandwidth when the MFMA pipes are busy; the 128 x 128 design needs more LDS
+// bandwidth than the CU has.
+//
+// K is staged 64 at a time: global loads two stages ahead into registers
+// (coalesced: a wavefront reads 8 whole 128-byte rows per instruction), one
+// LDS write per stage into a double buffer, one barrier per stage. LDS rows
+// are 128 bytes; chunk c of row r sits at slot c ^ ((r >> 1) & 7), which keeps
+// every 16 consecutive lanes of a fragment read, and of a stage write, on
+// distinct banks.
+//
+// Gated tiles hold, for 128 output columns, per wavefront row half: 64 gate
+// rows then the 64 matching up rows, so SiLU(gate) * up is formed from the
+// wavefront's own accumulators.
+constexpr int kBandTiles = 4; // token tiles per raster band
+constexpr int kBigBK = 64;
+
+template <bool GATED>
+struct Big {
+  static constexpr int COLS = GATED ? 128 : 256;   // output columns per tile
+  static constexpr int OP_BYTES = 256 * kBigBK * 2;  // one operand of one stage
+  static constexpr int LDS_BYTES = 2 * 2 * OP_BYTES; // [stage buffer][W | X]
+
+  __device__ static __forceinline__ int swz(int row, int chunk) {
+    return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+  }
+
+  __device__ static void run(const GemmArgs& a, int e, int row0, int rows, int nb, char* lds, int tid) {
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;   // weight rows wm*128.., tokens wn*128..
+    const int lr = tid >> 3, lc = tid & 7;     // staging: tile rows lr + 32 i, chunk lc
+    const uint32_t pitch = (uint32_t)a.K * 2;
+
+    // Weights: tile row group i (32 rows) -> first weight row wbase[i]; the
+    // lane adds its row lr. Uniform parts go to the scalar offset.
+    const __amdgpu_buffer_rsrc_t wbuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.W + (size_t)e * a.N * a.K), 0, (int)(a.N * pitch), kBufferConfig);
+    int wso[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int base;
+      if (GATED) {
+        const int wmi = i >> 2, q = i & 3;   // group q of wavefront half wmi
+        base = ((q < 2) ? 0 : a.inter) + nb * COLS + wmi * 64 + (q & 1) * 32;
+      } else {
+        base = nb * 256 + i * 32;
+      }
+      wso[i] = base * (int)pitch;
+    }
+    const uint32_t wv = (uint32_t)lr * pitch + lc * 16;
+    // Tokens: rows past the tile's end read its first row (not stored).
+    const __amdgpu_buffer_rsrc_t xbuf = __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, -1, kBufferConfig);
+    uint32_t xv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = lr + 32 * i;
+      xv[i] = row0 + (r < rows ? r : 0);
+    }
+    a_rows<8>(a, xv);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xv[i] = xv[i] * pitch + lc * 16;
+
+    u32x4_t rw[1][8], rx[1][8];
+    auto gload = [&](u32x4_t (&w)[8], u32x4_t (&x)[8], int kt) {
+      const int ko = kt * kBigBK * 2;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, wv, wso[i] + ko, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_raw_buffer_load_b128(xbuf, xv[i], ko, 0);
+    };
+    auto sstore = [&](const u32x4_t (&w)[8], const u32x4_t (&x)[8], int buf) {
+      char* lw = lds + buf * 2 * OP_BYTES;
+      char* lx = lw + OP_BYTES;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *(u32x4_t*)(lw + swz(lr + 32 * i, lc)) = w[i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *(u32x4_t*)(lx + swz(lr + 32 * i, lc)) = x[i];
+    };
+
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+
+    const int fr = lane & 31, fh = lane >> 5;  // fragment row, k half
+    auto compute = [&](int buf) {
+      const char* lw = lds + buf * 2 * OP_BYTES;
+      const char* lx = lw + OP_BYTES;
+#pragma unroll
+      for (int q = 0; q < kBigBK / 16; ++q) {
+        const int chunk = q * 2 + fh;
+        bf16x8_t av[4], bv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = *(const bf16x8_t*)(lw + swz(wm * 128 + i * 32 + fr, chunk));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[j] = *(const bf16x8_t*)(lx + swz(wn * 128 + j * 32 + fr, chunk));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      }
+    };
+
+    // One register set: the loads of stage kt + 1 are issued before stage kt
+    // is multiplied and written to the other LDS buffer after it; every
+    // wavefront finished reading that buffer before the previous barrier.
+    // (A second register set, to issue loads two stages ahead, does not fit
+    // beside the 256 accumulators without spills.)
+    const int nk = a.K / kBigBK;
+    gload(rw[0], rx[0], 0);
+    sstore(rw[0], rx[0], 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool more = kt + 1 < nk;
+      if (more) gload(rw[0], rx[0], kt + 1);
+      compute(kt & 1);
+      if (more) sstore(rw[0], rx[0], (kt + 1) & 1);
+      __syncthreads();
+    }
+
+    // acc[i][j][r]: token wn*128 + j*32 + lane%32; wavefront weight row
+    // i*32 + (r/4)*8 + (lane/32)*4 + r%4.
+    // One fragment column at a time (all lanes compute, only the store is
+    // guarded), so the accumulators are read out piecewise.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int t = wn * 128 + j * 32 + fr;
+      const bool ok = t < rows;
+      uint16_t* crow = a.C + (size_t)(row0 + (ok ? t : 0)) * a.ldc;
+      if (GATED) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = nb * COLS + wm * 64 + i * 32 + q * 8 + fh * 4;
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = silu(acc[i][j][q * 4 + r]) * acc[i + 2][j][q * 4 + r];
+            const uint2 pk = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+            if (ok) *(uint2*)(crow + col) = pk;
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = nb * COLS + wm * 128 + i * 32 + q * 8 + fh * 4;
+            const f32x16_t& c = acc[i][j];
+            const uint2 pk = make_uint2(pack_bf16x2(c[q * 4], c[q * 4 + 1]),
+                                        pack_bf16x2(c[q * 4 + 2], c[q * 4 + 3]));
+            if (ok) *(uint2*)(crow + col) = pk;
+          }
+      }
+    }
+  }
+};
+
+// Tiles of the experts with more than kStreamRows rows, 256 tokens each; a
+// persistent loop over them, one workgroup per CU.
+template <bool GATED>
+__global__ __launch_bounds__(256, 1) void ffn_big_kernel(GemmArgs a) {
+  using B = Big<GATED>;
+  __shared__ __attribute__((aligned(16))) char smem[B::LDS_BYTES];
+  __shared__ int s_first[kMaxLocal + 1];
+  __shared__ int t_first[kMaxLocal + 1];
+  __shared__ int s_lo[kMaxLocal + 1];
+  __shared__ int wsum[12];
+  int n_chunks, n_tiles, n_big;
+  build_lists(a, kBigBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big);
+  const int nblk = (GATED ? a.inter : a.N) / B::COLS;
+  const int total = n_tiles * nblk;
+  if (total < a.big_min_items) return;  // the persistent kernel does these tiles
+  // Workgroup b runs on XCD b % 8 (round-robin dispatch). Each XCD takes a
+  // contiguous range of work items, and items are ordered in bands of
+  // kBandTiles token tiles: down a band's tiles first, then the next N block.
+  // The 32 workgroups an XCD runs at once then cover about 4 token tiles x 8
+  // N blocks, which share their operands through that XCD's L2 while they
+  // move through K at about the same pace. The grid is a multiple of 8 and
+  // at least total.
+  const int per = (total + 7) / 8;
+  for (int b = blockIdx.x; b < 8 * per; b += gridDim.x) {
+    const int w = (b % 8) * per + b / 8;
+    if (w >= total) continue;
+    const int band = w / (kBandTiles * nblk), r = w % (kBandTiles * nblk);
+    const int h = min(kBandTiles, n_tiles - band * kBandTiles);
+    const int tile = __builtin_amdgcn_readfirstlane(band * kBandTiles + r % h);
+    const int nb = __builtin_amdgcn_readfirstlane(r / h);
+    const int e = __builtin_amdgcn_readfirstlane(find_expert(t_first, a.nloc, tile));
+    const int row0 = __builtin_amdgcn_readfirstlane(s_lo[e] + (tile - t_first[e]) * kBigBM);
+    const int rows = __builtin_amdgcn_readfirstlane(min(kBigBM, s_lo[e + 1] - row0));
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));  // keeps per-thread setup inside the tile loop
+    B::run(a, e, row0, rows, nb, smem, tid);
+    __syncthreads();  // the LDS buffers are reused by the next tile
+  }
+}
+
 // ---------------------------------------------------------------- the GEMM kernel
 
 // One persistent kernel per GEMM: first the streamed row chunks, then the row
@@ -528,13 +756,16 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(GemmArgs a) {
   __shared__ int s_first[kMaxLocal + 1];
   __shared__ int t_first[kMaxLocal + 1];
   __shared__ int s_lo[kMaxLocal + 1];
-  __shared__ int wsum[8];
-  int n_chunks, n_tiles;
-  build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles);
+  __shared__ int wsum[12];
+  int n_chunks, n_tiles, n_big;
+  build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big);
   const int ncols = GATED ? a.inter : a.N;
   const int slabs = ncols / S::COLS, nblk = ncols / T::COLS;
   const int n_stream = n_chunks * slabs;
-  const int total = n_stream + n_tiles * nblk;
+  // Same decision as ffn_big_kernel: it takes the tiled experts when it has
+  // enough tiles to fill the GPU, else they are done here in 128 x 128 tiles.
+  const bool big = a.big_ok && n_big * (ncols / Big<GATED>::COLS) >= a.big_min_items;
+  const int total = n_stream + (big ? 0 : n_tiles * nblk);
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     if (w < n_stream) {
       const int c = w / slabs;
@@ -644,11 +875,25 @@ int stream_ks(int K) {
   return 1;
 }
 
+// Experts with more than kStreamRows rows go to ffn_big_kernel when the
+// output width allows its tiles, the row capacity is prefill-sized and (on
+// the device) they make at least one tile per CU; else to the 128 x 128 tiles
+// of the persistent kernel. Both paths are complete; the capacity test keeps
+// decode-sized calls from paying for a second launch that finds no work.
+template <bool GATED>
+bool use_big(const GemmArgs& g) {
+  return kUseBigTiles && g.capacity >= kBigMinCapacity &&
+         (GATED ? g.inter % 128 == 0 : g.N % 256 == 0);
+}
+
 template <bool GATED, int KS>
-hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s) {
+hipError_t launch_gemm_t(const GemmArgs& g0, hipStream_t s) {
   constexpr int NTW = 2;
   using S = Stream<NTW, KS, GATED, kStreamDW, kStreamDA>;
   using T = Tiled<GATED>;
+  GemmArgs g = g0;
+  g.big_ok = use_big<GATED>(g) ? 1 : 0;
+  g.big_min_items = cu_count();
   auto kernel = ffn_gemm_kernel<NTW, KS, GATED>;
   static const int occ = occupancy(kernel, 256);
   const int ncols = GATED ? g.inter : g.N;
@@ -658,6 +903,15 @@ hipError_t launch_gemm_t(const GemmArgs& g, hipStream_t s) {
   const long max_work = max_chunks * (ncols / S::COLS) + max_tiles * (ncols / T::COLS);
   const int grid = (int)std::max<long>(1, std::min<long>(max_work, (long)cu_count() * occ));
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, g);
+  if (!g.big_ok) return hipGetLastError();
+  // tiles <= ceil(capacity / 256) + (number of experts above kStreamRows rows)
+  const long max_big = ((long)(g.capacity + kBigBM - 1) / kBigBM +
+                        std::min<long>(g.nloc, (long)g.capacity / (kStreamRows + 1))) *
+                       (ncols / Big<GATED>::COLS);
+  // persistent: one workgroup per CU (a multiple of 8, so each keeps its XCD's range)
+  const long cus8 = std::max(8, cu_count() / 8 * 8);
+  const int grid_big = (int)std::max<long>(8, std::min<long>((max_big + 7) / 8 * 8, cus8));
+  hipLaunchKernelGGL(ffn_big_kernel<GATED>, dim3(grid_big), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 

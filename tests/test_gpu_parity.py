@@ -279,8 +279,11 @@ def test_layer_toy_fp32(fuse):
     (300, 32, 8, 8, 4, 256, 64, 4, 12),     # local range in the middle, I = 64
     (40, 64, 6, 8, 4, 1024, 192, 0, 64),    # many experts with 0-9 rows
     (700, 8, 2, 1, 1, 256, 256, 0, 8),      # > 64 rows per expert
-    (1200, 4, 2, 1, 1, 512, 128, 0, 4),     # > 256 rows per expert: 256-row tiles, ragged
-    (1500, 4, 2, 1, 1, 2048, 1024, 0, 4),   # 256-row tiles in XCD patches
+    (1200, 4, 2, 1, 1, 512, 128, 0, 4),     # > 256 rows per expert: 128 x 128 tiles, ragged
+    (1500, 4, 2, 1, 1, 2048, 1024, 0, 4),   # 128 x 128 tiles, K = 2048
+    (2100, 16, 8, 2, 1, 512, 256, 0, 16),   # row capacity >= 16384 but too few large tiles: 128 x 128
+    (2100, 16, 8, 2, 1, 512, 192, 2, 12),   # same capacity, I % 128 != 0: 128 x 128 tiles
+    (2060, 16, 8, 4, 2, 4096, 512, 0, 16),  # >= one 256 x 256 tile per CU in both GEMMs, ragged
 ])
 @pytest.mark.parametrize("fuse", [True, False])
 def test_layer_bf16_small(T, E, k, ng, tg, d, I, begin, nloc, fuse):
