@@ -540,86 +540,124 @@ struct Tiled {
 // Experts with more than kStreamRows rows (prefill), as an alternative to the
 // 128 x 128 tiles above: 256 weight rows x 256 tokens per tile, one workgroup
 // of 4 wavefronts per CU, each wavefront 128 x 128 on v_mfma_f32_32x32x16_bf16
-// (4 x 4 fragments, 256 float32 accumulators per lane). Per 64-k stage a
-// wavefront reads 32 KB of fragments from LDS for 64 MFMAs, so the LDS traffic
-// (reads plus the stage writes) stays at about three quarters of its
-// bandwidth when the MFMA pipes are busy; the 128 x 128 design needs more LDS
-// bandwidth than the CU has.
+// (4 x 4 fragments, 256 float32 accumulators per lane). Per k16 step a
+// wavefront reads 8 KB of fragments from LDS for 16 MFMAs, which leaves the
+// LDS with headroom while the MFMA pipes are busy (a 128 x 128 wavefront
+// tile is what makes that ratio work; 64 x 64 needs more LDS bandwidth than
+// the CU has).
 //
-// K is staged 64 at a time: global loads two stages ahead into registers
-// (coalesced: a wavefront reads 8 whole 128-byte rows per instruction), one
-// LDS write per stage into a double buffer, one barrier per stage. LDS rows
-// are 128 bytes; chunk c of row r sits at slot c ^ ((r >> 1) & 7), which keeps
-// every 16 consecutive lanes of a fragment read, and of a stage write, on
-// distinct banks.
+// K is staged 32 at a time in a ring of kBigStages LDS buffers filled by LDS
+// DMA (buffer_load_dwordx4 ... lds: the data goes from memory to LDS without
+// registers; lane l of one instruction writes 16 bytes at M0 + 16 l), issued
+// kBigStages - 1 stages ahead. The compiler waits for every outstanding LDS
+// DMA at each barrier, which would cap the look-ahead at one stage, so the
+// DMA is issued from inline assembly and its completion is waited for
+// explicitly (vmcnt counts the outstanding stages; nothing else uses vector
+// memory inside the K loop). One barrier per stage both publishes stage kt
+// and frees the buffer stage kt + 3 overwrites.
+//
+// LDS rows are 64 bytes (4 chunks of 16 bytes); chunk c of row r sits at slot
+// c ^ ((r >> 2) & 3), so the 16 rows one fragment read touches per 16 lanes
+// fall on distinct banks. A DMA instruction writes 16 rows in lane order
+// (lane l: row l / 4, slot l % 4), so lane l loads chunk (l % 4) ^ ((l / 16) % 4).
 //
 // Gated tiles hold, for 128 output columns, per wavefront row half: 64 gate
 // rows then the 64 matching up rows, so SiLU(gate) * up is formed from the
 // wavefront's own accumulators.
-constexpr int kBandTiles = 4; // token tiles per raster band
-constexpr int kBigBK = 64;
+constexpr int kBigBK = 32;
+constexpr int kBigStages = 4;
+
+// Memory -> LDS copy of 16 bytes per lane: LDS byte address lds + 16 * lane,
+// memory offset voff + soff in buffer rsrc. m0 is saved and restored.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, const i32x4_t& rsrc, uint32_t voff, uint32_t soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"  // one wait state between an SALU write of m0 and an LDS DMA
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt bits [3:0] and [15:14], the other
+// counters left at their maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = kBufferConfig;
+  return r;
+}
 
 template <bool GATED>
 struct Big {
-  static constexpr int COLS = GATED ? 128 : 256;   // output columns per tile
-  static constexpr int OP_BYTES = 256 * kBigBK * 2;  // one operand of one stage
-  static constexpr int LDS_BYTES = 2 * 2 * OP_BYTES; // [stage buffer][W | X]
+  static constexpr int COLS = GATED ? 128 : 256;            // output columns per tile
+  static constexpr int OP_BYTES = 256 * kBigBK * 2;          // one operand of one stage (16 KB)
+  static constexpr int STAGE_BYTES = 2 * OP_BYTES;
+  static constexpr int LDS_BYTES = kBigStages * STAGE_BYTES;  // 128 KB
+  static constexpr int DMA_PER_STAGE = 8;                    // per wavefront: 4 weight + 4 token loads
 
   __device__ static __forceinline__ int swz(int row, int chunk) {
-    return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
+    return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
   }
 
   __device__ static void run(const GemmArgs& a, int e, int row0, int rows, int nb, char* lds, int tid) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;   // weight rows wm*128.., tokens wn*128..
-    const int lr = tid >> 3, lc = tid & 7;     // staging: tile rows lr + 32 i, chunk lc
     const uint32_t pitch = (uint32_t)a.K * 2;
+    const int lrow = lane >> 2;                               // row within a 16-row DMA block
+    const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);        // chunk this lane fetches
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
 
-    // Weights: tile row group i (32 rows) -> first weight row wbase[i]; the
-    // lane adds its row lr. Uniform parts go to the scalar offset.
-    const __amdgpu_buffer_rsrc_t wbuf = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.W + (size_t)e * a.N * a.K), 0, (int)(a.N * pitch), kBufferConfig);
-    int wso[8];
+    // This wavefront fills 16-row blocks g = wave * 4 + i (i = 0..3) of both
+    // operands. Weights: block g -> first weight row wrow[i] (uniform).
+    const i32x4_t wbuf = buffer_rsrc(a.W + (size_t)e * a.N * a.K, (uint32_t)(a.N * pitch));
+    int wso[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
+      const int g = wave * 4 + i, r = g * 16;   // first tile row of the block
       int base;
       if (GATED) {
-        const int wmi = i >> 2, q = i & 3;   // group q of wavefront half wmi
-        base = ((q < 2) ? 0 : a.inter) + nb * COLS + wmi * 64 + (q & 1) * 32;
+        const int grp = r >> 5, wmi = grp >> 2, q = grp & 3;
+        base = ((q < 2) ? 0 : a.inter) + nb * COLS + wmi * 64 + (q & 1) * 32 + (r & 31);
       } else {
-        base = nb * 256 + i * 32;
+        base = nb * 256 + r;
       }
-      wso[i] = base * (int)pitch;
+      wso[i] = __builtin_amdgcn_readfirstlane(base * (int)pitch);
     }
-    const uint32_t wv = (uint32_t)lr * pitch + lc * 16;
+    const uint32_t wv = (uint32_t)lrow * pitch + lchunk * 16;
     // Tokens: rows past the tile's end read its first row (not stored).
-    const __amdgpu_buffer_rsrc_t xbuf = __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, -1, kBufferConfig);
-    uint32_t xv[8];
+    const i32x4_t xbuf = buffer_rsrc(a.A, 0xFFFFFFFFu);
+    uint32_t xv[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = lr + 32 * i;
+    for (int i = 0; i < 4; ++i) {
+      const int r = (wave * 4 + i) * 16 + lrow;
       xv[i] = row0 + (r < rows ? r : 0);
     }
-    a_rows<8>(a, xv);
+    a_rows<4>(a, xv);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xv[i] = xv[i] * pitch + lc * 16;
+    for (int i = 0; i < 4; ++i) xv[i] = xv[i] * pitch + lchunk * 16;
 
-    u32x4_t rw[1][8], rx[1][8];
-    auto gload = [&](u32x4_t (&w)[8], u32x4_t (&x)[8], int kt) {
-      const int ko = kt * kBigBK * 2;
+    auto issue = [&](int kt) {   // DMA of stage kt into ring slot kt % kBigStages
+      const uint32_t lw = lds_base + (kt % kBigStages) * STAGE_BYTES;
+      const uint32_t lx = lw + OP_BYTES;
+      const uint32_t ko = (uint32_t)kt * kBigBK * 2;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, wv, wso[i] + ko, 0);
+      for (int i = 0; i < 4; ++i) lds_dma16(lw + (wave * 4 + i) * 1024, wbuf, wv, wso[i] + ko);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = __builtin_amdgcn_raw_buffer_load_b128(xbuf, xv[i], ko, 0);
-    };
-    auto sstore = [&](const u32x4_t (&w)[8], const u32x4_t (&x)[8], int buf) {
-      char* lw = lds + buf * 2 * OP_BYTES;
-      char* lx = lw + OP_BYTES;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) *(u32x4_t*)(lw + swz(lr + 32 * i, lc)) = w[i];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) *(u32x4_t*)(lx + swz(lr + 32 * i, lc)) = x[i];
+      for (int i = 0; i < 4; ++i) lds_dma16(lx + (wave * 4 + i) * 1024, xbuf, xv[i], ko);
     };
 
     f32x16_t acc[4][4];
@@ -629,8 +667,8 @@ struct Big {
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
     const int fr = lane & 31, fh = lane >> 5;  // fragment row, k half
-    auto compute = [&](int buf) {
-      const char* lw = lds + buf * 2 * OP_BYTES;
+    auto compute = [&](int slot) {
+      const char* lw = lds + slot * STAGE_BYTES;
       const char* lx = lw + OP_BYTES;
 #pragma unroll
       for (int q = 0; q < kBigBK / 16; ++q) {
@@ -648,27 +686,28 @@ struct Big {
       }
     };
 
-    // One register set: the loads of stage kt + 1 are issued before stage kt
-    // is multiplied and written to the other LDS buffer after it; every
-    // wavefront finished reading that buffer before the previous barrier.
-    // (A second register set, to issue loads two stages ahead, does not fit
-    // beside the 256 accumulators without spills.)
+    // Iteration kt: wait until this wavefront's DMA of stage kt has landed
+    // (stages kt + 1 and kt + 2 may stay in flight), barrier (every
+    // wavefront's share of stage kt is in LDS, and every wavefront has
+    // finished stage kt - 1, whose slot stage kt + 3 reuses), issue stage
+    // kt + 3, multiply stage kt.
     const int nk = a.K / kBigBK;
-    gload(rw[0], rx[0], 0);
-    sstore(rw[0], rx[0], 0);
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kBigStages - 1; ++j)
+      if (j < nk) issue(j);
     for (int kt = 0; kt < nk; ++kt) {
-      const bool more = kt + 1 < nk;
-      if (more) gload(rw[0], rx[0], kt + 1);
-      compute(kt & 1);
-      if (more) sstore(rw[0], rx[0], (kt + 1) & 1);
+      if (kt + 2 < nk) wait_vmcnt<2 * DMA_PER_STAGE>();
+      else if (kt + 1 < nk) wait_vmcnt<DMA_PER_STAGE>();
+      else wait_vmcnt<0>();
       __syncthreads();
+      if (kt + kBigStages - 1 < nk) issue(kt + kBigStages - 1);
+      compute(kt % kBigStages);
     }
 
-    // acc[i][j][r]: token wn*128 + j*32 + lane%32; wavefront weight row
-    // i*32 + (r/4)*8 + (lane/32)*4 + r%4.
     // One fragment column at a time (all lanes compute, only the store is
     // guarded), so the accumulators are read out piecewise.
+    // acc[i][j][r]: token wn*128 + j*32 + lane%32; wavefront weight row
+    // i*32 + (r/4)*8 + (lane/32)*4 + r%4.
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       __builtin_amdgcn_sched_barrier(0);
@@ -718,21 +757,19 @@ __global__ __launch_bounds__(256, 1) void ffn_big_kernel(GemmArgs a) {
   const int nblk = (GATED ? a.inter : a.N) / B::COLS;
   const int total = n_tiles * nblk;
   if (total < a.big_min_items) return;  // the persistent kernel does these tiles
-  // Workgroup b runs on XCD b % 8 (round-robin dispatch). Each XCD takes a
-  // contiguous range of work items, and items are ordered in bands of
-  // kBandTiles token tiles: down a band's tiles first, then the next N block.
-  // The 32 workgroups an XCD runs at once then cover about 4 token tiles x 8
-  // N blocks, which share their operands through that XCD's L2 while they
-  // move through K at about the same pace. The grid is a multiple of 8 and
-  // at least total.
+  // Items are (token tile, N block) with N blocks fastest, taken round-robin
+  // by a grid that is a multiple of 8: workgroup b runs on XCD b % 8 and its
+  // items keep the same N block whenever nblk divides the grid, so its weight
+  // block stays in that XCD's L2 from one token tile to the next, while the
+  // XCDs read the same token tiles at about the same time (shared through the
+  // last-level cache).
+  // (The loop runs over a multiple of 8 items and skips the ones past the
+  // end; this form compiles without register spills.)
   const int per = (total + 7) / 8;
-  for (int b = blockIdx.x; b < 8 * per; b += gridDim.x) {
-    const int w = (b % 8) * per + b / 8;
+  for (int w = blockIdx.x; w < 8 * per; w += gridDim.x) {
     if (w >= total) continue;
-    const int band = w / (kBandTiles * nblk), r = w % (kBandTiles * nblk);
-    const int h = min(kBandTiles, n_tiles - band * kBandTiles);
-    const int tile = __builtin_amdgcn_readfirstlane(band * kBandTiles + r % h);
-    const int nb = __builtin_amdgcn_readfirstlane(r / h);
+    const int tile = __builtin_amdgcn_readfirstlane(w / nblk);
+    const int nb = __builtin_amdgcn_readfirstlane(w % nblk);
     const int e = __builtin_amdgcn_readfirstlane(find_expert(t_first, a.nloc, tile));
     const int row0 = __builtin_amdgcn_readfirstlane(s_lo[e] + (tile - t_first[e]) * kBigBM);
     const int rows = __builtin_amdgcn_readfirstlane(min(kBigBM, s_lo[e + 1] - row0));
