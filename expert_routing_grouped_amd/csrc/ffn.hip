@@ -392,6 +392,187 @@ struct Stream {
   }
 };
 
+// ---------------------------------------------------------------- walk path
+
+// Plain GEMMs with a short K = 64 * KQ (KQ = 1, 2; the down projection of
+// narrow experts): streaming K would give each work item a single K step, so
+// here a wavefront keeps the chunk's activations (all of K) as MFMA fragments
+// in registers and walks along N instead, one group of NTW 16-row weight
+// tiles per step: load (two steps ahead, coalesced, through the same
+// XOR-swizzled LDS tiles as the streaming path), multiply, store. A work item
+// is a chunk and ITEM_COLS output columns, J steps per wavefront.
+template <int KQ>
+struct Walk {
+  static constexpr int NTW = 2 / KQ;
+  static constexpr int MT = kStreamMT;
+  static constexpr int J = 8;                        // steps per wavefront per item
+  static constexpr int STEP_COLS = NTW * 16;
+  static constexpr int ITEM_COLS = 4 * J * STEP_COLS;
+  static constexpr int TILE_BYTES = 16 * 128;
+  static constexpr int WAVE_LDS = (MT + NTW) * KQ * TILE_BYTES;
+  static constexpr int LDS_BYTES = 4 * WAVE_LDS;
+
+  template <int MTA>
+  __device__ static void run_mt(const GemmArgs& a, int e, int lo, int m, int item, char* smem) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int fr = lane & 15, g = lane >> 4;
+    const int lr = lane >> 3, lc = lane & 7;
+    const uint32_t pitch = (uint32_t)a.K * 2;
+    const int c0 = item * ITEM_COLS + wave * J * STEP_COLS;   // this wavefront's first column
+    const int steps = __builtin_amdgcn_readfirstlane(max(0, min(J, (a.N - c0) / STEP_COLS)));
+    if (steps == 0) return;
+
+    char* xs = smem + wave * WAVE_LDS;   // MT * KQ activation tiles, then NTW * KQ weight tiles
+    char* ws = xs + MT * KQ * TILE_BYTES;
+    const int woff[2] = {lr * 128 + ((lc ^ lr) << 4), (8 + lr) * 128 + ((lc ^ lr) << 4)};
+    const int roff[2] = {fr * 128 + ((g ^ (fr & 7)) << 4), fr * 128 + (((4 + g) ^ (fr & 7)) << 4)};
+
+    // Activations: all K of the chunk's rows, once (rows past the end read row 0).
+    const __amdgpu_buffer_rsrc_t abuf = __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, -1, kBufferConfig);
+    uint32_t av[MTA][2];
+#pragma unroll
+    for (int i = 0; i < MTA; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = i * 16 + h * 8 + lr;
+        av[i][h] = lo + (r < m ? r : 0);
+      }
+    a_rows<MTA * 2>(a, &av[0][0]);
+    {
+      u32x4_t ax[MTA][KQ][2];
+#pragma unroll
+      for (int i = 0; i < MTA; ++i)
+#pragma unroll
+        for (int q = 0; q < KQ; ++q)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            ax[i][q][h] = __builtin_amdgcn_raw_buffer_load_b128(abuf, av[i][h] * pitch + lc * 16, q * 128, 0);
+#pragma unroll
+      for (int i = 0; i < MTA; ++i)
+#pragma unroll
+        for (int q = 0; q < KQ; ++q)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) *(u32x4_t*)(xs + (i * KQ + q) * TILE_BYTES + woff[h]) = ax[i][q][h];
+    }
+    bf16x8_t af[MTA][KQ][2];
+#pragma unroll
+    for (int i = 0; i < MTA; ++i)
+#pragma unroll
+      for (int q = 0; q < KQ; ++q)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) af[i][q][u] = *(const bf16x8_t*)(xs + (i * KQ + q) * TILE_BYTES + roff[u]);
+
+    // Weights: step j, tile t, half h: rows c0 + j*STEP_COLS + t*16 + 8h + lr.
+    const __amdgpu_buffer_rsrc_t wbuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.W + (size_t)e * a.N * a.K), 0, (int)(a.N * pitch), kBufferConfig);
+    const uint32_t wv = (uint32_t)(c0 + lr) * pitch + lc * 16;
+    u32x4_t wr[3][NTW][KQ][2];
+    auto load_w = [&](u32x4_t (&w)[NTW][KQ][2], int j) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int q = 0; q < KQ; ++q)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            w[t][q][h] = __builtin_amdgcn_raw_buffer_load_b128(
+                wbuf, wv, (j * STEP_COLS + t * 16 + h * 8) * (int)pitch + q * 128, kNonTemporal);
+    };
+    // Outputs go out in whole 128-byte row segments (64 columns): SEG steps
+    // are staged in the activation tiles' LDS (free once the fragments are in
+    // registers), XOR-swizzled by 16-byte chunk, then each store instruction
+    // writes 8 rows x 128 bytes.
+    constexpr int SEG = 64 / STEP_COLS;
+    char* os = xs;  // [64 rows][128 bytes]
+    auto step = [&](const u32x4_t (&w)[NTW][KQ][2], int j) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int q = 0; q < KQ; ++q)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) *(u32x4_t*)(ws + (t * KQ + q) * TILE_BYTES + woff[h]) = w[t][q][h];
+      f32x4_t acc[MTA][NTW];
+#pragma unroll
+      for (int i = 0; i < MTA; ++i)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int q = 0; q < KQ; ++q)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          bf16x8_t wf[NTW];
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) wf[t] = *(const bf16x8_t*)(ws + (t * KQ + q) * TILE_BYTES + roff[u]);
+#pragma unroll
+          for (int i = 0; i < MTA; ++i)
+#pragma unroll
+            for (int t = 0; t < NTW; ++t)
+              acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[t], af[i][q][u], acc[i][t], 0, 0, 0);
+        }
+      // Lane holds output row i*16 + lane % 16, columns t*16 + 4*(lane/16) + (0..3)
+      // of this step: staged at column (j % 2) * STEP_COLS + ... of the row segment.
+#pragma unroll
+      for (int i = 0; i < MTA; ++i) {
+        const int row = i * 16 + fr;
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          const int cb = ((j % SEG) * STEP_COLS + t * 16 + g * 4) * 2;   // byte in the row segment
+          const int off = row * 128 + ((((cb >> 4) ^ (row & 7))) << 4) + (cb & 15);
+          *(uint2*)(os + off) = make_uint2(pack_bf16x2(acc[i][t][0], acc[i][t][1]),
+                                           pack_bf16x2(acc[i][t][2], acc[i][t][3]));
+        }
+      }
+      if (j % SEG == SEG - 1 || j + 1 == steps) {
+        // row segment of columns c0 + (j - j % SEG) * STEP_COLS .. + 64, of
+        // which the walk filled the first chunks (all, unless it ended early)
+        const int colb = c0 + (j - j % SEG) * STEP_COLS;
+        const int chunks = (j % SEG + 1) * STEP_COLS / 8;
+#pragma unroll
+        for (int rr = 0; rr < MTA * 2; ++rr) {
+          const int row = rr * 8 + lr;
+          const u32x4_t v = *(const u32x4_t*)(os + row * 128 + ((lc ^ (row & 7)) << 4));
+          if (row < m && lc < chunks)
+            *(u32x4_t*)(a.C + (size_t)(lo + row) * a.ldc + colb + lc * 8) = v;
+        }
+      }
+    };
+
+    // Weights two steps ahead in three register sets (steps past the end
+    // reload the last one); the main loop runs whole periods of three.
+    load_w(wr[0], 0);
+    load_w(wr[1], min(1, steps - 1));
+    int j = 0;
+#define MOE_WALK(q)                                 \
+  load_w(wr[((q) + 2) % 3], min(j + 2, steps - 1)); \
+  __builtin_amdgcn_sched_barrier(0);                \
+  step(wr[(q) % 3], j);                             \
+  __builtin_amdgcn_sched_barrier(0);                \
+  ++j;
+    for (; j + 3 <= steps;) {
+      MOE_WALK(0) MOE_WALK(1) MOE_WALK(2)
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (j >= steps) break;
+      MOE_WALK(q)
+    }
+#undef MOE_WALK
+  }
+
+  __device__ static void run(const GemmArgs& a, const int* s_lo, int e, int chunk, int item, char* smem) {
+    e = __builtin_amdgcn_readfirstlane(e);
+    const int lo = __builtin_amdgcn_readfirstlane(s_lo[e] + chunk * kChunkRows);
+    const int m = __builtin_amdgcn_readfirstlane(min(kChunkRows, s_lo[e + 1] - lo));
+    item = __builtin_amdgcn_readfirstlane(item);
+    switch ((m + 15) >> 4) {
+      case 1: run_mt<1>(a, e, lo, m, item, smem); break;
+      case 2: run_mt<2>(a, e, lo, m, item, smem); break;
+      case 3: run_mt<3>(a, e, lo, m, item, smem); break;
+      default: run_mt<4>(a, e, lo, m, item, smem); break;
+    }
+  }
+};
+
 // ---------------------------------------------------------------- tiled path
 
 // Experts with more than kStreamRows rows (prefill): 128 weight rows x 128
@@ -784,11 +965,15 @@ __global__ __launch_bounds__(256, 1) void ffn_big_kernel(GemmArgs a) {
 
 // One persistent kernel per GEMM: first the streamed row chunks, then the row
 // tiles of larger experts. The two paths share the LDS buffer.
-template <int NTW, int KS, bool GATED>
+// KQ = 0: chunks on the streaming path; KQ = 1, 2 (plain GEMMs with K = 64 KQ):
+// chunks on the walk path.
+template <int NTW, int KS, bool GATED, int KQ>
 __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(GemmArgs a) {
   using S = Stream<NTW, KS, GATED, kStreamDW, kStreamDA>;
+  using Wk = Walk<KQ == 0 ? 1 : KQ>;
   using T = Tiled<GATED>;
-  constexpr int SMEM = S::LDS_BYTES > T::LDS_BYTES ? S::LDS_BYTES : T::LDS_BYTES;
+  constexpr int SL = KQ == 0 ? S::LDS_BYTES : Wk::LDS_BYTES;
+  constexpr int SMEM = SL > T::LDS_BYTES ? SL : T::LDS_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ int s_first[kMaxLocal + 1];
   __shared__ int t_first[kMaxLocal + 1];
@@ -797,7 +982,8 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(GemmArgs a) {
   int n_chunks, n_tiles, n_big;
   build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big);
   const int ncols = GATED ? a.inter : a.N;
-  const int slabs = ncols / S::COLS, nblk = ncols / T::COLS;
+  const int slabs = KQ == 0 ? ncols / S::COLS : (ncols + Wk::ITEM_COLS - 1) / Wk::ITEM_COLS;
+  const int nblk = ncols / T::COLS;
   const int n_stream = n_chunks * slabs;
   // Same decision as ffn_big_kernel: it takes the tiled experts when it has
   // enough tiles to fill the GPU, else they are done here in 128 x 128 tiles.
@@ -807,7 +993,8 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(GemmArgs a) {
     if (w < n_stream) {
       const int c = w / slabs;
       const int e = find_expert(s_first, a.nloc, c);
-      S::run(a, s_lo, e, c - s_first[e], w % slabs, smem);
+      if (KQ == 0) S::run(a, s_lo, e, c - s_first[e], w % slabs, smem);
+      else Wk::run(a, s_lo, e, c - s_first[e], w % slabs, smem);
       __syncthreads();  // the LDS buffer is reused by the next work item
     } else {
       const int tile = (w - n_stream) / nblk, nb = (w - n_stream) % nblk;
@@ -923,7 +1110,7 @@ bool use_big(const GemmArgs& g) {
          (GATED ? g.inter % 128 == 0 : g.N % 256 == 0);
 }
 
-template <bool GATED, int KS>
+template <bool GATED, int KS, int KQ = 0>
 hipError_t launch_gemm_t(const GemmArgs& g0, hipStream_t s) {
   constexpr int NTW = 2;
   using S = Stream<NTW, KS, GATED, kStreamDW, kStreamDA>;
@@ -931,13 +1118,15 @@ hipError_t launch_gemm_t(const GemmArgs& g0, hipStream_t s) {
   GemmArgs g = g0;
   g.big_ok = use_big<GATED>(g) ? 1 : 0;
   g.big_min_items = cu_count();
-  auto kernel = ffn_gemm_kernel<NTW, KS, GATED>;
+  auto kernel = ffn_gemm_kernel<NTW, KS, GATED, KQ>;
   static const int occ = occupancy(kernel, 256);
   const int ncols = GATED ? g.inter : g.N;
   const long max_chunks = std::min<long>((long)g.nloc * (kStreamRows / kChunkRows),
                                          (long)(g.capacity + kChunkRows - 1) / kChunkRows + g.nloc);
   const long max_tiles = (long)(g.capacity + kTileBM - 1) / kTileBM + g.nloc;
-  const long max_work = max_chunks * (ncols / S::COLS) + max_tiles * (ncols / T::COLS);
+  const long per_chunk = KQ == 0 ? ncols / S::COLS
+                                 : (ncols + Walk<KQ == 0 ? 1 : KQ>::ITEM_COLS - 1) / Walk<KQ == 0 ? 1 : KQ>::ITEM_COLS;
+  const long max_work = max_chunks * per_chunk + max_tiles * (ncols / T::COLS);
   const int grid = (int)std::max<long>(1, std::min<long>(max_work, (long)cu_count() * occ));
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, g);
   if (!g.big_ok) return hipGetLastError();
@@ -954,6 +1143,8 @@ hipError_t launch_gemm_t(const GemmArgs& g0, hipStream_t s) {
 
 template <bool GATED>
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
+  if (!GATED && g.K == 64) return launch_gemm_t<false, 1, 1>(g, s);
+  if (!GATED && g.K == 128) return launch_gemm_t<false, 1, 2>(g, s);
   switch (stream_ks<GATED>(g.K)) {
     case 4: return launch_gemm_t<GATED, 4>(g, s);
     case 2: return launch_gemm_t<GATED, 2>(g, s);
