@@ -60,6 +60,9 @@ struct GemmArgs {
   int ldc;
   int big_ok;             // the large-tile kernel is launched too
   int big_min_items;      // ... and takes the tiled experts when it has at least this many tiles
+  float* partials;        // shared-activation path: float32 K-part sums (null: one K part)
+  int kparts;             // shared-activation path: K parts per chunk
+  int* chunk_desc;        // shared-activation path: [0] = chunks, then (lo, m) per chunk
 };
 
 // Replaces each permuted row number by the row of A that holds it. All index
@@ -92,14 +95,16 @@ constexpr int kNonTemporal = 2;
 
 // Splits the local experts by row count m, in expert order (and leaves the
 // clamped row bounds in s_lo: rows of expert e are [s_lo[e], s_lo[e] + m);
-// n_big = the tiles of kBigBM rows the tiled experts need):
+// n_big = the tiles of kBigBM rows the tiled experts need; with all_chunks
+// every expert is cut into chunks):
 //   1 <= m <= kStreamRows: streamed, in ceil(m / kChunkRows) row chunks;
 //                          s_first[e] = first chunk of expert e, s_first[nloc] = chunks
 //   m > kStreamRows:       tiled, in ceil(m / bm) row tiles;
 //                          t_first[e] = first tile of expert e, t_first[nloc] = tiles
 // Every thread of the 256-thread workgroup calls this; 4 experts per thread.
 __device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_first, int* s_lo,
-                            int* wsum, int& n_chunks, int& n_tiles, int& n_big) {
+                            int* wsum, int& n_chunks, int& n_tiles, int& n_big,
+                            bool all_chunks = false) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int cc[4], tc[4], cs = 0, ct = 0, cb = 0;
 #pragma unroll
@@ -113,8 +118,9 @@ __device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_firs
       s_lo[e] = lo;
       if (e == a.nloc - 1) s_lo[a.nloc] = max(lo, hi);
     }
-    cc[q] = (m > 0 && m <= kStreamRows) ? (m + kChunkRows - 1) / kChunkRows : 0;
-    tc[q] = (m > kStreamRows) ? (m + bm - 1) / bm : 0;
+    const bool chunked = all_chunks || m <= kStreamRows;
+    cc[q] = (m > 0 && chunked) ? (m + kChunkRows - 1) / kChunkRows : 0;
+    tc[q] = (m > 0 && !chunked) ? (m + bm - 1) / bm : 0;
     cs += cc[q];
     ct += tc[q];
     cb += (m > kStreamRows) ? (m + kBigBM - 1) / kBigBM : 0;
@@ -572,6 +578,233 @@ struct Walk {
     }
   }
 };
+
+// ---------------------------------------------------------------- shared-activation path
+
+// Gated GEMMs of narrow experts (inter a multiple of 64, at most 128): a
+// workgroup owns 64 output columns of one chunk -- 64 gate rows and the 64
+// matching up rows of the weights, 16 + 16 per wavefront -- so all four
+// wavefronts multiply the same activation K step. Each step's activation
+// tile is loaded once, cooperatively, into a shared double-buffered LDS tile
+// (one barrier per step) instead of once per 16-column slab, which cuts the
+// activation traffic by the 4 slabs' repeat. With few columns per expert the
+// work is then split over KP parts of K: each item writes float32 partial
+// sums, and ffn_finalize_kernel adds the parts in order (deterministic) and
+// applies SiLU(gate) * up. Every expert is cut into 64-row chunks here, large
+// ones included.
+constexpr int kShareCols = 64;   // output columns per item
+
+struct SharedA {
+  static constexpr int NSET = 4;   // register sets: loads NSET - 1 steps ahead
+  static constexpr int MT = kStreamMT;
+  static constexpr int KSTEP = 64;
+  static constexpr int TILE_BYTES = 16 * 128;
+  static constexpr int A_BUF = MT * TILE_BYTES;                 // one step's activation tiles
+  static constexpr int W_OFF = 2 * A_BUF;                       // after the two activation buffers
+  static constexpr int DUMMY_OFF = W_OFF + 4 * 2 * TILE_BYTES;  // per-wave sink for unused shares
+  static constexpr int LDS_BYTES = DUMMY_OFF + 4 * 1024;
+  static constexpr int PART_FLOATS = 64 * 2 * kShareCols;      // one item's partial sums
+
+  template <int MTA>
+  __device__ static void run_mt(const GemmArgs& a, int e, int lo, int m, int slab, int kp,
+                                float* part, char* smem) {
+    constexpr int HALVES = 2 * MTA;            // 8-row half tiles of one activation step
+    constexpr int NSH = (HALVES + 3) / 4;      // shares per wavefront
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int fr = lane & 15, g = lane >> 4;
+    const int lr = lane >> 3, lc = lane & 7;
+    const uint32_t pitch = (uint32_t)a.K * 2;
+    const int woff[2] = {lr * 128 + ((lc ^ lr) << 4), (8 + lr) * 128 + ((lc ^ lr) << 4)};
+    const int roff[2] = {fr * 128 + ((g ^ (fr & 7)) << 4), fr * 128 + (((4 + g) ^ (fr & 7)) << 4)};
+
+    // Weights: gate rows slab*64 + 16*wave + (8h + lr), up rows inter + the same.
+    const __amdgpu_buffer_rsrc_t wbuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.W + (size_t)e * a.N * a.K), 0, (int)(a.N * pitch), kBufferConfig);
+    const uint32_t wv = (uint32_t)(slab * kShareCols + 16 * wave + lr) * pitch + lc * 16;
+    // Activation share j of this wavefront: half tile hh = wave + 4j (tile hh / 2,
+    // half hh % 2); shares past the step's half tiles load row 0 into a sink.
+    const __amdgpu_buffer_rsrc_t abuf = __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, -1, kBufferConfig);
+    uint32_t av[NSH];
+    int aoff[NSH];
+#pragma unroll
+    for (int j = 0; j < NSH; ++j) {
+      const int hh = wave + 4 * j;
+      const int r = (hh >> 1) * 16 + (hh & 1) * 8 + lr;
+      av[j] = lo + ((hh < HALVES && r < m) ? r : 0);
+      aoff[j] = hh < HALVES ? (hh >> 1) * TILE_BYTES + woff[hh & 1] : DUMMY_OFF + wave * 1024 + lane * 16;
+    }
+    a_rows<NSH>(a, av);
+#pragma unroll
+    for (int j = 0; j < NSH; ++j) av[j] = av[j] * pitch + lc * 16;
+
+    const int kw = a.K / a.kparts, kbeg = kp * kw, klast = kbeg + kw - KSTEP;
+    const int steps = kw / KSTEP;
+    char* wl = smem + W_OFF + wave * 2 * TILE_BYTES;
+
+    f32x4_t acc[MTA][2];
+#pragma unroll
+    for (int i = 0; i < MTA; ++i) acc[i][0] = acc[i][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    u32x4_t wr[NSET][2][2], ar[NSET][NSH];
+    auto load = [&](int set, int kk) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          wr[set][t][h] = __builtin_amdgcn_raw_buffer_load_b128(
+              wbuf, wv, ((t ? a.inter : 0) + 8 * h) * (int)pitch + kk * 2, kNonTemporal);
+#pragma unroll
+      for (int j = 0; j < NSH; ++j) ar[set][j] = __builtin_amdgcn_raw_buffer_load_b128(abuf, av[j], kk * 2, 0);
+    };
+    auto step = [&](int set, int buf) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) *(u32x4_t*)(wl + t * TILE_BYTES + woff[h]) = wr[set][t][h];
+#pragma unroll
+      for (int j = 0; j < NSH; ++j) *(u32x4_t*)(smem + (aoff[j] < DUMMY_OFF ? buf * A_BUF : 0) + aoff[j]) = ar[set][j];
+      __syncthreads();  // the step's activation tiles are complete
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8_t wf[2], xf[MTA];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) wf[t] = *(const bf16x8_t*)(wl + t * TILE_BYTES + roff[u]);
+#pragma unroll
+        for (int i = 0; i < MTA; ++i) xf[i] = *(const bf16x8_t*)(smem + buf * A_BUF + i * TILE_BYTES + roff[u]);
+#pragma unroll
+        for (int i = 0; i < MTA; ++i)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[t], xf[i], acc[i][t], 0, 0, 0);
+      }
+    };
+
+    // Loads NSET - 1 steps ahead in NSET register sets. Step s writes
+    // activation buffer s % 2, which every wavefront finished reading in step
+    // s - 2, before the barrier of step s - 1. The main loop runs whole
+    // periods of NSET steps (NSET even).
+#pragma unroll
+    for (int j = 0; j < NSET - 1; ++j) load(j, min(kbeg + j * KSTEP, klast));
+    int kk = kbeg, st = 0;
+#define MOE_SHARED(q)                                             \
+  load(((q) + NSET - 1) % NSET, min(kk + (NSET - 1) * KSTEP, klast)); \
+  __builtin_amdgcn_sched_barrier(0);                              \
+  step((q) % NSET, (q) % 2);                                      \
+  __builtin_amdgcn_sched_barrier(0);                              \
+  kk += KSTEP;
+    for (; st + NSET <= steps; st += NSET) {
+#pragma unroll
+      for (int q = 0; q < NSET; ++q) { MOE_SHARED(q) }
+    }
+#pragma unroll
+    for (int q = 0; q < NSET - 1; ++q) {
+      if (st + q >= steps) break;
+      MOE_SHARED(q)
+    }
+#undef MOE_SHARED
+
+    // Lane holds rows i*16 + lane % 16 and, per t (0 gate, 1 up), columns
+    // 16*wave + 4*(lane/16) + (0..3) of the item's 64.
+#pragma unroll
+    for (int i = 0; i < MTA; ++i) {
+      const int row = i * 16 + fr;
+      if (row >= m) continue;
+      const int col = 16 * wave + 4 * g;
+      if (part) {
+        float* prow = part + row * 2 * kShareCols;
+        *(f32x4_t*)(prow + col) = acc[i][0];
+        *(f32x4_t*)(prow + kShareCols + col) = acc[i][1];
+      } else {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = silu(acc[i][0][r]) * acc[i][1][r];
+        *(uint2*)(a.C + (size_t)(lo + row) * a.ldc + slab * kShareCols + col) =
+            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+      }
+    }
+  }
+
+  __device__ static void run(const GemmArgs& a, const int* s_lo, int e, int chunk, int slab, int kp,
+                             float* part, char* smem) {
+    e = __builtin_amdgcn_readfirstlane(e);
+    const int lo = __builtin_amdgcn_readfirstlane(s_lo[e] + chunk * kChunkRows);
+    const int m = __builtin_amdgcn_readfirstlane(min(kChunkRows, s_lo[e + 1] - lo));
+    switch ((m + 15) >> 4) {
+      case 1: run_mt<1>(a, e, lo, m, slab, kp, part, smem); break;
+      case 2: run_mt<2>(a, e, lo, m, slab, kp, part, smem); break;
+      case 3: run_mt<3>(a, e, lo, m, slab, kp, part, smem); break;
+      default: run_mt<4>(a, e, lo, m, slab, kp, part, smem); break;
+    }
+  }
+};
+
+// Items (chunk, slab, K part), K parts fastest; item w's partial sums are
+// partials[w * PART_FLOATS ...] as [64 rows][gate 64 | up 64].
+__global__ __launch_bounds__(256, 2) void ffn_shared_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[SharedA::LDS_BYTES];
+  __shared__ int s_first[kMaxLocal + 1];
+  __shared__ int t_first[kMaxLocal + 1];
+  __shared__ int s_lo[kMaxLocal + 1];
+  __shared__ int wsum[12];
+  int n_chunks, n_tiles, n_big;
+  build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big, true);
+  const int slabs = a.inter / kShareCols, kp = a.kparts;
+  const int total = n_chunks * slabs * kp;
+  if (a.chunk_desc && blockIdx.x == 0 && threadIdx.x == 0) a.chunk_desc[0] = n_chunks;
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int c = __builtin_amdgcn_readfirstlane(w / (slabs * kp));
+    const int slab = __builtin_amdgcn_readfirstlane((w / kp) % slabs);
+    const int part = __builtin_amdgcn_readfirstlane(w % kp);
+    const int e = find_expert(s_first, a.nloc, c);
+    if (a.chunk_desc && slab == 0 && part == 0 && threadIdx.x == 0) {  // for ffn_finalize_kernel
+      const int lo = s_lo[e] + (c - s_first[e]) * kChunkRows;
+      a.chunk_desc[1 + 2 * c] = lo;
+      a.chunk_desc[2 + 2 * c] = min(kChunkRows, s_lo[e + 1] - lo);
+    }
+    SharedA::run(a, s_lo, e, c - s_first[e], slab, part,
+                 a.partials ? a.partials + (size_t)w * SharedA::PART_FLOATS : nullptr, smem);
+    __syncthreads();  // LDS is reused by the next item
+  }
+}
+
+// h = SiLU(sum of gate parts) * (sum of up parts) for every (chunk, slab),
+// parts added in order. The chunk count and each chunk's rows come from the
+// table ffn_shared_kernel writes.
+__global__ __launch_bounds__(256) void ffn_finalize_kernel(GemmArgs a) {
+  const int slabs = a.inter / kShareCols, kp = a.kparts;
+  const int total = a.chunk_desc[0] * slabs;   // written by ffn_shared_kernel
+  const int row = threadIdx.x >> 2, c16 = (threadIdx.x & 3) * 16;  // 64 rows x 4 column groups
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int c = w / slabs, slab = w % slabs;
+    const int lo = a.chunk_desc[1 + 2 * c], m = a.chunk_desc[2 + 2 * c];
+    if (row >= m) continue;
+    const float* p = a.partials + ((size_t)w * kp) * SharedA::PART_FLOATS + row * 2 * kShareCols + c16;
+    f32x4_t gs[4], us[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      gs[q] = *(const f32x4_t*)(p + 4 * q);
+      us[q] = *(const f32x4_t*)(p + kShareCols + 4 * q);
+    }
+    for (int k = 1; k < kp; ++k) {
+      const float* pk = p + (size_t)k * SharedA::PART_FLOATS;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        gs[q] += *(const f32x4_t*)(pk + 4 * q);
+        us[q] += *(const f32x4_t*)(pk + kShareCols + 4 * q);
+      }
+    }
+    uint32_t o[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[2 * q] = pack_bf16x2(silu(gs[q][0]) * us[q][0], silu(gs[q][1]) * us[q][1]);
+      o[2 * q + 1] = pack_bf16x2(silu(gs[q][2]) * us[q][2], silu(gs[q][3]) * us[q][3]);
+    }
+    uint4* dst = (uint4*)(a.C + (size_t)(lo + row) * a.ldc + slab * kShareCols + c16);
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
 
 // ---------------------------------------------------------------- tiled path
 
@@ -1152,13 +1385,51 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   }
 }
 
+// The shared-activation path serves gated GEMMs of narrow experts (inter a
+// multiple of 64, at most 128); K is split into this many parts.
+bool use_shared(int hidden, int inter) { return inter % kShareCols == 0 && inter <= 128 && hidden >= 1024; }
+int shared_kparts(int hidden) { return hidden >= 4096 ? 4 : hidden >= 2048 ? 2 : 1; }
+long shared_max_chunks(int num_local, int capacity) {
+  return (long)(capacity + kChunkRows - 1) / kChunkRows + num_local;
+}
+
 }  // namespace
 
 size_t ffn_workspace_size(int num_local, int hidden, int inter, int capacity, bool bf16) {
-  (void)num_local;
-  (void)hidden;
-  return align256((size_t)capacity * inter * (bf16 ? 2 : 4));  // h
+  size_t bytes = align256((size_t)capacity * inter * (bf16 ? 2 : 4));  // h
+  if (bf16 && use_shared(hidden, inter) && shared_kparts(hidden) > 1) {  // K-part sums, chunk table
+    const size_t chunks = (size_t)shared_max_chunks(num_local, capacity);
+    bytes += align256(chunks * (inter / kShareCols) * shared_kparts(hidden) * SharedA::PART_FLOATS *
+                      sizeof(float));
+    bytes += align256((1 + 2 * chunks) * sizeof(int));
+  }
+  return bytes;
 }
+
+namespace {
+
+hipError_t launch_gate_up_shared(const GemmArgs& g0, size_t h_bytes, void* workspace, hipStream_t s) {
+  GemmArgs g = g0;
+  g.kparts = shared_kparts(g.K);
+  const long chunks = shared_max_chunks(g.nloc, g.capacity);
+  const long items = chunks * (g.inter / kShareCols);
+  g.partials = nullptr;
+  g.chunk_desc = nullptr;
+  if (g.kparts > 1) {
+    char* p = (char*)workspace + align256(h_bytes);
+    g.partials = (float*)p;
+    g.chunk_desc = (int*)(p + align256((size_t)items * g.kparts * SharedA::PART_FLOATS * sizeof(float)));
+  }
+  static const int occ = occupancy(ffn_shared_kernel, 256);
+  const int grid = (int)std::max<long>(1, std::min<long>(items * g.kparts, (long)cu_count() * occ));
+  hipLaunchKernelGGL(ffn_shared_kernel, dim3(grid), dim3(256), 0, s, g);
+  if (g.kparts == 1) return hipGetLastError();
+  const int grid_f = (int)std::max<long>(1, std::min<long>(items, (long)cu_count() * 4));
+  hipLaunchKernelGGL(ffn_finalize_kernel, dim3(grid_f), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.capacity == 0) return hipSuccess;
@@ -1169,7 +1440,9 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
                 (uint16_t*)a.workspace, I};
     GemmArgs g2{(const uint16_t*)a.workspace, nullptr, 1, a.offsets, a.num_local, a.capacity,
                 (const uint16_t*)a.w_down, d, I, I, (uint16_t*)a.o_sorted, d};
-    const hipError_t err = launch_gemm<true>(g1, s);
+    const hipError_t err = use_shared(d, I)
+        ? launch_gate_up_shared(g1, (size_t)a.capacity * I * 2, a.workspace, s)
+        : launch_gemm<true>(g1, s);
     if (err != hipSuccess) return err;
     return launch_gemm<false>(g2, s);
   }

@@ -284,6 +284,11 @@ def test_layer_toy_fp32(fuse):
     (2100, 16, 8, 2, 1, 512, 256, 0, 16),   # row capacity >= 16384 but too few large tiles: 128 x 128
     (2100, 16, 8, 2, 1, 512, 192, 2, 12),   # same capacity, I % 128 != 0: 128 x 128 tiles
     (2060, 16, 8, 4, 2, 4096, 512, 0, 16),  # >= one 256 x 256 tile per CU in both GEMMs, ragged
+    # narrow experts: shared activation tiles, K split in 2 / 1 / 4 parts + finalize
+    (300, 32, 8, 8, 4, 2048, 64, 4, 12),
+    (200, 16, 4, 4, 2, 1024, 128, 0, 16),
+    (700, 8, 2, 1, 1, 4096, 128, 0, 8),
+    (1200, 4, 2, 1, 1, 1024, 64, 0, 4),     # > 256 rows per expert, all in 64-row chunks
 ])
 @pytest.mark.parametrize("fuse", [True, False])
 def test_layer_bf16_small(T, E, k, ng, tg, d, I, begin, nloc, fuse):
