@@ -202,6 +202,11 @@ __global__ __launch_bounds__(256) void block_scatter_kernel(
   wave_scatter(ids, lo, hi, begin, nloc, nbits, cnt + w * nloc, sorted_assign, assign_pos);
 }
 
+// Single-workgroup sort (n <= kSingleBlockMax): each wavefront's chunk is
+// loaded once, all its 64-id groups at a time, and kept in registers (local
+// expert and the mask of equal keys) for both the count and the scatter pass.
+constexpr int kSortGroups = kSingleBlockMax / kSortWaves / 64;   // 64-id groups per wavefront
+
 __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids, int n, int begin,
                                                     int nloc, int nbits, int* __restrict__ counts,
                                                     int* __restrict__ offsets,
@@ -211,15 +216,33 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids,
   int* cnt = lds;                              // [kSortWaves][nloc]
   int* wbase = lds + kSortWaves * nloc;        // [kSortWaves]
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
   for (int i = threadIdx.x; i < kSortWaves * nloc; i += blockDim.x) cnt[i] = 0;
-  __syncthreads();
 
-  const int per_wave = (((n + kSortWaves - 1) / kSortWaves) + 63) & ~63;
+  const int per_wave = (((n + kSortWaves - 1) / kSortWaves) + 63) & ~63;   // <= 64 * kSortGroups
   const int lo = min(n, w * per_wave), hi = min(n, lo + per_wave);
   int* my_cnt = cnt + w * nloc;
 
-  // pass 1: counts per (wave, expert)
-  wave_count(ids, lo, hi, begin, nloc, nbits, my_cnt);
+  // load the chunk: one id per lane and group
+  int raw[kSortGroups];
+#pragma unroll
+  for (int g = 0; g < kSortGroups; ++g) {
+    const int a = lo + g * 64 + lane;
+    raw[g] = a < hi ? ids[a] - begin : -1;
+  }
+  int ev[kSortGroups];
+  uint64_t peers[kSortGroups];
+#pragma unroll
+  for (int g = 0; g < kSortGroups; ++g) {
+    ev[g] = (unsigned)raw[g] < (unsigned)nloc ? raw[g] : -1;
+    peers[g] = match_key(ev[g], ev[g] >= 0, nbits);
+  }
+  __syncthreads();  // counters cleared
+
+  // pass 1: counts per (wave, expert); the lowest lane of each key group adds
+#pragma unroll
+  for (int g = 0; g < kSortGroups; ++g)
+    if (ev[g] >= 0 && (peers[g] & lt_mask) == 0ull) my_cnt[ev[g]] += __popcll(peers[g]);
   __syncthreads();
 
   // scan: per-expert column prefix over waves, then exclusive scan over experts
@@ -252,8 +275,23 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids,
   }
   __syncthreads();
 
-  // pass 2: scatter in chunk order
-  wave_scatter(ids, lo, hi, begin, nloc, nbits, my_cnt, sorted_assign, assign_pos);
+  // pass 2: scatter in chunk order; LDS operations of one wave execute in
+  // order, so every lane reads the running base before its group's leader
+  // advances it
+#pragma unroll
+  for (int g = 0; g < kSortGroups; ++g) {
+    const int a = lo + g * 64 + lane;
+    if (a < hi) {
+      if (ev[g] >= 0) {
+        const int p = my_cnt[ev[g]] + __popcll(peers[g] & lt_mask);
+        sorted_assign[p] = a;
+        assign_pos[a] = p;
+      } else {
+        assign_pos[a] = -1;
+      }
+    }
+    if (ev[g] >= 0 && (peers[g] & lt_mask) == 0ull) my_cnt[ev[g]] += __popcll(peers[g]);
+  }
 }
 
 __global__ void zero_counts_kernel(int nloc, int* counts, int* offsets) {
