@@ -960,26 +960,27 @@ struct Tiled {
 // tile is what makes that ratio work; 64 x 64 needs more LDS bandwidth than
 // the CU has).
 //
-// K is staged 32 at a time in a ring of kBigStages LDS buffers filled by LDS
-// DMA (buffer_load_dwordx4 ... lds: the data goes from memory to LDS without
-// registers; lane l of one instruction writes 16 bytes at M0 + 16 l), issued
-// kBigStages - 1 stages ahead. The compiler waits for every outstanding LDS
-// DMA at each barrier, which would cap the look-ahead at one stage, so the
-// DMA is issued from inline assembly and its completion is waited for
-// explicitly (vmcnt counts the outstanding stages; nothing else uses vector
-// memory inside the K loop). One barrier per stage both publishes stage kt
-// and frees the buffer stage kt + 3 overwrites.
+// K is staged 64 at a time in two LDS buffers filled by LDS DMA
+// (buffer_load_dwordx4 ... lds: the data goes from memory to LDS without
+// registers; lane l of one instruction writes 16 bytes at M0 + 16 l). Each
+// DMA instruction covers 8 rows x 128 bytes, whole cache lines (from L2, an
+// instruction over 16 half lines moved about half the bytes per clock of
+// one over 8 whole lines). While one buffer is multiplied the next stage
+// (64 KB) is loaded into the other. The DMA is issued from inline assembly
+// and waited for explicitly: the compiler would otherwise wait for every
+// outstanding LDS DMA at each barrier.
 //
-// LDS rows are 64 bytes (4 chunks of 16 bytes); chunk c of row r sits at slot
-// c ^ ((r >> 2) & 3), so the 16 rows one fragment read touches per 16 lanes
-// fall on distinct banks. A DMA instruction writes 16 rows in lane order
-// (lane l: row l / 4, slot l % 4), so lane l loads chunk (l % 4) ^ ((l / 16) % 4).
+// LDS rows are 128 bytes (8 chunks of 16 bytes); chunk c of row r sits at
+// slot c ^ ((r >> 1) & 7), so the 16 rows one fragment read touches per 16
+// lanes fall on 16 distinct 16-byte bank groups. A DMA instruction writes 8
+// rows in lane order (lane l: row l / 8, slot l % 8), so in block b (rows
+// 8b..8b+7) lane l loads chunk (l % 8) ^ (4 (b % 2) + l / 16).
 //
 // Gated tiles hold, for 128 output columns, per wavefront row half: 64 gate
 // rows then the 64 matching up rows, so SiLU(gate) * up is formed from the
 // wavefront's own accumulators.
-constexpr int kBigBK = 32;
-constexpr int kBigStages = 4;
+constexpr int kBigBK = 64;
+constexpr int kBigStages = 2;
 
 // Memory -> LDS copy of 16 bytes per lane: LDS byte address lds + 16 * lane,
 // memory offset voff + soff in buffer rsrc. m0 is saved and restored.
@@ -1017,31 +1018,28 @@ __device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes)
 template <bool GATED>
 struct Big {
   static constexpr int COLS = GATED ? 128 : 256;            // output columns per tile
-  static constexpr int OP_BYTES = 256 * kBigBK * 2;          // one operand of one stage (16 KB)
+  static constexpr int OP_BYTES = 256 * kBigBK * 2;          // one operand of one stage (32 KB)
   static constexpr int STAGE_BYTES = 2 * OP_BYTES;
   static constexpr int LDS_BYTES = kBigStages * STAGE_BYTES;  // 128 KB
-  static constexpr int DMA_PER_STAGE = 8;                    // per wavefront: 4 weight + 4 token loads
-
-  __device__ static __forceinline__ int swz(int row, int chunk) {
-    return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
-  }
+  static constexpr int BLOCKS = 8;                            // 8-row DMA blocks per operand per wavefront
 
   __device__ static void run(const GemmArgs& a, int e, int row0, int rows, int nb, char* lds, int tid) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;   // weight rows wm*128.., tokens wn*128..
     const uint32_t pitch = (uint32_t)a.K * 2;
-    const int lrow = lane >> 2;                               // row within a 16-row DMA block
-    const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);        // chunk this lane fetches
+    const int lrow = lane >> 3;                               // row within an 8-row DMA block
+    const int lchunk = (lane & 7) ^ (lane >> 4);              // chunk fetched in even blocks
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
 
-    // This wavefront fills 16-row blocks g = wave * 4 + i (i = 0..3) of both
-    // operands. Weights: block g -> first weight row wrow[i] (uniform).
+    // This wavefront fills 8-row blocks g = wave * 8 + i (i = 0..7) of both
+    // operands; odd blocks fetch chunk lchunk ^ 4. Weights: block g -> first
+    // weight row (uniform).
     const i32x4_t wbuf = buffer_rsrc(a.W + (size_t)e * a.N * a.K, (uint32_t)(a.N * pitch));
-    int wso[4];
+    int wso[BLOCKS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = wave * 4 + i, r = g * 16;   // first tile row of the block
+    for (int i = 0; i < BLOCKS; ++i) {
+      const int r = (wave * BLOCKS + i) * 8;   // first tile row of the block
       int base;
       if (GATED) {
         const int grp = r >> 5, wmi = grp >> 2, q = grp & 3;
@@ -1051,27 +1049,34 @@ struct Big {
       }
       wso[i] = __builtin_amdgcn_readfirstlane(base * (int)pitch);
     }
-    const uint32_t wv = (uint32_t)lrow * pitch + lchunk * 16;
+    const uint32_t wv[2] = {(uint32_t)lrow * pitch + lchunk * 16, (uint32_t)lrow * pitch + (lchunk ^ 4) * 16};
     // Tokens: rows past the tile's end read its first row (not stored).
     const i32x4_t xbuf = buffer_rsrc(a.A, 0xFFFFFFFFu);
-    uint32_t xv[4];
+    uint32_t xv[BLOCKS];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = (wave * 4 + i) * 16 + lrow;
+    for (int i = 0; i < BLOCKS; ++i) {
+      const int r = (wave * BLOCKS + i) * 8 + lrow;
       xv[i] = row0 + (r < rows ? r : 0);
     }
-    a_rows<4>(a, xv);
+    a_rows<BLOCKS>(a, xv);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xv[i] = xv[i] * pitch + lchunk * 16;
+    for (int i = 0; i < BLOCKS; ++i) xv[i] = xv[i] * pitch + (lchunk ^ ((i & 1) << 2)) * 16;
 
-    auto issue = [&](int kt) {   // DMA of stage kt into ring slot kt % kBigStages
-      const uint32_t lw = lds_base + (kt % kBigStages) * STAGE_BYTES;
+    auto issue_all = [&](int kt) {   // this wavefront's share of stage kt
+      const uint32_t lw = lds_base + (kt & 1) * STAGE_BYTES;
       const uint32_t lx = lw + OP_BYTES;
       const uint32_t ko = (uint32_t)kt * kBigBK * 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds_dma16(lw + (wave * 4 + i) * 1024, wbuf, wv, wso[i] + ko);
+      for (int i = 0; i < BLOCKS; ++i) lds_dma16(lw + (wave * BLOCKS + i) * 1024, wbuf, wv[i & 1], wso[i] + ko);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds_dma16(lx + (wave * 4 + i) * 1024, xbuf, xv[i], ko);
+      for (int i = 0; i < BLOCKS; ++i) lds_dma16(lx + (wave * BLOCKS + i) * 1024, xbuf, xv[i], ko);
+    };
+    // DMA number d (0..15) of that share: weight blocks first, then token blocks.
+    auto issue_one = [&](int kt, int d) {
+      const uint32_t lw = lds_base + (kt & 1) * STAGE_BYTES;
+      const uint32_t ko = (uint32_t)kt * kBigBK * 2;
+      if (d < BLOCKS) lds_dma16(lw + (wave * BLOCKS + d) * 1024, wbuf, wv[d & 1], wso[d] + ko);
+      else lds_dma16(lw + OP_BYTES + (wave * BLOCKS + d - BLOCKS) * 1024, xbuf, xv[d - BLOCKS], ko);
     };
 
     f32x16_t acc[4][4];
@@ -1081,41 +1086,65 @@ struct Big {
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
 
     const int fr = lane & 31, fh = lane >> 5;  // fragment row, k half
-    auto compute = [&](int slot) {
-      const char* lw = lds + slot * STAGE_BYTES;
-      const char* lx = lw + OP_BYTES;
+    const int fsw = (fr >> 1) & 7;               // the swizzle of every row this lane reads
+    // Multiplies stage `slot` and issues the DMA of stage knext (if >= 0) into
+    // the other buffer, one instruction after every second MFMA of the first
+    // half. A wavefront that issues a burst of vector-memory instructions
+    // stalls until the CU's address unit has taken them, and with one
+    // wavefront per SIMD nothing else keeps the SIMD's MFMA pipe busy
+    // meanwhile; spread out, they issue without stalls, and the last one still
+    // has half a stage to land. Fragments of the next 16 k are read while the
+    // current ones are multiplied.
+    auto compute = [&](int slot, int knext) {
+      const char* lw = lds + slot * STAGE_BYTES + (wm * 128 + fr) * 128;
+      const char* lx = lds + slot * STAGE_BYTES + OP_BYTES + (wn * 128 + fr) * 128;
+      constexpr int NQ = kBigBK / 16;
+      bf16x8_t av[4], bv[4];
+      {
+        const int off = (fh ^ fsw) << 4;
 #pragma unroll
-      for (int q = 0; q < kBigBK / 16; ++q) {
-        const int chunk = q * 2 + fh;
-        bf16x8_t av[4], bv[4];
+        for (int i = 0; i < 4; ++i) av[i] = *(const bf16x8_t*)(lw + i * 32 * 128 + off);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) av[i] = *(const bf16x8_t*)(lw + swz(wm * 128 + i * 32 + fr, chunk));
+        for (int j = 0; j < 4; ++j) bv[j] = *(const bf16x8_t*)(lx + j * 32 * 128 + off);
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bv[j] = *(const bf16x8_t*)(lx + swz(wn * 128 + j * 32 + fr, chunk));
+      for (int q = 0; q < NQ; ++q) {
+        const int offn = (((q + 1) * 2 + fh) ^ fsw) << 4;
+        bf16x8_t an[4], bn[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          if (q + 1 < NQ) {
+            an[i] = *(const bf16x8_t*)(lw + i * 32 * 128 + offn);
+            bn[i] = *(const bf16x8_t*)(lx + i * 32 * 128 + offn);
+          }
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 4; ++j) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+            const int m = q * 16 + i * 4 + j;   // MFMA number within the stage
+            if (m % 2 == 1 && m / 2 < 2 * BLOCKS) {
+              __builtin_amdgcn_sched_barrier(0);
+              if (knext >= 0) issue_one(knext, m / 2);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+        if (q + 1 < NQ) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { av[i] = an[i]; bv[i] = bn[i]; }
+        }
       }
     };
 
-    // Iteration kt: wait until this wavefront's DMA of stage kt has landed
-    // (stages kt + 1 and kt + 2 may stay in flight), barrier (every
-    // wavefront's share of stage kt is in LDS, and every wavefront has
-    // finished stage kt - 1, whose slot stage kt + 3 reuses), issue stage
-    // kt + 3, multiply stage kt.
+    // Iteration kt: wait until this wavefront's DMA of stage kt has landed,
+    // barrier (every wavefront's share of stage kt is in LDS, and every
+    // wavefront has finished stage kt - 1, whose buffer stage kt + 1 reuses),
+    // multiply stage kt while issuing stage kt + 1.
     const int nk = a.K / kBigBK;
-#pragma unroll
-    for (int j = 0; j < kBigStages - 1; ++j)
-      if (j < nk) issue(j);
+    issue_all(0);
     for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 2 < nk) wait_vmcnt<2 * DMA_PER_STAGE>();
-      else if (kt + 1 < nk) wait_vmcnt<DMA_PER_STAGE>();
-      else wait_vmcnt<0>();
+      wait_vmcnt<0>();
       __syncthreads();
-      if (kt + kBigStages - 1 < nk) issue(kt + kBigStages - 1);
-      compute(kt % kBigStages);
+      compute(kt & 1, kt + 1 < nk ? kt + 1 : -1);
     }
 
     // One fragment column at a time (all lanes compute, only the store is
@@ -1339,7 +1368,7 @@ int stream_ks(int K) {
 // decode-sized calls from paying for a second launch that finds no work.
 template <bool GATED>
 bool use_big(const GemmArgs& g) {
-  return kUseBigTiles && g.capacity >= kBigMinCapacity &&
+  return kUseBigTiles && g.capacity >= kBigMinCapacity && g.K % kBigBK == 0 &&
          (GATED ? g.inter % 128 == 0 : g.N % 256 == 0);
 }
 
