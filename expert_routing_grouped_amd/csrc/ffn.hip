@@ -60,8 +60,8 @@ struct GemmArgs {
   int ldc;
   int big_ok;             // the large-tile kernel is launched too
   int big_min_items;      // ... and takes the tiled experts when it has at least this many tiles
-  float* partials;        // shared-activation path: float32 K-part sums (null: one K part)
-  int kparts;             // shared-activation path: K parts per chunk
+  float* partials;        // shared-activation path: float32 partial sums of split K ranges
+  int sk_grid;            // shared-activation path: workgroups that share out the K steps
   int* chunk_desc;        // shared-activation path: [0] = chunks, then (lo, m) per chunk
 };
 
@@ -407,27 +407,25 @@ struct Stream {
 // tiles per step: load (two steps ahead, coalesced, through the same
 // XOR-swizzled LDS tiles as the streaming path), multiply, store. A work item
 // is a chunk and ITEM_COLS output columns, J steps per wavefront.
+constexpr int kWalkDepth = 3;
+
 template <int KQ>
 struct Walk {
   static constexpr int NTW = 2 / KQ;
   static constexpr int MT = kStreamMT;
-  static constexpr int J = 8;                        // steps per wavefront per item
   static constexpr int STEP_COLS = NTW * 16;
-  static constexpr int ITEM_COLS = 4 * J * STEP_COLS;
+  static constexpr int WD = kWalkDepth;               // weight register sets
   static constexpr int TILE_BYTES = 16 * 128;
   static constexpr int WAVE_LDS = (MT + NTW) * KQ * TILE_BYTES;
   static constexpr int LDS_BYTES = 4 * WAVE_LDS;
 
   template <int MTA>
-  __device__ static void run_mt(const GemmArgs& a, int e, int lo, int m, int item, char* smem) {
+  __device__ static void run_mt(const GemmArgs& a, int e, int lo, int m, int c0, int steps, char* smem) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int fr = lane & 15, g = lane >> 4;
     const int lr = lane >> 3, lc = lane & 7;
     const uint32_t pitch = (uint32_t)a.K * 2;
-    const int c0 = item * ITEM_COLS + wave * J * STEP_COLS;   // this wavefront's first column
-    const int steps = __builtin_amdgcn_readfirstlane(max(0, min(J, (a.N - c0) / STEP_COLS)));
-    if (steps == 0) return;
 
     char* xs = smem + wave * WAVE_LDS;   // MT * KQ activation tiles, then NTW * KQ weight tiles
     char* ws = xs + MT * KQ * TILE_BYTES;
@@ -473,7 +471,7 @@ struct Walk {
     const __amdgpu_buffer_rsrc_t wbuf = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.W + (size_t)e * a.N * a.K), 0, (int)(a.N * pitch), kBufferConfig);
     const uint32_t wv = (uint32_t)(c0 + lr) * pitch + lc * 16;
-    u32x4_t wr[3][NTW][KQ][2];
+    u32x4_t wr[WD][NTW][KQ][2];
     auto load_w = [&](u32x4_t (&w)[NTW][KQ][2], int j) {
 #pragma unroll
       for (int t = 0; t < NTW; ++t)
@@ -543,38 +541,43 @@ struct Walk {
       }
     };
 
-    // Weights two steps ahead in three register sets (steps past the end
-    // reload the last one); the main loop runs whole periods of three.
-    load_w(wr[0], 0);
-    load_w(wr[1], min(1, steps - 1));
+    // Weights WD - 1 steps ahead in WD register sets (steps past the end
+    // reload the last one); the main loop runs whole periods of WD.
+#pragma unroll
+    for (int q = 0; q < WD - 1; ++q) load_w(wr[q], min(q, steps - 1));
     int j = 0;
-#define MOE_WALK(q)                                 \
-  load_w(wr[((q) + 2) % 3], min(j + 2, steps - 1)); \
-  __builtin_amdgcn_sched_barrier(0);                \
-  step(wr[(q) % 3], j);                             \
-  __builtin_amdgcn_sched_barrier(0);                \
+#define MOE_WALK(q)                                           \
+  load_w(wr[((q) + WD - 1) % WD], min(j + WD - 1, steps - 1)); \
+  __builtin_amdgcn_sched_barrier(0);                          \
+  step(wr[(q) % WD], j);                                      \
+  __builtin_amdgcn_sched_barrier(0);                          \
   ++j;
-    for (; j + 3 <= steps;) {
-      MOE_WALK(0) MOE_WALK(1) MOE_WALK(2)
+    for (; j + WD <= steps;) {
+#pragma unroll
+      for (int q = 0; q < WD; ++q) { MOE_WALK(q) }
     }
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < WD - 1; ++q) {
       if (j >= steps) break;
       MOE_WALK(q)
     }
 #undef MOE_WALK
   }
 
-  __device__ static void run(const GemmArgs& a, const int* s_lo, int e, int chunk, int item, char* smem) {
+  // Columns [c0, c0 + steps * STEP_COLS) of chunk `chunk` of expert e, by
+  // this wavefront alone (its own LDS region).
+  __device__ static void run(const GemmArgs& a, const int* s_lo, int e, int chunk, int c0, int steps,
+                             char* smem) {
     e = __builtin_amdgcn_readfirstlane(e);
     const int lo = __builtin_amdgcn_readfirstlane(s_lo[e] + chunk * kChunkRows);
     const int m = __builtin_amdgcn_readfirstlane(min(kChunkRows, s_lo[e + 1] - lo));
-    item = __builtin_amdgcn_readfirstlane(item);
+    c0 = __builtin_amdgcn_readfirstlane(c0);
+    steps = __builtin_amdgcn_readfirstlane(steps);
     switch ((m + 15) >> 4) {
-      case 1: run_mt<1>(a, e, lo, m, item, smem); break;
-      case 2: run_mt<2>(a, e, lo, m, item, smem); break;
-      case 3: run_mt<3>(a, e, lo, m, item, smem); break;
-      default: run_mt<4>(a, e, lo, m, item, smem); break;
+      case 1: run_mt<1>(a, e, lo, m, c0, steps, smem); break;
+      case 2: run_mt<2>(a, e, lo, m, c0, steps, smem); break;
+      case 3: run_mt<3>(a, e, lo, m, c0, steps, smem); break;
+      default: run_mt<4>(a, e, lo, m, c0, steps, smem); break;
     }
   }
 };
@@ -606,7 +609,7 @@ struct SharedA {
   static constexpr int PART_FLOATS = 64 * 2 * kShareCols;      // one item's partial sums
 
   template <int MTA>
-  __device__ static void run_mt(const GemmArgs& a, int e, int lo, int m, int slab, int kp,
+  __device__ static void run_mt(const GemmArgs& a, int e, int lo, int m, int slab, int k0, int steps,
                                 float* part, char* smem) {
     constexpr int HALVES = 2 * MTA;            // 8-row half tiles of one activation step
     constexpr int NSH = (HALVES + 3) / 4;      // shares per wavefront
@@ -638,8 +641,7 @@ struct SharedA {
 #pragma unroll
     for (int j = 0; j < NSH; ++j) av[j] = av[j] * pitch + lc * 16;
 
-    const int kw = a.K / a.kparts, kbeg = kp * kw, klast = kbeg + kw - KSTEP;
-    const int steps = kw / KSTEP;
+    const int kbeg = k0 * KSTEP, klast = kbeg + (steps - 1) * KSTEP;
     char* wl = smem + W_OFF + wave * 2 * TILE_BYTES;
 
     f32x4_t acc[MTA][2];
@@ -725,23 +727,76 @@ struct SharedA {
     }
   }
 
-  __device__ static void run(const GemmArgs& a, const int* s_lo, int e, int chunk, int slab, int kp,
-                             float* part, char* smem) {
+  __device__ static void run(const GemmArgs& a, const int* s_lo, int e, int chunk, int slab, int k0,
+                             int steps, float* part, char* smem) {
     e = __builtin_amdgcn_readfirstlane(e);
     const int lo = __builtin_amdgcn_readfirstlane(s_lo[e] + chunk * kChunkRows);
     const int m = __builtin_amdgcn_readfirstlane(min(kChunkRows, s_lo[e + 1] - lo));
     switch ((m + 15) >> 4) {
-      case 1: run_mt<1>(a, e, lo, m, slab, kp, part, smem); break;
-      case 2: run_mt<2>(a, e, lo, m, slab, kp, part, smem); break;
-      case 3: run_mt<3>(a, e, lo, m, slab, kp, part, smem); break;
-      default: run_mt<4>(a, e, lo, m, slab, kp, part, smem); break;
+      case 1: run_mt<1>(a, e, lo, m, slab, k0, steps, part, smem); break;
+      case 2: run_mt<2>(a, e, lo, m, slab, k0, steps, part, smem); break;
+      case 3: run_mt<3>(a, e, lo, m, slab, k0, steps, part, smem); break;
+      default: run_mt<4>(a, e, lo, m, slab, k0, steps, part, smem); break;
     }
   }
 };
 
-// Items (chunk, slab, K part), K parts fastest; item w's partial sums are
-// partials[w * PART_FLOATS ...] as [64 rows][gate 64 | up 64].
-__global__ __launch_bounds__(256, 2) void ffn_shared_kernel(GemmArgs a) {
+// Stream-K split: the K steps of all (chunk, slab) pairs, pair cs = chunk *
+// slabs + slab, are laid end to end (nk steps each, global step index cs * nk
+// + k) and shared out over the grid's G workgroups by cost, so that every
+// workgroup moves about the same number of bytes: a step of a chunk with m
+// rows loads 128 weight rows and m activation rows, cost 128 + m. With the
+// step costs laid end to end (total C), workgroup v takes the steps whose
+// starting cost lies in [ceil(C v / G), ceil(C (v+1) / G)), i.e. step owner
+// = floor(start cost * G / C). A workgroup's range covers pieces of one or
+// more pairs. A piece that is a whole pair writes h itself; any other piece
+// writes its float32 partial sums, [64 rows][gate 64 | up 64], to slot v +
+// cs (unique: along the sequence of pieces neither v nor cs decreases and one
+// of them grows), and ffn_finalize_kernel adds a pair's pieces in K order.
+// Workgroups of one XCD (b % 8) take consecutive ranges, so a pair's pieces
+// and the chunks of one expert, which read the same weight rows, mostly share
+// that XCD's L2. One workgroup per CU: with more, the workgroups sharing a CU
+// get very unequal shares of its bandwidth and the last ones set the time.
+// Only the first Ge = min(G, C / 192) workgroups take part: each range is then
+// at least as wide as the costliest step, so every one of them owns a step
+// and the pieces of a pair belong to a contiguous run of workgroups.
+//
+// Chunks are contiguous in rows, so chunk c starting at row lo_c costs
+// nk * slabs * (128 c + lo_c - lo_0) before it, and within an expert whose
+// first chunk is f every chunk but the last has 64 rows.
+struct SkCost {
+  long long nks;   // nk * slabs
+  int nk, slabs, lo0;
+  int wrows;       // weight rows a step loads: 128 here, 64 on the walk path
+  __device__ long long chunk_start(int c, int lo_c) const { return nks * ((long long)wrows * c + lo_c - lo0); }
+};
+
+// First global step whose starting cost is >= x (x < C), from the expert lists:
+// the last expert starting at or before x, then its chunk (all but the last
+// have 64 rows), slab and step.
+__device__ long long sk_step_at(const SkCost& q, long long x, const int* s_first, const int* s_lo, int nloc) {
+  int lo = 0, hi = nloc - 1;   // last expert whose cost start is <= x
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (q.chunk_start(s_first[mid], s_lo[mid]) <= x) lo = mid; else hi = mid - 1;
+  }
+  const int e = lo;
+  const long long y = x - q.chunk_start(s_first[e], s_lo[e]);
+  const int full = q.wrows + 64;   // step cost of a 64-row chunk
+  const int j = (int)(y / (q.nks * full));
+  const int c = s_first[e] + j, lo_c = s_lo[e] + 64 * j;
+  const int u = q.wrows + min(64, s_lo[e + 1] - lo_c);
+  const long long y2 = y - q.nks * full * j;
+  const int slab = (int)(y2 / ((long long)q.nk * u));
+  const long long y3 = y2 - (long long)slab * q.nk * u;
+  return ((long long)c * q.slabs + slab) * q.nk + (y3 + u - 1) / u;
+}
+
+__device__ __forceinline__ int sk_active(long long C, int grid) {
+  return (int)max(1LL, min((long long)grid, C / 192));
+}
+
+__global__ __launch_bounds__(256, 1) void ffn_shared_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[SharedA::LDS_BYTES];
   __shared__ int s_first[kMaxLocal + 1];
   __shared__ int t_first[kMaxLocal + 1];
@@ -749,60 +804,143 @@ __global__ __launch_bounds__(256, 2) void ffn_shared_kernel(GemmArgs a) {
   __shared__ int wsum[12];
   int n_chunks, n_tiles, n_big;
   build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big, true);
-  const int slabs = a.inter / kShareCols, kp = a.kparts;
-  const int total = n_chunks * slabs * kp;
-  if (a.chunk_desc && blockIdx.x == 0 && threadIdx.x == 0) a.chunk_desc[0] = n_chunks;
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const int c = __builtin_amdgcn_readfirstlane(w / (slabs * kp));
-    const int slab = __builtin_amdgcn_readfirstlane((w / kp) % slabs);
-    const int part = __builtin_amdgcn_readfirstlane(w % kp);
+  SkCost q;
+  q.nk = a.K / SharedA::KSTEP;
+  q.slabs = a.inter / kShareCols;
+  q.nks = (long long)q.nk * q.slabs;
+  q.lo0 = s_lo[0];
+  q.wrows = 128;
+  const long long C = q.chunk_start(n_chunks, s_lo[a.nloc]);
+  const long long total = (long long)n_chunks * q.nks;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.chunk_desc[0] = n_chunks;
+  if (C == 0) return;
+  const int G = sk_active(C, a.sk_grid);
+  const int v = (blockIdx.x % 8) * (a.sk_grid / 8) + blockIdx.x / 8;   // sk_grid == gridDim.x, a multiple of 8
+  if (v >= G) return;
+  const long long x0 = (C * v + G - 1) / G, x1 = (C * (v + 1) + G - 1) / G;
+  long long st = x0 < C ? sk_step_at(q, x0, s_first, s_lo, a.nloc) : total;
+  const long long s1 = x1 < C ? sk_step_at(q, x1, s_first, s_lo, a.nloc) : total;
+  while (st < s1) {
+    const int cs = __builtin_amdgcn_readfirstlane((int)(st / q.nk));
+    const int k0 = __builtin_amdgcn_readfirstlane((int)(st - (long long)cs * q.nk));
+    const int steps = __builtin_amdgcn_readfirstlane((int)min(s1 - st, (long long)(q.nk - k0)));
+    const int c = cs / q.slabs, slab = cs % q.slabs;
     const int e = find_expert(s_first, a.nloc, c);
-    if (a.chunk_desc && slab == 0 && part == 0 && threadIdx.x == 0) {  // for ffn_finalize_kernel
+    if (k0 == 0 && slab == 0 && threadIdx.x == 0) {  // for ffn_finalize_kernel
       const int lo = s_lo[e] + (c - s_first[e]) * kChunkRows;
       a.chunk_desc[1 + 2 * c] = lo;
       a.chunk_desc[2 + 2 * c] = min(kChunkRows, s_lo[e + 1] - lo);
     }
-    SharedA::run(a, s_lo, e, c - s_first[e], slab, part,
-                 a.partials ? a.partials + (size_t)w * SharedA::PART_FLOATS : nullptr, smem);
-    __syncthreads();  // LDS is reused by the next item
+    float* part = (k0 == 0 && steps == q.nk) ? nullptr : a.partials + (size_t)(v + cs) * SharedA::PART_FLOATS;
+    SharedA::run(a, s_lo, e, c - s_first[e], slab, k0, steps, part, smem);
+    __syncthreads();  // LDS is reused by the next piece
+    st += steps;
   }
 }
 
-// h = SiLU(sum of gate parts) * (sum of up parts) for every (chunk, slab),
-// parts added in order. The chunk count and each chunk's rows come from the
-// table ffn_shared_kernel writes.
+// h = SiLU(sum of gate pieces) * (sum of up pieces) for every (chunk, slab)
+// pair that was split, pieces added in K order. The chunk count and each
+// chunk's rows come from the table ffn_shared_kernel writes.
 __global__ __launch_bounds__(256) void ffn_finalize_kernel(GemmArgs a) {
-  const int slabs = a.inter / kShareCols, kp = a.kparts;
-  const int total = a.chunk_desc[0] * slabs;   // written by ffn_shared_kernel
+  const int n_chunks = a.chunk_desc[0];   // written by ffn_shared_kernel
+  if (n_chunks == 0) return;
+  SkCost q;
+  q.nk = a.K / SharedA::KSTEP;
+  q.slabs = a.inter / kShareCols;
+  q.nks = (long long)q.nk * q.slabs;
+  q.lo0 = a.chunk_desc[1];
+  q.wrows = 128;
+  const int pairs = n_chunks * q.slabs;
+  const long long C = q.chunk_start(n_chunks, a.chunk_desc[2 * n_chunks - 1] + a.chunk_desc[2 * n_chunks]);
+  const int G = sk_active(C, a.sk_grid);
   const int row = threadIdx.x >> 2, c16 = (threadIdx.x & 3) * 16;  // 64 rows x 4 column groups
-  for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const int c = w / slabs, slab = w % slabs;
+  for (int w = blockIdx.x; w < pairs; w += gridDim.x) {
+    const int c = w / q.slabs, slab = w % q.slabs;
     const int lo = a.chunk_desc[1 + 2 * c], m = a.chunk_desc[2 + 2 * c];
+    const int u = q.wrows + m;
+    const long long p = q.chunk_start(c, lo) + (long long)slab * q.nk * u;   // cost at the pair's step 0
+    const int v0 = (int)(p * G / C), v1 = (int)((p + (long long)(q.nk - 1) * u) * G / C);
+    if (v0 == v1) continue;   // one piece: h written directly
     if (row >= m) continue;
-    const float* p = a.partials + ((size_t)w * kp) * SharedA::PART_FLOATS + row * 2 * kShareCols + c16;
     f32x4_t gs[4], us[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      gs[q] = *(const f32x4_t*)(p + 4 * q);
-      us[q] = *(const f32x4_t*)(p + kShareCols + 4 * q);
-    }
-    for (int k = 1; k < kp; ++k) {
-      const float* pk = p + (size_t)k * SharedA::PART_FLOATS;
+    for (int i = 0; i < 4; ++i) gs[i] = us[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // The pieces of workgroups v0..v1, in K order, four at a time: the loads
+    // go out together, the sums are taken in order.
+    for (int v = v0; v <= v1; v += 4) {
+      const int nv = min(4, v1 + 1 - v);
+      f32x4_t pg[4][4], pu[4][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        gs[q] += *(const f32x4_t*)(pk + 4 * q);
-        us[q] += *(const f32x4_t*)(pk + kShareCols + 4 * q);
+      for (int b = 0; b < 4; ++b) {
+        if (b >= nv) break;
+        const float* pk = a.partials + (size_t)(v + b + w) * SharedA::PART_FLOATS + row * 2 * kShareCols + c16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pg[b][i] = *(const f32x4_t*)(pk + 4 * i);
+          pu[b][i] = *(const f32x4_t*)(pk + kShareCols + 4 * i);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (b >= nv) break;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { gs[i] += pg[b][i]; us[i] += pu[b][i]; }
       }
     }
     uint32_t o[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      o[2 * q] = pack_bf16x2(silu(gs[q][0]) * us[q][0], silu(gs[q][1]) * us[q][1]);
-      o[2 * q + 1] = pack_bf16x2(silu(gs[q][2]) * us[q][2], silu(gs[q][3]) * us[q][3]);
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = pack_bf16x2(silu(gs[i][0]) * us[i][0], silu(gs[i][1]) * us[i][1]);
+      o[2 * i + 1] = pack_bf16x2(silu(gs[i][2]) * us[i][2], silu(gs[i][3]) * us[i][3]);
     }
     uint4* dst = (uint4*)(a.C + (size_t)(lo + row) * a.ldc + slab * kShareCols + c16);
     dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
     dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  }
+}
+
+// Plain GEMMs with K = 64 KQ on the walk path: every expert is cut into 64-row
+// chunks and each chunk's output columns into 64-column units (one 128-byte
+// row segment); a unit loads 64 weight rows and stores m output rows, cost 64
+// + m. The units of all chunks, laid end to end, are shared out by cost over
+// all wavefronts of the grid (the same split as ffn_shared_kernel's, per
+// wavefront; no K split, so no partial sums): every wavefront walks the
+// columns of one or more chunk pieces on its own, in its own LDS region.
+// Wavefronts of one XCD take consecutive ranges, so the chunks of one
+// expert, which read the same weight rows, mostly share that XCD's L2.
+template <int KQ>
+__global__ __launch_bounds__(256, 2) void ffn_walk_kernel(GemmArgs a) {
+  using Wk = Walk<KQ>;
+  __shared__ __attribute__((aligned(16))) char smem[Wk::LDS_BYTES];
+  __shared__ int s_first[kMaxLocal + 1];
+  __shared__ int t_first[kMaxLocal + 1];
+  __shared__ int s_lo[kMaxLocal + 1];
+  __shared__ int wsum[12];
+  int n_chunks, n_tiles, n_big;
+  build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big, true);
+  SkCost q;
+  q.nk = a.N / 64;   // units per chunk
+  q.slabs = 1;
+  q.nks = q.nk;
+  q.lo0 = s_lo[0];
+  q.wrows = 64;
+  const long long C = q.chunk_start(n_chunks, s_lo[a.nloc]);
+  if (C == 0) return;
+  const long long total = (long long)n_chunks * q.nk;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int NW = gridDim.x * 4;   // gridDim.x is a multiple of 8
+  const int vw = ((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8) * 4 + wave;
+  const long long x0 = (C * vw + NW - 1) / NW, x1 = (C * (vw + 1) + NW - 1) / NW;
+  long long st = x0 < C ? sk_step_at(q, x0, s_first, s_lo, a.nloc) : total;
+  const long long s1 = x1 < C ? sk_step_at(q, x1, s_first, s_lo, a.nloc) : total;
+  constexpr int SPU = 64 / Wk::STEP_COLS;   // walk steps per unit
+  while (st < s1) {
+    const int c = __builtin_amdgcn_readfirstlane((int)(st / q.nk));
+    const int u0 = __builtin_amdgcn_readfirstlane((int)(st - (long long)c * q.nk));
+    const int n = __builtin_amdgcn_readfirstlane((int)min(s1 - st, (long long)(q.nk - u0)));
+    const int e = find_expert(s_first, a.nloc, c);
+    Wk::run(a, s_lo, e, c - s_first[e], u0 * 64, n * SPU, smem);
+    st += n;
   }
 }
 
@@ -1227,14 +1365,11 @@ __global__ __launch_bounds__(256, 1) void ffn_big_kernel(GemmArgs a) {
 
 // One persistent kernel per GEMM: first the streamed row chunks, then the row
 // tiles of larger experts. The two paths share the LDS buffer.
-// KQ = 0: chunks on the streaming path; KQ = 1, 2 (plain GEMMs with K = 64 KQ):
-// chunks on the walk path.
-template <int NTW, int KS, bool GATED, int KQ>
+template <int NTW, int KS, bool GATED>
 __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(GemmArgs a) {
   using S = Stream<NTW, KS, GATED, kStreamDW, kStreamDA>;
-  using Wk = Walk<KQ == 0 ? 1 : KQ>;
   using T = Tiled<GATED>;
-  constexpr int SL = KQ == 0 ? S::LDS_BYTES : Wk::LDS_BYTES;
+  constexpr int SL = S::LDS_BYTES;
   constexpr int SMEM = SL > T::LDS_BYTES ? SL : T::LDS_BYTES;
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ int s_first[kMaxLocal + 1];
@@ -1244,7 +1379,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(GemmArgs a) {
   int n_chunks, n_tiles, n_big;
   build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big);
   const int ncols = GATED ? a.inter : a.N;
-  const int slabs = KQ == 0 ? ncols / S::COLS : (ncols + Wk::ITEM_COLS - 1) / Wk::ITEM_COLS;
+  const int slabs = ncols / S::COLS;
   const int nblk = ncols / T::COLS;
   const int n_stream = n_chunks * slabs;
   // Same decision as ffn_big_kernel: it takes the tiled experts when it has
@@ -1255,8 +1390,7 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(GemmArgs a) {
     if (w < n_stream) {
       const int c = w / slabs;
       const int e = find_expert(s_first, a.nloc, c);
-      if (KQ == 0) S::run(a, s_lo, e, c - s_first[e], w % slabs, smem);
-      else Wk::run(a, s_lo, e, c - s_first[e], w % slabs, smem);
+      S::run(a, s_lo, e, c - s_first[e], w % slabs, smem);
       __syncthreads();  // the LDS buffer is reused by the next work item
     } else {
       const int tile = (w - n_stream) / nblk, nb = (w - n_stream) % nblk;
@@ -1372,7 +1506,7 @@ bool use_big(const GemmArgs& g) {
          (GATED ? g.inter % 128 == 0 : g.N % 256 == 0);
 }
 
-template <bool GATED, int KS, int KQ = 0>
+template <bool GATED, int KS>
 hipError_t launch_gemm_t(const GemmArgs& g0, hipStream_t s) {
   constexpr int NTW = 2;
   using S = Stream<NTW, KS, GATED, kStreamDW, kStreamDA>;
@@ -1380,14 +1514,13 @@ hipError_t launch_gemm_t(const GemmArgs& g0, hipStream_t s) {
   GemmArgs g = g0;
   g.big_ok = use_big<GATED>(g) ? 1 : 0;
   g.big_min_items = cu_count();
-  auto kernel = ffn_gemm_kernel<NTW, KS, GATED, KQ>;
+  auto kernel = ffn_gemm_kernel<NTW, KS, GATED>;
   static const int occ = occupancy(kernel, 256);
   const int ncols = GATED ? g.inter : g.N;
   const long max_chunks = std::min<long>((long)g.nloc * (kStreamRows / kChunkRows),
                                          (long)(g.capacity + kChunkRows - 1) / kChunkRows + g.nloc);
   const long max_tiles = (long)(g.capacity + kTileBM - 1) / kTileBM + g.nloc;
-  const long per_chunk = KQ == 0 ? ncols / S::COLS
-                                 : (ncols + Walk<KQ == 0 ? 1 : KQ>::ITEM_COLS - 1) / Walk<KQ == 0 ? 1 : KQ>::ITEM_COLS;
+  const long per_chunk = ncols / S::COLS;
   const long max_work = max_chunks * per_chunk + max_tiles * (ncols / T::COLS);
   const int grid = (int)std::max<long>(1, std::min<long>(max_work, (long)cu_count() * occ));
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, g);
@@ -1403,10 +1536,19 @@ hipError_t launch_gemm_t(const GemmArgs& g0, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Walk path: all the wavefronts the grid can keep resident, the grid a multiple of 8.
+template <int KQ>
+hipError_t launch_walk(const GemmArgs& g, hipStream_t s) {
+  static const int occ = occupancy(ffn_walk_kernel<KQ>, 256);
+  const int grid = std::max(8, cu_count() * occ / 8 * 8);
+  hipLaunchKernelGGL(ffn_walk_kernel<KQ>, dim3(grid), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
 template <bool GATED>
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  if (!GATED && g.K == 64) return launch_gemm_t<false, 1, 1>(g, s);
-  if (!GATED && g.K == 128) return launch_gemm_t<false, 1, 2>(g, s);
+  if (!GATED && g.K == 64) return launch_walk<1>(g, s);
+  if (!GATED && g.K == 128) return launch_walk<2>(g, s);
   switch (stream_ks<GATED>(g.K)) {
     case 4: return launch_gemm_t<GATED, 4>(g, s);
     case 2: return launch_gemm_t<GATED, 2>(g, s);
@@ -1415,22 +1557,22 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
 }
 
 // The shared-activation path serves gated GEMMs of narrow experts (inter a
-// multiple of 64, at most 128); K is split into this many parts.
+// multiple of 64, at most 128).
 bool use_shared(int hidden, int inter) { return inter % kShareCols == 0 && inter <= 128 && hidden >= 1024; }
-int shared_kparts(int hidden) { return hidden >= 4096 ? 4 : hidden >= 2048 ? 2 : 1; }
-long shared_max_chunks(int num_local, int capacity) {
-  return (long)(capacity + kChunkRows - 1) / kChunkRows + num_local;
+long shared_max_pairs(int num_local, int capacity, int inter) {
+  return ((long)(capacity + kChunkRows - 1) / kChunkRows + num_local) * (inter / kShareCols);
 }
+// Workgroups of the shared-activation kernel: one per CU, a multiple of 8.
+int shared_grid() { return std::max(8, cu_count() / 8 * 8); }
 
 }  // namespace
 
 size_t ffn_workspace_size(int num_local, int hidden, int inter, int capacity, bool bf16) {
   size_t bytes = align256((size_t)capacity * inter * (bf16 ? 2 : 4));  // h
-  if (bf16 && use_shared(hidden, inter) && shared_kparts(hidden) > 1) {  // K-part sums, chunk table
-    const size_t chunks = (size_t)shared_max_chunks(num_local, capacity);
-    bytes += align256(chunks * (inter / kShareCols) * shared_kparts(hidden) * SharedA::PART_FLOATS *
-                      sizeof(float));
-    bytes += align256((1 + 2 * chunks) * sizeof(int));
+  if (bf16 && use_shared(hidden, inter)) {  // partial sums (slots v + cs), chunk table
+    const size_t pairs = (size_t)shared_max_pairs(num_local, capacity, inter);
+    bytes += align256((pairs + shared_grid()) * SharedA::PART_FLOATS * sizeof(float));
+    bytes += align256((1 + 2 * pairs) * sizeof(int));
   }
   return bytes;
 }
@@ -1439,21 +1581,13 @@ namespace {
 
 hipError_t launch_gate_up_shared(const GemmArgs& g0, size_t h_bytes, void* workspace, hipStream_t s) {
   GemmArgs g = g0;
-  g.kparts = shared_kparts(g.K);
-  const long chunks = shared_max_chunks(g.nloc, g.capacity);
-  const long items = chunks * (g.inter / kShareCols);
-  g.partials = nullptr;
-  g.chunk_desc = nullptr;
-  if (g.kparts > 1) {
-    char* p = (char*)workspace + align256(h_bytes);
-    g.partials = (float*)p;
-    g.chunk_desc = (int*)(p + align256((size_t)items * g.kparts * SharedA::PART_FLOATS * sizeof(float)));
-  }
-  static const int occ = occupancy(ffn_shared_kernel, 256);
-  const int grid = (int)std::max<long>(1, std::min<long>(items * g.kparts, (long)cu_count() * occ));
-  hipLaunchKernelGGL(ffn_shared_kernel, dim3(grid), dim3(256), 0, s, g);
-  if (g.kparts == 1) return hipGetLastError();
-  const int grid_f = (int)std::max<long>(1, std::min<long>(items, (long)cu_count() * 4));
+  const long pairs = shared_max_pairs(g.nloc, g.capacity, g.inter);
+  g.sk_grid = shared_grid();
+  char* p = (char*)workspace + align256(h_bytes);
+  g.partials = (float*)p;
+  g.chunk_desc = (int*)(p + align256((size_t)(pairs + g.sk_grid) * SharedA::PART_FLOATS * sizeof(float)));
+  hipLaunchKernelGGL(ffn_shared_kernel, dim3(g.sk_grid), dim3(256), 0, s, g);
+  const int grid_f = (int)std::max<long>(1, std::min<long>(pairs, (long)cu_count() * 4));
   hipLaunchKernelGGL(ffn_finalize_kernel, dim3(grid_f), dim3(256), 0, s, g);
   return hipGetLastError();
 }
