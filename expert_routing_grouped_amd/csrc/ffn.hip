@@ -62,7 +62,8 @@ struct GemmArgs {
   int big_min_items;      // ... and takes the tiled experts when it has at least this many tiles
   float* partials;        // shared-activation path: float32 partial sums of split K ranges
   int sk_grid;            // shared-activation path: workgroups that share out the K steps
-  int* chunk_desc;        // shared-activation path: [0] = chunks, then (lo, m) per chunk
+  int sk_items;           // shared-activation path: finalize items (largest pair count x row blocks)
+  int* chunk_desc;        // shared-activation path: [0] = pairs, then (lo, m, v0, v1) per (chunk, slab) pair
 };
 
 // Replaces each permuted row number by the row of A that holds it. All index
@@ -96,7 +97,7 @@ constexpr int kNonTemporal = 2;
 // Splits the local experts by row count m, in expert order (and leaves the
 // clamped row bounds in s_lo: rows of expert e are [s_lo[e], s_lo[e] + m);
 // n_big = the tiles of kBigBM rows the tiled experts need; with all_chunks
-// every expert is cut into chunks):
+// every expert is cut into chunks of chunk_rows rows):
 //   1 <= m <= kStreamRows: streamed, in ceil(m / kChunkRows) row chunks;
 //                          s_first[e] = first chunk of expert e, s_first[nloc] = chunks
 //   m > kStreamRows:       tiled, in ceil(m / bm) row tiles;
@@ -104,7 +105,7 @@ constexpr int kNonTemporal = 2;
 // Every thread of the 256-thread workgroup calls this; 4 experts per thread.
 __device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_first, int* s_lo,
                             int* wsum, int& n_chunks, int& n_tiles, int& n_big,
-                            bool all_chunks = false) {
+                            bool all_chunks = false, int chunk_rows = kChunkRows) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int cc[4], tc[4], cs = 0, ct = 0, cb = 0;
 #pragma unroll
@@ -119,7 +120,7 @@ __device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_firs
       if (e == a.nloc - 1) s_lo[a.nloc] = max(lo, hi);
     }
     const bool chunked = all_chunks || m <= kStreamRows;
-    cc[q] = (m > 0 && chunked) ? (m + kChunkRows - 1) / kChunkRows : 0;
+    cc[q] = (m > 0 && chunked) ? (m + chunk_rows - 1) / chunk_rows : 0;
     tc[q] = (m > 0 && !chunked) ? (m + bm - 1) / bm : 0;
     cs += cc[q];
     ct += tc[q];
@@ -596,17 +597,18 @@ struct Walk {
 // applies SiLU(gate) * up. Every expert is cut into 64-row chunks here, large
 // ones included.
 constexpr int kShareCols = 64;   // output columns per item
+constexpr int kShareRows = 128;  // rows per chunk: an expert's weights are read once per 128 rows
 
 struct SharedA {
   static constexpr int NSET = 4;   // register sets: loads NSET - 1 steps ahead
-  static constexpr int MT = kStreamMT;
+  static constexpr int MT = kShareRows / 16;
   static constexpr int KSTEP = 64;
   static constexpr int TILE_BYTES = 16 * 128;
   static constexpr int A_BUF = MT * TILE_BYTES;                 // one step's activation tiles
   static constexpr int W_OFF = 2 * A_BUF;                       // after the two activation buffers
   static constexpr int DUMMY_OFF = W_OFF + 4 * 2 * TILE_BYTES;  // per-wave sink for unused shares
   static constexpr int LDS_BYTES = DUMMY_OFF + 4 * 1024;
-  static constexpr int PART_FLOATS = 64 * 2 * kShareCols;      // one item's partial sums
+  static constexpr int PART_FLOATS = kShareRows * 2 * kShareCols;   // one piece's partial sums
 
   template <int MTA>
   __device__ static void run_mt(const GemmArgs& a, int e, int lo, int m, int slab, int k0, int steps,
@@ -730,14 +732,17 @@ struct SharedA {
   __device__ static void run(const GemmArgs& a, const int* s_lo, int e, int chunk, int slab, int k0,
                              int steps, float* part, char* smem) {
     e = __builtin_amdgcn_readfirstlane(e);
-    const int lo = __builtin_amdgcn_readfirstlane(s_lo[e] + chunk * kChunkRows);
-    const int m = __builtin_amdgcn_readfirstlane(min(kChunkRows, s_lo[e + 1] - lo));
-    switch ((m + 15) >> 4) {
-      case 1: run_mt<1>(a, e, lo, m, slab, k0, steps, part, smem); break;
-      case 2: run_mt<2>(a, e, lo, m, slab, k0, steps, part, smem); break;
-      case 3: run_mt<3>(a, e, lo, m, slab, k0, steps, part, smem); break;
-      default: run_mt<4>(a, e, lo, m, slab, k0, steps, part, smem); break;
-    }
+    const int lo = __builtin_amdgcn_readfirstlane(s_lo[e] + chunk * kShareRows);
+    const int m = __builtin_amdgcn_readfirstlane(min(kShareRows, s_lo[e + 1] - lo));
+    // 16-row tiles, rounded up to one of a few counts
+    const int t = (m + 15) >> 4;
+    static_assert(kShareRows == 128, "tile counts below");
+    if (t <= 1) run_mt<1>(a, e, lo, m, slab, k0, steps, part, smem);
+    else if (t <= 2) run_mt<2>(a, e, lo, m, slab, k0, steps, part, smem);
+    else if (t <= 3) run_mt<3>(a, e, lo, m, slab, k0, steps, part, smem);
+    else if (t <= 4) run_mt<4>(a, e, lo, m, slab, k0, steps, part, smem);
+    else if (t <= 6) run_mt<6>(a, e, lo, m, slab, k0, steps, part, smem);
+    else run_mt<8>(a, e, lo, m, slab, k0, steps, part, smem);
   }
 };
 
@@ -757,23 +762,24 @@ struct SharedA {
 // and the chunks of one expert, which read the same weight rows, mostly share
 // that XCD's L2. One workgroup per CU: with more, the workgroups sharing a CU
 // get very unequal shares of its bandwidth and the last ones set the time.
-// Only the first Ge = min(G, C / 192) workgroups take part: each range is then
+// Only the first Ge = min(G, C / (128 + kShareRows)) workgroups take part: each range is then
 // at least as wide as the costliest step, so every one of them owns a step
 // and the pieces of a pair belong to a contiguous run of workgroups.
 //
-// Chunks are contiguous in rows, so chunk c starting at row lo_c costs
-// nk * slabs * (128 c + lo_c - lo_0) before it, and within an expert whose
-// first chunk is f every chunk but the last has 64 rows.
+// Chunks (kShareRows rows, the last of an expert fewer) are contiguous in
+// rows, so the steps before chunk c, starting at row lo_c, cost nk * slabs *
+// (128 c + lo_c - lo_0).
 struct SkCost {
   long long nks;   // nk * slabs
   int nk, slabs, lo0;
   int wrows;       // weight rows a step loads: 128 here, 64 on the walk path
+  int crows;       // rows per chunk: kShareRows here, kChunkRows on the walk path
   __device__ long long chunk_start(int c, int lo_c) const { return nks * ((long long)wrows * c + lo_c - lo0); }
 };
 
 // First global step whose starting cost is >= x (x < C), from the expert lists:
 // the last expert starting at or before x, then its chunk (all but the last
-// have 64 rows), slab and step.
+// are full), slab and step.
 __device__ long long sk_step_at(const SkCost& q, long long x, const int* s_first, const int* s_lo, int nloc) {
   int lo = 0, hi = nloc - 1;   // last expert whose cost start is <= x
   while (lo < hi) {
@@ -782,10 +788,10 @@ __device__ long long sk_step_at(const SkCost& q, long long x, const int* s_first
   }
   const int e = lo;
   const long long y = x - q.chunk_start(s_first[e], s_lo[e]);
-  const int full = q.wrows + 64;   // step cost of a 64-row chunk
+  const int full = q.wrows + q.crows;   // step cost of a full chunk
   const int j = (int)(y / (q.nks * full));
-  const int c = s_first[e] + j, lo_c = s_lo[e] + 64 * j;
-  const int u = q.wrows + min(64, s_lo[e + 1] - lo_c);
+  const int c = s_first[e] + j, lo_c = s_lo[e] + q.crows * j;
+  const int u = q.wrows + min(q.crows, s_lo[e + 1] - lo_c);
   const long long y2 = y - q.nks * full * j;
   const int slab = (int)(y2 / ((long long)q.nk * u));
   const long long y3 = y2 - (long long)slab * q.nk * u;
@@ -793,7 +799,7 @@ __device__ long long sk_step_at(const SkCost& q, long long x, const int* s_first
 }
 
 __device__ __forceinline__ int sk_active(long long C, int grid) {
-  return (int)max(1LL, min((long long)grid, C / 192));
+  return (int)max(1LL, min((long long)grid, C / (128 + kShareRows)));
 }
 
 __global__ __launch_bounds__(256, 1) void ffn_shared_kernel(GemmArgs a) {
@@ -803,16 +809,17 @@ __global__ __launch_bounds__(256, 1) void ffn_shared_kernel(GemmArgs a) {
   __shared__ int s_lo[kMaxLocal + 1];
   __shared__ int wsum[12];
   int n_chunks, n_tiles, n_big;
-  build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big, true);
+  build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big, true, kShareRows);
   SkCost q;
   q.nk = a.K / SharedA::KSTEP;
   q.slabs = a.inter / kShareCols;
   q.nks = (long long)q.nk * q.slabs;
   q.lo0 = s_lo[0];
   q.wrows = 128;
+  q.crows = kShareRows;
   const long long C = q.chunk_start(n_chunks, s_lo[a.nloc]);
   const long long total = (long long)n_chunks * q.nks;
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.chunk_desc[0] = n_chunks;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.chunk_desc[0] = n_chunks * (a.inter / kShareCols);
   if (C == 0) return;
   const int G = sk_active(C, a.sk_grid);
   const int v = (blockIdx.x % 8) * (a.sk_grid / 8) + blockIdx.x / 8;   // sk_grid == gridDim.x, a multiple of 8
@@ -826,10 +833,12 @@ __global__ __launch_bounds__(256, 1) void ffn_shared_kernel(GemmArgs a) {
     const int steps = __builtin_amdgcn_readfirstlane((int)min(s1 - st, (long long)(q.nk - k0)));
     const int c = cs / q.slabs, slab = cs % q.slabs;
     const int e = find_expert(s_first, a.nloc, c);
-    if (k0 == 0 && slab == 0 && threadIdx.x == 0) {  // for ffn_finalize_kernel
-      const int lo = s_lo[e] + (c - s_first[e]) * kChunkRows;
-      a.chunk_desc[1 + 2 * c] = lo;
-      a.chunk_desc[2 + 2 * c] = min(kChunkRows, s_lo[e + 1] - lo);
+    if (k0 == 0 && threadIdx.x == 0) {  // the pair's record, for ffn_finalize_kernel
+      const int lo = s_lo[e] + (c - s_first[e]) * kShareRows;
+      const int m = min(kShareRows, s_lo[e + 1] - lo), u = q.wrows + m;
+      const long long p = q.chunk_start(c, lo) + (long long)slab * q.nk * u;   // cost at the pair's step 0
+      int4* rec = (int4*)(a.chunk_desc + 4) + cs;
+      *rec = make_int4(lo, m, v, (int)((p + (long long)(q.nk - 1) * u) * G / C));
     }
     float* part = (k0 == 0 && steps == q.nk) ? nullptr : a.partials + (size_t)(v + cs) * SharedA::PART_FLOATS;
     SharedA::run(a, s_lo, e, c - s_first[e], slab, k0, steps, part, smem);
@@ -839,63 +848,59 @@ __global__ __launch_bounds__(256, 1) void ffn_shared_kernel(GemmArgs a) {
 }
 
 // h = SiLU(sum of gate pieces) * (sum of up pieces) for every (chunk, slab)
-// pair that was split, pieces added in K order. The chunk count and each
-// chunk's rows come from the table ffn_shared_kernel writes.
+// pair that was split, pieces added in K order. ffn_shared_kernel leaves the
+// pair count and, per pair, its rows and the workgroups v0..v1 that hold its
+// pieces (slots v + pair).
 __global__ __launch_bounds__(256) void ffn_finalize_kernel(GemmArgs a) {
-  const int n_chunks = a.chunk_desc[0];   // written by ffn_shared_kernel
-  if (n_chunks == 0) return;
-  SkCost q;
-  q.nk = a.K / SharedA::KSTEP;
-  q.slabs = a.inter / kShareCols;
-  q.nks = (long long)q.nk * q.slabs;
-  q.lo0 = a.chunk_desc[1];
-  q.wrows = 128;
-  const int pairs = n_chunks * q.slabs;
-  const long long C = q.chunk_start(n_chunks, a.chunk_desc[2 * n_chunks - 1] + a.chunk_desc[2 * n_chunks]);
-  const int G = sk_active(C, a.sk_grid);
-  const int row = threadIdx.x >> 2, c16 = (threadIdx.x & 3) * 16;  // 64 rows x 4 column groups
-  for (int w = blockIdx.x; w < pairs; w += gridDim.x) {
-    const int c = w / q.slabs, slab = w % q.slabs;
-    const int lo = a.chunk_desc[1 + 2 * c], m = a.chunk_desc[2 + 2 * c];
-    const int u = q.wrows + m;
-    const long long p = q.chunk_start(c, lo) + (long long)slab * q.nk * u;   // cost at the pair's step 0
-    const int v0 = (int)(p * G / C), v1 = (int)((p + (long long)(q.nk - 1) * u) * G / C);
+  const int c16 = (threadIdx.x & 3) * 16;  // 64 rows x 4 column groups
+  constexpr int RB = kShareRows / 64;     // 64-row blocks per chunk
+  // items (pair, row block) up to the largest possible pair count; the pair
+  // count and the pair's record are loaded together
+  for (int it = blockIdx.x; it < a.sk_items; it += gridDim.x) {
+    const int w = it / RB, rb = it % RB;
+    const int pairs = a.chunk_desc[0];   // written by ffn_shared_kernel
+    const int4 rec = ((const int4*)(a.chunk_desc + 4))[w];
+    if (w >= pairs) continue;
+    const int lo = rec.x, m = rec.y, v0 = rec.z, v1 = rec.w;
+    const int slab = w % (a.inter / kShareCols);
     if (v0 == v1) continue;   // one piece: h written directly
-    if (row >= m) continue;
-    f32x4_t gs[4], us[4];
+    const int row = rb * 64 + (threadIdx.x >> 2);
+    if (row < m) {
+      f32x4_t gs[4], us[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gs[i] = us[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // The pieces of workgroups v0..v1, in K order, four at a time: the loads
-    // go out together, the sums are taken in order.
-    for (int v = v0; v <= v1; v += 4) {
-      const int nv = min(4, v1 + 1 - v);
-      f32x4_t pg[4][4], pu[4][4];
+      for (int i = 0; i < 4; ++i) gs[i] = us[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // The pieces of workgroups v0..v1, in K order, four at a time: the loads
+      // go out together, the sums are taken in order.
+      for (int v = v0; v <= v1; v += 4) {
+        const int nv = min(4, v1 + 1 - v);
+        f32x4_t pg[4][4], pu[4][4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (b >= nv) break;
-        const float* pk = a.partials + (size_t)(v + b + w) * SharedA::PART_FLOATS + row * 2 * kShareCols + c16;
+        for (int b = 0; b < 4; ++b) {
+          if (b >= nv) break;
+          const float* pk = a.partials + (size_t)(v + b + w) * SharedA::PART_FLOATS + row * 2 * kShareCols + c16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pg[b][i] = *(const f32x4_t*)(pk + 4 * i);
-          pu[b][i] = *(const f32x4_t*)(pk + kShareCols + 4 * i);
+          for (int i = 0; i < 4; ++i) {
+            pg[b][i] = *(const f32x4_t*)(pk + 4 * i);
+            pu[b][i] = *(const f32x4_t*)(pk + kShareCols + 4 * i);
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          if (b >= nv) break;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { gs[i] += pg[b][i]; us[i] += pu[b][i]; }
         }
       }
+      uint32_t o[8];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (b >= nv) break;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { gs[i] += pg[b][i]; us[i] += pu[b][i]; }
+      for (int i = 0; i < 4; ++i) {
+        o[2 * i] = pack_bf16x2(silu(gs[i][0]) * us[i][0], silu(gs[i][1]) * us[i][1]);
+        o[2 * i + 1] = pack_bf16x2(silu(gs[i][2]) * us[i][2], silu(gs[i][3]) * us[i][3]);
       }
+      uint4* dst = (uint4*)(a.C + (size_t)(lo + row) * a.ldc + slab * kShareCols + c16);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
     }
-    uint32_t o[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[2 * i] = pack_bf16x2(silu(gs[i][0]) * us[i][0], silu(gs[i][1]) * us[i][1]);
-      o[2 * i + 1] = pack_bf16x2(silu(gs[i][2]) * us[i][2], silu(gs[i][3]) * us[i][3]);
-    }
-    uint4* dst = (uint4*)(a.C + (size_t)(lo + row) * a.ldc + slab * kShareCols + c16);
-    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
   }
 }
 
@@ -924,6 +929,7 @@ __global__ __launch_bounds__(256, 2) void ffn_walk_kernel(GemmArgs a) {
   q.nks = q.nk;
   q.lo0 = s_lo[0];
   q.wrows = 64;
+  q.crows = kChunkRows;
   const long long C = q.chunk_start(n_chunks, s_lo[a.nloc]);
   if (C == 0) return;
   const long long total = (long long)n_chunks * q.nk;
@@ -1560,7 +1566,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
 // multiple of 64, at most 128).
 bool use_shared(int hidden, int inter) { return inter % kShareCols == 0 && inter <= 128 && hidden >= 1024; }
 long shared_max_pairs(int num_local, int capacity, int inter) {
-  return ((long)(capacity + kChunkRows - 1) / kChunkRows + num_local) * (inter / kShareCols);
+  return ((long)(capacity + kShareRows - 1) / kShareRows + num_local) * (inter / kShareCols);
 }
 // Workgroups of the shared-activation kernel: one per CU, a multiple of 8.
 int shared_grid() { return std::max(8, cu_count() / 8 * 8); }
@@ -1572,7 +1578,7 @@ size_t ffn_workspace_size(int num_local, int hidden, int inter, int capacity, bo
   if (bf16 && use_shared(hidden, inter)) {  // partial sums (slots v + cs), chunk table
     const size_t pairs = (size_t)shared_max_pairs(num_local, capacity, inter);
     bytes += align256((pairs + shared_grid()) * SharedA::PART_FLOATS * sizeof(float));
-    bytes += align256((1 + 2 * pairs) * sizeof(int));
+    bytes += align256((4 + 4 * pairs) * sizeof(int));
   }
   return bytes;
 }
@@ -1587,7 +1593,8 @@ hipError_t launch_gate_up_shared(const GemmArgs& g0, size_t h_bytes, void* works
   g.partials = (float*)p;
   g.chunk_desc = (int*)(p + align256((size_t)(pairs + g.sk_grid) * SharedA::PART_FLOATS * sizeof(float)));
   hipLaunchKernelGGL(ffn_shared_kernel, dim3(g.sk_grid), dim3(256), 0, s, g);
-  const int grid_f = (int)std::max<long>(1, std::min<long>(pairs, (long)cu_count() * 4));
+  g.sk_items = (int)(pairs * (kShareRows / 64));
+  const int grid_f = (int)std::max<long>(1, std::min<long>(g.sk_items, (long)cu_count() * 4));
   hipLaunchKernelGGL(ffn_finalize_kernel, dim3(grid_f), dim3(256), 0, s, g);
   return hipGetLastError();
 }
