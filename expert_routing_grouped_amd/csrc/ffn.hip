@@ -409,11 +409,12 @@ struct Stream {
 // XOR-swizzled LDS tiles as the streaming path), multiply, store. A work item
 // is a chunk and ITEM_COLS output columns, J steps per wavefront.
 constexpr int kWalkDepth = 3;
+constexpr int kWalkRows = 128;   // rows per chunk on the walk path
 
 template <int KQ>
 struct Walk {
   static constexpr int NTW = 2 / KQ;
-  static constexpr int MT = kStreamMT;
+  static constexpr int MT = kWalkRows / 16;
   static constexpr int STEP_COLS = NTW * 16;
   static constexpr int WD = kWalkDepth;               // weight register sets
   static constexpr int TILE_BYTES = 16 * 128;
@@ -570,16 +571,18 @@ struct Walk {
   __device__ static void run(const GemmArgs& a, const int* s_lo, int e, int chunk, int c0, int steps,
                              char* smem) {
     e = __builtin_amdgcn_readfirstlane(e);
-    const int lo = __builtin_amdgcn_readfirstlane(s_lo[e] + chunk * kChunkRows);
-    const int m = __builtin_amdgcn_readfirstlane(min(kChunkRows, s_lo[e + 1] - lo));
+    const int lo = __builtin_amdgcn_readfirstlane(s_lo[e] + chunk * kWalkRows);
+    const int m = __builtin_amdgcn_readfirstlane(min(kWalkRows, s_lo[e + 1] - lo));
     c0 = __builtin_amdgcn_readfirstlane(c0);
     steps = __builtin_amdgcn_readfirstlane(steps);
-    switch ((m + 15) >> 4) {
-      case 1: run_mt<1>(a, e, lo, m, c0, steps, smem); break;
-      case 2: run_mt<2>(a, e, lo, m, c0, steps, smem); break;
-      case 3: run_mt<3>(a, e, lo, m, c0, steps, smem); break;
-      default: run_mt<4>(a, e, lo, m, c0, steps, smem); break;
-    }
+    static_assert(kWalkRows == 128, "tile counts below");
+    const int t = (m + 15) >> 4;   // 16-row tiles, rounded up to one of a few counts
+    if (t <= 1) run_mt<1>(a, e, lo, m, c0, steps, smem);
+    else if (t <= 2) run_mt<2>(a, e, lo, m, c0, steps, smem);
+    else if (t <= 3) run_mt<3>(a, e, lo, m, c0, steps, smem);
+    else if (t <= 4) run_mt<4>(a, e, lo, m, c0, steps, smem);
+    else if (t <= 6) run_mt<6>(a, e, lo, m, c0, steps, smem);
+    else run_mt<8>(a, e, lo, m, c0, steps, smem);
   }
 };
 
@@ -773,7 +776,7 @@ struct SkCost {
   long long nks;   // nk * slabs
   int nk, slabs, lo0;
   int wrows;       // weight rows a step loads: 128 here, 64 on the walk path
-  int crows;       // rows per chunk: kShareRows here, kChunkRows on the walk path
+  int crows;       // rows per chunk: kShareRows here, kWalkRows on the walk path
   __device__ long long chunk_start(int c, int lo_c) const { return nks * ((long long)wrows * c + lo_c - lo0); }
 };
 
@@ -904,8 +907,8 @@ __global__ __launch_bounds__(256) void ffn_finalize_kernel(GemmArgs a) {
   }
 }
 
-// Plain GEMMs with K = 64 KQ on the walk path: every expert is cut into 64-row
-// chunks and each chunk's output columns into 64-column units (one 128-byte
+// Plain GEMMs with K = 64 KQ on the walk path: every expert is cut into chunks
+// of up to kWalkRows rows and each chunk's output columns into 64-column units (one 128-byte
 // row segment); a unit loads 64 weight rows and stores m output rows, cost 64
 // + m. The units of all chunks, laid end to end, are shared out by cost over
 // all wavefronts of the grid (the same split as ffn_shared_kernel's, per
@@ -914,7 +917,7 @@ __global__ __launch_bounds__(256) void ffn_finalize_kernel(GemmArgs a) {
 // Wavefronts of one XCD take consecutive ranges, so the chunks of one
 // expert, which read the same weight rows, mostly share that XCD's L2.
 template <int KQ>
-__global__ __launch_bounds__(256, 2) void ffn_walk_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256, 1) void ffn_walk_kernel(GemmArgs a) {
   using Wk = Walk<KQ>;
   __shared__ __attribute__((aligned(16))) char smem[Wk::LDS_BYTES];
   __shared__ int s_first[kMaxLocal + 1];
@@ -922,14 +925,14 @@ __global__ __launch_bounds__(256, 2) void ffn_walk_kernel(GemmArgs a) {
   __shared__ int s_lo[kMaxLocal + 1];
   __shared__ int wsum[12];
   int n_chunks, n_tiles, n_big;
-  build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big, true);
+  build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big, true, kWalkRows);
   SkCost q;
   q.nk = a.N / 64;   // units per chunk
   q.slabs = 1;
   q.nks = q.nk;
   q.lo0 = s_lo[0];
   q.wrows = 64;
-  q.crows = kChunkRows;
+  q.crows = kWalkRows;
   const long long C = q.chunk_start(n_chunks, s_lo[a.nloc]);
   if (C == 0) return;
   const long long total = (long long)n_chunks * q.nk;
