@@ -96,16 +96,18 @@ constexpr int kNonTemporal = 2;
 
 // Splits the local experts by row count m, in expert order (and leaves the
 // clamped row bounds in s_lo: rows of expert e are [s_lo[e], s_lo[e] + m);
-// n_big = the tiles of kBigBM rows the tiled experts need; with all_chunks
-// every expert is cut into chunks of chunk_rows rows):
-//   1 <= m <= kStreamRows: streamed, in ceil(m / kChunkRows) row chunks;
-//                          s_first[e] = first chunk of expert e, s_first[nloc] = chunks
-//   m > kStreamRows:       tiled, in ceil(m / bm) row tiles;
-//                          t_first[e] = first tile of expert e, t_first[nloc] = tiles
+// n_big = the tiles of kBigBM rows that the experts above kStreamRows rows
+// need, whatever stream_max is; with all_chunks every expert is cut into
+// chunks of chunk_rows rows):
+//   1 <= m <= stream_max: streamed, in ceil(m / chunk_rows) row chunks;
+//                         s_first[e] = first chunk of expert e, s_first[nloc] = chunks
+//   m > stream_max:       tiled, in ceil(m / bm) row tiles;
+//                         t_first[e] = first tile of expert e, t_first[nloc] = tiles
 // Every thread of the 256-thread workgroup calls this; 4 experts per thread.
 __device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_first, int* s_lo,
                             int* wsum, int& n_chunks, int& n_tiles, int& n_big,
-                            bool all_chunks = false, int chunk_rows = kChunkRows) {
+                            bool all_chunks = false, int chunk_rows = kChunkRows,
+                            int stream_max = kStreamRows) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int cc[4], tc[4], cs = 0, ct = 0, cb = 0;
 #pragma unroll
@@ -119,7 +121,7 @@ __device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_firs
       s_lo[e] = lo;
       if (e == a.nloc - 1) s_lo[a.nloc] = max(lo, hi);
     }
-    const bool chunked = all_chunks || m <= kStreamRows;
+    const bool chunked = all_chunks || m <= stream_max;
     cc[q] = (m > 0 && chunked) ? (m + chunk_rows - 1) / chunk_rows : 0;
     tc[q] = (m > 0 && !chunked) ? (m + bm - 1) / bm : 0;
     cs += cc[q];
@@ -1345,8 +1347,14 @@ __global__ __launch_bounds__(256, 1) void ffn_big_kernel(GemmArgs a) {
   int n_chunks, n_tiles, n_big;
   build_lists(a, kBigBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big);
   const int nblk = (GATED ? a.inter : a.N) / B::COLS;
+  if (n_big * nblk < a.big_min_items) return;  // the persistent kernel does these experts
+  // This kernel takes every expert with more than kChunkRows rows: for one
+  // with 65 .. kStreamRows rows a row of (partly filled) 256 x 256 tiles
+  // costs less than streaming its weights once per 64-row chunk, and the
+  // extra items land in the partly idle last round.
+  build_lists(a, kBigBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big, false, kChunkRows,
+              kChunkRows);
   const int total = n_tiles * nblk;
-  if (total < a.big_min_items) return;  // the persistent kernel does these tiles
   // Items are (token tile, N block) with N blocks fastest, taken round-robin
   // by a grid that is a multiple of 8: workgroup b runs on XCD b % 8 and its
   // items keep the same N block whenever nblk divides the grid, so its weight
@@ -1390,10 +1398,15 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(GemmArgs a) {
   const int ncols = GATED ? a.inter : a.N;
   const int slabs = ncols / S::COLS;
   const int nblk = ncols / T::COLS;
-  const int n_stream = n_chunks * slabs;
-  // Same decision as ffn_big_kernel: it takes the tiled experts when it has
-  // enough tiles to fill the GPU, else they are done here in 128 x 128 tiles.
+  // Same decision as ffn_big_kernel: when the experts above kStreamRows rows
+  // fill the GPU with its tiles, it takes every expert with more than
+  // kChunkRows rows and only the smaller ones are streamed here; else the
+  // experts above kStreamRows rows are done here in 128 x 128 tiles.
   const bool big = a.big_ok && n_big * (ncols / Big<GATED>::COLS) >= a.big_min_items;
+  if (big)
+    build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big, false, kChunkRows,
+                kChunkRows);
+  const int n_stream = n_chunks * slabs;
   const int total = n_stream + (big ? 0 : n_tiles * nblk);
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     if (w < n_stream) {

@@ -340,3 +340,12 @@ def test_layer_prefill_sampled(name):
     e_y = rel_err(as_f64(g["y"][toks]), y_ref)
     print(f"  M={M} sampled rows={rows.size} rel_err o={e_o:.3e} y={e_y:.3e}", flush=True)
     assert e_o <= TOL_BF16 and e_y <= TOL_BF16
+
+
+def test_layer_prefill_routing_every_row():
+    """The prefill_straggler routing (experts of 2 .. 2659 rows) at d = 2048, I = 2048: the
+    large-tile kernel runs both GEMMs and takes every expert above 64 rows (the ones with 97
+    and 102 rows as single partly filled tiles), the streaming kernel the rest; every row of
+    o and y is checked against the oracle."""
+    wl = W.WORKLOADS["prefill_straggler"].replace(name="prefill_straggler_d2048", hidden=2048)
+    check_full(wl, W.generate(wl), TOL_BF16)
