@@ -156,22 +156,33 @@ __global__ __launch_bounds__(256) void block_scatter_kernel(
   const int hi = (int)min((long)n, (long)lo + per_wave);
   wave_count(ids, lo, hi, begin, nloc, nbits, cnt + w * nloc);
 
-  // totals and this block's preceding counts for experts tid*4 .. tid*4+3
+  // totals and this block's preceding counts for experts tid*4 .. tid*4+3;
+  // the per-block counts are loaded eight blocks at a time (all eight loads
+  // in flight before the first is added)
   int tot[4], before[4], sum = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int e = tid * 4 + q;
     tot[q] = 0;
     before[q] = 0;
-    if (e < nloc) {
-      for (int bb = 0; bb < nblocks; ++bb) {
-        const int c = ws[bb * nloc + e];
-        tot[q] += c;
-        if (bb < b) before[q] += c;
-      }
-    }
-    sum += tot[q];
   }
+  for (int bb = 0; bb < nblocks; bb += 8) {
+    int c[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid * 4 + q;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c[q][i] = (e < nloc && bb + i < nblocks) ? ws[(bb + i) * nloc + e] : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        tot[q] += c[q][i];
+        if (bb + i < b) before[q] += c[q][i];
+      }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sum += tot[q];
   const int incl = wave_inclusive_scan(sum);
   if (lane == 63) wsum[w] = incl;
   __syncthreads();  // also orders the recount above before the reads below
