@@ -46,6 +46,25 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
+// Ids are read kBatch groups of 64 at a time: all of a batch's loads are in
+// flight before the first is used.
+constexpr int kBatch = 8;
+
+// Local expert of assignment a (-1 if a >= hi or its expert is not local),
+// for the kBatch groups of 64 starting at base.
+__device__ __forceinline__ void load_batch(const int* __restrict__ ids, int base, int hi, int begin,
+                                           int nloc, int (&ev)[kBatch]) {
+  const int lane = threadIdx.x & 63;
+  int raw[kBatch];
+#pragma unroll
+  for (int g = 0; g < kBatch; ++g) {
+    const int a = base + g * 64 + lane;
+    raw[g] = a < hi ? ids[a] - begin : -1;
+  }
+#pragma unroll
+  for (int g = 0; g < kBatch; ++g) ev[g] = (unsigned)raw[g] < (unsigned)nloc ? raw[g] : -1;
+}
+
 // Counts one wavefront's assignments [lo, hi) per local expert into my_cnt
 // (this wavefront's LDS row). The lowest lane of each group of equal keys adds
 // the group's size, so no two lanes write the same counter.
@@ -53,15 +72,14 @@ __device__ __forceinline__ void wave_count(const int* __restrict__ ids, int lo, 
                                            int nloc, int nbits, int* my_cnt) {
   const int lane = threadIdx.x & 63;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-  for (int base = lo; base < hi; base += 64) {
-    const int a = base + lane;
-    int e = -1;
-    if (a < hi) {
-      const int x = ids[a] - begin;
-      if ((unsigned)x < (unsigned)nloc) e = x;
+  for (int base = lo; base < hi; base += 64 * kBatch) {
+    int ev[kBatch];
+    load_batch(ids, base, hi, begin, nloc, ev);
+#pragma unroll
+    for (int g = 0; g < kBatch; ++g) {
+      const uint64_t peers = match_key(ev[g], ev[g] >= 0, nbits);
+      if (ev[g] >= 0 && (peers & lt_mask) == 0ull) my_cnt[ev[g]] += __popcll(peers);
     }
-    const uint64_t peers = match_key(e, e >= 0, nbits);
-    if (e >= 0 && (peers & lt_mask) == 0ull) my_cnt[e] += __popcll(peers);
   }
 }
 
@@ -74,26 +92,27 @@ __device__ __forceinline__ void wave_scatter(const int* __restrict__ ids, int lo
                                              int* __restrict__ assign_pos) {
   const int lane = threadIdx.x & 63;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-  for (int base = lo; base < hi; base += 64) {
-    const int a = base + lane;
-    int e = -1;
-    if (a < hi) {
-      const int x = ids[a] - begin;
-      if ((unsigned)x < (unsigned)nloc) e = x;
-    }
-    const uint64_t peers = match_key(e, e >= 0, nbits);
-    if (a < hi) {
-      if (e >= 0) {
-        const int p = my_base[e] + __popcll(peers & lt_mask);
-        sorted_assign[p] = a;
-        assign_pos[a] = p;
-      } else {
-        assign_pos[a] = -1;
+  for (int base = lo; base < hi; base += 64 * kBatch) {
+    int ev[kBatch];
+    load_batch(ids, base, hi, begin, nloc, ev);
+#pragma unroll
+    for (int g = 0; g < kBatch; ++g) {
+      const int a = base + g * 64 + lane;
+      const int e = ev[g];
+      const uint64_t peers = match_key(e, e >= 0, nbits);
+      if (a < hi) {
+        if (e >= 0) {
+          const int p = my_base[e] + __popcll(peers & lt_mask);
+          sorted_assign[p] = a;
+          assign_pos[a] = p;
+        } else {
+          assign_pos[a] = -1;
+        }
       }
+      // LDS operations of one wave execute in order: every lane has read the
+      // running base above before the leader advances it here.
+      if (e >= 0 && (peers & lt_mask) == 0ull) my_base[e] += __popcll(peers);
     }
-    // LDS operations of one wave execute in order: every lane has read the
-    // running base above before the leader advances it here.
-    if (e >= 0 && (peers & lt_mask) == 0ull) my_base[e] += __popcll(peers);
   }
 }
 
