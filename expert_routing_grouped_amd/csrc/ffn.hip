@@ -1393,19 +1393,18 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(GemmArgs a) {
   __shared__ int t_first[kMaxLocal + 1];
   __shared__ int s_lo[kMaxLocal + 1];
   __shared__ int wsum[12];
+  // Experts with more than kChunkRows rows are tiled (a tile reads the
+  // weights once per kTileBM rows, a streamed chunk once per kChunkRows).
   int n_chunks, n_tiles, n_big;
-  build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big);
+  build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big, false, kChunkRows,
+              kChunkRows);
   const int ncols = GATED ? a.inter : a.N;
   const int slabs = ncols / S::COLS;
   const int nblk = ncols / T::COLS;
   // Same decision as ffn_big_kernel: when the experts above kStreamRows rows
-  // fill the GPU with its tiles, it takes every expert with more than
-  // kChunkRows rows and only the smaller ones are streamed here; else the
-  // experts above kStreamRows rows are done here in 128 x 128 tiles.
+  // fill the GPU with its tiles, it takes every tiled expert and only the
+  // streamed ones are done here; else the tiles are done here, 128 x 128.
   const bool big = a.big_ok && n_big * (ncols / Big<GATED>::COLS) >= a.big_min_items;
-  if (big)
-    build_lists(a, kTileBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big, false, kChunkRows,
-                kChunkRows);
   const int n_stream = n_chunks * slabs;
   const int total = n_stream + (big ? 0 : n_tiles * nblk);
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
