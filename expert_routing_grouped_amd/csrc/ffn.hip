@@ -1438,11 +1438,20 @@ struct GemmArgsF32 {
   int ldc;
 };
 
-// 16 rows x 16 output columns per workgroup, plain FMA, bounds-checked in N and K.
-// blockIdx.y = expert * max_row_tiles + row tile; blockIdx.x = column block.
+// 16 rows x 16 output columns per workgroup, plain FMA, bounds-checked in N
+// and K. K goes in chunks of 256: thread (ty, tx) loads elements tx + 16 j
+// (j = 0..15) of the chunk for row ty of each operand (coalesced, all loads
+// of a chunk in flight together), the next chunk's loads are issued before
+// the current one is multiplied, and each output accumulates over k in
+// ascending order. blockIdx.y = expert * max_row_tiles + row tile;
+// blockIdx.x = column block.
+constexpr int kF32KC = 256;
+constexpr int kF32J = kF32KC / 16;   // elements per thread and operand of one chunk
+
 template <bool GATED>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF32 a) {
-  __shared__ float As[16][17], Bg[16][17], Bu[16][17];
+  // rows padded by 4 floats: 16-byte aligned for float4 reads
+  __shared__ __attribute__((aligned(16))) float As[16][kF32KC + 4], Bg[16][kF32KC + 4], Bu[16][kF32KC + 4];
   const int e = blockIdx.y / a.max_row_tiles, tile = blockIdx.y % a.max_row_tiles;
   const int lo = min(a.offsets[e], a.capacity), hi = min(a.offsets[e + 1], a.capacity);
   const int row0 = lo + tile * 16;
@@ -1458,18 +1467,45 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgsF32 a) {
     const int r = row0 + ty;
     arow = a.A + (size_t)(a.row_index ? a.row_index[r] / a.row_div : r) * K;
   }
-  float gs = 0.f, us = 0.f;
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    const int kk = k0 + tx;
-    As[ty][tx] = (arow && kk < K) ? arow[kk] : 0.f;
-    const int n = col0 + ty;
-    Bg[ty][tx] = (n < n_out && kk < K) ? We[(size_t)n * K + kk] : 0.f;
-    if (GATED) Bu[ty][tx] = (n < n_out && kk < K) ? We[(size_t)(a.inter + n) * K + kk] : 0.f;
-    __syncthreads();
+  const int n = col0 + ty;   // the weight row this thread loads
+  const float* grow = n < n_out ? We + (size_t)n * K : nullptr;
+  const float* urow = (GATED && n < n_out) ? We + (size_t)(a.inter + n) * K : nullptr;
+  float ra[kF32J], rg[kF32J], ru[kF32J];
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      gs += As[ty][q] * Bg[tx][q];
-      if (GATED) us += As[ty][q] * Bu[tx][q];
+    for (int j = 0; j < kF32J; ++j) {
+      const int kk = k0 + tx + 16 * j;
+      ra[j] = (arow && kk < K) ? arow[kk] : 0.f;
+      rg[j] = (grow && kk < K) ? grow[kk] : 0.f;
+      if (GATED) ru[j] = (urow && kk < K) ? urow[kk] : 0.f;
+    }
+  };
+  float gs = 0.f, us = 0.f;
+  load(0);
+  for (int k0 = 0; k0 < K; k0 += kF32KC) {
+#pragma unroll
+    for (int j = 0; j < kF32J; ++j) {
+      As[ty][tx + 16 * j] = ra[j];
+      Bg[ty][tx + 16 * j] = rg[j];
+      if (GATED) Bu[ty][tx + 16 * j] = ru[j];
+    }
+    __syncthreads();
+    if (k0 + kF32KC < K) load(k0 + kF32KC);
+#pragma unroll
+    for (int q = 0; q < kF32KC; q += 4) {
+      const float4 av = *(const float4*)&As[ty][q];
+      const float4 gv = *(const float4*)&Bg[tx][q];
+      gs = fmaf(av.x, gv.x, gs);
+      gs = fmaf(av.y, gv.y, gs);
+      gs = fmaf(av.z, gv.z, gs);
+      gs = fmaf(av.w, gv.w, gs);
+      if (GATED) {
+        const float4 uv = *(const float4*)&Bu[tx][q];
+        us = fmaf(av.x, uv.x, us);
+        us = fmaf(av.y, uv.y, us);
+        us = fmaf(av.z, uv.z, us);
+        us = fmaf(av.w, uv.w, us);
+      }
     }
     __syncthreads();
   }
