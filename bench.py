@@ -44,7 +44,10 @@ def parse():
                    help="weight copies rotated over the timed steps (0 = enough to exceed the cache)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                    help="only run a plain device-to-device copy of MB megabytes, 5 times "
-                        "(the known-size reference for hardware byte counters)")
+                        "(the known-size reference for hardware byte counters), and report its rate")
+    p.add_argument("--operands", choices=["random", "zeros"], default="random",
+                   help="zeros: a diagnostic run with x and the expert weights all zero (same routing), "
+                        "which shows how much of the GEMM time depends on the operand values")
     return p.parse_args()
 
 
@@ -53,10 +56,16 @@ def calibrate_copy(mb, torch):
     src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    for _ in range(5):
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    ev[0].record(stream)
+    for i in range(5):
         dst.copy_(src)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
+    us = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(5))
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": 5, "median_us": us[2],
+                      "read_plus_write_gbs": 2 * n / (us[2] * 1e-6) / 1e9}))
 
 
 FFN_SOURCES = ["expert_routing_grouped_amd/csrc/ffn.hip", "expert_routing_grouped_amd/csrc/device_common.h",
@@ -98,10 +107,14 @@ def ffn_accounting(wl, counts):
                 weight_bytes=weight_bytes, act_bytes=act_bytes)
 
 
-def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host):
+def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, operands="random"):
     dev = "cuda:0"
     t0 = time.time()
     inp = W.generate(wl)
+    if operands == "zeros" and wl.has_ffn:   # same routing, all-zero GEMM operands
+        inp.x = np.zeros_like(inp.x)
+        inp.w_gate_up = np.zeros_like(inp.w_gate_up)
+        inp.w_down = np.zeros_like(inp.w_down)
     gen_s = time.time() - t0
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     mode = moe.MOE_SCORE_SOFTMAX if wl.score_mode == "softmax" else moe.MOE_SCORE_RAW
@@ -244,13 +257,15 @@ def main():
     wl = W.WORKLOADS[args.workload]
     print(f"bench: workload {wl.name}, steps {args.steps}, warmup {args.warmup}", file=sys.stderr,
           flush=True)
-    head = run_workload(wl, args.steps, args.warmup, args.copies, torch, moe, to_device, to_host)
+    head = run_workload(wl, args.steps, args.warmup, args.copies, torch, moe, to_device, to_host,
+                        args.operands)
     inp = head.pop("_inputs")
     out = {
         "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32", "data": "synthetic",
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic" if args.operands == "random" else "synthetic, all-zero GEMM operands (diagnostic)",
         "config": {"workload": wl.name, "tokens": wl.T, "experts": wl.E, "top_k": wl.top_k,
                    "groups": f"{wl.num_groups} keep {wl.topk_groups}", "hidden": wl.hidden,
                    "inter": wl.inter, "local_experts": f"[{wl.expert_begin}, {wl.expert_begin + wl.num_local})",
@@ -271,7 +286,7 @@ def main():
                            "algorithmic_flops": head["ffn_gflop"] * 1e9}
     out["detail"] = {k: v for k, v in head.items() if k not in ("tokens_per_s",)}
     print(f"bench: {wl.name} {head['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
-    if not args.no_cpu_baseline and wl.has_ffn:
+    if not args.no_cpu_baseline and wl.has_ffn and args.operands == "random":
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, wl)
     del inp
