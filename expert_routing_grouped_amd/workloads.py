@@ -18,6 +18,9 @@ Draw recipe (the order of draws is part of the definition):
   ``0.02 * standard_normal((2I, d), float32)`` (rows [0, I) gate, rows
   [I, 2I) up), and after all of them, expert by expert, the down weight
   ``0.02 * standard_normal((d, I), float32)``.
+* The capacity workload (routing and capped dispatch only) draws its scores
+  the same way, with the shape of the capacity-factor example in section 4.3
+  of the ch15 page ("第十五章：多节点大模型推理", se7en.mintlify.app).
 * bf16 workloads round x and the weights to bf16 (round to nearest even);
   the toy workload keeps float32 and draws its router logits with
   ``standard_normal((T, E), float32)`` before x.
@@ -47,6 +50,7 @@ class Workload:
     num_local: int         # experts owned by this GPU
     dtype: str             # "f32" or "bf16" for x, weights and outputs
     seed: int = 0
+    capacity_factor: str | None = None   # per-expert cap C = ceil(c T k / E), c as an exact decimal
 
     @property
     def has_ffn(self) -> bool:
@@ -78,6 +82,13 @@ WORKLOADS = {
     "prefill_literal": Workload("prefill_literal", T=8192, E=256, top_k=8, num_groups=8, topk_groups=4,
                                 score_mode="raw", renormalize=True, bias_std=2.0,
                                 hidden=7168, inter=2048, expert_begin=0, num_local=32, dtype="bf16"),
+    # The capacity-factor example of ch15 section 4.3 (T = 5600 tokens, k = 16
+    # of E = 896 experts, c = 1.2: C = 120), routing and capped dispatch only:
+    # no groups, scores drawn as above (the page gives no score distribution).
+    "capacity_route": Workload("capacity_route", T=5600, E=896, top_k=16, num_groups=1, topk_groups=1,
+                               score_mode="raw", renormalize=True, bias_std=1.0,
+                               hidden=0, inter=0, expert_begin=0, num_local=896, dtype="f32",
+                               capacity_factor="1.2"),
 }
 
 

@@ -24,7 +24,9 @@ Sources (web pages; section names as printed on them):
   gating picks top-k experts per token, dispatch sends each token to its
   experts, combine returns results to token order and merges them;
   section 4.1: gating picks *logical* experts; section 4.3: the imbalance
-  metric max_e n_e / mean_e n_e.
+  metric max_e n_e / mean_e n_e, the capacity factor C = ceil(c T k / E)
+  with its worked example (T = 5600, k = 16 of E = 896 experts, c = 1.2:
+  mean 100, C = 120) and the table of overflow policies.
 * [TRACE] "追踪一个 Token 在 MoE 推理中穿越 TP/CP/SP/EP/DP/PP 的路径"
   (attain.fans), hop 4 "分发到两个专家": the combined output is the
   router-weighted sum of the selected experts' outputs,
@@ -58,12 +60,15 @@ design notes of the repository):
 """
 from __future__ import annotations
 
+import math
+from fractions import Fraction
+
 import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64", "route_softmax_topk", "route_grouped", "route",
-    "dispatch", "gather_rows", "expert_ffn", "expert_ffn_rows", "combine",
-    "layer",
+    "dispatch", "expert_capacity", "dispatch_capacity", "gather_rows", "expert_ffn",
+    "expert_ffn_rows", "combine", "layer",
 ]
 
 
@@ -177,6 +182,48 @@ def dispatch(topk_ids: np.ndarray, expert_begin: int, num_local: int):
     assign_pos[sorted_assign] = np.arange(sorted_assign.shape[0])
     return (counts.astype(np.int32), offsets.astype(np.int32),
             sorted_assign.astype(np.int32), assign_pos.astype(np.int32))
+
+
+def expert_capacity(num_tokens: int, top_k: int, num_experts: int, factor) -> int:
+    """Per-expert capacity C = ceil(c * T * k / E) [CH15 section 4.3, "Capacity Factor"].
+
+    factor is taken as an exact rational (a fractions.Fraction, an int, or a
+    decimal string such as "1.2"), so that the ceiling is not moved by binary
+    rounding: c = 1.2 with T = 5600, k = 16, E = 896 gives exactly 120.
+    """
+    c = Fraction(factor)
+    return math.ceil(c * num_tokens * top_k / num_experts)
+
+
+def dispatch_capacity(topk_ids: np.ndarray, expert_begin: int, num_local: int, capacity: int):
+    """Dispatch with a per-expert capacity and the drop policy [CH15 section 4.3, capacity
+    factor and the table of overflow policies: drop / residual path].
+
+    Each local expert keeps its first `capacity` assignments in assignment order
+    a = t * k + j (first come, first served); later ones are dropped: they get
+    no row (assign_pos = -1) and contribute nothing to the combine.
+    Returns (counts = rows kept per expert, offsets, sorted_assign [M],
+    assign_pos [T * k], demand = assignments per expert before the cap), int32.
+    Written as one pass over the assignments in order, with a running count
+    per expert.
+    """
+    flat = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    demand = np.zeros(num_local, dtype=np.int64)
+    kept = [[] for _ in range(num_local)]
+    for a, expert in enumerate(flat.tolist()):
+        e = expert - expert_begin
+        if 0 <= e < num_local:
+            if demand[e] < capacity:
+                kept[e].append(a)
+            demand[e] += 1
+    counts = np.array([len(r) for r in kept], dtype=np.int64)
+    offsets = np.zeros(num_local + 1, dtype=np.int64)
+    np.cumsum(counts, out=offsets[1:])
+    sorted_assign = np.array([a for r in kept for a in r], dtype=np.int64)
+    assign_pos = np.full(flat.shape[0], -1, dtype=np.int64)
+    assign_pos[sorted_assign] = np.arange(sorted_assign.shape[0])
+    return (counts.astype(np.int32), offsets.astype(np.int32), sorted_assign.astype(np.int32),
+            assign_pos.astype(np.int32), demand.astype(np.int32))
 
 
 def gather_rows(x: np.ndarray, sorted_assign: np.ndarray, top_k: int) -> np.ndarray:

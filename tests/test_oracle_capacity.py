@@ -1,0 +1,84 @@
+"""Pins of the oracle's capacity-limited dispatch (CH15 section 4.3, "Capacity Factor", and its
+table of overflow policies; drop policy, first come first served in assignment order).
+
+CPU only."""
+import numpy as np
+import pytest
+
+import oracle
+from expert_routing_grouped_amd import workloads as W
+
+
+def test_capacity_of_the_pages_worked_example():
+    # T = 5600 tokens, k = 16 of E = 896 experts: 100 assignments per expert on
+    # average; capacity factor 1.2 gives a cap of about 120 (the page's figures)
+    assert 5600 * 16 // 896 == 100 and 5600 * 16 % 896 == 0
+    assert oracle.expert_capacity(5600, 16, 896, "1.2") == 120
+    assert oracle.expert_capacity(5600, 16, 896, 1) == 100
+    assert oracle.expert_capacity(5600, 16, 896, "1.5") == 150
+    assert oracle.expert_capacity(10, 3, 7, 1) == 5          # ceil(30 / 7)
+
+
+def test_hand_example():
+    # 4 tokens, k = 2, experts 0..2 all local, capacity 2
+    ids = np.array([[0, 1], [0, 2], [1, 0], [0, 1]], dtype=np.int32)
+    counts, offsets, sa, pos, demand = oracle.dispatch_capacity(ids, 0, 3, 2)
+    # expert 0 gets a = 0, 2, 5, 6 -> keeps 0, 2; expert 1 gets 1, 4, 7 -> keeps 1, 4; expert 2 gets 3
+    assert demand.tolist() == [4, 3, 1]
+    assert counts.tolist() == [2, 2, 1]
+    assert offsets.tolist() == [0, 2, 4, 5]
+    assert sa.tolist() == [0, 2, 1, 4, 3]
+    assert pos.tolist() == [0, 2, 1, 4, 3, -1, -1, -1]
+
+
+def test_local_range_and_dropped_non_local():
+    ids = np.array([[5, 6], [6, 7], [6, 5]], dtype=np.int32)
+    counts, offsets, sa, pos, demand = oracle.dispatch_capacity(ids, 6, 2, 1)   # experts 6, 7
+    assert demand.tolist() == [3, 1] and counts.tolist() == [1, 1]
+    assert sa.tolist() == [1, 3] and pos.tolist() == [-1, 0, -1, 1, -1, -1]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_large_capacity_equals_dropless(seed):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, 20, size=(300, 4)).astype(np.int32)
+    ref = oracle.dispatch(ids, 3, 12)
+    got = oracle.dispatch_capacity(ids, 3, 12, 10 ** 6)
+    for r, g in zip(ref, got[:4]):
+        assert np.array_equal(r, g)
+    assert np.array_equal(got[4], ref[0])
+
+
+def test_zero_capacity_drops_everything():
+    ids = np.arange(24, dtype=np.int32).reshape(6, 4) % 5
+    counts, offsets, sa, pos, demand = oracle.dispatch_capacity(ids, 0, 5, 0)
+    assert not counts.any() and not offsets.any() and sa.size == 0 and (pos == -1).all()
+    assert demand.sum() == 24
+
+
+@pytest.mark.parametrize("cap", [1, 3, 7])
+def test_properties_against_the_dropless_sort(cap):
+    # the kept rows of an expert are the first `cap` of its rows in the dropless
+    # (stable) order, and nothing else changes order
+    rng = np.random.default_rng(cap)
+    ids = rng.integers(0, 16, size=(200, 6)).astype(np.int32)
+    c0, o0, s0, p0 = oracle.dispatch(ids, 2, 10)
+    counts, offsets, sa, pos, demand = oracle.dispatch_capacity(ids, 2, 10, cap)
+    assert np.array_equal(demand, c0)
+    assert np.array_equal(counts, np.minimum(c0, cap))
+    for e in range(10):
+        assert np.array_equal(sa[offsets[e]:offsets[e + 1]], s0[o0[e]:o0[e] + counts[e]])
+    kept = pos >= 0
+    assert np.array_equal(sa[pos[kept]], np.nonzero(kept)[0])
+    assert kept.sum() == counts.sum() == offsets[-1]
+
+
+def test_kimi_shape_workload():
+    wl = W.WORKLOADS["capacity_route"]
+    assert (wl.T, wl.E, wl.top_k, wl.num_groups) == (5600, 896, 16, 1)
+    ids, _ = oracle.route(W.generate(wl).scores, wl.top_k, 1, 1, "raw", True)
+    cap = oracle.expert_capacity(wl.T, wl.top_k, wl.E, wl.capacity_factor)
+    counts, offsets, sa, pos, demand = oracle.dispatch_capacity(ids, 0, wl.E, cap)
+    assert cap == 120 and demand.sum() == wl.T * wl.top_k
+    assert counts.max() <= cap and (demand > cap).any()      # the bias makes some experts overflow
+    assert offsets[-1] == np.minimum(demand, cap).sum()
