@@ -84,9 +84,11 @@ WORKLOADS = {
                                 hidden=7168, inter=2048, expert_begin=0, num_local=32, dtype="bf16"),
     # The capacity-factor example of ch15 section 4.3 (T = 5600 tokens, k = 16
     # of E = 896 experts, c = 1.2: C = 120), routing and capped dispatch only:
-    # no groups, scores drawn as above (the page gives no score distribution).
+    # no groups, scores drawn as above (the page gives no score distribution)
+    # with a bias std of 0.1, which puts the hottest expert at 3.5x the mean
+    # load, within the 2.9-4.0 busiest/mean range of the EPLB page's simulation.
     "capacity_route": Workload("capacity_route", T=5600, E=896, top_k=16, num_groups=1, topk_groups=1,
-                               score_mode="raw", renormalize=True, bias_std=1.0,
+                               score_mode="raw", renormalize=True, bias_std=0.1,
                                hidden=0, inter=0, expert_begin=0, num_local=896, dtype="f32",
                                capacity_factor="1.2"),
 }
