@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -61,13 +61,14 @@ size_t moe_dispatch_workspace_size(int32_t num_tokens, int32_t top_k, int32_t nu
   return moe::dispatch_workspace_size((int)n, num_local_experts);
 }
 
-moe_status_t moe_dispatch(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
-                          int32_t expert_begin, int32_t num_local_experts, const void* x,
-                          int32_t hidden, int32_t dtype, int32_t* expert_counts,
-                          int32_t* expert_offsets, int32_t* sorted_assign, int32_t* assign_pos,
-                          void* x_sorted, void* workspace, size_t workspace_bytes,
-                          hipStream_t stream) {
-  if (num_tokens < 0 || top_k < 1 || expert_begin < 0 || num_local_experts < 1)
+static moe_status_t dispatch_impl(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
+                                  int32_t expert_begin, int32_t num_local_experts, const void* x,
+                                  int32_t hidden, int32_t dtype, int32_t* expert_counts,
+                                  int32_t* expert_offsets, int32_t* sorted_assign,
+                                  int32_t* assign_pos, void* x_sorted, void* workspace,
+                                  size_t workspace_bytes, int32_t capacity, int32_t* demand,
+                                  hipStream_t stream) {
+  if (num_tokens < 0 || top_k < 1 || expert_begin < 0 || num_local_experts < 1 || capacity < 0)
     return MOE_ERR_INVALID;
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
   if (num_local_experts > moe::kDispatchMaxLocal) return MOE_ERR_UNSUPPORTED;
@@ -89,8 +90,31 @@ moe_status_t moe_dispatch(const int32_t* topk_ids, int32_t num_tokens, int32_t t
     return MOE_ERR_WORKSPACE;
   moe::DispatchArgs a{topk_ids, (int)n, top_k, expert_begin, num_local_experts, expert_counts,
                       expert_offsets, sorted_assign, assign_pos, x, x_sorted, row_bytes,
-                      workspace};
+                      workspace, capacity, demand};
   return from_hip(moe::launch_dispatch(a, stream));
+}
+
+moe_status_t moe_dispatch(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
+                          int32_t expert_begin, int32_t num_local_experts, const void* x,
+                          int32_t hidden, int32_t dtype, int32_t* expert_counts,
+                          int32_t* expert_offsets, int32_t* sorted_assign, int32_t* assign_pos,
+                          void* x_sorted, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  return dispatch_impl(topk_ids, num_tokens, top_k, expert_begin, num_local_experts, x, hidden,
+                       dtype, expert_counts, expert_offsets, sorted_assign, assign_pos, x_sorted,
+                       workspace, workspace_bytes, INT32_MAX, nullptr, stream);
+}
+
+moe_status_t moe_dispatch_capacity(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
+                                   int32_t expert_begin, int32_t num_local_experts,
+                                   int32_t expert_capacity, const void* x, int32_t hidden,
+                                   int32_t dtype, int32_t* expert_counts, int32_t* expert_offsets,
+                                   int32_t* expert_demand, int32_t* sorted_assign,
+                                   int32_t* assign_pos, void* x_sorted, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  return dispatch_impl(topk_ids, num_tokens, top_k, expert_begin, num_local_experts, x, hidden,
+                       dtype, expert_counts, expert_offsets, sorted_assign, assign_pos, x_sorted,
+                       workspace, workspace_bytes, expert_capacity, expert_demand, stream);
 }
 
 static moe_status_t check_ffn_sizes(int32_t num_local_experts, int32_t hidden, int32_t inter,

@@ -11,8 +11,14 @@
 // found with one ballot per key bit (a wave-wide "match"), which gives each
 // lane its rank among equal keys in the step without atomics. Pass 1 counts
 // per (wave, expert) in LDS; a scan turns the counts into per-(wave, expert)
-// start positions; pass 2 re-walks the chunk and writes each assignment at
-// start + rank. All integer, no atomics: bit-for-bit deterministic.
+// rank bases (assignments of the expert in earlier waves) and per-expert
+// offsets; pass 2 re-walks the chunk and writes each assignment at offset +
+// rank. All integer, no atomics: bit-for-bit deterministic.
+//
+// With a per-expert capacity C (the capacity factor of ch15 section 4.3,
+// drop policy) an expert keeps the assignments of rank < C, i.e. its first C
+// in assignment order; the offsets are the prefix sums of min(count, C) and a
+// dropped assignment gets assign_pos = -1, like a non-local one.
 #include <algorithm>
 
 #include "device_common.h"
@@ -84,11 +90,12 @@ __device__ __forceinline__ void wave_count(const int* __restrict__ ids, int lo, 
 }
 
 // Writes one wavefront's assignments [lo, hi) in order: assignment a with
-// local expert e goes to my_base[e] + (earlier assignments of e in this
-// wavefront's range). Non-local assignments get assign_pos = -1.
+// local expert e has rank r = my_base[e] + (earlier assignments of e in this
+// wavefront's range) and goes to ebase[e] + r when r < cap. Non-local and
+// dropped assignments get assign_pos = -1.
 __device__ __forceinline__ void wave_scatter(const int* __restrict__ ids, int lo, int hi, int begin,
-                                             int nloc, int nbits, int* my_base,
-                                             int* __restrict__ sorted_assign,
+                                             int nloc, int nbits, int* my_base, const int* ebase,
+                                             int cap, int* __restrict__ sorted_assign,
                                              int* __restrict__ assign_pos) {
   const int lane = threadIdx.x & 63;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
@@ -101,8 +108,9 @@ __device__ __forceinline__ void wave_scatter(const int* __restrict__ ids, int lo
       const int e = ev[g];
       const uint64_t peers = match_key(e, e >= 0, nbits);
       if (a < hi) {
-        if (e >= 0) {
-          const int p = my_base[e] + __popcll(peers & lt_mask);
+        const int r = e >= 0 ? my_base[e] + __popcll(peers & lt_mask) : cap;
+        if (r < cap) {
+          const int p = ebase[e] + r;
           sorted_assign[p] = a;
           assign_pos[a] = p;
         } else {
@@ -162,11 +170,13 @@ __global__ __launch_bounds__(256) void block_count_kernel(const int* __restrict_
 // wavefronts, then scatters. Block 0 also writes counts and offsets.
 __global__ __launch_bounds__(256) void block_scatter_kernel(
     const int* __restrict__ ids, int n, int per_block, int begin, int nloc, int nbits,
-    const int* __restrict__ ws, int nblocks, int* __restrict__ counts, int* __restrict__ offsets,
-    int* __restrict__ sorted_assign, int* __restrict__ assign_pos) {
+    const int* __restrict__ ws, int nblocks, int cap, int* __restrict__ counts,
+    int* __restrict__ offsets, int* __restrict__ demand, int* __restrict__ sorted_assign,
+    int* __restrict__ assign_pos) {
   extern __shared__ int lds[];
   int* cnt = lds;                          // [kBlkWaves][nloc]
   int* wsum = lds + kBlkWaves * nloc;      // [4]
+  int* ebase = wsum + 4;                   // [nloc] expert offsets
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, b = blockIdx.x;
   for (int i = tid; i < kBlkWaves * nloc; i += blockDim.x) cnt[i] = 0;
   __syncthreads();
@@ -201,7 +211,7 @@ __global__ __launch_bounds__(256) void block_scatter_kernel(
       }
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) sum += tot[q];
+  for (int q = 0; q < 4; ++q) sum += min(tot[q], cap);   // rows kept
   const int incl = wave_inclusive_scan(sum);
   if (lane == 63) wsum[w] = incl;
   __syncthreads();  // also orders the recount above before the reads below
@@ -214,22 +224,26 @@ __global__ __launch_bounds__(256) void block_scatter_kernel(
     const int e = tid * 4 + q;
     if (e < nloc) {
       if (b == 0) {
-        counts[e] = tot[q];
+        counts[e] = min(tot[q], cap);
         offsets[e] = run;
+        if (demand) demand[e] = tot[q];
       }
-      // wave bases: block start + counts of the block's earlier wavefronts
-      int s = run + before[q];
+      ebase[e] = run;
+      // wave rank bases: the expert's assignments in earlier blocks and in
+      // the block's earlier wavefronts
+      int s = before[q];
       for (int ww = 0; ww < kBlkWaves; ++ww) {
         const int c = cnt[ww * nloc + e];
         cnt[ww * nloc + e] = s;
         s += c;
       }
     }
-    run += tot[q];
+    run += min(tot[q], cap);
   }
   if (b == 0 && tid == 0) offsets[nloc] = total;
   __syncthreads();
-  wave_scatter(ids, lo, hi, begin, nloc, nbits, cnt + w * nloc, sorted_assign, assign_pos);
+  wave_scatter(ids, lo, hi, begin, nloc, nbits, cnt + w * nloc, ebase, cap, sorted_assign,
+               assign_pos);
 }
 
 // Single-workgroup sort (n <= kSingleBlockMax): each wavefront's chunk is
@@ -238,13 +252,16 @@ __global__ __launch_bounds__(256) void block_scatter_kernel(
 constexpr int kSortGroups = kSingleBlockMax / kSortWaves / 64;   // 64-id groups per wavefront
 
 __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids, int n, int begin,
-                                                    int nloc, int nbits, int* __restrict__ counts,
+                                                    int nloc, int nbits, int cap,
+                                                    int* __restrict__ counts,
                                                     int* __restrict__ offsets,
+                                                    int* __restrict__ demand,
                                                     int* __restrict__ sorted_assign,
                                                     int* __restrict__ assign_pos) {
   extern __shared__ int lds[];
   int* cnt = lds;                              // [kSortWaves][nloc]
   int* wbase = lds + kSortWaves * nloc;        // [kSortWaves]
+  int* ebase = wbase + kSortWaves;             // [nloc] expert offsets
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   for (int i = threadIdx.x; i < kSortWaves * nloc; i += blockDim.x) cnt[i] = 0;
@@ -275,7 +292,8 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids,
     if (ev[g] >= 0 && (peers[g] & lt_mask) == 0ull) my_cnt[ev[g]] += __popcll(peers[g]);
   __syncthreads();
 
-  // scan: per-expert column prefix over waves, then exclusive scan over experts
+  // scan: per-expert column prefix over waves (the wave rank bases), then an
+  // exclusive scan over experts of the rows kept
   int total = 0;
   for (int e = threadIdx.x; e < nloc; e += blockDim.x) {  // nloc <= blockDim.x: one expert per thread
     for (int ww = 0; ww < kSortWaves; ++ww) {
@@ -284,7 +302,8 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids,
       total += c;
     }
   }
-  const int incl = wave_inclusive_scan(total);
+  const int kept = min(total, cap);
+  const int incl = wave_inclusive_scan(kept);
   if (lane == 63) wbase[w] = incl;
   __syncthreads();
   if (w == 0) {
@@ -295,12 +314,13 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids,
   __syncthreads();
   {
     const int e = threadIdx.x;
-    const int excl = incl - total + wbase[w];
+    const int excl = incl - kept + wbase[w];
     if (e < nloc) {
-      counts[e] = total;
+      counts[e] = kept;
       offsets[e] = excl;
-      for (int ww = 0; ww < kSortWaves; ++ww) cnt[ww * nloc + e] += excl;
-      if (e == nloc - 1) offsets[nloc] = excl + total;
+      ebase[e] = excl;
+      if (demand) demand[e] = total;
+      if (e == nloc - 1) offsets[nloc] = excl + kept;
     }
   }
   __syncthreads();
@@ -312,8 +332,9 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids,
   for (int g = 0; g < kSortGroups; ++g) {
     const int a = lo + g * 64 + lane;
     if (a < hi) {
-      if (ev[g] >= 0) {
-        const int p = my_cnt[ev[g]] + __popcll(peers[g] & lt_mask);
+      const int r = ev[g] >= 0 ? my_cnt[ev[g]] + __popcll(peers[g] & lt_mask) : cap;
+      if (r < cap) {
+        const int p = ebase[ev[g]] + r;
         sorted_assign[p] = a;
         assign_pos[a] = p;
       } else {
@@ -324,9 +345,12 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids,
   }
 }
 
-__global__ void zero_counts_kernel(int nloc, int* counts, int* offsets) {
+__global__ void zero_counts_kernel(int nloc, int* counts, int* offsets, int* demand) {
   for (int e = threadIdx.x; e <= nloc; e += blockDim.x) {
-    if (e < nloc) counts[e] = 0;
+    if (e < nloc) {
+      counts[e] = 0;
+      if (demand) demand[e] = 0;
+    }
     offsets[e] = 0;
   }
 }
@@ -357,25 +381,26 @@ size_t dispatch_workspace_size(int n, int num_local) {
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   if (a.n == 0) {
     hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(256), 0, s, a.num_local, a.counts,
-                       a.offsets);
+                       a.offsets, a.demand);
     return hipGetLastError();
   }
   int nbits = 1;
   while ((1 << nbits) < a.num_local) ++nbits;
   if (a.n <= kSingleBlockMax) {
-    const size_t lds = (size_t)(kSortWaves * a.num_local + kSortWaves) * sizeof(int);
+    const size_t lds = (size_t)((kSortWaves + 1) * a.num_local + kSortWaves) * sizeof(int);
     hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(kSortWaves * 64), lds, s, a.ids, a.n,
-                       a.expert_begin, a.num_local, nbits, a.counts, a.offsets, a.sorted_assign,
-                       a.assign_pos);
+                       a.expert_begin, a.num_local, nbits, a.capacity, a.counts, a.offsets,
+                       a.demand, a.sorted_assign, a.assign_pos);
   } else {
     const int blocks = sort_blocks(a.n), per_block = sort_per_block(a.n);
     const size_t lds = (size_t)(kBlkWaves * a.num_local + 4) * sizeof(int);
     hipLaunchKernelGGL(block_count_kernel, dim3(blocks), dim3(256), lds, s, a.ids, a.n, per_block,
                        a.expert_begin, a.num_local, nbits, (int*)a.workspace);
-    hipLaunchKernelGGL(block_scatter_kernel, dim3(blocks), dim3(256), lds, s, a.ids, a.n,
+    const size_t lds2 = lds + (size_t)a.num_local * sizeof(int);
+    hipLaunchKernelGGL(block_scatter_kernel, dim3(blocks), dim3(256), lds2, s, a.ids, a.n,
                        per_block, a.expert_begin, a.num_local, nbits, (const int*)a.workspace,
-                       blocks,
-                       a.counts, a.offsets, a.sorted_assign, a.assign_pos);
+                       blocks, a.capacity, a.counts, a.offsets, a.demand, a.sorted_assign,
+                       a.assign_pos);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.row_bytes == 0) return err;

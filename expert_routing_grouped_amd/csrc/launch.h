@@ -28,10 +28,12 @@ struct DispatchArgs {
   void* x_sorted;
   int row_bytes;  // hidden * element size; 0 = no gather
   void* workspace;
+  int capacity;   // rows kept per expert (first come, first served); INT32_MAX = no limit
+  int* demand;    // null, or [num_local] out: assignments per expert before the cap
 };
 size_t dispatch_workspace_size(int n, int num_local);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
-constexpr int kDispatchMaxLocal = 1000;  // per-(wave, expert) counters fit in 64 KiB of LDS
+constexpr int kDispatchMaxLocal = 1000;  // per-(wave, expert) counters and offsets fit in 68 KiB of LDS
 
 struct FfnArgs {
   const void* x;         // permuted rows, or token rows read through row_index

@@ -30,6 +30,8 @@ _SIGNATURES = {
     "moe_dispatch_workspace_size": (ctypes.c_size_t, [_I, _I, _I]),
     "moe_dispatch": (ctypes.c_int, [_P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P,
                                     ctypes.c_size_t, _P]),
+    "moe_dispatch_capacity": (ctypes.c_int, [_P, _I, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P,
+                                             _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "moe_expert_ffn": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P,
                                       ctypes.c_size_t, _P]),
@@ -112,8 +114,13 @@ def moe_route(scores, top_k, num_groups=1, topk_groups=1, score_mode=MOE_SCORE_R
     return topk_ids, topk_weights
 
 
-def moe_dispatch(topk_ids, expert_begin, num_local_experts, x=None, out=None, stream=None):
-    """Counting-sort dispatch. Returns dict(counts, offsets, sorted_assign, assign_pos, x_sorted)."""
+def moe_dispatch(topk_ids, expert_begin, num_local_experts, x=None, out=None, stream=None,
+                 capacity=None):
+    """Counting-sort dispatch. Returns dict(counts, offsets, sorted_assign, assign_pos, x_sorted).
+
+    With capacity = C (an int) it calls moe_dispatch_capacity: each expert keeps its first C
+    assignments, counts are clamped and the result also holds demand (assignments per expert
+    before the cap)."""
     _dev(topk_ids, torch.int32, "topk_ids")
     T, k = topk_ids.shape
     dev = topk_ids.device
@@ -138,12 +145,23 @@ def moe_dispatch(topk_ids, expert_begin, num_local_experts, x=None, out=None, st
     ws = o.get("workspace")
     if need and (ws is None or ws.numel() < need):
         ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    _check(lib().moe_dispatch(_ptr(topk_ids), T, k, expert_begin, num_local_experts, _ptr(x),
-                              hidden, dtype, _ptr(o["counts"]), _ptr(o["offsets"]),
-                              _ptr(o["sorted_assign"]), _ptr(o["assign_pos"]),
-                              _ptr(o["x_sorted"]), _ptr(ws if need else None),
-                              ws.numel() if (need and ws is not None) else 0, _stream(stream)),
-           "moe_dispatch")
+    ws_ptr = _ptr(ws if need else None)
+    ws_bytes = ws.numel() if (need and ws is not None) else 0
+    if capacity is None:
+        _check(lib().moe_dispatch(_ptr(topk_ids), T, k, expert_begin, num_local_experts, _ptr(x),
+                                  hidden, dtype, _ptr(o["counts"]), _ptr(o["offsets"]),
+                                  _ptr(o["sorted_assign"]), _ptr(o["assign_pos"]),
+                                  _ptr(o["x_sorted"]), ws_ptr, ws_bytes, _stream(stream)),
+               "moe_dispatch")
+        return o
+    o.setdefault("demand", torch.empty(num_local_experts, dtype=torch.int32, device=dev))
+    _dev(o["demand"], torch.int32, "demand")
+    _check(lib().moe_dispatch_capacity(_ptr(topk_ids), T, k, expert_begin, num_local_experts,
+                                       int(capacity), _ptr(x), hidden, dtype, _ptr(o["counts"]),
+                                       _ptr(o["offsets"]), _ptr(o["demand"]),
+                                       _ptr(o["sorted_assign"]), _ptr(o["assign_pos"]),
+                                       _ptr(o["x_sorted"]), ws_ptr, ws_bytes, _stream(stream)),
+           "moe_dispatch_capacity")
     return o
 
 
@@ -218,13 +236,14 @@ class MoELayer:
 
     def __init__(self, *, num_tokens, num_experts, top_k, num_groups, topk_groups, score_mode,
                  renormalize, expert_begin, num_local_experts, hidden, inter, dtype, device,
-                 fuse_gather=True):
+                 fuse_gather=True, expert_capacity=None):
         self.T, self.E, self.k = num_tokens, num_experts, top_k
         self.num_groups, self.topk_groups = num_groups, topk_groups
         self.score_mode, self.renormalize = score_mode, renormalize
         self.expert_begin, self.num_local = expert_begin, num_local_experts
         self.hidden, self.inter, self.dtype = hidden, inter, dtype
         self.fuse_gather = fuse_gather
+        self.expert_capacity = expert_capacity
         cap = num_tokens * top_k
         self.cap = cap
         dev = torch.device(device)
@@ -260,10 +279,14 @@ class MoELayer:
         out = {n: b[n] for n in ("counts", "offsets", "sorted_assign", "assign_pos")}
         if "dispatch_ws" in b:
             out["workspace"] = b["dispatch_ws"]
+        if self.expert_capacity is not None:
+            out["demand"] = b.setdefault("demand", torch.empty_like(b["counts"]))
         if x is not None and not self.fuse_gather:
             out["x_sorted"] = b["x_sorted"]
-            return moe_dispatch(b["topk_ids"], self.expert_begin, self.num_local, x, out, stream)
-        return moe_dispatch(b["topk_ids"], self.expert_begin, self.num_local, None, out, stream)
+            return moe_dispatch(b["topk_ids"], self.expert_begin, self.num_local, x, out, stream,
+                                self.expert_capacity)
+        return moe_dispatch(b["topk_ids"], self.expert_begin, self.num_local, None, out, stream,
+                            self.expert_capacity)
 
     def ffn(self, w_gate_up, w_down, x=None, stream=None):
         b = self.buf

@@ -4,6 +4,7 @@
  *
  *   moe_route       group-limited top-k routing of each token
  *   moe_dispatch    counting-sort permutation of token rows to local experts
+ *                   (moe_dispatch_capacity: the same with a per-expert capacity)
  *   moe_expert_ffn  grouped SwiGLU expert FFN (fused gate_up GEMM, SiLU*up, down GEMM)
  *   moe_combine     router-weighted sum of the expert outputs, back in token order
  *
@@ -28,7 +29,8 @@
  *   ai-infra-handbooks serving/moe/ep-deploy), section "EPLB 与路由约束":
  *   group-limited routing and its seeded simulation.
  * - "第十五章：多节点大模型推理——并行部署、解码优化与 MoE 路由"
- *   (se7en.mintlify.app ch15), sections 3.4 and 4.1: gating, dispatch, combine.
+ *   (se7en.mintlify.app ch15), sections 3.4 and 4.1: gating, dispatch, combine;
+ *   section 4.3: the capacity factor and the overflow policies.
  * - "追踪一个 Token 在 MoE 推理中穿越 TP/CP/SP/EP/DP/PP 的路径" (attain.fans),
  *   hop 4: y = p5 E5(x) + p27 E27(x).
  * - "Lecture 6 · 并行" (semidirectx.com cs349d lecture06), section 2.2: the
@@ -131,6 +133,31 @@ moe_status_t moe_dispatch(const int32_t* topk_ids, int32_t num_tokens, int32_t t
                           int32_t* expert_counts, int32_t* expert_offsets,
                           int32_t* sorted_assign, int32_t* assign_pos, void* x_sorted,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_dispatch_capacity -- moe_dispatch with a per-expert capacity and the
+ * drop policy, the capacity factor of ch15 section 4.3 ("负载均衡" section,
+ * "Capacity Factor": C = ceil(c * T * k / E), and its table of overflow
+ * policies). expert_capacity = C, computed by the caller (>= 0).
+ *
+ * Each local expert keeps its first C assignments in assignment order
+ * a = t * k + j; the others are dropped: not in sorted_assign, assign_pos = -1
+ * (so moe_combine leaves them out, as it does non-local ones).
+ * expert_counts   [E_loc] out: rows kept, min(assignments, C).
+ * expert_offsets  [E_loc + 1] out: exclusive prefix sum of expert_counts.
+ * expert_demand   [E_loc] int32 out, or NULL: assignments per local expert
+ *                 before the cap (demand - counts were dropped).
+ * Every other argument, the workspace and the limits are those of
+ * moe_dispatch; with C >= T * k the result equals moe_dispatch's.
+ * Errors: as moe_dispatch; MOE_ERR_INVALID also for expert_capacity < 0.
+ */
+moe_status_t moe_dispatch_capacity(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
+                                   int32_t expert_begin, int32_t num_local_experts,
+                                   int32_t expert_capacity, const void* x, int32_t hidden,
+                                   int32_t dtype, int32_t* expert_counts, int32_t* expert_offsets,
+                                   int32_t* expert_demand, int32_t* sorted_assign,
+                                   int32_t* assign_pos, void* x_sorted, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Bytes of device workspace moe_expert_ffn needs for these sizes; 0 when the

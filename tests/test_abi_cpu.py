@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = moe.lib()
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
     assert moe.status_string(0) == "ok"
     assert moe.status_string(1) == "invalid argument"
     assert moe.status_string(3).startswith("workspace")
@@ -77,6 +77,18 @@ def test_dispatch_validation():
     assert l.moe_dispatch_workspace_size(8192, 8, 32) == 32 * 32 * 4
     assert l.moe_dispatch(p, 8192, 8, 0, 32, None, 0, 1, p, p, p, p, None, None, 0, None) == 3
     assert l.moe_dispatch(p, 8192, 8, 0, 32, None, 0, 1, p, p, p, p, None, p, 100, None) == 3
+
+
+def test_dispatch_capacity_validation():
+    l = moe.lib()
+    p = ctypes.c_void_p(16)
+    W = (None, 0, None)
+    # (ids, T, k, begin, nloc, capacity, x, hidden, dtype, counts, offsets, demand, sorted, pos, x_sorted, ws...)
+    assert l.moe_dispatch_capacity(p, 4, 8, 0, 8, -1, None, 0, 1, p, p, None, p, p, None, *W) == 1
+    assert l.moe_dispatch_capacity(p, 4, 0, 0, 8, 10, None, 0, 1, p, p, None, p, p, None, *W) == 1
+    assert l.moe_dispatch_capacity(p, 4, 8, 0, 2000, 10, None, 0, 1, p, p, None, p, p, None, *W) == 2
+    assert l.moe_dispatch_capacity(None, 4, 8, 0, 8, 10, None, 0, 1, p, p, None, p, p, None, *W) == 1
+    assert l.moe_dispatch_capacity(p, 8192, 8, 0, 32, 10, None, 0, 1, p, p, p, p, p, None, *W) == 3
 
 
 def test_ffn_validation_and_workspace():

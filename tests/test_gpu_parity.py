@@ -349,3 +349,79 @@ def test_layer_prefill_routing_every_row():
     o and y is checked against the oracle."""
     wl = W.WORKLOADS["prefill_straggler"].replace(name="prefill_straggler_d2048", hidden=2048)
     check_full(wl, W.generate(wl), TOL_BF16)
+
+
+# ------------------------------------------------------------------ capacity-limited dispatch
+
+def check_dispatch_capacity(ids, begin, nloc, cap, x=None):
+    k = ids.shape[1]
+    print(f"dispatch_capacity T={ids.shape[0]} k={k} local=[{begin},{begin + nloc}) C={cap}", flush=True)
+    d_ids = to_device(np.ascontiguousarray(ids, dtype=np.int32), DEV)
+    d_x = to_device(x, DEV) if x is not None else None
+    out = moe.moe_dispatch(d_ids, begin, nloc, d_x, capacity=cap)
+    torch.cuda.synchronize()
+    counts, offsets, sa, pos, demand = oracle.dispatch_capacity(ids, begin, nloc, cap)
+    M = int(offsets[-1])
+    assert np.array_equal(to_host(out["counts"]), counts)
+    assert np.array_equal(to_host(out["offsets"]), offsets)
+    assert np.array_equal(to_host(out["demand"]), demand)
+    assert np.array_equal(to_host(out["sorted_assign"])[:M], sa)
+    assert np.array_equal(to_host(out["assign_pos"])[:ids.size], pos)
+    if x is not None:
+        assert np.array_equal(to_host(out["x_sorted"])[:M], oracle.gather_rows(x, sa, k))
+    return out
+
+
+def test_dispatch_capacity_workload():
+    """The capacity-factor example of ch15 section 4.3 (T = 5600, k = 16 of E = 896, C = 120):
+    routing then the capped dispatch, bit-exact against the oracle."""
+    wl = W.WORKLOADS["capacity_route"]
+    scores = inputs("capacity_route", with_ffn=False).scores
+    ids, _ = oracle.route(scores, wl.top_k, 1, 1, "raw", True)
+    d_ids, _ = moe.moe_route(to_device(scores, DEV), wl.top_k, 1, 1, moe.MOE_SCORE_RAW, True)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(d_ids), ids)
+    cap = oracle.expert_capacity(wl.T, wl.top_k, wl.E, wl.capacity_factor)
+    out = check_dispatch_capacity(ids, 0, wl.E, cap)
+    assert (to_host(out["demand"]) > cap).any()
+
+
+@pytest.mark.parametrize("T,k,E,begin,nloc,cap", [
+    (40, 4, 16, 0, 16, 3),           # single-workgroup sort
+    (500, 8, 64, 5, 40, 50),
+    (300, 6, 20, 0, 20, 0),          # everything dropped
+    (300, 6, 20, 0, 20, 10 ** 6),    # nothing dropped: equals moe_dispatch
+    (3000, 8, 300, 0, 300, 70),      # multi-workgroup sort
+    (70001, 8, 256, 5, 200, 2000),   # beyond 256 blocks
+    (9000, 2, 4, 1, 2, 1)])
+def test_dispatch_capacity_ragged(T, k, E, begin, nloc, cap):
+    rng = np.random.default_rng(T + cap)
+    # skewed expert choice, so that caps bite
+    p = rng.random(E) ** 4
+    p /= p.sum()
+    ids = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    x = rng.standard_normal((T, 32)).astype(np.float32) if T <= 3000 else None
+    check_dispatch_capacity(ids, begin, nloc, cap, x)
+    if cap >= T * k:
+        check_dispatch(ids, begin, nloc)
+
+
+def test_layer_with_capacity_drops_contributions():
+    """Capped dispatch feeding the FFN and combine: dropped slots contribute nothing."""
+    wl = small_bf16_workload(400, 16, 4, 4, 2, 512, 128, 0, 16, seed=11)
+    inp = W.generate(wl)
+    ids, w = oracle.route(inp.scores, wl.top_k, wl.num_groups, wl.topk_groups, "raw", True)
+    cap = 40
+    layer = moe.MoELayer(num_tokens=wl.T, num_experts=wl.E, top_k=wl.top_k, num_groups=wl.num_groups,
+                         topk_groups=wl.topk_groups, score_mode=moe.MOE_SCORE_RAW, renormalize=True,
+                         expert_begin=0, num_local_experts=wl.num_local, hidden=wl.hidden,
+                         inter=wl.inter, dtype=torch.bfloat16, device=DEV, expert_capacity=cap)
+    y = layer.forward(to_device(inp.scores, DEV), to_device(inp.x, DEV), to_device(inp.w_gate_up, DEV),
+                      to_device(inp.w_down, DEV))
+    torch.cuda.synchronize()
+    counts, offsets, sa, pos, demand = oracle.dispatch_capacity(ids, 0, wl.num_local, cap)
+    assert (demand > cap).any()
+    assert np.array_equal(to_host(layer.buf["assign_pos"])[:ids.size], pos)
+    o_ref = oracle.expert_ffn(oracle.gather_rows(inp.x, sa, wl.top_k), offsets, inp.w_gate_up, inp.w_down)
+    y_ref = oracle.combine(o_ref, pos, w)
+    assert rel_err(as_f64(to_host(y)), y_ref) <= TOL_BF16
