@@ -118,11 +118,16 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
     gen_s = time.time() - t0
     dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
     mode = moe.MOE_SCORE_SOFTMAX if wl.score_mode == "softmax" else moe.MOE_SCORE_RAW
+    cap = None
+    if wl.capacity_factor is not None:   # C = ceil(c T k / E), c an exact decimal
+        from fractions import Fraction
+        import math
+        cap = math.ceil(Fraction(wl.capacity_factor) * wl.T * wl.top_k / wl.E)
     layer = moe.MoELayer(num_tokens=wl.T, num_experts=wl.E, top_k=wl.top_k,
                          num_groups=wl.num_groups, topk_groups=wl.topk_groups, score_mode=mode,
                          renormalize=wl.renormalize, expert_begin=wl.expert_begin,
                          num_local_experts=wl.num_local, hidden=wl.hidden, inter=wl.inter,
-                         dtype=dt, device=dev)
+                         dtype=dt, device=dev, expert_capacity=cap)
     scores = to_device(inp.scores, dev)
     x = to_device(inp.x, dev) if wl.has_ffn else None
     weights = []
@@ -211,6 +216,10 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
         M = int(counts.sum())
         route_bytes = wl.T * wl.E * 4 + wl.T * wl.top_k * 8
         res.update(M=M, route_gbs=route_bytes / (parts_us[0] * 1e-6) / 1e9)
+        if cap is not None:
+            demand = to_host(layer.buf["demand"])
+            res.update(capacity=cap, assignments=int(demand.sum()), dropped=int(demand.sum()) - M,
+                       experts_over_capacity=int((demand > cap).sum()))
     res["_inputs"] = inp
     return res
 
