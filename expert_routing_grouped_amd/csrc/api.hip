@@ -5,11 +5,13 @@
 
 #include <stdint.h>
 
+#include <cmath>
+
 #include "launch.h"
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -179,6 +181,44 @@ moe_status_t moe_combine(const void* o_sorted, const int32_t* assign_pos,
   moe::CombineArgs a{o_sorted, assign_pos, topk_weights, num_tokens, top_k, hidden,
                      dtype == MOE_BF16, out_dtype == MOE_BF16, y};
   return from_hip(moe::launch_combine(a, stream));
+}
+
+moe_status_t moe_eplb_place(const double* load, int32_t num_experts, int32_t num_groups,
+                            int32_t num_nodes, int32_t num_gpus, int32_t num_physical,
+                            int32_t hierarchical, int32_t* phys_to_logical,
+                            int32_t* replica_offsets, int32_t* replica_slots) {
+  if (num_experts < 1 || num_groups < 1 || num_nodes < 1 || num_gpus < 1) return MOE_ERR_INVALID;
+  if (num_experts % num_groups != 0 || num_gpus % num_nodes != 0) return MOE_ERR_INVALID;
+  if (num_physical < num_experts || num_physical % num_gpus != 0) return MOE_ERR_INVALID;
+  if (num_nodes > 64) return MOE_ERR_UNSUPPORTED;
+  if (hierarchical) {   // whole groups per node, whole per-node slot and GPU counts
+    if (num_groups % num_nodes != 0 || num_physical % num_nodes != 0) return MOE_ERR_INVALID;
+    if ((num_physical / num_nodes) % (num_gpus / num_nodes) != 0) return MOE_ERR_INVALID;
+  }
+  if ((int64_t)num_physical >= ((int64_t)1 << 30)) return MOE_ERR_UNSUPPORTED;
+  if (!load || !phys_to_logical || !replica_offsets || !replica_slots) return MOE_ERR_INVALID;
+  for (int32_t e = 0; e < num_experts; ++e)
+    if (!std::isfinite(load[e]) || load[e] < 0.0) return MOE_ERR_INVALID;
+  const int n = moe::eplb_place(load, num_experts, num_groups, num_nodes, num_gpus, num_physical,
+                                hierarchical != 0, phys_to_logical, replica_offsets, replica_slots);
+  return n == num_physical ? MOE_OK : MOE_ERR_INVALID;
+}
+
+moe_status_t moe_eplb_remap(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
+                            const int32_t* replica_offsets, const int32_t* replica_slots,
+                            int32_t num_experts, int32_t num_physical, int32_t num_gpus,
+                            int32_t num_nodes, int32_t* physical_ids, hipStream_t stream) {
+  if (num_tokens < 0 || top_k < 1 || num_experts < 1 || num_gpus < 1 || num_nodes < 1)
+    return MOE_ERR_INVALID;
+  if (num_physical < num_experts || num_physical % num_gpus != 0 || num_gpus % num_nodes != 0)
+    return MOE_ERR_INVALID;
+  if (num_nodes > 64) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)num_tokens * top_k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MOE_OK;
+  if (!topk_ids || !replica_offsets || !replica_slots || !physical_ids) return MOE_ERR_INVALID;
+  return from_hip(moe::launch_eplb_remap(topk_ids, num_tokens, top_k, replica_offsets, replica_slots,
+                                         num_physical / num_gpus, num_gpus / num_nodes,
+                                         physical_ids, stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,144 @@
+// EPLB: placement of logical experts (with redundant replicas) on GPUs, and
+// the choice of a physical replica for every routed (token, slot).
+//
+// From the page "大规模 EP 部署：分层 EPLB、DP 注意力的负载与双 batch 重叠"
+// (anrans.github.io), section "EPLB 与路由约束". Hierarchical strategy: pack
+// the expert groups onto the nodes, balanced by load with the same number of
+// groups per node; inside each node give the hottest experts extra replicas;
+// pack each node's physical experts onto its GPUs, balanced, the same number
+// per GPU. Global strategy: the same over all experts and GPUs at once.
+// Balanced packing takes items heaviest first (equal weights: lower index
+// first) into the lightest pack that still has room (equal totals: lower
+// pack); replication repeatedly adds a replica to the expert with the highest
+// load per replica (equal: the expert listed first). Sums are float64 in
+// placement order.
+//
+// The replica choice follows the page's simulation: a token slot uses a
+// replica on a node the token already goes to when there is one (the lowest
+// such slot), else the lowest slot on the lowest-numbered node holding one.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <vector>
+
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+std::vector<std::vector<int>> balanced_pack(const std::vector<double>& w, int n_packs) {
+  const int n = (int)w.size();
+  const int room = n / n_packs;
+  std::vector<int> order(n);
+  for (int i = 0; i < n; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return w[a] > w[b]; });
+  std::vector<std::vector<int>> packs(n_packs);
+  std::vector<double> total(n_packs, 0.0);
+  for (int item : order) {
+    int target = -1;
+    for (int p = 0; p < n_packs; ++p)
+      if ((int)packs[p].size() < room && (target < 0 || total[p] < total[target])) target = p;
+    packs[target].push_back(item);
+    total[target] += w[item];
+  }
+  return packs;
+}
+
+}  // namespace
+
+int eplb_place(const double* load, int E, int num_groups, int num_nodes, int num_gpus, int num_physical,
+               bool hierarchical, int* phys_to_logical, int* replica_offsets, int* replica_slots) {
+  const int G = E / num_groups;
+  std::vector<std::vector<int>> node_experts;
+  if (hierarchical) {
+    std::vector<double> group_load(num_groups, 0.0);
+    for (int g = 0; g < num_groups; ++g)
+      for (int e = g * G; e < (g + 1) * G; ++e) group_load[g] += load[e];
+    for (const auto& groups : balanced_pack(group_load, num_nodes)) {
+      std::vector<int> experts;
+      for (int g : groups)
+        for (int e = g * G; e < (g + 1) * G; ++e) experts.push_back(e);
+      node_experts.push_back(experts);
+    }
+  } else {
+    std::vector<int> all(E);
+    for (int e = 0; e < E; ++e) all[e] = e;
+    node_experts.push_back(all);
+  }
+  std::vector<int> count(E, 0);
+  int slot = 0;
+  for (const auto& experts : node_experts) {
+    const int n = (int)experts.size();
+    const int n_phys = (int)((long)num_physical * n / E);
+    const int n_gpus = (int)((long)num_gpus * n / E);
+    for (int e : experts) count[e] = 1;
+    for (int r = n; r < n_phys; ++r) {
+      int best = experts[0];
+      for (int i = 1; i < n; ++i) {
+        const int e = experts[i];
+        if (load[e] / count[e] > load[best] / count[best]) best = e;
+      }
+      ++count[best];
+    }
+    std::vector<int> physical;
+    std::vector<double> weight;
+    for (int e : experts)
+      for (int c = 0; c < count[e]; ++c) {
+        physical.push_back(e);
+        weight.push_back(load[e] / count[e]);
+      }
+    for (const auto& pack : balanced_pack(weight, n_gpus))
+      for (int i : pack) phys_to_logical[slot++] = physical[i];
+  }
+  // replica table: slots of each expert in ascending order (a counting sort)
+  for (int e = 0; e <= E; ++e) replica_offsets[e] = 0;
+  for (int s = 0; s < num_physical; ++s) ++replica_offsets[phys_to_logical[s] + 1];
+  for (int e = 0; e < E; ++e) replica_offsets[e + 1] += replica_offsets[e];
+  std::vector<int> fill(replica_offsets, replica_offsets + E);
+  for (int s = 0; s < num_physical; ++s) replica_slots[fill[phys_to_logical[s]]++] = s;
+  return slot;
+}
+
+namespace {
+
+// One thread per token; its nodes so far in a 64-bit mask.
+__global__ __launch_bounds__(256) void remap_kernel(const int* __restrict__ ids, int T, int k,
+                                                    const int* __restrict__ offsets,
+                                                    const int* __restrict__ slots, int slots_per_gpu,
+                                                    int gpus_per_node, int* __restrict__ phys) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  uint64_t used = 0;
+  const int per_node = slots_per_gpu * gpus_per_node;
+  for (int j = 0; j < k; ++j) {
+    const int e = ids[(size_t)t * k + j];
+    const int r0 = offsets[e], r1 = offsets[e + 1];
+    int on_used = -1, lowest = -1, lowest_node = 1 << 30;
+    for (int r = r0; r < r1; ++r) {   // ascending slots
+      const int s = slots[r];
+      const int node = s / per_node;
+      if (on_used < 0 && ((used >> node) & 1ull)) on_used = s;
+      if (node < lowest_node) { lowest_node = node; lowest = s; }
+    }
+    if (on_used >= 0) {
+      phys[(size_t)t * k + j] = on_used;
+    } else {
+      phys[(size_t)t * k + j] = lowest;
+      used |= 1ull << lowest_node;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_eplb_remap(const int* ids, int T, int k, const int* offsets, const int* slots,
+                             int slots_per_gpu, int gpus_per_node, int* phys, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(remap_kernel, dim3((T + 255) / 256), dim3(256), 0, s, ids, T, k, offsets, slots,
+                     slots_per_gpu, gpus_per_node, phys);
+  return hipGetLastError();
+}
+
+}  // namespace moe

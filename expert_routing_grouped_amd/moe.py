@@ -36,6 +36,8 @@ _SIGNATURES = {
     "moe_expert_ffn": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P,
                                       ctypes.c_size_t, _P]),
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+    "moe_eplb_place": (ctypes.c_int, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_eplb_remap": (ctypes.c_int, [_P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P]),
 }
 
 _lib = None
@@ -225,6 +227,41 @@ def moe_combine(o_sorted, assign_pos, topk_weights, out_dtype=None, y=None, stre
                              _code(o_sorted.dtype), _code(out_dtype), _ptr(y), _stream(stream)),
            "moe_combine")
     return y
+
+
+def moe_eplb_place(load, num_groups, num_nodes, num_gpus, num_physical, hierarchical):
+    """EPLB placement on the host (see moe_eplb_place in include/moe.h).
+
+    load: per-expert loads (any array-like, converted to float64 on the host).
+    Returns numpy int32 arrays (phys_to_logical [P], replica_offsets [E + 1], replica_slots [P]).
+    """
+    import numpy as np
+    ld = np.ascontiguousarray(np.asarray(load, dtype=np.float64))
+    E = ld.shape[0]
+    p2l = np.empty(num_physical, dtype=np.int32)
+    offs = np.empty(E + 1, dtype=np.int32)
+    slots = np.empty(num_physical, dtype=np.int32)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    _check(lib().moe_eplb_place(ptr(ld), E, num_groups, num_nodes, num_gpus, num_physical,
+                                int(bool(hierarchical)), ptr(p2l), ptr(offs), ptr(slots)),
+           "moe_eplb_place")
+    return p2l, offs, slots
+
+
+def moe_eplb_remap(topk_ids, replica_offsets, replica_slots, num_gpus, num_nodes, physical_ids=None,
+                   stream=None):
+    """Physical slot per routed (token, slot); the replica table given as device tensors."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    _dev(replica_offsets, torch.int32, "replica_offsets")
+    _dev(replica_slots, torch.int32, "replica_slots")
+    T, k = topk_ids.shape
+    if physical_ids is None:
+        physical_ids = torch.empty_like(topk_ids)
+    _dev(physical_ids, torch.int32, "physical_ids")
+    _check(lib().moe_eplb_remap(_ptr(topk_ids), T, k, _ptr(replica_offsets), _ptr(replica_slots),
+                                replica_offsets.numel() - 1, replica_slots.numel(), num_gpus,
+                                num_nodes, _ptr(physical_ids), _stream(stream)), "moe_eplb_remap")
+    return physical_ids
 
 
 class MoELayer:

@@ -8,9 +8,13 @@
  *   moe_expert_ffn  grouped SwiGLU expert FFN (fused gate_up GEMM, SiLU*up, down GEMM)
  *   moe_combine     router-weighted sum of the expert outputs, back in token order
  *
+ * and, for placement across GPUs, moe_eplb_place (host planner) and
+ * moe_eplb_remap (logical to physical replica per routed slot).
+ *
  * Conventions shared by every call
  * --------------------------------
- * - Every array argument is a DEVICE pointer owned by the caller; the library
+ * - Every array argument is a DEVICE pointer owned by the caller (except
+ *   those of moe_eplb_place, which are host pointers); the library
  *   keeps no pointer after a call returns and allocates no memory.
  * - Calls are asynchronous on `stream` (0 = the default stream). They do not
  *   synchronise with the host, so a sequence of calls can be captured in a
@@ -27,7 +31,7 @@
  * Sources (web pages; sections as printed on them):
  * - "大规模 EP 部署：分层 EPLB、DP 注意力的负载与双 batch 重叠" (anrans.github.io,
  *   ai-infra-handbooks serving/moe/ep-deploy), section "EPLB 与路由约束":
- *   group-limited routing and its seeded simulation.
+ *   group-limited routing, its seeded simulation, and the EPLB strategies.
  * - "第十五章：多节点大模型推理——并行部署、解码优化与 MoE 路由"
  *   (se7en.mintlify.app ch15), sections 3.4 and 4.1: gating, dispatch, combine;
  *   section 4.3: the capacity factor and the overflow policies.
@@ -68,6 +72,61 @@ typedef enum {
 
 /* Version of this ABI (incremented on any incompatible change). */
 int32_t moe_abi_version(void);
+
+/*
+ * moe_eplb_place -- EPLB placement, on the HOST (page "大规模 EP 部署：分层 EPLB、
+ * DP 注意力的负载与双 batch 重叠", section "EPLB 与路由约束"): logical experts,
+ * with redundant replicas, onto num_gpus GPUs in num_nodes nodes.
+ *   hierarchical != 0: the expert groups (contiguous, num_experts / num_groups
+ *   each) are packed onto the nodes, balanced by load, the same number of
+ *   groups per node; each node's hottest experts get extra replicas up to its
+ *   share of num_physical; each node's physical experts are packed onto its
+ *   GPUs, balanced, the same number per GPU.
+ *   hierarchical == 0: the same over all experts and GPUs at once.
+ * Balanced packing: items heaviest first (equal: lower index first), each into
+ * the lightest pack with room (equal totals: lower pack). Replication: a
+ * replica at a time to the expert with the highest load per replica (equal:
+ * lower expert, in the node's expert order). float64 sums in placement order.
+ *
+ * load             [num_experts] float64, HOST: per-expert load (e.g. assignment
+ *                  counts of a routed batch); finite and >= 0.
+ * phys_to_logical  [num_physical] int32 HOST out: logical expert of each
+ *                  physical slot; slot s sits on GPU s / (num_physical / num_gpus),
+ *                  GPU g on node g / (num_gpus / num_nodes).
+ * replica_offsets  [num_experts + 1] int32 HOST out, replica_slots
+ *                  [num_physical] int32 HOST out: the slots holding expert e are
+ *                  replica_slots[replica_offsets[e] .. replica_offsets[e + 1]),
+ *                  ascending (the table moe_eplb_remap reads, once copied to the GPU).
+ * Limits: num_experts % num_groups == 0; num_physical >= num_experts and a
+ * multiple of num_gpus; num_gpus % num_nodes == 0; num_nodes <= 64;
+ * hierarchical also needs num_groups and num_physical to be multiples of
+ * num_nodes and the slots per node a multiple of the GPUs per node.
+ * Synchronous; touches no device memory.
+ */
+moe_status_t moe_eplb_place(const double* load, int32_t num_experts, int32_t num_groups,
+                            int32_t num_nodes, int32_t num_gpus, int32_t num_physical,
+                            int32_t hierarchical, int32_t* phys_to_logical,
+                            int32_t* replica_offsets, int32_t* replica_slots);
+
+/*
+ * moe_eplb_remap -- logical to physical expert per routed (token, slot), on
+ * the GPU: the replica choice of the EPLB page's simulation. Per token, slots
+ * in order: among the slots holding the expert that sit on a node the token
+ * already goes to, the lowest; if none, the lowest slot on the lowest-numbered
+ * node holding the expert, and that node is added to the token's nodes.
+ *
+ * topk_ids         [T, k] int32 (logical experts, from moe_route).
+ * replica_offsets  [num_experts + 1], replica_slots [num_physical] int32: the
+ *                  table moe_eplb_place writes, in device memory.
+ * physical_ids     [T, k] int32 out: physical slots (GPU s / (num_physical /
+ *                  num_gpus)).
+ * Limits: as moe_eplb_place; every expert in topk_ids has at least one slot
+ * (not checked on the device). T = 0 is a valid no-op.
+ */
+moe_status_t moe_eplb_remap(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
+                            const int32_t* replica_offsets, const int32_t* replica_slots,
+                            int32_t num_experts, int32_t num_physical, int32_t num_gpus,
+                            int32_t num_nodes, int32_t* physical_ids, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status; host only, never NULL. */
 const char* moe_status_string(moe_status_t status);

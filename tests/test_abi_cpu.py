@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = moe.lib()
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
     assert moe.status_string(0) == "ok"
     assert moe.status_string(1) == "invalid argument"
     assert moe.status_string(3).startswith("workspace")

@@ -425,3 +425,26 @@ def test_layer_with_capacity_drops_contributions():
     o_ref = oracle.expert_ffn(oracle.gather_rows(inp.x, sa, wl.top_k), offsets, inp.w_gate_up, inp.w_down)
     y_ref = oracle.combine(o_ref, pos, w)
     assert rel_err(as_f64(to_host(y)), y_ref) <= TOL_BF16
+
+
+# ------------------------------------------------------------------ EPLB replica choice
+
+@pytest.mark.parametrize("nodes,gpus,phys,hier", [(4, 32, 288, False), (4, 32, 288, True),
+                                                  (8, 64, 320, False), (8, 64, 320, True),
+                                                  (1, 8, 256, False)])
+def test_eplb_remap_matches_oracle(nodes, gpus, phys, hier):
+    """Placement of the EPLB page's simulation (native planner), then the GPU replica choice for
+    all 20000 routed tokens against the oracle; the first 2000 tokens reproduce the page's
+    printed nodes-per-token figure."""
+    from oracle import eplb
+    scores = W.page_simulation_scores()
+    ids, _ = oracle.route_grouped(scores, 8, 8, 4)
+    load = np.bincount(ids.ravel(), minlength=256).astype(float)
+    p2l, offs, slots = moe.moe_eplb_place(load, 8, nodes, gpus, phys, hier)
+    print(f"eplb remap nodes={nodes} gpus={gpus} phys={phys} hier={hier}", flush=True)
+    got = moe.moe_eplb_remap(to_device(ids, DEV), to_device(offs, DEV), to_device(slots, DEV), gpus, nodes)
+    torch.cuda.synchronize()
+    gpus_list = [p2l[g * (phys // gpus):(g + 1) * (phys // gpus)].tolist() for g in range(gpus)]
+    ref = eplb.remap(ids, gpus_list, nodes)
+    assert np.array_equal(to_host(got), ref)
+    assert np.array_equal(p2l[to_host(got)], ids)

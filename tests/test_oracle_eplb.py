@@ -97,3 +97,61 @@ def test_remap_picks_replicas_of_the_right_expert(page_sim):
     flat = np.array([e for g in gpus for e in g])
     phys = eplb.remap(ids[:500], gpus, 8)
     assert np.array_equal(flat[phys], ids[:500])
+
+
+# ---- the library's native planner (host code: runs without a GPU) against the oracle
+
+def _native():
+    from expert_routing_grouped_amd import moe
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.skip("library not built")
+    return moe
+
+
+def _check_native(moe, load, groups, nodes, gpus, phys, hier):
+    p2l, offs, slots = moe.moe_eplb_place(load, groups, nodes, gpus, phys, hier)
+    ref = np.array([e for g in eplb.place(load, groups, nodes, gpus, phys, hier) for e in g])
+    assert np.array_equal(p2l, ref)
+    E = len(load)
+    for e in range(E):   # the replica table lists exactly the slots holding e, ascending
+        assert np.array_equal(slots[offs[e]:offs[e + 1]], np.nonzero(ref == e)[0])
+    assert offs[-1] == phys
+
+
+def test_native_planner_matches_oracle_on_the_page_cases(page_sim):
+    moe = _native()
+    g, _, load = page_sim
+    for c in g["cases"]:
+        _check_native(moe, load, g["inputs"]["num_groups"], c["nodes"], c["gpus"], c["physical"],
+                      c["strategy"] == "hierarchical")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_native_planner_matches_oracle_on_random_loads(seed):
+    moe = _native()
+    rng = np.random.default_rng(seed)
+    E, groups = [(64, 8), (96, 12), (256, 8)][seed % 3]
+    # integer loads (many ties) or float loads, some zero
+    load = rng.integers(0, 6, E).astype(float) if seed % 2 else rng.random(E) ** 3
+    load[rng.integers(0, E, 4)] = 0.0
+    for nodes, gpus, extra, hier in [(2, 8, 8, True), (4, 16, 16, True), (1, 4, 4, False),
+                                     (4, 8, 8, False)]:
+        if groups % nodes:
+            continue
+        _check_native(moe, load, groups, nodes, gpus, E + extra, hier)
+
+
+def test_native_planner_validation():
+    moe = _native()
+    l = moe.lib()
+    p = np.zeros(16, dtype=np.int32).ctypes.data_as(__import__("ctypes").c_void_p)
+    load = np.ones(16).ctypes.data_as(__import__("ctypes").c_void_p)
+    assert l.moe_eplb_place(load, 16, 4, 2, 4, 15, 1, p, p, p) == 1     # fewer slots than experts
+    assert l.moe_eplb_place(load, 16, 3, 1, 4, 16, 0, p, p, p) == 1     # 3 does not divide 16
+    assert l.moe_eplb_place(load, 16, 4, 3, 3, 18, 1, p, p, p) == 1     # 4 groups on 3 nodes
+    assert l.moe_eplb_place(load, 16, 4, 2, 4, 18, 0, p, p, p) == 1     # 18 slots on 4 GPUs
+    assert l.moe_eplb_place(None, 16, 4, 2, 4, 16, 1, p, p, p) == 1
+    bad = np.ones(16)
+    bad[3] = np.nan
+    assert l.moe_eplb_place(bad.ctypes.data_as(__import__("ctypes").c_void_p), 16, 4, 2, 4, 16, 1,
+                            p, p, p) == 1
