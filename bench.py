@@ -224,6 +224,38 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
     return res
 
 
+def run_eplb(torch, moe, to_device, to_host):
+    """EPLB on the routed table of the EPLB page's simulation (20000 tokens, 256 experts in 8
+    groups): the host planner for its two cluster shapes and strategies, and the GPU replica
+    choice for all 20000 x 8 routed slots."""
+    scores = torch.from_numpy(W.page_simulation_scores()).to("cuda:0")
+    ids, _ = moe.moe_route(scores, 8, 8, 4)
+    torch.cuda.synchronize()
+    ids_h = to_host(ids)
+    load = np.bincount(ids_h.ravel(), minlength=256).astype(float)
+    out = {}
+    stream = torch.cuda.current_stream()
+    for nodes, gpus, phys in ((4, 32, 288), (8, 64, 320)):
+        for hier in (False, True):
+            t0 = time.perf_counter()
+            p2l, offs, slots = moe.moe_eplb_place(load, 8, nodes, gpus, phys, hier)
+            plan_us = (time.perf_counter() - t0) * 1e6
+            d_offs, d_slots = to_device(offs, "cuda:0"), to_device(slots, "cuda:0")
+            phys_ids = moe.moe_eplb_remap(ids, d_offs, d_slots, gpus, nodes)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                moe.moe_eplb_remap(ids, d_offs, d_slots, gpus, nodes, phys_ids)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per = phys // gpus
+            gpu_load = np.bincount(to_host(phys_ids).ravel() // per, minlength=gpus)
+            out[f"{nodes}n_{gpus}g_{'hier' if hier else 'global'}"] = dict(
+                plan_us=plan_us, remap_us=e0.elapsed_time(e1) / 20 * 1e3,
+                busiest_gpu_over_mean_after_remap=float(gpu_load.max() / gpu_load.mean()))
+    return out
+
+
 def cpu_baseline(inp, wl, min_seconds=10.0):
     """The oracle as it stands, on the host cores: whole layer passes over the
     workload, repeated until about min_seconds of CPU work."""
@@ -310,6 +342,8 @@ def main():
             r.pop("_inputs")
             others[name] = r
             torch.cuda.empty_cache()
+        print("bench: eplb", file=sys.stderr, flush=True)
+        others["eplb"] = run_eplb(torch, moe, to_device, to_host)
         out["workloads"] = others
     print(json.dumps(out, default=float))
 
