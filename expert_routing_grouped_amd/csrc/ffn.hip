@@ -15,12 +15,13 @@
 //
 // Each GEMM is one persistent kernel that reads expert_offsets on the device
 // (the row counts never return to the host) and builds its work lists in LDS:
-// * streaming path -- experts with at most 256 rows (decode), in 64-row
-//   chunks. Bound by the weight read: weight bytes go from HBM straight into
-//   MFMA registers, with the next two K steps' loads in flight during the
-//   current MFMAs.
-// * tiled path -- experts with more rows (prefill): 128 x 128 tiles staged
-//   through LDS on 32x32x16 bf16 MFMA.
+// * streaming path -- experts with at most 64 rows (decode), one row chunk
+//   each. Bound by the weight read: coalesced weight loads pass through a
+//   wavefront-private LDS tile into MFMA registers, with the next two K
+//   steps' loads in flight during the current MFMAs.
+// * tiled path -- experts with more rows: 128 x 128 tiles staged through LDS
+//   on 32x32x16 bf16 MFMA, or, when the experts above 256 rows fill the GPU
+//   with them (prefill), 256 x 256 tiles in ffn_big_kernel.
 // Experts with no rows appear in neither list, so their weights are not read.
 #include <hip/hip_runtime.h>
 
@@ -35,7 +36,7 @@ namespace {
 
 constexpr int kStreamMT = 4;                  // row tiles of 16 per streamed row chunk
 constexpr int kChunkRows = kStreamMT * 16;    // rows per streamed chunk
-constexpr int kStreamRows = 4 * kChunkRows;   // experts with more rows are tiled
+constexpr int kStreamRows = 4 * kChunkRows;   // experts with more rows decide the large-tile path
 constexpr int kTileBM = 128;                  // tokens per tile in the tiled path
 constexpr int kBigBM = 256;                   // tokens per tile in the large-tile path
 constexpr int kStreamDW = 3;                  // weight register sets of the streaming path
@@ -957,8 +958,8 @@ __global__ __launch_bounds__(256, 1) void ffn_walk_kernel(GemmArgs a) {
 
 // ---------------------------------------------------------------- tiled path
 
-// Experts with more than kStreamRows rows (prefill): 128 weight rows x 128
-// tokens per tile, K staged through LDS 64 at a time (double-buffered through
+// Experts with more than kChunkRows rows, when ffn_big_kernel does not take
+// them: 128 weight rows x 128 tokens per tile, K staged through LDS 64 at a time (double-buffered through
 // registers), 4 wavefronts of 64 x 64 on v_mfma_f32_32x32x16_bf16 with
 // float32 accumulators.
 //
@@ -1100,8 +1101,9 @@ struct Tiled {
 
 // ---------------------------------------------------------------- large-tile path
 
-// Experts with more than kStreamRows rows (prefill), as an alternative to the
-// 128 x 128 tiles above: 256 weight rows x 256 tokens per tile, one workgroup
+// Experts with more than kChunkRows rows when the experts above kStreamRows
+// rows fill the GPU with these tiles (prefill), instead of the 128 x 128
+// tiles above: 256 weight rows x 256 tokens per tile, one workgroup
 // of 4 wavefronts per CU, each wavefront 128 x 128 on v_mfma_f32_32x32x16_bf16
 // (4 x 4 fragments, 256 float32 accumulators per lane). Per k16 step a
 // wavefront reads 8 KB of fragments from LDS for 16 MFMAs, which leaves the
@@ -1334,7 +1336,7 @@ struct Big {
   }
 };
 
-// Tiles of the experts with more than kStreamRows rows, 256 tokens each; a
+// Tiles of the experts with more than kChunkRows rows, 256 tokens each; a
 // persistent loop over them, one workgroup per CU.
 template <bool GATED>
 __global__ __launch_bounds__(256, 1) void ffn_big_kernel(GemmArgs a) {
@@ -1552,9 +1554,9 @@ int stream_ks(int K) {
   return 1;
 }
 
-// Experts with more than kStreamRows rows go to ffn_big_kernel when the
-// output width allows its tiles, the row capacity is prefill-sized and (on
-// the device) they make at least one tile per CU; else to the 128 x 128 tiles
+// Tiled experts go to ffn_big_kernel when the output width allows its tiles,
+// the row capacity is prefill-sized and (on the device) the experts above
+// kStreamRows rows make at least one tile per CU; else to the 128 x 128 tiles
 // of the persistent kernel. Both paths are complete; the capacity test keeps
 // decode-sized calls from paying for a second launch that finds no work.
 template <bool GATED>
