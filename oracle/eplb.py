@@ -85,8 +85,12 @@ def place(load, num_groups: int, num_nodes: int, num_gpus: int, num_physical: in
     E = len(load)
     G = E // num_groups
     if hierarchical:
-        group_load = [float(np.sum(np.asarray(load[g * G:(g + 1) * G], dtype=np.float64)))
-                      for g in range(num_groups)]
+        group_load = []
+        for g in range(num_groups):   # sequential float64 sum, expert order
+            total = 0.0
+            for e in range(g * G, (g + 1) * G):
+                total += float(load[e])
+            group_load.append(total)
         node_experts = [[e for g in groups for e in range(g * G, (g + 1) * G)]
                         for groups in balanced_pack(group_load, num_nodes)]
     else:
