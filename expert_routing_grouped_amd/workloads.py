@@ -21,6 +21,10 @@ Draw recipe (the order of draws is part of the definition):
 * The capacity workload (routing and capped dispatch only) draws its scores
   the same way, with the shape of the capacity-factor example in section 4.3
   of the ch15 page ("第十五章：多节点大模型推理", se7en.mintlify.app).
+* The FP8 workload draws x and the weights as above; x is rounded to bf16
+  (the layer quantises it), the weights are stored as OCP e4m3 codes with
+  one float32 scale per 128 x 128 block (scale = amax / 448, nearest e4m3
+  value, ties to the even code).
 * bf16 workloads round x and the weights to bf16 (round to nearest even);
   the toy workload keeps float32 and draws its router logits with
   ``standard_normal((T, E), float32)`` before x.
@@ -51,6 +55,7 @@ class Workload:
     dtype: str             # "f32" or "bf16" for x, weights and outputs
     seed: int = 0
     capacity_factor: str | None = None   # per-expert cap C = ceil(c T k / E), c as an exact decimal
+    weight_format: str = "same"          # "fp8_e4m3_b128": x and expert weights as e4m3 with block scales
 
     @property
     def has_ffn(self) -> bool:
@@ -82,6 +87,12 @@ WORKLOADS = {
     "prefill_literal": Workload("prefill_literal", T=8192, E=256, top_k=8, num_groups=8, topk_groups=4,
                                 score_mode="raw", renormalize=True, bias_std=2.0,
                                 hidden=7168, inter=2048, expert_begin=0, num_local=32, dtype="bf16"),
+    # decode_ep on FP8 operands: e4m3 weights with float32 128 x 128 block
+    # scales; the layer quantises x and h per row and 128 features.
+    "decode_ep_fp8": Workload("decode_ep_fp8", T=512, E=256, top_k=8, num_groups=8, topk_groups=4,
+                              score_mode="raw", renormalize=True, bias_std=1.0,
+                              hidden=7168, inter=2048, expert_begin=0, num_local=8, dtype="bf16",
+                              weight_format="fp8_e4m3_b128"),
     # The capacity-factor example of ch15 section 4.3 (T = 5600 tokens, k = 16
     # of E = 896 experts, c = 1.2: C = 120), routing and capped dispatch only:
     # no groups, scores drawn as above (the page gives no score distribution)
@@ -104,6 +115,58 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
 
 
+# OCP FP8 E4M3 (no infinities; S.1111.111 is NaN; largest finite 448):
+# the value of every code 0x00 .. 0x7E (the positive half; the sign is bit 7).
+def _e4m3_positive_values() -> np.ndarray:
+    v = np.empty(127, dtype=np.float64)
+    for code in range(127):
+        e, m = code >> 3, code & 7
+        v[code] = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return v
+
+
+_E4M3 = _e4m3_positive_values()
+FP8_BLOCK = 128
+
+
+def quantize_e4m3_blocks(w: np.ndarray, block_rows: int = 1):
+    """w [..., R, K] float32 -> (codes uint8 [..., R, K], scales float32 [..., R / block_rows, K / 128]).
+
+    One scale per block of block_rows rows by 128 consecutive k: scale =
+    amax / 448 (1 for an all-zero block); each value is divided by its scale
+    and stored as the nearest e4m3 value, ties to the even code (all in
+    float32). Input preparation only: the layer takes the codes and scales as
+    given.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    R, K = w.shape[-2], w.shape[-1]
+    assert K % FP8_BLOCK == 0 and R % block_rows == 0
+    lead = w.shape[:-2]
+    flat = w.reshape((-1, block_rows, K // FP8_BLOCK, FP8_BLOCK))
+    code = np.empty(flat.shape, dtype=np.uint8)
+    scale = np.empty((flat.shape[0], K // FP8_BLOCK), dtype=np.float32)
+    step = max(1, (1 << 19) // (block_rows * K))   # row blocks per pass (temporaries of ~2 MB)
+    for b0 in range(0, flat.shape[0], step):
+        blk = flat[b0:b0 + step]
+        q = np.abs(blk)
+        amax = q.max(axis=(1, 3))
+        sc = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+        q /= sc[:, None, :, None]
+        np.minimum(q, np.float32(448.0), out=q)
+        # q >= 2^-6: keep 3 mantissa bits of the float32 pattern, rounded to
+        # nearest even (a carry moves into the exponent), and rebias the
+        # exponent from 127 to 7; below 2^-6 the code is rint(q * 2^9).
+        u = q.view(np.uint32)
+        normal = ((u + np.uint32(0x7FFFF) + ((u >> np.uint32(20)) & np.uint32(1))) >> np.uint32(20)) - np.uint32(120 << 3)
+        sub = np.rint(q * np.float32(512.0)).astype(np.uint32)
+        c = np.where(q >= np.float32(2.0 ** -6), normal, sub).astype(np.uint8)
+        c |= ((blk.view(np.uint32) >> np.uint32(31)).astype(np.uint8) << np.uint8(7))
+        code[b0:b0 + step] = c
+        scale[b0:b0 + step] = sc
+    scale = scale.reshape(lead + (R // block_rows, K // FP8_BLOCK))
+    return code.reshape(w.shape), scale
+
+
 @dataclass
 class Inputs:
     workload: Workload
@@ -111,9 +174,20 @@ class Inputs:
     x: np.ndarray | None = None        # [T, d] float32, or uint16 bf16 bits
     w_gate_up: np.ndarray | None = None  # [E_loc, 2I, d] float32 or uint16 bf16 bits
     w_down: np.ndarray | None = None     # [E_loc, d, I]  float32 or uint16 bf16 bits
+    # fp8 format: codes (uint8, same shapes as above) and scales [E_loc, N / 128, K / 128] float32
+    w_gate_up_scale: np.ndarray | None = None
+    w_down_scale: np.ndarray | None = None
 
 
-def _weights(rng: np.random.Generator, n: int, shape: tuple, bf16: bool) -> np.ndarray:
+def _weights(rng: np.random.Generator, n: int, shape: tuple, bf16: bool, fp8: bool = False):
+    if fp8:
+        codes = np.empty((n,) + shape, dtype=np.uint8)
+        scales = np.empty((n, shape[0] // FP8_BLOCK, shape[1] // FP8_BLOCK), dtype=np.float32)
+        for e in range(n):
+            w = rng.standard_normal(shape, dtype=np.float32)
+            w *= np.float32(0.02)
+            codes[e], scales[e] = quantize_e4m3_blocks(w, FP8_BLOCK)
+        return codes, scales
     out = np.empty((n,) + shape, dtype=np.uint16 if bf16 else np.float32)
     for e in range(n):
         w = rng.standard_normal(shape, dtype=np.float32)
@@ -137,6 +211,10 @@ def generate(w: Workload, with_ffn: bool = True) -> Inputs:
     bf16 = w.dtype == "bf16"
     x = rng.standard_normal((w.T, w.hidden), dtype=np.float32)
     inp.x = f32_to_bf16_bits(x) if bf16 else x
+    if w.weight_format == "fp8_e4m3_b128":
+        inp.w_gate_up, inp.w_gate_up_scale = _weights(rng, w.num_local, (2 * w.inter, w.hidden), bf16, True)
+        inp.w_down, inp.w_down_scale = _weights(rng, w.num_local, (w.hidden, w.inter), bf16, True)
+        return inp
     inp.w_gate_up = _weights(rng, w.num_local, (2 * w.inter, w.hidden), bf16)
     inp.w_down = _weights(rng, w.num_local, (w.hidden, w.inter), bf16)
     return inp
