@@ -2,7 +2,9 @@
 
 A step is one pass of the whole path over one batch of seeded synthetic input:
 moe_route -> moe_dispatch (count, scan, permute, row gather) -> moe_expert_ffn
-(gate_up GEMM + SiLU*up, down GEMM) -> moe_combine. Inputs are resident in HBM
+(gate_up GEMM + SiLU*up, down GEMM) -> moe_combine. The FP8 workload adds
+moe_quantize_e4m3 of the token rows after the dispatch and runs
+moe_expert_ffn_fp8 on e4m3 weights. Inputs are resident in HBM
 before the timed region. Decode weight sets (0.35-0.7 GB) are comparable to
 the 256 MB last-level cache, so the timed steps rotate over several copies of
 the weights and every step reads its weights from HBM.
@@ -27,6 +29,7 @@ from expert_routing_grouped_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, published
 F32_PEAK_TFLOPS = 157.3      # MI355X fp32 vector, published
 METRIC = "MoE layer tokens/s + grouped-GEMM %HBM-BW (decode) / %MFMA peak (prefill)"
 HEADLINE = "decode_ep"
@@ -103,6 +106,11 @@ def ffn_accounting(wl, counts):
     flops = 6.0 * M * I * d
     weight_bytes = hit * 3.0 * I * d * es
     act_bytes = 2.0 * M * d * es            # permuted rows in, expert outputs out
+    if wl.weight_format == "fp8_e4m3_b128":
+        # e4m3 weights + one float32 scale per 128 x 128 block; FP8 rows with a
+        # float32 scale per 128 features in, bf16 rows out
+        weight_bytes = hit * 3.0 * I * d * (1 + 4 / 128 ** 2)
+        act_bytes = M * d * (1 + 4 / 128) + M * d * 2.0
     return dict(M=M, hit=hit, flops=flops, bytes=weight_bytes + act_bytes,
                 weight_bytes=weight_bytes, act_bytes=act_bytes)
 
@@ -111,6 +119,7 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
     dev = "cuda:0"
     t0 = time.time()
     inp = W.generate(wl)
+    fp8 = wl.weight_format == "fp8_e4m3_b128"
     if operands == "zeros" and wl.has_ffn:   # same routing, all-zero GEMM operands
         inp.x = np.zeros_like(inp.x)
         inp.w_gate_up = np.zeros_like(inp.w_gate_up)
@@ -127,7 +136,7 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
                          num_groups=wl.num_groups, topk_groups=wl.topk_groups, score_mode=mode,
                          renormalize=wl.renormalize, expert_begin=wl.expert_begin,
                          num_local_experts=wl.num_local, hidden=wl.hidden, inter=wl.inter,
-                         dtype=dt, device=dev, expert_capacity=cap)
+                         dtype=dt, device=dev, expert_capacity=cap, fp8=fp8)
     scores = to_device(inp.scores, dev)
     x = to_device(inp.x, dev) if wl.has_ffn else None
     weights = []
@@ -135,23 +144,32 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
         wbytes = (inp.w_gate_up.nbytes + inp.w_down.nbytes)
         n = copies or max(1, min(8, int(np.ceil(768e6 / wbytes)) + 1))
         for _ in range(n):
-            weights.append((to_device(inp.w_gate_up, dev), to_device(inp.w_down, dev)))
+            if fp8:
+                weights.append((to_device(inp.w_gate_up, dev), to_device(inp.w_down, dev),
+                                to_device(inp.w_gate_up_scale, dev), to_device(inp.w_down_scale, dev)))
+            else:
+                weights.append((to_device(inp.w_gate_up, dev), to_device(inp.w_down, dev), None, None))
     else:
-        weights.append((None, None))
+        weights.append((None, None, None, None))
     stream = torch.cuda.current_stream()
 
+    def ffn(i):
+        wgu, wd, wgs, wds = weights[i % len(weights)]
+        layer.ffn(wgu, wd, x, w_gate_up_scales=wgs, w_down_scales=wds)
+
     def step(i, ev=None):
-        wgu, wd = weights[i % len(weights)]
         if ev is not None:
             ev[0].record(stream)
         layer.route(scores)
         if ev is not None:
             ev[1].record(stream)
         layer.dispatch(x)
+        if fp8:
+            layer.quantize(x)      # FP8 rows and scales, as the EP page dispatches them
         if ev is not None:
             ev[2].record(stream)
         if x is not None:
-            layer.ffn(wgu, wd, x)
+            ffn(i)
             if ev is not None:
                 ev[3].record(stream)
             layer.combine()
@@ -189,11 +207,11 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
         # the last step stays in place): the per-launch duration of the roofline
         n_ffn = max(steps, 10)
         for i in range(2):
-            layer.ffn(*weights[i % len(weights)], x)
+            ffn(i)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(n_ffn):
-            layer.ffn(*weights[i % len(weights)], x)
+            ffn(i)
         e1.record(stream)
         torch.cuda.synchronize()
         ffn_us = e0.elapsed_time(e1) / n_ffn * 1e3
@@ -211,7 +229,8 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
                    ffn_tflops=acc["flops"] / t_ffn / 1e12, ffn_gbs=acc["bytes"] / t_ffn / 1e9,
                    layer_tflops=acc["flops"] / (ms_per_step * 1e-3) / 1e12)
         ai = acc["flops"] / acc["bytes"]
-        res["ffn_bound"] = "mfma" if ai > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+        res["mfma_peak_tflops"] = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
+        res["ffn_bound"] = "mfma" if ai > res["mfma_peak_tflops"] * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
     else:
         M = int(counts.sum())
         route_bytes = wl.T * wl.E * 4 + wl.T * wl.top_k * 8
@@ -268,9 +287,19 @@ def cpu_baseline(inp, wl, min_seconds=10.0):
     runs, t = 0, 0.0
     while runs == 0 or t < min_seconds:
         t0 = time.perf_counter()
-        oracle.layer(inp.scores, inp.x, inp.w_gate_up, inp.w_down, top_k=wl.top_k,
-                     num_groups=wl.num_groups, topk_groups=wl.topk_groups, score_mode=wl.score_mode,
-                     renormalize=wl.renormalize, expert_begin=wl.expert_begin, num_local=wl.num_local)
+        if wl.weight_format == "fp8_e4m3_b128":
+            from oracle import fp8 as F
+            ids, w = oracle.route(inp.scores, wl.top_k, wl.num_groups, wl.topk_groups, wl.score_mode,
+                                  wl.renormalize)
+            _, offsets, sa, pos = oracle.dispatch(ids, wl.expert_begin, wl.num_local)
+            xq, xs = F.quantize_rows(oracle.bf16_bits_to_f64(inp.x).astype(np.float32))
+            o, _, _ = F.expert_ffn_fp8(xq, xs, sa, wl.top_k, offsets, inp.w_gate_up, inp.w_gate_up_scale,
+                                       inp.w_down, inp.w_down_scale, wl.inter)
+            oracle.combine(o, pos, w)
+        else:
+            oracle.layer(inp.scores, inp.x, inp.w_gate_up, inp.w_down, top_k=wl.top_k,
+                         num_groups=wl.num_groups, topk_groups=wl.topk_groups, score_mode=wl.score_mode,
+                         renormalize=wl.renormalize, expert_begin=wl.expert_begin, num_local=wl.num_local)
         t += time.perf_counter() - t0
         runs += 1
     return {"value": wl.T * runs / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
@@ -296,6 +325,7 @@ def main():
     moe.lib()
 
     wl = W.WORKLOADS[args.workload]
+    fp8 = wl.weight_format == "fp8_e4m3_b128"
     print(f"bench: workload {wl.name}, steps {args.steps}, warmup {args.warmup}", file=sys.stderr,
           flush=True)
     head = run_workload(wl, args.steps, args.warmup, args.copies, torch, moe, to_device, to_host,
@@ -305,7 +335,7 @@ def main():
         "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "dtype": "fp8_e4m3" if fp8 else ("bf16" if wl.dtype == "bf16" else "f32"),
         "data": "synthetic" if args.operands == "random" else "synthetic, all-zero GEMM operands (diagnostic)",
         "config": {"workload": wl.name, "tokens": wl.T, "experts": wl.E, "top_k": wl.top_k,
                    "groups": f"{wl.num_groups} keep {wl.topk_groups}", "hidden": wl.hidden,
@@ -317,11 +347,12 @@ def main():
         if bound == "hbm":
             ach, peak, unit = head["ffn_gbs"], HBM_PEAK_GBS, "GB/s"
         else:
-            ach, peak, unit = head["ffn_tflops"], BF16_PEAK_TFLOPS, "TFLOP/s"
+            ach, peak, unit = head["ffn_tflops"], head["mfma_peak_tflops"], "TFLOP/s"
         out["roofline"] = {"bound": bound, "achieved": ach, "peak": peak, "unit": unit,
                            "frac": ach / peak, "traffic": measured_traffic(wl.name),
                            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                           "kernel": "moe_expert_ffn (gate_up GEMM + SiLU*up, down GEMM)",
+                           "kernel": ("moe_expert_ffn_fp8 (gate_up GEMM + SiLU*up, h quantiser, down GEMM)"
+                                      if fp8 else "moe_expert_ffn (gate_up GEMM + SiLU*up, down GEMM)"),
                            "us_per_launch": head["ffn_us_per_launch"],
                            "algorithmic_bytes": head["ffn_bytes_mb"] * 1e6,
                            "algorithmic_flops": head["ffn_gflop"] * 1e9}

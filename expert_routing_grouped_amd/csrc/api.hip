@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -165,6 +165,56 @@ moe_status_t moe_expert_ffn(const void* x, const int32_t* row_index, int32_t row
                  num_local_experts, hidden, inter, row_capacity, dtype == MOE_BF16, o_sorted,
                  workspace};
   return from_hip(moe::launch_ffn(a, stream));
+}
+
+moe_status_t moe_quantize_e4m3(const void* x, int32_t rows, int32_t cols, int32_t dtype, void* codes,
+                               float* scales, hipStream_t stream) {
+  if (rows < 0 || cols < 128 || cols % 128 != 0) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if ((int64_t)rows * cols >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!x || !codes || !scales) return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return MOE_ERR_INVALID;
+  return from_hip(moe::launch_quantize_rows(x, rows, cols, dtype == MOE_BF16, (uint8_t*)codes, scales, stream));
+}
+
+static moe_status_t check_ffn_fp8_sizes(int32_t num_local_experts, int32_t hidden, int32_t inter,
+                                        int32_t row_capacity) {
+  if (num_local_experts < 1 || hidden < 1 || inter < 1 || row_capacity < 0) return MOE_ERR_INVALID;
+  if (num_local_experts > 1024) return MOE_ERR_UNSUPPORTED;
+  if (hidden % 512 != 0 || inter % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)2 * inter * hidden >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  // h (float32) and the permuted rows are addressed with 32-bit byte offsets
+  if ((int64_t)row_capacity * inter * 4 >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_expert_ffn_fp8_workspace_size(int32_t num_local_experts, int32_t hidden, int32_t inter,
+                                         int32_t row_capacity) {
+  if (check_ffn_fp8_sizes(num_local_experts, hidden, inter, row_capacity) != MOE_OK) return 0;
+  return moe::ffn_fp8_workspace_size(hidden, inter, row_capacity);
+}
+
+moe_status_t moe_expert_ffn_fp8(const void* x_codes, const float* x_scales, const int32_t* row_index,
+                                int32_t row_index_div, const int32_t* expert_offsets,
+                                const void* w_gate_up, const float* w_gate_up_scales, const void* w_down,
+                                const float* w_down_scales, int32_t num_local_experts, int32_t hidden,
+                                int32_t inter, int32_t row_capacity, void* o_sorted, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  const moe_status_t st = check_ffn_fp8_sizes(num_local_experts, hidden, inter, row_capacity);
+  if (st != MOE_OK) return st;
+  if (!expert_offsets || !w_gate_up || !w_gate_up_scales || !w_down || !w_down_scales) return MOE_ERR_INVALID;
+  if (row_index && row_index_div < 1) return MOE_ERR_INVALID;
+  if (row_capacity > 0 && (!x_codes || !x_scales || !o_sorted)) return MOE_ERR_INVALID;
+  if (!aligned16(x_codes) || !aligned16(x_scales) || !aligned16(o_sorted) || !aligned16(w_gate_up) ||
+      !aligned16(w_down) || !aligned16(w_gate_up_scales) || !aligned16(w_down_scales))
+    return MOE_ERR_INVALID;
+  const size_t need = moe::ffn_fp8_workspace_size(hidden, inter, row_capacity);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
+  moe::FfnFp8Args a{x_codes, x_scales, row_index, row_index ? row_index_div : 1, expert_offsets,
+                    w_gate_up, w_gate_up_scales, w_down, w_down_scales, num_local_experts, hidden, inter,
+                    row_capacity, o_sorted, workspace};
+  return from_hip(moe::launch_ffn_fp8(a, stream));
 }
 
 moe_status_t moe_combine(const void* o_sorted, const int32_t* assign_pos,

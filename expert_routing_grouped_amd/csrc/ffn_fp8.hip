@@ -1,0 +1,527 @@
+// FP8 variant of the grouped SwiGLU expert FFN, and the row quantiser.
+//
+// Operands are OCP e4m3 codes with float32 block scales: token rows (x, and
+// h between the two GEMMs) take one scale per row and 128 consecutive
+// features, weights one per 128 x 128 block; a value is code * scale. The
+// pages count an expert's weights as 44 MB of FP8 and send a dispatched
+// token as FP8 plus 224 bytes of scales ("大规模 EP 部署：分层 EPLB、DP 注意力的
+// 负载与双 batch 重叠", anrans.github.io, section "双 batch 重叠"), and measure
+// the fused gate_up grouped GEMM on FP8 weights ("推理 INFRA 方法论（2）",
+// johneyzheng.top); the block shapes are this library's reading.
+//
+// Per local expert e (rows [off[e], off[e+1]) of the permuted rows):
+//   [g | u] = X_e W_gate_up[e]^T      (float32 accumulation)
+//   h       = silu(g) * u             float32, written to the workspace
+//   (hq, hs)= quantise h per row and 128 columns
+//   o       = hq W_down[e]^T          bf16 out
+//
+// Quantising a block of 128 values: scale = amax / 448 (1 for an all-zero
+// block), code = the e4m3 value nearest to v / scale, ties to the even code,
+// magnitudes above 448 saturate; both divisions are correctly rounded float32.
+//
+// The GEMMs stream the weights: every expert is cut into row chunks of up to
+// 64 rows, and a work item is one chunk and one slab of output columns. A K
+// step is 128 k, one 128-byte line of each row, loaded coalesced (8 rows per
+// instruction) into a wavefront-private XOR-swizzled LDS tile and read back
+// as MFMA fragments for v_mfma_scale_f32_16x16x128_f8f6f4 (block scales of
+// the instruction left at 1): one instruction covers exactly one scale block
+// of k, so its float32 result is multiplied by (row scale x weight block
+// scale) and added to the accumulator. Loads run two K steps ahead.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kQBlock = 128;      // features per scale
+constexpr int kF8Rows = 64;       // rows per chunk
+constexpr int kF8MT = kF8Rows / 16;
+constexpr int kF8Depth = 3;       // register sets: loads run kF8Depth - 1 steps ahead
+constexpr int kF8MaxLocal = 1024;
+constexpr int kF8Config = 0x00020000;   // buffer resource word 3 (raw buffer loads)
+constexpr int kF8NonTemporal = 2;
+
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
+
+// Nearest e4m3 code of a float32 value, ties to the even code, saturating.
+// From 2^-6 up the code is the float32 pattern with its mantissa rounded to
+// 3 bits (a carry moves into the exponent) and the exponent rebiased from
+// 127 to 7; below 2^-6 it is the integer nearest to |q| * 2^9.
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
+  const float a = fminf(fabsf(q), 448.0f);
+  uint32_t c;
+  if (a >= 0x1p-6f) {
+    const uint32_t u = __float_as_uint(a);
+    c = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
+  } else {
+    c = (uint32_t)__builtin_rintf(a * 512.0f);
+  }
+  return c | sign;
+}
+
+// ---------------------------------------------------------------- quantiser
+
+// One wavefront per (row, 128-feature block), two values per lane; the row
+// count is rows, or min(rows, *rows_dev) when rows_dev is given.
+template <bool BF16_IN>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const void* in, int rows, const int* rows_dev,
+                                                           int cols, uint8_t* codes, float* scales) {
+  int n = rows;
+  if (rows_dev) n = min(n, max(0, *rows_dev));
+  const int nb = cols / kQBlock;
+  const long total = (long)n * nb;
+  const int lane = threadIdx.x & 63;
+  const long stride = (long)gridDim.x * 4;
+  for (long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6); w < total; w += stride) {
+    const long r = w / nb;
+    const int b = (int)(w - r * nb);
+    const size_t pair = ((size_t)r * cols + (size_t)b * kQBlock) / 2 + lane;   // values 2 * pair, +1
+    float v0, v1;
+    if (BF16_IN) {
+      const uint32_t p = ((const uint32_t*)in)[pair];
+      v0 = bf16_lo(p);
+      v1 = bf16_hi(p);
+    } else {
+      const float2 p = ((const float2*)in)[pair];
+      v0 = p.x;
+      v1 = p.y;
+    }
+    const float amax = wave_max_f32(fmaxf(fabsf(v0), fabsf(v1)));
+    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+    ((uint16_t*)codes)[pair] = (uint16_t)(e4m3_code(v0 / s) | (e4m3_code(v1 / s) << 8));
+    if (lane == 0) scales[(size_t)r * nb + b] = s;
+  }
+}
+
+// ---------------------------------------------------------------- GEMMs
+
+struct F8Args {
+  const uint8_t* A;       // activation codes: permuted rows, or token rows read through row_index
+  const float* As;        // their scales, [rows, K / 128]
+  const int* row_index;   // null, or sorted_assign: permuted row i is A row row_index[i] / row_div
+  int row_div;
+  const int* offsets;     // [nloc + 1]
+  int nloc, capacity;
+  const uint8_t* W;       // [nloc, N, K] codes, K contiguous
+  const float* Ws;        // [nloc, N / 128, K / 128]
+  int N, K, inter;        // gated GEMMs pair weight row n with row inter + n
+  void* C;                // gated: float h [capacity, ldc]; plain: bf16 [capacity, ldc]
+  int ldc;
+};
+
+// Chunks of every expert with rows, in expert order: c_first[e] = first chunk
+// of expert e, c_first[nloc] = chunks; c_lo[e] = first row (clamped to the
+// capacity), c_lo[nloc] = end of the last expert. 4 experts per thread of the
+// 256-thread workgroup; returns the chunk count.
+__device__ int f8_chunk_lists(const F8Args& a, int* c_first, int* c_lo, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int cnt[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    int m = 0;
+    if (e < a.nloc) {
+      const int lo = min(a.offsets[e], a.capacity);
+      const int hi = min(a.offsets[e + 1], a.capacity);
+      m = max(0, hi - lo);
+      c_lo[e] = lo;
+      if (e == a.nloc - 1) c_lo[a.nloc] = max(lo, hi);
+    }
+    cnt[q] = (m + kF8Rows - 1) / kF8Rows;
+    sum += cnt[q];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, MOE_WAVE);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < w) before += wsum[i];
+    total += wsum[i];
+  }
+  int p = before + incl - sum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    if (e < a.nloc) {
+      c_first[e] = p;
+      p += cnt[q];
+    }
+  }
+  if (tid == 0) c_first[a.nloc] = total;
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(total);
+}
+
+__device__ __forceinline__ int f8_find_expert(const int* first, int nloc, int idx) {
+  int lo = 0, hi = nloc - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (first[mid] <= idx) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Permuted row numbers -> rows of A. The division by row_div is
+// floor((v + 0.5) / row_div) in float64, exact for v < 2^31 (the error of the
+// float64 quotient stays far below the distance 0.5 / row_div to an integer).
+template <int N>
+__device__ __forceinline__ void f8_rows(const F8Args& a, uint32_t* rows) {
+  if (!a.row_index) return;
+#pragma unroll
+  for (int j = 0; j < N; ++j) rows[j] = (uint32_t)a.row_index[rows[j]];
+  int div = a.row_div;
+  asm volatile("" : "+s"(div));
+  if (div != 1) {
+    const double inv = 1.0 / (double)div;
+#pragma unroll
+    for (int j = 0; j < N; ++j) rows[j] = (uint32_t)(((double)rows[j] + 0.5) * inv);
+  }
+}
+
+// A work item: a row chunk of expert e and a slab of output columns. The
+// workgroup's 4 wavefronts split K into KS slices and (4 / KS) groups of NTW
+// 16-row weight tiles (gated: a gate tile and the matching up tile). The
+// weight tile is the MFMA A operand, the activations the B operand, so a
+// lane holds 4 consecutive output columns of one row.
+//
+// Loads: lane l takes the 16-byte chunk l % 8 of row 8h + l / 8 of a 16-row
+// tile (h = 0, 1) and writes it to row * 128 + ((chunk ^ row % 8) * 16) of its
+// wavefront's LDS tile; fragments are read back with lane (r = l % 16,
+// g = l / 16) taking chunks g and 4 + g of row r -- 32 bytes, the same k set
+// for weights and activations, so the product sums each k once.
+template <int NTW, int KS, bool GATED>
+struct Stream8 {
+  static constexpr int D = kF8Depth;
+  static constexpr int MT = kF8MT;
+  static constexpr int NWN = 4 / KS;
+  static constexpr int HT = GATED ? NTW / 2 : NTW;
+  static constexpr int COLS = NWN * HT * 16;        // output columns per slab
+  static constexpr int KSTEP = 128;
+  static constexpr int TILE_BYTES = 16 * 128;
+  static constexpr int WAVE_LDS = (NTW + MT) * TILE_BYTES;
+  static constexpr int LDS_BYTES = 4 * WAVE_LDS;
+  static_assert(!GATED || NTW % 2 == 0, "gated slabs pair gate and up tiles");
+  static_assert(MT * NTW * 1024 <= WAVE_LDS, "K-slice partial sums fit in the wavefront's tiles");
+  static_assert(HT * 16 <= kQBlock && kQBlock % (HT * 16) == 0, "a wavefront's tiles share a weight scale block");
+
+  template <int MTA, bool NT>
+  __device__ static void run_mt(const F8Args& a, int e, int lo, int m, int slab, char* smem) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ks = wave % KS, wn = wave / KS;
+    const int fr = lane & 15, g = lane >> 4;
+    const int lr = lane >> 3, lc = lane & 7;
+    const int col0 = (slab * NWN + wn) * HT * 16;
+    const uint32_t pitch = (uint32_t)a.K;          // bytes per row
+    const int KB = a.K / kQBlock;
+
+    // Weights and their block scales: one buffer per expert.
+    const __amdgpu_buffer_rsrc_t wbuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.W + (size_t)e * a.N * a.K), 0, (int)(a.N * pitch), kF8Config);
+    const __amdgpu_buffer_rsrc_t wsbuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.Ws + (size_t)e * (a.N / kQBlock) * KB), 0, (a.N / kQBlock) * KB * 4, kF8Config);
+    const uint32_t wv = (uint32_t)(col0 + lr) * pitch + lc * 16;
+    int wso[NTW][2], wsc[NTW];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      const int n0 = col0 + (t % HT) * 16 + ((GATED && t >= HT) ? a.inter : 0);
+      wsc[t] = (n0 / kQBlock - col0 / kQBlock) * KB * 4;   // relative to the wavefront's first block row
+#pragma unroll
+      for (int h = 0; h < 2; ++h) wso[t][h] = ((t % HT) * 16 + h * 8 + ((GATED && t >= HT) ? a.inter : 0)) * (int)pitch;
+    }
+    const uint32_t wsv = (uint32_t)(col0 / kQBlock) * KB * 4;
+    // Activations: rows past the chunk's end read its first row (their output
+    // column is not stored). av: the load rows; sv: the row of the lane's
+    // MFMA column, for its scale.
+    const __amdgpu_buffer_rsrc_t abuf = __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, -1, kF8Config);
+    const __amdgpu_buffer_rsrc_t asbuf = __builtin_amdgcn_make_buffer_rsrc((void*)a.As, 0, -1, kF8Config);
+    uint32_t av[MTA][2], sv[MTA];
+#pragma unroll
+    for (int i = 0; i < MTA; ++i) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = i * 16 + h * 8 + lr;
+        av[i][h] = lo + (r < m ? r : 0);
+      }
+      const int r = i * 16 + fr;
+      sv[i] = lo + (r < m ? r : 0);
+    }
+    f8_rows<MTA * 2>(a, &av[0][0]);
+    f8_rows<MTA>(a, sv);
+#pragma unroll
+    for (int i = 0; i < MTA; ++i) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) av[i][h] = av[i][h] * pitch + lc * 16;
+      sv[i] = sv[i] * (uint32_t)KB * 4;
+    }
+
+    char* xs = smem + wave * WAVE_LDS;
+    const int woff[2] = {lr * 128 + ((lc ^ lr) << 4), (8 + lr) * 128 + ((lc ^ lr) << 4)};
+    const int roff[2] = {fr * 128 + ((g ^ (fr & 7)) << 4), fr * 128 + (((4 + g) ^ (fr & 7)) << 4)};
+
+    f32x4_t acc[MTA][NTW];
+#pragma unroll
+    for (int i = 0; i < MTA; ++i)
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) acc[i][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    u32x4_t wr[D][NTW][2], ar[D][MTA][2];
+    float wsr[D][NTW], asr[D][MTA];
+    auto load = [&](int q, int kk) {
+      const int kb4 = (kk / kQBlock) * 4;
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          wr[q][t][h] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, wv, wso[t][h] + kk, NT ? kF8NonTemporal : 0);
+        wsr[q][t] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wsbuf, wsv, wsc[t] + kb4, 0));
+      }
+#pragma unroll
+      for (int i = 0; i < MTA; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) ar[q][i][h] = __builtin_amdgcn_raw_buffer_load_b128(abuf, av[i][h], kk, 0);
+        asr[q][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(asbuf, sv[i], kb4, 0));
+      }
+    };
+    auto mma = [&](int q) {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) *(u32x4_t*)(xs + t * TILE_BYTES + woff[h]) = wr[q][t][h];
+#pragma unroll
+      for (int i = 0; i < MTA; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) *(u32x4_t*)(xs + (NTW + i) * TILE_BYTES + woff[h]) = ar[q][i][h];
+      i32x8_t wf[NTW], af[MTA];
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) {
+        const i32x4_t lo4 = *(const i32x4_t*)(xs + t * TILE_BYTES + roff[0]);
+        const i32x4_t hi4 = *(const i32x4_t*)(xs + t * TILE_BYTES + roff[1]);
+        wf[t] = i32x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < MTA; ++i) {
+        const i32x4_t lo4 = *(const i32x4_t*)(xs + (NTW + i) * TILE_BYTES + roff[0]);
+        const i32x4_t hi4 = *(const i32x4_t*)(xs + (NTW + i) * TILE_BYTES + roff[1]);
+        af[i] = i32x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      }
+      f32x4_t p[MTA][NTW];
+#pragma unroll
+      for (int i = 0; i < MTA; ++i)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+          p[i][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[t], af[i], f32x4_t{0.f, 0.f, 0.f, 0.f},
+                                                                     0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int i = 0; i < MTA; ++i)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          const float sc = asr[q][i] * wsr[q][t];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][t][r] = fmaf(p[i][t][r], sc, acc[i][t][r]);
+        }
+    };
+
+    // Step s issues the loads of step s + D - 1 (steps past the end reload the
+    // last one), then consumes step s; loads complete in issue order, so each
+    // step waits only for its own data.
+    const int kw = a.K / KS, kbeg = ks * kw, klast = kbeg + kw - KSTEP;
+    const int steps = kw / KSTEP;
+#pragma unroll
+    for (int j = 0; j < D - 1; ++j) load(j, min(kbeg + j * KSTEP, klast));
+    int kk = kbeg, s = 0;
+#define MOE_F8_STEP(q)                                   \
+  load(((q) + D - 1) % D, min(kk + (D - 1) * KSTEP, klast)); \
+  __builtin_amdgcn_sched_barrier(0);                     \
+  mma((q) % D);                                          \
+  __builtin_amdgcn_sched_barrier(0);                     \
+  kk += KSTEP;
+    for (; s + D <= steps; s += D) {
+#pragma unroll
+      for (int q = 0; q < D; ++q) { MOE_F8_STEP(q) }
+    }
+#pragma unroll
+    for (int q = 0; q < D - 1; ++q) {
+      if (s + q >= steps) break;
+      MOE_F8_STEP(q)
+    }
+#undef MOE_F8_STEP
+
+    if (KS > 1) {
+      f32x4_t* red = (f32x4_t*)xs;
+#pragma unroll
+      for (int i = 0; i < MTA; ++i)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) red[(i * NTW + t) * 64 + lane] = acc[i][t];
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < MTA; ++i) {
+        if (i % KS != ks) continue;
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) {
+          f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int q = 0; q < KS; ++q)
+            sum += ((const f32x4_t*)(smem + (wn * KS + q) * WAVE_LDS))[(i * NTW + t) * 64 + lane];
+          acc[i][t] = sum;
+        }
+      }
+    }
+    // Lane holds output row i*16 + lane % 16, columns col0 + t*16 + 4*(lane/16) + (0..3).
+#pragma unroll
+    for (int i = 0; i < MTA; ++i) {
+      if (KS > 1 && i % KS != ks) continue;
+      const int row = i * 16 + fr;
+      if (row >= m) continue;
+      if (GATED) {
+        float* crow = (float*)a.C + (size_t)(lo + row) * a.ldc + col0 + g * 4;
+#pragma unroll
+        for (int t = 0; t < HT; ++t) {
+          f32x4_t v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = silu_f(acc[i][t][r]) * acc[i][t + HT][r];
+          *(f32x4_t*)(crow + t * 16) = v;
+        }
+      } else {
+        uint16_t* crow = (uint16_t*)a.C + (size_t)(lo + row) * a.ldc + col0 + g * 4;
+#pragma unroll
+        for (int t = 0; t < HT; ++t) {
+          const f32x4_t v = acc[i][t];
+          *(uint2*)(crow + t * 16) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+        }
+      }
+    }
+  }
+
+  // Chunk `chunk` of expert e, output slab `slab`. The weights of an expert
+  // with a single chunk are read once per GEMM, non-temporally.
+  __device__ static void run(const F8Args& a, const int* c_lo, int e, int chunk, int slab, char* smem) {
+    e = __builtin_amdgcn_readfirstlane(e);
+    const int lo = __builtin_amdgcn_readfirstlane(c_lo[e] + chunk * kF8Rows);
+    const int m = __builtin_amdgcn_readfirstlane(min(kF8Rows, c_lo[e + 1] - lo));
+    const bool nt = __builtin_amdgcn_readfirstlane(c_lo[e + 1] - c_lo[e]) <= kF8Rows;
+    slab = __builtin_amdgcn_readfirstlane(slab);
+    switch (((m + 15) >> 4) * 2 + (nt ? 1 : 0)) {
+      case 2: run_mt<1, false>(a, e, lo, m, slab, smem); break;
+      case 3: run_mt<1, true>(a, e, lo, m, slab, smem); break;
+      case 4: run_mt<2, false>(a, e, lo, m, slab, smem); break;
+      case 5: run_mt<2, true>(a, e, lo, m, slab, smem); break;
+      case 6: run_mt<3, false>(a, e, lo, m, slab, smem); break;
+      case 7: run_mt<3, true>(a, e, lo, m, slab, smem); break;
+      case 9: run_mt<4, true>(a, e, lo, m, slab, smem); break;
+      default: run_mt<4, false>(a, e, lo, m, slab, smem); break;
+    }
+  }
+};
+
+template <int NTW, int KS, bool GATED>
+__global__ __launch_bounds__(256, 2) void ffn_fp8_kernel(F8Args a) {
+  using S = Stream8<NTW, KS, GATED>;
+  __shared__ __attribute__((aligned(16))) char smem[S::LDS_BYTES];
+  __shared__ int c_first[kF8MaxLocal + 1];
+  __shared__ int c_lo[kF8MaxLocal + 1];
+  __shared__ int wsum[4];
+  const int chunks = f8_chunk_lists(a, c_first, c_lo, wsum);
+  const int slabs = (GATED ? a.inter : a.N) / S::COLS;
+  const int total = chunks * slabs;
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int c = w / slabs;
+    const int e = f8_find_expert(c_first, a.nloc, c);
+    S::run(a, c_lo, e, c - c_first[e], w % slabs, smem);
+    __syncthreads();  // the LDS buffer is reused by the next work item
+  }
+}
+
+int f8_cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int NTW, int KS, bool GATED>
+hipError_t launch_fp8_gemm(const F8Args& g, hipStream_t s) {
+  using S = Stream8<NTW, KS, GATED>;
+  auto kernel = ffn_fp8_kernel<NTW, KS, GATED>;
+  static const int occ = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ffn_fp8_kernel<NTW, KS, GATED>, 256, 0) != hipSuccess ||
+        n <= 0)
+      n = 1;
+    return n;
+  }();
+  const long max_chunks = (long)(g.capacity + kF8Rows - 1) / kF8Rows + g.nloc;
+  const long max_work = max_chunks * ((GATED ? g.inter : g.N) / S::COLS);
+  const int grid = (int)std::max<long>(1, std::min<long>(max_work, (long)f8_cu_count() * occ));
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+inline size_t f8_align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int quantize_grid(long blocks) {
+  return (int)std::max<long>(1, std::min<long>((blocks + 3) / 4, (long)f8_cu_count() * 8));
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const void* x, int rows, int cols, bool bf16_in, uint8_t* codes, float* scales,
+                                hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int grid = quantize_grid((long)rows * (cols / kQBlock));
+  if (bf16_in)
+    hipLaunchKernelGGL(quantize_rows_kernel<true>, dim3(grid), dim3(256), 0, s, x, rows, nullptr, cols, codes, scales);
+  else
+    hipLaunchKernelGGL(quantize_rows_kernel<false>, dim3(grid), dim3(256), 0, s, x, rows, nullptr, cols, codes,
+                       scales);
+  return hipGetLastError();
+}
+
+size_t ffn_fp8_workspace_size(int hidden, int inter, int capacity) {
+  (void)hidden;
+  return f8_align256((size_t)capacity * inter * 4) + f8_align256((size_t)capacity * inter) +
+         f8_align256((size_t)capacity * (inter / kQBlock) * 4);
+}
+
+hipError_t launch_ffn_fp8(const FfnFp8Args& a, hipStream_t s) {
+  if (a.capacity == 0) return hipSuccess;
+  const int I = a.inter, d = a.hidden;
+  char* ws = (char*)a.workspace;
+  float* h = (float*)ws;
+  uint8_t* hq = (uint8_t*)(ws + f8_align256((size_t)a.capacity * I * 4));
+  float* hs = (float*)((char*)hq + f8_align256((size_t)a.capacity * I));
+  F8Args g1{(const uint8_t*)a.x_codes, a.x_scales, a.row_index, a.row_div, a.offsets, a.num_local, a.capacity,
+            (const uint8_t*)a.w_gate_up, a.w_gate_up_scales, 2 * I, d, I, h, I};
+  F8Args g2{hq, hs, nullptr, 1, a.offsets, a.num_local, a.capacity,
+            (const uint8_t*)a.w_down, a.w_down_scales, d, I, I, a.o_sorted, d};
+  hipError_t err = launch_fp8_gemm<2, 4, true>(g1, s);
+  if (err != hipSuccess) return err;
+  const int grid = quantize_grid((long)a.capacity * (I / kQBlock));
+  hipLaunchKernelGGL(quantize_rows_kernel<false>, dim3(grid), dim3(256), 0, s, (const void*)h, a.capacity,
+                     a.offsets + a.num_local, I, hq, hs);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_fp8_gemm<2, 2, false>(g2, s);
+}
+
+}  // namespace moe

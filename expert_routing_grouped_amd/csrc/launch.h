@@ -50,6 +50,26 @@ struct FfnArgs {
 size_t ffn_workspace_size(int num_local, int hidden, int inter, int capacity, bool bf16);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 
+// FP8 (e4m3 codes, float32 block scales) expert FFN and row quantiser.
+struct FfnFp8Args {
+  const void* x_codes;     // [rows, hidden] e4m3: permuted rows, or token rows read through row_index
+  const float* x_scales;   // [rows, hidden / 128]
+  const int* row_index;
+  int row_div;
+  const int* offsets;
+  const void* w_gate_up;   // [nloc, 2 * inter, hidden] e4m3
+  const float* w_gate_up_scales;  // [nloc, 2 * inter / 128, hidden / 128]
+  const void* w_down;      // [nloc, hidden, inter] e4m3
+  const float* w_down_scales;     // [nloc, hidden / 128, inter / 128]
+  int num_local, hidden, inter, capacity;
+  void* o_sorted;          // [capacity, hidden] bf16
+  void* workspace;
+};
+size_t ffn_fp8_workspace_size(int hidden, int inter, int capacity);
+hipError_t launch_ffn_fp8(const FfnFp8Args& a, hipStream_t s);
+hipError_t launch_quantize_rows(const void* x, int rows, int cols, bool bf16_in, uint8_t* codes, float* scales,
+                                hipStream_t s);
+
 struct CombineArgs {
   const void* o_sorted;
   const int* assign_pos;

@@ -35,6 +35,10 @@ _SIGNATURES = {
     "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "moe_expert_ffn": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P,
                                       ctypes.c_size_t, _P]),
+    "moe_quantize_e4m3": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P]),
+    "moe_expert_ffn_fp8_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "moe_expert_ffn_fp8": (ctypes.c_int, [_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P,
+                                          ctypes.c_size_t, _P]),
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_eplb_place": (ctypes.c_int, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moe_eplb_remap": (ctypes.c_int, [_P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P]),
@@ -212,6 +216,71 @@ def moe_expert_ffn(x, expert_offsets, w_gate_up, w_down, row_index=None, row_ind
     return o_sorted
 
 
+def moe_quantize_e4m3(x, codes=None, scales=None, stream=None):
+    """Rows of x [R, C] (float32 or bf16) -> (e4m3 codes uint8 [R, C], scales float32 [R, C / 128])."""
+    _dev(x, x.dtype, "x")
+    R, C = x.shape
+    if codes is None:
+        codes = torch.empty((R, C), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((R, C // 128), dtype=torch.float32, device=x.device)
+    _dev(codes, torch.uint8, "codes")
+    _dev(scales, torch.float32, "scales")
+    if tuple(codes.shape) != (R, C) or scales.numel() < R * (C // 128):
+        raise MoeError("moe_quantize_e4m3: output shapes do not match x")
+    _check(lib().moe_quantize_e4m3(_ptr(x), R, C, _code(x.dtype), _ptr(codes), _ptr(scales),
+                                   _stream(stream)), "moe_quantize_e4m3")
+    return codes, scales
+
+
+def ffn_fp8_workspace_size(num_local_experts, hidden, inter, row_capacity) -> int:
+    return int(lib().moe_expert_ffn_fp8_workspace_size(num_local_experts, hidden, inter, row_capacity))
+
+
+def moe_expert_ffn_fp8(x_codes, x_scales, expert_offsets, w_gate_up, w_gate_up_scales, w_down,
+                       w_down_scales, row_index=None, row_index_div=1, row_capacity=None,
+                       o_sorted=None, workspace=None, stream=None):
+    """Grouped SwiGLU FFN on e4m3 operands with float32 block scales; returns o_sorted (bf16)."""
+    _dev(x_codes, torch.uint8, "x_codes")
+    _dev(x_scales, torch.float32, "x_scales")
+    _dev(expert_offsets, torch.int32, "expert_offsets")
+    _dev(w_gate_up, torch.uint8, "w_gate_up")
+    _dev(w_down, torch.uint8, "w_down")
+    _dev(w_gate_up_scales, torch.float32, "w_gate_up_scales")
+    _dev(w_down_scales, torch.float32, "w_down_scales")
+    if row_index is not None:
+        _dev(row_index, torch.int32, "row_index")
+        cap = row_index.numel() if row_capacity is None else row_capacity
+    else:
+        cap = x_codes.shape[0] if row_capacity is None else row_capacity
+    hidden = x_codes.shape[1]
+    E_loc, two_i, d2 = w_gate_up.shape
+    inter = two_i // 2
+    if d2 != hidden or tuple(w_down.shape) != (E_loc, hidden, inter):
+        raise MoeError("weight shapes do not match x")
+    if tuple(w_gate_up_scales.shape) != (E_loc, two_i // 128, hidden // 128) or \
+            tuple(w_down_scales.shape) != (E_loc, hidden // 128, inter // 128):
+        raise MoeError("weight scale shapes do not match the weights")
+    if tuple(x_scales.shape) != (x_codes.shape[0], hidden // 128):
+        raise MoeError("x_scales shape does not match x_codes")
+    if o_sorted is None:
+        o_sorted = torch.empty((max(cap, 1), hidden), dtype=torch.bfloat16, device=x_codes.device)
+    _dev(o_sorted, torch.bfloat16, "o_sorted")
+    if o_sorted.shape[0] < cap or (row_index is None and x_codes.shape[0] < cap):
+        raise MoeError("row buffers are smaller than row_capacity")
+    need = ffn_fp8_workspace_size(E_loc, hidden, inter, cap)
+    if need == 0:
+        raise MoeError("moe_expert_ffn_fp8: unsupported sizes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x_codes.device)
+    _check(lib().moe_expert_ffn_fp8(_ptr(x_codes), _ptr(x_scales), _ptr(row_index), int(row_index_div),
+                                    _ptr(expert_offsets), _ptr(w_gate_up), _ptr(w_gate_up_scales),
+                                    _ptr(w_down), _ptr(w_down_scales), E_loc, hidden, inter, cap,
+                                    _ptr(o_sorted), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)), "moe_expert_ffn_fp8")
+    return o_sorted
+
+
 def moe_combine(o_sorted, assign_pos, topk_weights, out_dtype=None, y=None, stream=None):
     """y [T, d] = router-weighted sum of each token's local expert outputs."""
     _dev(o_sorted, o_sorted.dtype, "o_sorted")
@@ -273,7 +342,7 @@ class MoELayer:
 
     def __init__(self, *, num_tokens, num_experts, top_k, num_groups, topk_groups, score_mode,
                  renormalize, expert_begin, num_local_experts, hidden, inter, dtype, device,
-                 fuse_gather=True, expert_capacity=None):
+                 fuse_gather=True, expert_capacity=None, fp8=False):
         self.T, self.E, self.k = num_tokens, num_experts, top_k
         self.num_groups, self.topk_groups = num_groups, topk_groups
         self.score_mode, self.renormalize = score_mode, renormalize
@@ -281,6 +350,9 @@ class MoELayer:
         self.hidden, self.inter, self.dtype = hidden, inter, dtype
         self.fuse_gather = fuse_gather
         self.expert_capacity = expert_capacity
+        self.fp8 = fp8   # e4m3 weights with block scales; x is quantised per row in forward()
+        if fp8 and not fuse_gather:
+            raise MoeError("the FP8 layer reads the token rows through sorted_assign (fuse_gather=True)")
         cap = num_tokens * top_k
         self.cap = cap
         dev = torch.device(device)
@@ -296,7 +368,16 @@ class MoELayer:
         dneed = int(lib().moe_dispatch_workspace_size(num_tokens, top_k, num_local_experts))
         if dneed:
             self.buf["dispatch_ws"] = torch.empty(dneed, dtype=torch.uint8, device=dev)
-        if hidden:
+        if hidden and fp8:
+            self.buf["x_codes"] = torch.empty((num_tokens, hidden), dtype=torch.uint8, device=dev)
+            self.buf["x_scales"] = torch.empty((num_tokens, hidden // 128), dtype=torch.float32, device=dev)
+            self.buf["o_sorted"] = torch.empty((max(cap, 1), hidden), dtype=torch.bfloat16, device=dev)
+            self.buf["y"] = torch.empty((num_tokens, hidden), dtype=torch.bfloat16, device=dev)
+            need = ffn_fp8_workspace_size(num_local_experts, hidden, inter, max(cap, 1))
+            if need == 0:
+                raise MoeError("unsupported FFN sizes")
+            self.buf["workspace"] = torch.empty(need, dtype=torch.uint8, device=dev)
+        elif hidden:
             if not fuse_gather:
                 self.buf["x_sorted"] = torch.empty((max(cap, 1), hidden), dtype=dtype, device=dev)
             self.buf["o_sorted"] = torch.empty((max(cap, 1), hidden), dtype=dtype, device=dev)
@@ -325,8 +406,20 @@ class MoELayer:
         return moe_dispatch(b["topk_ids"], self.expert_begin, self.num_local, None, out, stream,
                             self.expert_capacity)
 
-    def ffn(self, w_gate_up, w_down, x=None, stream=None):
+    def quantize(self, x, stream=None):
+        """FP8 layer: the token rows to e4m3 codes and per-row block scales (the form the
+        EP page dispatches them in)."""
         b = self.buf
+        return moe_quantize_e4m3(x, b["x_codes"], b["x_scales"], stream)
+
+    def ffn(self, w_gate_up, w_down, x=None, stream=None, w_gate_up_scales=None, w_down_scales=None):
+        """The expert FFN; the FP8 layer reads the codes that quantize() left in self.buf."""
+        b = self.buf
+        if self.fp8:
+            return moe_expert_ffn_fp8(b["x_codes"], b["x_scales"], b["offsets"], w_gate_up, w_gate_up_scales, w_down,
+                                      w_down_scales, row_index=b["sorted_assign"], row_index_div=self.k,
+                                      row_capacity=self.cap, o_sorted=b["o_sorted"],
+                                      workspace=b["workspace"], stream=stream)
         if self.fuse_gather:
             return moe_expert_ffn(x, b["offsets"], w_gate_up, w_down, row_index=b["sorted_assign"],
                                   row_index_div=self.k, row_capacity=self.cap,
@@ -337,13 +430,16 @@ class MoELayer:
 
     def combine(self, stream=None):
         b = self.buf
-        return moe_combine(b["o_sorted"], b["assign_pos"], b["topk_weights"], self.dtype, b["y"],
+        return moe_combine(b["o_sorted"], b["assign_pos"], b["topk_weights"], b["y"].dtype, b["y"],
                            stream)
 
-    def forward(self, scores, x=None, w_gate_up=None, w_down=None, stream=None):
+    def forward(self, scores, x=None, w_gate_up=None, w_down=None, stream=None, w_gate_up_scales=None,
+                w_down_scales=None):
         self.route(scores, stream)
         self.dispatch(x, stream)
         if x is None:
             return None
-        self.ffn(w_gate_up, w_down, x, stream)
+        if self.fp8:
+            self.quantize(x, stream)
+        self.ffn(w_gate_up, w_down, x, stream, w_gate_up_scales, w_down_scales)
         return self.combine(stream)

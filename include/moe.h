@@ -8,8 +8,9 @@
  *   moe_expert_ffn  grouped SwiGLU expert FFN (fused gate_up GEMM, SiLU*up, down GEMM)
  *   moe_combine     router-weighted sum of the expert outputs, back in token order
  *
- * and, for placement across GPUs, moe_eplb_place (host planner) and
- * moe_eplb_remap (logical to physical replica per routed slot).
+ * the FP8 variant of the expert FFN (moe_quantize_e4m3 for the token rows,
+ * moe_expert_ffn_fp8), and, for placement across GPUs, moe_eplb_place (host
+ * planner) and moe_eplb_remap (logical to physical replica per routed slot).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -41,7 +42,9 @@
  *   gated MLP with W_gate, W_up, W_down.
  * - "推理 INFRA 方法论（2）：分布式推理：TP、DP、EP、CP 与 PP" (johneyzheng.top):
  *   gate and up fused into one GEMM with N = 2I; experts that no token hits
- *   are skipped.
+ *   are skipped; the fused gate_up grouped GEMM measured on FP8 weights.
+ * - The EP deployment page above, section "双 batch 重叠": an expert's weights
+ *   are 44 MB of FP8, and a dispatched token is FP8 plus 224 bytes of scales.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -255,6 +258,73 @@ moe_status_t moe_expert_ffn(const void* x, const int32_t* row_index, int32_t row
                             const void* w_down, int32_t num_local_experts, int32_t hidden,
                             int32_t inter, int32_t row_capacity, int32_t dtype, void* o_sorted,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * FP8 operands (moe_quantize_e4m3, moe_expert_ffn_fp8). Values are OCP FP8
+ * E4M3 codes (1 byte: sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ * largest finite 448; 0x7F and 0xFF are NaN) with float32 scales; a value is
+ * code * scale. Token rows take one scale per row and 128 consecutive
+ * features (224 B for 7168 features, the EP page's per-token count); weights
+ * one per 128 x 128 block. The block shapes are this library's reading: the
+ * pages give only the byte counts.
+ */
+
+/*
+ * moe_quantize_e4m3 -- token rows to FP8, the form in which the EP page
+ * dispatches them. For each row r and block b of 128 features:
+ *   scale[r, b] = amax / 448 (float32; 1.0 for an all-zero block),
+ *   code[r, c]  = the e4m3 value nearest to x[r, c] / scale[r, b] (float32
+ *                 division), ties to the even code, magnitudes above 448
+ *                 saturating to 448; the sign bit is x's sign bit.
+ * x       [rows, cols] (dtype: MOE_F32 or MOE_BF16); finite values.
+ * codes   [rows, cols] uint8 out.
+ * scales  [rows, cols / 128] float32 out.
+ * Limits: cols % 128 == 0; x, codes and scales 16-byte aligned. rows = 0
+ * does nothing.
+ */
+moe_status_t moe_quantize_e4m3(const void* x, int32_t rows, int32_t cols, int32_t dtype, void* codes,
+                               float* scales, hipStream_t stream);
+
+/*
+ * Bytes of device workspace moe_expert_ffn_fp8 needs; 0 when the sizes are
+ * invalid.
+ */
+size_t moe_expert_ffn_fp8_workspace_size(int32_t num_local_experts, int32_t hidden, int32_t inter,
+                                         int32_t row_capacity);
+
+/*
+ * moe_expert_ffn_fp8 -- moe_expert_ffn on FP8 operands. For each local
+ * expert e with rows [off[e], off[e+1]):
+ *   [g | u] = X_e * W_gate_up[e]^T   (dequantised operands, float32 accumulation)
+ *   h       = silu(g) * u            (float32)
+ *   (hq, hs)= h quantised per row and 128 columns exactly as moe_quantize_e4m3
+ *   o       = dequant(hq, hs) * W_down[e]^T, rounded to bf16.
+ *
+ * x_codes, x_scales  the permuted rows in FP8 (moe_quantize_e4m3 layout), in
+ *                 one of two forms as in moe_expert_ffn: row_index == NULL:
+ *                 [row_capacity, hidden] permuted rows; else token rows, with
+ *                 permuted row i = row row_index[i] / row_index_div (pass
+ *                 sorted_assign and top_k to fuse the dispatch gather).
+ * expert_offsets  [E_loc + 1] int32 (moe_dispatch); read on the device only.
+ * w_gate_up       [E_loc, 2 * inter, hidden] e4m3: rows [0, I) gate, [I, 2I) up.
+ * w_gate_up_scales [E_loc, 2 * inter / 128, hidden / 128] float32.
+ * w_down          [E_loc, hidden, inter] e4m3.
+ * w_down_scales   [E_loc, hidden / 128, inter / 128] float32.
+ * o_sorted        [row_capacity, hidden] bf16 out: rows [0, M) written.
+ * workspace       >= moe_expert_ffn_fp8_workspace_size bytes (holds h in
+ *                 float32 and in FP8); contents need not be initialised.
+ * Limits: hidden % 512 == 0, inter % 256 == 0; E_loc <= 1024;
+ * row_capacity * inter * 4 < 2^31; the caller keeps x_codes below 2^32
+ * bytes. M = offsets[E_loc] must not exceed row_capacity. Every expert's rows
+ * are streamed in chunks of 64 (the weights are read once per chunk): the
+ * path is built for decode-sized calls.
+ */
+moe_status_t moe_expert_ffn_fp8(const void* x_codes, const float* x_scales, const int32_t* row_index,
+                                int32_t row_index_div, const int32_t* expert_offsets,
+                                const void* w_gate_up, const float* w_gate_up_scales, const void* w_down,
+                                const float* w_down_scales, int32_t num_local_experts, int32_t hidden,
+                                int32_t inter, int32_t row_capacity, void* o_sorted, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_combine -- the combine step (ch15 section 3.4; attain.fans hop 4):

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = moe.lib()
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
     assert moe.status_string(0) == "ok"
     assert moe.status_string(1) == "invalid argument"
     assert moe.status_string(3).startswith("workspace")
@@ -104,6 +104,37 @@ def test_ffn_validation_and_workspace():
     assert l.moe_expert_ffn(p, None, 1, p, p, p, 8, 7168, 2048, 64, 1, p, p, 16, None) == 3   # small ws
     assert l.moe_expert_ffn(p, None, 1, p, p, p, 8, 7168, 2048, 64, 1, p, None, 1 << 30, None) == 3
     assert l.moe_expert_ffn(p, None, 1, p, p, p, 8000, 256, 64, 64, 0, p, p, 1 << 30, None) == 2
+
+
+def test_fp8_validation_and_workspace():
+    l = moe.lib()
+    p = ctypes.c_void_p(256)
+    f = ctypes.cast(p, ctypes.POINTER(ctypes.c_float))
+    # quantiser: (x, rows, cols, dtype, codes, scales, stream)
+    assert l.moe_quantize_e4m3(p, 4, 100, 1, p, f, None) == 1        # cols % 128
+    assert l.moe_quantize_e4m3(p, 4, 256, 7, p, f, None) == 1        # bad dtype
+    assert l.moe_quantize_e4m3(None, 4, 256, 1, p, f, None) == 1     # NULL x
+    assert l.moe_quantize_e4m3(ctypes.c_void_p(8), 4, 256, 1, p, f, None) == 1   # unaligned
+    assert l.moe_quantize_e4m3(None, 0, 256, 1, None, None, None) == 0           # no rows: no-op
+    # FFN: workspace = h in float32, h codes, h scales (each 256-byte aligned)
+    assert l.moe_expert_ffn_fp8_workspace_size(8, 7168, 2048, 4096) == \
+        4096 * 2048 * 4 + 4096 * 2048 + 4096 * 16 * 4
+    assert l.moe_expert_ffn_fp8_workspace_size(8, 7168 + 256, 2048, 4096) == 0   # hidden % 512
+    assert l.moe_expert_ffn_fp8_workspace_size(8, 7168, 2048 + 128, 4096) == 0   # inter % 256
+    assert l.moe_expert_ffn_fp8_workspace_size(2000, 7168, 2048, 4096) == 0      # E_loc > 1024
+    W = (p, 1 << 30, None)
+    args = lambda **kw: [kw.get("x", p), kw.get("xs", f), kw.get("ri", None), kw.get("div", 1),
+                         kw.get("off", p), kw.get("wg", p), kw.get("wgs", f), kw.get("wd", p),
+                         kw.get("wds", f), kw.get("nloc", 8), kw.get("d", 7168), kw.get("I", 2048),
+                         kw.get("cap", 64), kw.get("o", p)]
+    assert l.moe_expert_ffn_fp8(*args(d=7000), *W) == 2
+    assert l.moe_expert_ffn_fp8(*args(off=None), *W) == 1
+    assert l.moe_expert_ffn_fp8(*args(wgs=None), *W) == 1
+    assert l.moe_expert_ffn_fp8(*args(ri=p, div=0), *W) == 1
+    assert l.moe_expert_ffn_fp8(*args(o=None), *W) == 1
+    assert l.moe_expert_ffn_fp8(*args(x=ctypes.c_void_p(264)), *W) == 1          # unaligned codes
+    assert l.moe_expert_ffn_fp8(*args(), p, 16, None) == 3                       # small workspace
+    assert l.moe_expert_ffn_fp8(*args(cap=300000), *W) == 2                      # h offsets >= 2^31
 
 
 def test_combine_validation():
