@@ -71,22 +71,30 @@ def calibrate_copy(mb, torch):
                       "read_plus_write_gbs": 2 * n / (us[2] * 1e-6) / 1e9}))
 
 
-FFN_SOURCES = ["expert_routing_grouped_amd/csrc/ffn.hip", "expert_routing_grouped_amd/csrc/device_common.h",
-               "expert_routing_grouped_amd/csrc/launch.h"]
-TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_ep_ffn_traffic.md")
+_CSRC = "expert_routing_grouped_amd/csrc/"
+# Committed rocprofv3 counter records: workload -> (the sources of its FFN kernels, record file).
+TRAFFIC_RECORDS = {
+    "decode_ep": ([_CSRC + "ffn.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
+                  os.path.join(ROOT, "profiles", "decode_ep_ffn_traffic.md")),
+    "decode_ep_fp8": ([_CSRC + "ffn_fp8.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
+                      os.path.join(ROOT, "profiles", "decode_ep_fp8_ffn_traffic.md")),
+}
 
 
 def measured_traffic(workload):
-    """HBM bytes per moe_expert_ffn call from the committed rocprofv3 counter summary,
-    or None when the GEMM sources changed since the counters were taken."""
+    """HBM bytes per FFN call from the committed rocprofv3 counter summary of this
+    workload, or None when there is none or the kernel sources changed since."""
     import hashlib
+    if workload not in TRAFFIC_RECORDS:
+        return None
+    sources, record = TRAFFIC_RECORDS[workload]
     try:
         rec = None
-        for line in open(TRAFFIC_RECORD):
+        for line in open(record):
             if line.startswith("traffic-record: "):
                 rec = json.loads(line[len("traffic-record: "):])
         h = hashlib.sha256()
-        for f in FFN_SOURCES:
+        for f in sources:
             with open(os.path.join(ROOT, f), "rb") as fh:
                 h.update(fh.read())
     except (OSError, ValueError):

@@ -69,35 +69,62 @@ __device__ __forceinline__ uint32_t e4m3_code(float q) {
 
 // ---------------------------------------------------------------- quantiser
 
-// One wavefront per (row, 128-feature block), two values per lane; the row
-// count is rows, or min(rows, *rows_dev) when rows_dev is given.
+// A wavefront takes 4 consecutive blocks of one row (512 values): lane l
+// holds 8 values of block l / 16, and the block's maximum is reduced over its
+// 16 lanes. Lanes past the row's last block do nothing. The row count is
+// rows, or min(rows, *rows_dev) when rows_dev is given.
 template <bool BF16_IN>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* in, int rows, const int* rows_dev,
                                                            int cols, uint8_t* codes, float* scales) {
   int n = rows;
   if (rows_dev) n = min(n, max(0, *rows_dev));
   const int nb = cols / kQBlock;
-  const long total = (long)n * nb;
+  const int groups = (nb + 3) / 4;
+  const long total = (long)n * groups;
   const int lane = threadIdx.x & 63;
   const long stride = (long)gridDim.x * 4;
   for (long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6); w < total; w += stride) {
-    const long r = w / nb;
-    const int b = (int)(w - r * nb);
-    const size_t pair = ((size_t)r * cols + (size_t)b * kQBlock) / 2 + lane;   // values 2 * pair, +1
-    float v0, v1;
-    if (BF16_IN) {
-      const uint32_t p = ((const uint32_t*)in)[pair];
-      v0 = bf16_lo(p);
-      v1 = bf16_hi(p);
+    const int r = (int)(w / groups);
+    const int b = (int)(w - (long)r * groups) * 4 + (lane >> 4);
+    const bool active = b < nb;
+    const size_t first = (size_t)r * cols + (size_t)b * kQBlock + (lane & 15) * 8;   // of 8 values
+    float v[8];
+    if (active) {
+      if (BF16_IN) {
+        const u32x4_t p = *(const u32x4_t*)((const uint16_t*)in + first);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[2 * j] = bf16_lo(p[j]);
+          v[2 * j + 1] = bf16_hi(p[j]);
+        }
+      } else {
+        const f32x4_t p0 = *(const f32x4_t*)((const float*)in + first);
+        const f32x4_t p1 = *(const f32x4_t*)((const float*)in + first + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[j] = p0[j];
+          v[4 + j] = p1[j];
+        }
+      }
     } else {
-      const float2 p = ((const float2*)in)[pair];
-      v0 = p.x;
-      v1 = p.y;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
     }
-    const float amax = wave_max_f32(fmaxf(fabsf(v0), fabsf(v1)));
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, MOE_WAVE));
+    if (!active) continue;
     const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-    ((uint16_t*)codes)[pair] = (uint16_t)(e4m3_code(v0 / s) | (e4m3_code(v1 / s) << 8));
-    if (lane == 0) scales[(size_t)r * nb + b] = s;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo |= e4m3_code(v[j] / s) << (8 * j);
+      hi |= e4m3_code(v[4 + j] / s) << (8 * j);
+    }
+    *(uint2*)(codes + first) = make_uint2(lo, hi);
+    if ((lane & 15) == 0) scales[(size_t)r * nb + b] = s;
   }
 }
 
@@ -479,8 +506,11 @@ hipError_t launch_fp8_gemm(const F8Args& g, hipStream_t s) {
 
 inline size_t f8_align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int quantize_grid(long blocks) {
-  return (int)std::max<long>(1, std::min<long>((blocks + 3) / 4, (long)f8_cu_count() * 8));
+// Workgroups of 4 wavefronts for rows x ceil(cols / 512) wavefront items, at
+// most max_per_cu per CU (the rest loop).
+int quantize_grid(long rows, int cols, int max_per_cu) {
+  const long items = rows * ((cols / kQBlock + 3) / 4);
+  return (int)std::max<long>(1, std::min<long>((items + 3) / 4, (long)f8_cu_count() * max_per_cu));
 }
 
 }  // namespace
@@ -488,7 +518,7 @@ int quantize_grid(long blocks) {
 hipError_t launch_quantize_rows(const void* x, int rows, int cols, bool bf16_in, uint8_t* codes, float* scales,
                                 hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  const int grid = quantize_grid((long)rows * (cols / kQBlock));
+  const int grid = quantize_grid(rows, cols, 16);
   if (bf16_in)
     hipLaunchKernelGGL(quantize_rows_kernel<true>, dim3(grid), dim3(256), 0, s, x, rows, nullptr, cols, codes, scales);
   else
@@ -516,7 +546,9 @@ hipError_t launch_ffn_fp8(const FfnFp8Args& a, hipStream_t s) {
             (const uint8_t*)a.w_down, a.w_down_scales, d, I, I, a.o_sorted, d};
   hipError_t err = launch_fp8_gemm<2, 4, true>(g1, s);
   if (err != hipSuccess) return err;
-  const int grid = quantize_grid((long)a.capacity * (I / kQBlock));
+  // h has offsets[E_loc] rows, known on the device only: one workgroup per CU
+  // covers a decode batch in one pass and loops over larger ones.
+  const int grid = quantize_grid(a.capacity, I, 1);
   hipLaunchKernelGGL(quantize_rows_kernel<false>, dim3(grid), dim3(256), 0, s, (const void*)h, a.capacity,
                      a.offsets + a.num_local, I, hq, hs);
   err = hipGetLastError();
