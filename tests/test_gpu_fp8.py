@@ -84,10 +84,20 @@ def test_quantize_no_rows():
 
 # ------------------------------------------------------------------ FFN
 
-def fp8_weights(rng, nloc, d, I, scale=0.05):
-    wgu = (rng.standard_normal((nloc, 2 * I, d)) * scale).astype(np.float32)
-    wd = (rng.standard_normal((nloc, d, I)) * scale).astype(np.float32)
-    return W.quantize_e4m3_blocks(wgu, 128) + W.quantize_e4m3_blocks(wd, 128)
+def fp8_weights(rng, nloc, d, I, scale=0.05, distinct=None):
+    """E4M3 weights with 128 x 128 block scales; with `distinct`, that many random experts
+    repeated in turn (cheap inputs for many local experts)."""
+    n = nloc if distinct is None else distinct
+    wgu = (rng.standard_normal((n, 2 * I, d)) * scale).astype(np.float32)
+    wd = (rng.standard_normal((n, d, I)) * scale).astype(np.float32)
+    out = W.quantize_e4m3_blocks(wgu, 128) + W.quantize_e4m3_blocks(wd, 128)
+    if n == nloc:
+        return out
+    idx = np.arange(nloc) % n
+    return tuple(np.ascontiguousarray(a[idx]) for a in out)
+
+
+SENTINEL = 0x7FC1   # a bf16 NaN pattern that no output row holds
 
 
 def run_ffn(xq, xs, sa, k, offsets, wts, I, cap):
@@ -97,9 +107,12 @@ def run_ffn(xq, xs, sa, k, offsets, wts, I, cap):
     ri = None if sa is None else dev(np.asarray(sa, np.int32))
     need = moe.ffn_fp8_workspace_size(nloc, d, I, cap)
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    o_buf = dev(np.full((cap, d), SENTINEL, np.uint16))
+    if sa is not None:   # token rows: pad the row index to the capacity
+        ri = dev(np.concatenate([np.asarray(sa, np.int32), np.zeros(max(0, cap - len(sa)), np.int32)]))
     o = moe.moe_expert_ffn_fp8(dev(xq), dev(xs), dev(np.asarray(offsets, np.int32)), dev(wgq), dev(wgs),
                                dev(wdq), dev(wds), row_index=ri, row_index_div=k, row_capacity=cap,
-                               workspace=ws)
+                               o_sorted=o_buf, workspace=ws)
     torch.cuda.synchronize()
     # The workspace holds h (float32, [cap, I]), then its codes and scales, each
     # region 256-byte aligned.
@@ -113,7 +126,7 @@ def run_ffn(xq, xs, sa, k, offsets, wts, I, cap):
     return to_host(o), h, hq, hs
 
 
-def check_ffn(counts, d, I, k, seed, permuted=False):
+def check_ffn(counts, d, I, k, seed, permuted=False, spare_rows=0, distinct=None):
     rng = np.random.default_rng(seed)
     counts = np.asarray(counts)
     nloc, M = counts.size, int(counts.sum())
@@ -122,14 +135,17 @@ def check_ffn(counts, d, I, k, seed, permuted=False):
     x = rng.standard_normal((T, d)).astype(np.float32)
     xq, xs = F.quantize_rows(x)
     sa = rng.permutation(T * k)[:M]                     # distinct assignments t * k + j
-    wts = fp8_weights(rng, nloc, d, I)
-    print(f"ffn_fp8 counts={counts.tolist()} d={d} I={I} k={k} permuted={permuted}", flush=True)
+    wts = fp8_weights(rng, nloc, d, I, distinct=distinct)
+    print(f"ffn_fp8 experts={nloc} rows={M} d={d} I={I} k={k} permuted={permuted} spare={spare_rows}",
+          flush=True)
+    cap = max(M, 1) + spare_rows
     if permuted:      # x given as permuted rows (row_index NULL)
-        rows = sa // k
-        g_o, g_h, g_hq, g_hs = run_ffn(xq[rows], xs[rows], None, 1, offsets, wts, I, max(M, 1))
+        rows = np.concatenate([sa // k, np.zeros(cap - M, np.int64)])
+        g_o, g_h, g_hq, g_hs = run_ffn(xq[rows], xs[rows], None, 1, offsets, wts, I, cap)
     else:
-        g_o, g_h, g_hq, g_hs = run_ffn(xq, xs, sa, k, offsets, wts, I, max(M, 1))
+        g_o, g_h, g_hq, g_hs = run_ffn(xq, xs, sa, k, offsets, wts, I, cap)
     o, hq, hs = F.expert_ffn_fp8(xq, xs, sa, k, offsets, *wts, I)
+    assert (g_o[M:] == SENTINEL).all()   # rows past offsets[E_loc] are not written
     if M == 0:
         return
     # h: float32 from the kernel's accumulation vs the oracle's float64
@@ -170,6 +186,17 @@ def test_ffn_fp8_permuted_rows():
 
 def test_ffn_fp8_no_rows():
     check_ffn([0, 0, 0], 512, 256, 2, seed=4)
+
+
+def test_ffn_fp8_capacity_above_rows():
+    check_ffn([20, 0, 45], 1024, 256, 4, seed=5, spare_rows=77)
+    check_ffn([20, 0, 45], 1024, 256, 4, seed=6, spare_rows=77, permuted=True)
+
+
+def test_ffn_fp8_1024_local_experts():
+    rng = np.random.default_rng(8)
+    counts = rng.integers(0, 4, 1024) * (rng.random(1024) < 0.3)
+    check_ffn(counts.tolist(), 512, 256, 8, seed=9, distinct=7)
 
 
 # ------------------------------------------------------------------ layer at the decode_ep_fp8 size
