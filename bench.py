@@ -318,7 +318,7 @@ def cpu_baseline(inp, wl, min_seconds=10.0):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU's share of the layer; run it with --gpus 1 "
+        print("bench.py measures one GPU's share of the layer; run it with --gpus 1 "
               "(no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     import torch
