@@ -217,6 +217,11 @@ def test_layer_decode_ep_fp8_sampled():
                   w_gate_up_scales=dev(inp.w_gate_up_scale), w_down_scales=dev(inp.w_down_scale))
     torch.cuda.synchronize()
     g = {k: to_host(v) for k, v in layer.buf.items() if k != "workspace"}
+    # a second pass gives the same bits (no atomics, fixed summation order)
+    y2 = to_host(layer.forward(dev(inp.scores), dev(inp.x), dev(inp.w_gate_up), dev(inp.w_down),
+                               w_gate_up_scales=dev(inp.w_gate_up_scale),
+                               w_down_scales=dev(inp.w_down_scale)))
+    assert np.array_equal(y2, g["y"])
     ids, w = oracle.route(inp.scores, wl.top_k, wl.num_groups, wl.topk_groups, wl.score_mode,
                           wl.renormalize)
     counts, offsets, sa, pos = oracle.dispatch(ids, wl.expert_begin, wl.num_local)
