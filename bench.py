@@ -76,6 +76,8 @@ _CSRC = "expert_routing_grouped_amd/csrc/"
 TRAFFIC_RECORDS = {
     "decode_ep": ([_CSRC + "ffn.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
                   os.path.join(ROOT, "profiles", "decode_ep_ffn_traffic.md")),
+    "decode_tp": ([_CSRC + "ffn.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
+                  os.path.join(ROOT, "profiles", "decode_tp_ffn_traffic.md")),
     "decode_ep_fp8": ([_CSRC + "ffn_fp8.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
                       os.path.join(ROOT, "profiles", "decode_ep_fp8_ffn_traffic.md")),
 }
