@@ -17,6 +17,10 @@ def test_capacity_of_the_pages_worked_example():
     assert oracle.expert_capacity(5600, 16, 896, 1) == 100
     assert oracle.expert_capacity(5600, 16, 896, "1.5") == 150
     assert oracle.expert_capacity(10, 3, 7, 1) == 5          # ceil(30 / 7)
+    # c is an exact decimal: 1.1 * 400 * 1 / 8 is 55, while binary floating point
+    # lands just above it (55.00000000000001) and its ceiling would be 56
+    assert 1.1 * 400 * 1 / 8 > 55
+    assert oracle.expert_capacity(400, 1, 8, "1.1") == 55
 
 
 def test_hand_example():

@@ -99,6 +99,17 @@ def test_remap_picks_replicas_of_the_right_expert(page_sim):
     assert np.array_equal(flat[phys], ids[:500])
 
 
+def test_remap_by_hand():
+    # 2 nodes x 1 GPU x 2 slots: GPU 0 = [A, B], GPU 1 = [A, C] with A = 0, B = 1, C = 2.
+    # Token [A, C]: A has no replica on a node in use yet -> the lowest node (slot 0);
+    # C only lives on node 1 (slot 3). Token [C, A]: C -> slot 3 puts node 1 in use,
+    # so A takes its replica there (slot 2). Token [B, A]: B -> slot 1 (node 0), then
+    # A on node 0 (slot 0).
+    gpus = [[0, 1], [0, 2]]
+    ids = np.array([[0, 2], [2, 0], [1, 0]])
+    assert eplb.remap(ids, gpus, 2).tolist() == [[0, 3], [3, 2], [1, 0]]
+
+
 # ---- the library's native planner (host code: runs without a GPU) against the oracle
 
 def _native():
