@@ -133,3 +133,26 @@ def test_random_fp8_ffn(seed):
     e_max, e_mean = np.abs(got - ref).max() / scale, np.abs(got - ref).mean() / scale
     print(f"  rel_err o={e_max:.2e} (mean {e_mean:.2e})", flush=True)
     assert e_max <= 2e-2 and e_mean <= 2e-3
+
+
+@pytest.mark.parametrize("d,I", [(256, 64), (1024, 64)])
+def test_layer_1000_local_experts(d, I):
+    """The largest local expert count of the whole layer (1000, the dispatch's limit): streaming
+    path (d = 256) and the shared-activation path for narrow experts (d = 1024, I = 64)."""
+    wl = W.Workload("local1000", T=512, E=1000, top_k=8, num_groups=8, topk_groups=4, score_mode="raw",
+                    renormalize=True, bias_std=1.0, hidden=d, inter=I, expert_begin=0, num_local=1000,
+                    dtype="bf16", seed=d + I)
+    print(f"{wl.name}: T={wl.T} E={wl.E} local=1000 d={d} I={I}", flush=True)
+    inp = W.generate(wl)
+    g = run_layer(wl, inp, True)
+    ref = oracle.layer(inp.scores, inp.x, inp.w_gate_up, inp.w_down, top_k=wl.top_k,
+                       num_groups=wl.num_groups, topk_groups=wl.topk_groups, score_mode="raw",
+                       renormalize=True, expert_begin=0, num_local=1000)
+    M = int(ref["offsets"][-1])
+    assert np.array_equal(g["topk_ids"], ref["topk_ids"])
+    assert np.array_equal(g["offsets"], ref["offsets"])
+    assert np.array_equal(g["sorted_assign"][:M], ref["sorted_assign"])
+    e_o = rel_err(oracle.bf16_bits_to_f64(g["o_sorted"][:M]), ref["o_sorted"])
+    e_y = rel_err(oracle.bf16_bits_to_f64(g["y"]), ref["y"])
+    print(f"  M={M} hit={int((ref['counts'] > 0).sum())} rel_err o={e_o:.2e} y={e_y:.2e}", flush=True)
+    assert e_o <= 2e-2 and e_y <= 2e-2
