@@ -238,6 +238,7 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
                    ffn_bytes_mb=acc["bytes"] / 1e6,
                    ffn_tflops=acc["flops"] / t_ffn / 1e12, ffn_gbs=acc["bytes"] / t_ffn / 1e9,
                    layer_tflops=acc["flops"] / (ms_per_step * 1e-3) / 1e12)
+        res["ffn_hbm_traffic_bytes"] = measured_traffic(wl.name)   # committed counter record, or None
         ai = acc["flops"] / acc["bytes"]
         res["mfma_peak_tflops"] = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
         res["ffn_bound"] = "mfma" if ai > res["mfma_peak_tflops"] * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
