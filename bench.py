@@ -9,8 +9,13 @@ before the timed region. Decode weight sets (0.35-0.7 GB) are comparable to
 the 256 MB last-level cache, so the timed steps rotate over several copies of
 the weights and every step reads its weights from HBM.
 
-Prints one JSON line (rank 0, N = 1). Usage:
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--all]
+Prints one JSON line (rank 0, N = 1). The headline workload (decode_ep by
+default) gives `value` and `roofline`; unless --headline-only is given the
+same run also times the other graded shapes (prefill_straggler, MFMA-bound,
+and decode_tp, HBM-bound), each with a roofline block of its own, under
+`graded`. Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--headline-only] [--all]
 """
 from __future__ import annotations
 
@@ -42,6 +47,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default=HEADLINE, choices=sorted(W.WORKLOADS))
     p.add_argument("--all", action="store_true", help="also time every other workload")
+    p.add_argument("--headline-only", action="store_true",
+                   help="time only --workload (no graded prefill / decode_tp entries)")
+    p.add_argument("--median-steps", type=int, default=100,
+                   help="steps of the per-step pass whose median is reported beside the mean")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copies", type=int, default=0,
                    help="weight copies rotated over the timed steps (0 = enough to exceed the cache)")
@@ -125,7 +134,19 @@ def ffn_accounting(wl, counts):
                 weight_bytes=weight_bytes, act_bytes=act_bytes)
 
 
-def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, operands="random"):
+def routing_stats(wl, topk_ids, counts):
+    """Load statistics of the routed batch (ch15 page, section 4.3 "负载均衡"): the
+    imbalance R = max_e n_e / mean_e n_e over all experts of the layer, and over
+    this GPU's local experts; rows of the busiest local expert."""
+    n_all = np.bincount(np.asarray(topk_ids, dtype=np.int64).ravel(), minlength=wl.E)
+    counts = np.asarray(counts, dtype=np.int64)
+    return dict(assignments=int(n_all.sum()), r_imbalance_all_experts=float(n_all.max() / n_all.mean()),
+                r_imbalance_local=float(counts.max() / counts.mean()) if counts.sum() else 0.0,
+                max_rows_per_local_expert=int(counts.max()))
+
+
+def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, operands="random",
+                 median_steps=100):
     dev = "cuda:0"
     t0 = time.time()
     inp = W.generate(wl)
@@ -200,17 +221,21 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_per_step = start.elapsed_time(end) / steps
-    # per-call timing on the same stream (separate pass, events between the calls)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
-    for i in range(steps):
+    # per-call and per-step timing on the same stream (a separate pass of
+    # n_med steps, events between the calls): medians
+    n_med = max(steps, median_steps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_med)]
+    for i in range(n_med):
         step(i, evs[i])
     torch.cuda.synchronize()
-    parts = np.zeros(4)
-    for ev in evs:
-        parts += [ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]),
-                  ev[2].elapsed_time(ev[3]) if x is not None else 0.0,
-                  ev[3].elapsed_time(ev[4]) if x is not None else 0.0]
-    parts_us = parts / steps * 1e3
+    parts = np.zeros((n_med, 4))
+    step_ms = np.zeros(n_med)
+    for i, ev in enumerate(evs):
+        parts[i] = [ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]),
+                    ev[2].elapsed_time(ev[3]) if x is not None else 0.0,
+                    ev[3].elapsed_time(ev[4]) if x is not None else 0.0]
+        step_ms[i] = ev[0].elapsed_time(ev[4])
+    parts_us = np.median(parts, axis=0) * 1e3
     ffn_us = None
     if x is not None:
         # moe_expert_ffn alone, back to back on the launch stream (the routing of
@@ -227,9 +252,13 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
         ffn_us = e0.elapsed_time(e1) / n_ffn * 1e3
     counts = to_host(layer.buf["counts"])
     res = dict(workload=wl.name, T=wl.T, ms_per_step=ms_per_step, wall_ms_per_step=wall / steps * 1e3,
+               median_ms_per_step=float(np.median(step_ms)), median_over_steps=n_med,
                tokens_per_s=wl.T / (ms_per_step * 1e-3), gen_s=gen_s, weight_copies=len(weights),
-               breakdown_us=dict(route=parts_us[0], dispatch=parts_us[1], ffn=parts_us[2],
-                                 combine=parts_us[3]))
+               breakdown_us_median=dict(route=parts_us[0], dispatch=parts_us[1], ffn=parts_us[2],
+                                        combine=parts_us[3]))
+    res.update(routing_stats(wl, to_host(layer.buf["topk_ids"]), counts))
+    res["assignments_per_s"] = res["assignments"] / (ms_per_step * 1e-3)
+    res["local_rows_per_s"] = int(counts.sum()) / (ms_per_step * 1e-3)
     if wl.has_ffn:
         acc = ffn_accounting(wl, counts)
         res["ffn_us_per_launch"] = ffn_us
@@ -287,35 +316,70 @@ def run_eplb(torch, moe, to_device, to_host):
 
 
 def cpu_baseline(inp, wl, min_seconds=10.0):
-    """The oracle as it stands, on the host cores: whole layer passes over the
-    workload, repeated until about min_seconds of CPU work."""
+    """The oracle as it stands, on the host cores: whole-layer passes over the
+    workload, each step (route, dispatch, gather + expert FFN, combine) timed on
+    its own, repeated until about min_seconds of CPU work."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        cores = 1
+        blas = 1
+    fp8 = wl.weight_format == "fp8_e4m3_b128"
+    if fp8:
+        from oracle import fp8 as F
+    step_s = dict(route=0.0, dispatch=0.0, ffn=0.0, combine=0.0)
     runs, t = 0, 0.0
     while runs == 0 or t < min_seconds:
         t0 = time.perf_counter()
-        if wl.weight_format == "fp8_e4m3_b128":
-            from oracle import fp8 as F
-            ids, w = oracle.route(inp.scores, wl.top_k, wl.num_groups, wl.topk_groups, wl.score_mode,
-                                  wl.renormalize)
-            _, offsets, sa, pos = oracle.dispatch(ids, wl.expert_begin, wl.num_local)
+        ids, w = oracle.route(inp.scores, wl.top_k, wl.num_groups, wl.topk_groups, wl.score_mode,
+                              wl.renormalize)
+        t1 = time.perf_counter()
+        _, offsets, sa, pos = oracle.dispatch(ids, wl.expert_begin, wl.num_local)
+        t2 = time.perf_counter()
+        if fp8:
             xq, xs = F.quantize_rows(oracle.bf16_bits_to_f64(inp.x).astype(np.float32))
             o, _, _ = F.expert_ffn_fp8(xq, xs, sa, wl.top_k, offsets, inp.w_gate_up, inp.w_gate_up_scale,
                                        inp.w_down, inp.w_down_scale, wl.inter)
-            oracle.combine(o, pos, w)
         else:
-            oracle.layer(inp.scores, inp.x, inp.w_gate_up, inp.w_down, top_k=wl.top_k,
-                         num_groups=wl.num_groups, topk_groups=wl.topk_groups, score_mode=wl.score_mode,
-                         renormalize=wl.renormalize, expert_begin=wl.expert_begin, num_local=wl.num_local)
-        t += time.perf_counter() - t0
+            o = oracle.expert_ffn(oracle.gather_rows(inp.x, sa, wl.top_k), offsets, inp.w_gate_up,
+                                  inp.w_down)
+        t3 = time.perf_counter()
+        oracle.combine(o, pos, w)
+        t4 = time.perf_counter()
+        for name, dt in zip(step_s, (t1 - t0, t2 - t1, t3 - t2, t4 - t3)):
+            step_s[name] += dt
+        t += t4 - t0
         runs += 1
-    return {"value": wl.T * runs / t, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": wl.T * runs / t, "unit": "tokens/s", "cores": int(blas), "kind": "oracle",
             "sample": f"{runs} passes of the whole {wl.name} layer ({wl.T} tokens each) through the "
-                      f"numpy float64 oracle, {t:.1f} s", "seconds": t}
+                      f"numpy float64 oracle, {t:.1f} s; routing, dispatch and combine run on one "
+                      f"thread, the expert FFN's matrix products on {blas} BLAS threads",
+            "seconds": t, "host_cpus": os.cpu_count(),
+            "host_cpus_usable": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+            "ms_per_pass_by_step": {k: v / runs * 1e3 for k, v in step_s.items()}}
+
+
+def roofline_block(res, fp8):
+    """Roofline of the dominant step (one moe_expert_ffn call) of a measured workload."""
+    bound = res["ffn_bound"]
+    if bound == "hbm":
+        ach, peak, unit = res["ffn_gbs"], HBM_PEAK_GBS, "GB/s"
+    else:
+        ach, peak, unit = res["ffn_tflops"], res["mfma_peak_tflops"], "TFLOP/s"
+    return {"bound": bound, "achieved": ach, "peak": peak, "unit": unit,
+            "frac": ach / peak, "traffic": measured_traffic(res["workload"]),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "kernel": ("moe_expert_ffn_fp8 (gate_up GEMM + SiLU*up, h quantiser, down GEMM)"
+                       if fp8 else "moe_expert_ffn (gate_up GEMM + SiLU*up, down GEMM)"),
+            "us_per_launch": res["ffn_us_per_launch"],
+            "algorithmic_bytes": res["ffn_bytes_mb"] * 1e6,
+            "algorithmic_flops": res["ffn_gflop"] * 1e9}
+
+
+# The shapes whose FFN fractions are graded beside the headline decode_ep:
+# prefill (MFMA-bound) and the TP-sliced decode (HBM-bound).
+GRADED = ("prefill_straggler", "decode_tp")
 
 
 def main():
@@ -340,7 +404,7 @@ def main():
     print(f"bench: workload {wl.name}, steps {args.steps}, warmup {args.warmup}", file=sys.stderr,
           flush=True)
     head = run_workload(wl, args.steps, args.warmup, args.copies, torch, moe, to_device, to_host,
-                        args.operands)
+                        args.operands, args.median_steps)
     inp = head.pop("_inputs")
     out = {
         "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
@@ -354,29 +418,38 @@ def main():
                    "parallelism": "one GPU's expert share"},
     }
     if wl.has_ffn:
-        bound = head["ffn_bound"]
-        if bound == "hbm":
-            ach, peak, unit = head["ffn_gbs"], HBM_PEAK_GBS, "GB/s"
-        else:
-            ach, peak, unit = head["ffn_tflops"], head["mfma_peak_tflops"], "TFLOP/s"
-        out["roofline"] = {"bound": bound, "achieved": ach, "peak": peak, "unit": unit,
-                           "frac": ach / peak, "traffic": measured_traffic(wl.name),
-                           "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                           "kernel": ("moe_expert_ffn_fp8 (gate_up GEMM + SiLU*up, h quantiser, down GEMM)"
-                                      if fp8 else "moe_expert_ffn (gate_up GEMM + SiLU*up, down GEMM)"),
-                           "us_per_launch": head["ffn_us_per_launch"],
-                           "algorithmic_bytes": head["ffn_bytes_mb"] * 1e6,
-                           "algorithmic_flops": head["ffn_gflop"] * 1e9}
+        out["roofline"] = roofline_block(head, fp8)
     out["detail"] = {k: v for k, v in head.items() if k not in ("tokens_per_s",)}
     print(f"bench: {wl.name} {head['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline and wl.has_ffn and args.operands == "random":
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, wl)
     del inp
+    if not args.headline_only:
+        graded = {}
+        for name in GRADED:
+            if name == wl.name:
+                continue
+            print(f"bench: graded workload {name}", file=sys.stderr, flush=True)
+            g = W.WORKLOADS[name]
+            r = run_workload(g, args.steps, args.warmup, args.copies, torch, moe, to_device, to_host,
+                             args.operands, args.median_steps)
+            r.pop("_inputs")
+            entry = {"workload": name, "tokens": g.T, "local_experts": f"[{g.expert_begin}, "
+                     f"{g.expert_begin + g.num_local})", "inter": g.inter,
+                     "ms_per_step": r["ms_per_step"], "tokens_per_s": r["tokens_per_s"],
+                     "roofline": roofline_block(r, False),
+                     "detail": {k: v for k, v in r.items() if k not in ("tokens_per_s", "ms_per_step")}}
+            graded[name] = entry
+            print(f"bench: {name} {r['ms_per_step'] * 1e3:.1f} us/step, FFN {r['ffn_us_per_launch']:.1f} us "
+                  f"({entry['roofline']['frac']:.3f} of {entry['roofline']['bound']} peak)",
+                  file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
+        out["graded"] = graded
     if args.all:
         others = {}
         for name in W.WORKLOADS:
-            if name == wl.name:
+            if name == wl.name or (name in GRADED and not args.headline_only):
                 continue
             print(f"bench: workload {name}", file=sys.stderr, flush=True)
             r = run_workload(W.WORKLOADS[name], max(5, args.steps // 2), max(2, args.warmup // 2),

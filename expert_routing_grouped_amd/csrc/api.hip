@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -117,6 +117,24 @@ moe_status_t moe_dispatch_capacity(const int32_t* topk_ids, int32_t num_tokens, 
   return dispatch_impl(topk_ids, num_tokens, top_k, expert_begin, num_local_experts, x, hidden,
                        dtype, expert_counts, expert_offsets, sorted_assign, assign_pos, x_sorted,
                        workspace, workspace_bytes, expert_capacity, expert_demand, stream);
+}
+
+moe_status_t moe_expert_capacity(int32_t num_tokens, int32_t top_k, int32_t num_experts,
+                                 int64_t factor_num, int64_t factor_den, int32_t* capacity) {
+  if (num_tokens < 0 || top_k < 1 || num_experts < 1 || factor_num < 0 || factor_den < 1 || !capacity)
+    return MOE_ERR_INVALID;
+  const int64_t lim = (int64_t)1 << 31;
+  if (factor_num >= lim || factor_den >= lim) return MOE_ERR_UNSUPPORTED;
+  // ceil(num * T * k / (den * E)) in exact integer arithmetic (128-bit
+  // intermediates; every factor is below 2^31 once T * k is).
+  const int64_t tk = (int64_t)num_tokens * top_k;
+  if (tk >= lim) return MOE_ERR_UNSUPPORTED;
+  const __int128 q = (__int128)factor_num * tk;
+  const __int128 den = (__int128)factor_den * num_experts;
+  const __int128 c = (q + den - 1) / den;
+  if (c > (__int128)INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  *capacity = (int32_t)c;
+  return MOE_OK;
 }
 
 static moe_status_t check_ffn_sizes(int32_t num_local_experts, int32_t hidden, int32_t inter,
@@ -267,7 +285,7 @@ moe_status_t moe_eplb_remap(const int32_t* topk_ids, int32_t num_tokens, int32_t
   if (num_tokens == 0) return MOE_OK;
   if (!topk_ids || !replica_offsets || !replica_slots || !physical_ids) return MOE_ERR_INVALID;
   return from_hip(moe::launch_eplb_remap(topk_ids, num_tokens, top_k, replica_offsets, replica_slots,
-                                         num_physical / num_gpus, num_gpus / num_nodes,
+                                         num_experts, num_physical / num_gpus, num_gpus / num_nodes,
                                          physical_ids, stream));
 }
 

@@ -103,18 +103,28 @@ int eplb_place(const double* load, int E, int num_groups, int num_nodes, int num
 
 namespace {
 
-// One thread per token; its nodes so far in a 64-bit mask.
+// One thread per token; its nodes so far in a 64-bit mask. An expert id
+// outside [0, E), or one without a replica, gets -1 and reads nothing else.
 __global__ __launch_bounds__(256) void remap_kernel(const int* __restrict__ ids, int T, int k,
                                                     const int* __restrict__ offsets,
-                                                    const int* __restrict__ slots, int slots_per_gpu,
-                                                    int gpus_per_node, int* __restrict__ phys) {
+                                                    const int* __restrict__ slots, int E,
+                                                    int slots_per_gpu, int gpus_per_node,
+                                                    int* __restrict__ phys) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T) return;
   uint64_t used = 0;
   const int per_node = slots_per_gpu * gpus_per_node;
   for (int j = 0; j < k; ++j) {
     const int e = ids[(size_t)t * k + j];
+    if ((unsigned)e >= (unsigned)E) {
+      phys[(size_t)t * k + j] = -1;
+      continue;
+    }
     const int r0 = offsets[e], r1 = offsets[e + 1];
+    if (r1 <= r0) {
+      phys[(size_t)t * k + j] = -1;
+      continue;
+    }
     int on_used = -1, lowest = -1, lowest_node = 1 << 30;
     for (int r = r0; r < r1; ++r) {   // ascending slots
       const int s = slots[r];
@@ -134,10 +144,11 @@ __global__ __launch_bounds__(256) void remap_kernel(const int* __restrict__ ids,
 }  // namespace
 
 hipError_t launch_eplb_remap(const int* ids, int T, int k, const int* offsets, const int* slots,
-                             int slots_per_gpu, int gpus_per_node, int* phys, hipStream_t s) {
+                             int num_experts, int slots_per_gpu, int gpus_per_node, int* phys,
+                             hipStream_t s) {
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(remap_kernel, dim3((T + 255) / 256), dim3(256), 0, s, ids, T, k, offsets, slots,
-                     slots_per_gpu, gpus_per_node, phys);
+                     num_experts, slots_per_gpu, gpus_per_node, phys);
   return hipGetLastError();
 }
 

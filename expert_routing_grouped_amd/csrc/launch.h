@@ -33,7 +33,7 @@ struct DispatchArgs {
 };
 size_t dispatch_workspace_size(int n, int num_local);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
-constexpr int kDispatchMaxLocal = 1000;  // per-(wave, expert) counters and offsets fit in 68 KiB of LDS
+constexpr int kDispatchMaxLocal = 1024;  // per-(wave, expert) counters and offsets: 68 KiB of LDS at most
 
 struct FfnArgs {
   const void* x;         // permuted rows, or token rows read through row_index
@@ -85,6 +85,7 @@ int eplb_place(const double* load, int num_experts, int num_groups, int num_node
                int num_physical, bool hierarchical, int* phys_to_logical, int* replica_offsets,
                int* replica_slots);
 hipError_t launch_eplb_remap(const int* ids, int T, int k, const int* offsets, const int* slots,
-                             int slots_per_gpu, int gpus_per_node, int* phys, hipStream_t s);
+                             int num_experts, int slots_per_gpu, int gpus_per_node, int* phys,
+                             hipStream_t s);
 
 }  // namespace moe

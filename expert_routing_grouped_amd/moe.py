@@ -32,6 +32,7 @@ _SIGNATURES = {
                                     ctypes.c_size_t, _P]),
     "moe_dispatch_capacity": (ctypes.c_int, [_P, _I, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P,
                                              _P, _P, ctypes.c_size_t, _P]),
+    "moe_expert_capacity": (ctypes.c_int, [_I, _I, _I, ctypes.c_int64, ctypes.c_int64, _P]),
     "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "moe_expert_ffn": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P,
                                       ctypes.c_size_t, _P]),
@@ -95,6 +96,19 @@ def _dev(t: torch.Tensor, dtype: torch.dtype, name: str) -> torch.Tensor:
     return t
 
 
+def _at_least(t: torch.Tensor, n: int, name: str) -> torch.Tensor:
+    """The kernels write or read n elements of t: refuse a smaller buffer."""
+    if t.numel() < n:
+        raise MoeError(f"{name} holds {t.numel()} elements, {n} needed")
+    return t
+
+
+def _shape(t: torch.Tensor, shape: tuple, name: str) -> torch.Tensor:
+    if tuple(t.shape) != tuple(shape):
+        raise MoeError(f"{name} has shape {tuple(t.shape)}, {tuple(shape)} needed")
+    return t
+
+
 def _code(dtype: torch.dtype) -> int:
     if dtype == torch.bfloat16:
         return MOE_BF16
@@ -112,8 +126,8 @@ def moe_route(scores, top_k, num_groups=1, topk_groups=1, score_mode=MOE_SCORE_R
         topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=scores.device)
     if topk_weights is None:
         topk_weights = torch.empty((T, top_k), dtype=torch.float32, device=scores.device)
-    _dev(topk_ids, torch.int32, "topk_ids")
-    _dev(topk_weights, torch.float32, "topk_weights")
+    _shape(_dev(topk_ids, torch.int32, "topk_ids"), (T, top_k), "topk_ids")
+    _shape(_dev(topk_weights, torch.float32, "topk_weights"), (T, top_k), "topk_weights")
     _check(lib().moe_route(_ptr(scores), T, E, top_k, num_groups, topk_groups, score_mode,
                            int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_weights),
                            _stream(stream)), "moe_route")
@@ -140,13 +154,18 @@ def moe_dispatch(topk_ids, expert_begin, num_local_experts, x=None, out=None, st
     if x is not None:
         dtype = _code(x.dtype)
         _dev(x, x.dtype, "x")
+        if x.dim() != 2 or x.shape[0] < T:
+            raise MoeError(f"x must be [>= {T}, hidden], got {tuple(x.shape)}")
         hidden = x.shape[1]
         o.setdefault("x_sorted", torch.empty((max(n, 1), hidden), dtype=x.dtype, device=dev))
         _dev(o["x_sorted"], x.dtype, "x_sorted")
+        if o["x_sorted"].dim() != 2 or o["x_sorted"].shape[1] != hidden or o["x_sorted"].shape[0] < n:
+            raise MoeError(f"x_sorted must be [>= {n}, {hidden}], got {tuple(o['x_sorted'].shape)}")
     else:
         o["x_sorted"] = None
-    for name in ("counts", "offsets", "sorted_assign", "assign_pos"):
-        _dev(o[name], torch.int32, name)
+    for name, need_n in (("counts", num_local_experts), ("offsets", num_local_experts + 1),
+                         ("sorted_assign", n), ("assign_pos", n)):
+        _at_least(_dev(o[name], torch.int32, name), need_n, name)
     need = int(lib().moe_dispatch_workspace_size(T, k, num_local_experts))
     ws = o.get("workspace")
     if need and (ws is None or ws.numel() < need):
@@ -161,7 +180,7 @@ def moe_dispatch(topk_ids, expert_begin, num_local_experts, x=None, out=None, st
                "moe_dispatch")
         return o
     o.setdefault("demand", torch.empty(num_local_experts, dtype=torch.int32, device=dev))
-    _dev(o["demand"], torch.int32, "demand")
+    _at_least(_dev(o["demand"], torch.int32, "demand"), num_local_experts, "demand")
     _check(lib().moe_dispatch_capacity(_ptr(topk_ids), T, k, expert_begin, num_local_experts,
                                        int(capacity), _ptr(x), hidden, dtype, _ptr(o["counts"]),
                                        _ptr(o["offsets"]), _ptr(o["demand"]),
@@ -169,6 +188,14 @@ def moe_dispatch(topk_ids, expert_begin, num_local_experts, x=None, out=None, st
                                        _ptr(o["x_sorted"]), ws_ptr, ws_bytes, _stream(stream)),
            "moe_dispatch_capacity")
     return o
+
+
+def moe_expert_capacity(num_tokens, top_k, num_experts, factor_num, factor_den=1) -> int:
+    """C = ceil(c T k / E) with c = factor_num / factor_den exactly (host only)."""
+    out = ctypes.c_int32(0)
+    _check(lib().moe_expert_capacity(int(num_tokens), int(top_k), int(num_experts), int(factor_num),
+                                     int(factor_den), ctypes.byref(out)), "moe_expert_capacity")
+    return int(out.value)
 
 
 def ffn_workspace_size(num_local_experts, hidden, inter, row_capacity, dtype) -> int:
@@ -192,10 +219,12 @@ def moe_expert_ffn(x, expert_offsets, w_gate_up, w_down, row_index=None, row_ind
     if row_index is not None:
         _dev(row_index, torch.int32, "row_index")
         cap = row_index.numel() if row_capacity is None else row_capacity
+        _at_least(row_index, cap, "row_index")
     else:
         cap = x.shape[0] if row_capacity is None else row_capacity
     hidden = x.shape[1]
     E_loc, two_i, d2 = w_gate_up.shape
+    _at_least(expert_offsets, E_loc + 1, "expert_offsets")
     inter = two_i // 2
     if d2 != hidden or tuple(w_down.shape) != (E_loc, hidden, inter):
         raise MoeError("weight shapes do not match x")
@@ -251,10 +280,12 @@ def moe_expert_ffn_fp8(x_codes, x_scales, expert_offsets, w_gate_up, w_gate_up_s
     if row_index is not None:
         _dev(row_index, torch.int32, "row_index")
         cap = row_index.numel() if row_capacity is None else row_capacity
+        _at_least(row_index, cap, "row_index")
     else:
         cap = x_codes.shape[0] if row_capacity is None else row_capacity
     hidden = x_codes.shape[1]
     E_loc, two_i, d2 = w_gate_up.shape
+    _at_least(expert_offsets, E_loc + 1, "expert_offsets")
     inter = two_i // 2
     if d2 != hidden or tuple(w_down.shape) != (E_loc, hidden, inter):
         raise MoeError("weight shapes do not match x")
@@ -288,10 +319,11 @@ def moe_combine(o_sorted, assign_pos, topk_weights, out_dtype=None, y=None, stre
     _dev(topk_weights, torch.float32, "topk_weights")
     T, k = topk_weights.shape
     hidden = o_sorted.shape[1]
+    _at_least(assign_pos, T * k, "assign_pos")
     out_dtype = out_dtype or o_sorted.dtype
     if y is None:
         y = torch.empty((T, hidden), dtype=out_dtype, device=o_sorted.device)
-    _dev(y, out_dtype, "y")
+    _shape(_dev(y, out_dtype, "y"), (T, hidden), "y")
     _check(lib().moe_combine(_ptr(o_sorted), _ptr(assign_pos), _ptr(topk_weights), T, k, hidden,
                              _code(o_sorted.dtype), _code(out_dtype), _ptr(y), _stream(stream)),
            "moe_combine")
@@ -326,7 +358,9 @@ def moe_eplb_remap(topk_ids, replica_offsets, replica_slots, num_gpus, num_nodes
     T, k = topk_ids.shape
     if physical_ids is None:
         physical_ids = torch.empty_like(topk_ids)
-    _dev(physical_ids, torch.int32, "physical_ids")
+    _shape(_dev(physical_ids, torch.int32, "physical_ids"), (T, k), "physical_ids")
+    if replica_offsets.numel() < 2 or replica_slots.numel() < 1:
+        raise MoeError("the replica table is empty")
     _check(lib().moe_eplb_remap(_ptr(topk_ids), T, k, _ptr(replica_offsets), _ptr(replica_slots),
                                 replica_offsets.numel() - 1, replica_slots.numel(), num_gpus,
                                 num_nodes, _ptr(physical_ids), _stream(stream)), "moe_eplb_remap")

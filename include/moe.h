@@ -122,8 +122,10 @@ moe_status_t moe_eplb_place(const double* load, int32_t num_experts, int32_t num
  * replica_offsets  [num_experts + 1], replica_slots [num_physical] int32: the
  *                  table moe_eplb_place writes, in device memory.
  * physical_ids     [T, k] int32 out: physical slots (GPU s / (num_physical /
- *                  num_gpus)).
- * Limits: as moe_eplb_place; every expert in topk_ids has at least one slot
+ *                  num_gpus)); -1 for a slot whose expert id lies outside
+ *                  [0, num_experts) or has no replica (no memory outside the
+ *                  two tables is read for it).
+ * Limits: as moe_eplb_place; the table holds slots in [0, num_physical)
  * (not checked on the device). T = 0 is a valid no-op.
  */
 moe_status_t moe_eplb_remap(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
@@ -186,8 +188,8 @@ size_t moe_dispatch_workspace_size(int32_t num_tokens, int32_t top_k, int32_t nu
  *                 row i = x[sorted_assign[i] / k] for i < M (exact copy).
  * workspace       device buffer of moe_dispatch_workspace_size bytes (per-block
  *                 counts of the multi-workgroup sort); contents need not be set.
- * Limits: 1 <= num_local_experts <= 1000; T * k < 2^31; hidden % 8 == 0
- * when x is given. T = 0 writes zero counts and offsets.
+ * Limits: 1 <= num_local_experts <= 1024 (as moe_expert_ffn); T * k < 2^31;
+ * hidden % 8 == 0 when x is given. T = 0 writes zero counts and offsets.
  */
 moe_status_t moe_dispatch(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
                           int32_t expert_begin, int32_t num_local_experts,
@@ -220,6 +222,21 @@ moe_status_t moe_dispatch_capacity(const int32_t* topk_ids, int32_t num_tokens, 
                                    int32_t* expert_demand, int32_t* sorted_assign,
                                    int32_t* assign_pos, void* x_sorted, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_capacity -- the per-expert capacity of the capacity factor, ch15
+ * section 4.3 ("负载均衡" section, "Capacity Factor"): C = ceil(c * T * k / E)
+ * with c = factor_num / factor_den taken exactly (integer arithmetic, so a
+ * factor such as 1.2 = 6/5 gives exactly 120 for T = 5600, k = 16, E = 896,
+ * where a binary floating-point product lands just above 120). HOST only;
+ * touches no device memory.
+ * capacity  HOST out: C, the value moe_dispatch_capacity takes.
+ * Errors: MOE_ERR_INVALID for T < 0, k < 1, E < 1, factor_num < 0,
+ * factor_den < 1 or a NULL capacity; MOE_ERR_UNSUPPORTED when C does not fit
+ * in int32 or factor_num, factor_den >= 2^31.
+ */
+moe_status_t moe_expert_capacity(int32_t num_tokens, int32_t top_k, int32_t num_experts,
+                                 int64_t factor_num, int64_t factor_den, int32_t* capacity);
 
 /*
  * Bytes of device workspace moe_expert_ffn needs for these sizes; 0 when the

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = moe.lib()
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 7
     assert moe.status_string(0) == "ok"
     assert moe.status_string(1) == "invalid argument"
     assert moe.status_string(3).startswith("workspace")
@@ -66,7 +66,7 @@ def test_dispatch_validation():
     W = (None, 0, None)       # no workspace, default stream
     assert l.moe_dispatch(None, 4, 0, 0, 8, None, 0, 1, p, p, p, p, None, *W) == 1
     assert l.moe_dispatch(p, 4, 8, 0, 0, None, 0, 1, p, p, p, p, None, *W) == 1
-    assert l.moe_dispatch(p, 4, 8, 0, 2000, None, 0, 1, p, p, p, p, None, *W) == 2
+    assert l.moe_dispatch(p, 4, 8, 0, 1025, None, 0, 1, p, p, p, p, None, *W) == 2   # > 1024 local
     assert l.moe_dispatch(p, 4, 8, 0, 8, p, 0, 1, p, p, p, p, None, *W) == 1      # x without x_sorted
     assert l.moe_dispatch(p, 4, 8, 0, 8, p, 12, 1, p, p, p, p, p, *W) == 1         # hidden % 8
     assert l.moe_dispatch(p, 4, 8, 0, 8, ctypes.c_void_p(8), 16, 1, p, p, p, p, p, *W) == 1  # unaligned
@@ -89,6 +89,31 @@ def test_dispatch_capacity_validation():
     assert l.moe_dispatch_capacity(p, 4, 8, 0, 2000, 10, None, 0, 1, p, p, None, p, p, None, *W) == 2
     assert l.moe_dispatch_capacity(None, 4, 8, 0, 8, 10, None, 0, 1, p, p, None, p, p, None, *W) == 1
     assert l.moe_dispatch_capacity(p, 8192, 8, 0, 32, 10, None, 0, 1, p, p, p, p, p, None, *W) == 3
+
+
+def test_expert_capacity_is_exact():
+    """moe_expert_capacity (a host function) against the oracle's exact-rational ceiling: the
+    page's example (T = 5600, k = 16, E = 896, c = 1.2 -> 120) and a case where binary floating
+    point lands above the integer (T = 400, k = 1, E = 8, c = 1.1 -> 55)."""
+    import math
+    from fractions import Fraction
+
+    import oracle
+    for T, k, E, c in ((5600, 16, 896, "1.2"), (400, 1, 8, "1.1"), (4096, 8, 256, "1"),
+                       (1, 1, 1000, "0.5"), (0, 8, 256, "1.25"), (8192, 8, 256, "2.75"),
+                       (12345, 7, 333, "1.2345"), (100, 3, 7, "0")):
+        f = Fraction(c)
+        assert moe.moe_expert_capacity(T, k, E, f.numerator, f.denominator) == \
+            oracle.expert_capacity(T, k, E, c)
+    assert math.ceil(1.1 * 400 * 1 / 8) == 56      # the float product the exact form avoids
+    l = moe.lib()
+    out = ctypes.c_int32(0)
+    assert l.moe_expert_capacity(10, 1, 1, 1, 0, ctypes.byref(out)) == 1      # den = 0
+    assert l.moe_expert_capacity(10, 0, 1, 1, 1, ctypes.byref(out)) == 1      # k = 0
+    assert l.moe_expert_capacity(10, 1, 1, -1, 1, ctypes.byref(out)) == 1     # c < 0
+    assert l.moe_expert_capacity(10, 1, 1, 1, 1, None) == 1                   # NULL out
+    assert l.moe_expert_capacity(1 << 30, 8, 1, 1, 1, ctypes.byref(out)) == 2  # T k >= 2^31
+    assert l.moe_expert_capacity(1 << 20, 1024, 1, 3, 1, ctypes.byref(out)) == 2  # C >= 2^31
 
 
 def test_ffn_validation_and_workspace():

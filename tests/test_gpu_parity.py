@@ -172,6 +172,7 @@ def test_dispatch_workloads(name, begin, nloc):
 
 @pytest.mark.parametrize("T,k,E,begin,nloc", [
     (1, 1, 4, 0, 4), (37, 3, 16, 3, 5), (1000, 8, 64, 0, 64), (513, 8, 1000, 0, 1000),
+    (513, 8, 1024, 0, 1024), (1100, 8, 1030, 3, 1024),
     (5, 2, 8, 6, 2), (4096, 2, 2, 0, 1),
     # above 8192 assignments: the multi-workgroup sort, ragged last block, and
     # beyond 256 blocks of 2048 where each block's share grows
@@ -448,3 +449,34 @@ def test_eplb_remap_matches_oracle(nodes, gpus, phys, hier):
     ref = eplb.remap(ids, gpus_list, nodes)
     assert np.array_equal(to_host(got), ref)
     assert np.array_equal(p2l[to_host(got)], ids)
+
+
+def test_eplb_remap_out_of_range_ids_get_minus_one():
+    """Expert ids outside [0, E) and experts without a replica map to -1; the other slots of the
+    same token keep the oracle's choice (the invalid slots add no node)."""
+    from oracle import eplb
+    rng = np.random.default_rng(5)
+    E, gpus, nodes, phys = 16, 4, 2, 16
+    load = rng.integers(1, 50, E).astype(float)
+    p2l, offs, slots = moe.moe_eplb_place(load, 4, nodes, gpus, phys, False)
+    ids = np.stack([rng.choice(E, size=4, replace=False) for _ in range(256)]).astype(np.int32)
+    bad = ids.copy()
+    bad[::3, 1] = E + 7
+    bad[1::5, 2] = -3
+    bad[2::7, 0] = 1 << 30
+    print("eplb remap with invalid ids", flush=True)
+    got = to_host(moe.moe_eplb_remap(to_device(bad, DEV), to_device(offs, DEV), to_device(slots, DEV),
+                                     gpus, nodes))
+    valid = (bad >= 0) & (bad < E)
+    assert (got[~valid] == -1).all()
+    gpus_list = [p2l[g * (phys // gpus):(g + 1) * (phys // gpus)].tolist() for g in range(gpus)]
+    for t in range(bad.shape[0]):   # the valid slots of each token, alone, through the oracle
+        keep = valid[t]
+        ref = eplb.remap(bad[t:t + 1, keep], gpus_list, nodes)
+        assert np.array_equal(got[t, keep], ref[0])
+    # an expert with no replica: a table where expert 0's range is empty
+    offs2 = offs.copy()
+    offs2[0] = offs2[1]
+    got2 = to_host(moe.moe_eplb_remap(to_device(ids, DEV), to_device(offs2, DEV), to_device(slots, DEV),
+                                      gpus, nodes))
+    assert (got2[ids == 0] == -1).all()

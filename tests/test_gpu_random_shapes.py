@@ -136,18 +136,18 @@ def test_random_fp8_ffn(seed):
 
 
 @pytest.mark.parametrize("d,I", [(256, 64), (1024, 64)])
-def test_layer_1000_local_experts(d, I):
-    """The largest local expert count of the whole layer (1000, the dispatch's limit): streaming
-    path (d = 256) and the shared-activation path for narrow experts (d = 1024, I = 64)."""
-    wl = W.Workload("local1000", T=512, E=1000, top_k=8, num_groups=8, topk_groups=4, score_mode="raw",
-                    renormalize=True, bias_std=1.0, hidden=d, inter=I, expert_begin=0, num_local=1000,
+def test_layer_1024_local_experts(d, I):
+    """The largest local expert count of the whole layer (1024, the limit of every call):
+    streaming path (d = 256) and the shared-activation path for narrow experts (d = 1024, I = 64)."""
+    wl = W.Workload("local1024", T=512, E=1024, top_k=8, num_groups=8, topk_groups=4, score_mode="raw",
+                    renormalize=True, bias_std=1.0, hidden=d, inter=I, expert_begin=0, num_local=1024,
                     dtype="bf16", seed=d + I)
-    print(f"{wl.name}: T={wl.T} E={wl.E} local=1000 d={d} I={I}", flush=True)
+    print(f"{wl.name}: T={wl.T} E={wl.E} local=1024 d={d} I={I}", flush=True)
     inp = W.generate(wl)
     g = run_layer(wl, inp, True)
     ref = oracle.layer(inp.scores, inp.x, inp.w_gate_up, inp.w_down, top_k=wl.top_k,
                        num_groups=wl.num_groups, topk_groups=wl.topk_groups, score_mode="raw",
-                       renormalize=True, expert_begin=0, num_local=1000)
+                       renormalize=True, expert_begin=0, num_local=1024)
     M = int(ref["offsets"][-1])
     assert np.array_equal(g["topk_ids"], ref["topk_ids"])
     assert np.array_equal(g["offsets"], ref["offsets"])
