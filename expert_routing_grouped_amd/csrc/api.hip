@@ -6,12 +6,36 @@
 #include <stdint.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "launch.h"
 
 namespace {
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
+
+// The fixed scratch of moe_expert_ffn_noalloc (h and partial sums). In host
+// code `scratch` names a host-side stand-in, not device memory: kernels get
+// the per-device address that hipGetSymbolAddress returns (scratch_ptr).
+static __device__ __align__(256) char scratch[MOE_FFN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device (with that
+// device current, as the calling thread has it); null on failure.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -30,6 +54,7 @@ const char* moe_status_string(moe_status_t status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_LAUNCH: return "kernel launch failed";
+    case MOE_ERR_SCRATCH: return "sizes exceed the fixed scratch of moe_expert_ffn_noalloc";
   }
   return "unknown status";
 }
@@ -164,11 +189,12 @@ size_t moe_expert_ffn_workspace_size(int32_t num_local_experts, int32_t hidden, 
                                  dtype == MOE_BF16);
 }
 
-moe_status_t moe_expert_ffn(const void* x, const int32_t* row_index, int32_t row_index_div,
-                            const int32_t* expert_offsets, const void* w_gate_up,
-                            const void* w_down, int32_t num_local_experts, int32_t hidden,
-                            int32_t inter, int32_t row_capacity, int32_t dtype, void* o_sorted,
-                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Validation of moe_expert_ffn's arguments other than the workspace.
+static moe_status_t check_ffn_args(const void* x, const int32_t* row_index, int32_t row_index_div,
+                                   const int32_t* expert_offsets, const void* w_gate_up,
+                                   const void* w_down, int32_t num_local_experts, int32_t hidden,
+                                   int32_t inter, int32_t row_capacity, int32_t dtype,
+                                   const void* o_sorted) {
   const moe_status_t st = check_ffn_sizes(num_local_experts, hidden, inter, row_capacity, dtype);
   if (st != MOE_OK) return st;
   if (!expert_offsets || !w_gate_up || !w_down) return MOE_ERR_INVALID;
@@ -176,12 +202,43 @@ moe_status_t moe_expert_ffn(const void* x, const int32_t* row_index, int32_t row
   if (row_capacity > 0 && (!x || !o_sorted)) return MOE_ERR_INVALID;
   if (!aligned16(x) || !aligned16(o_sorted) || !aligned16(w_gate_up) || !aligned16(w_down))
     return MOE_ERR_INVALID;
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_ffn(const void* x, const int32_t* row_index, int32_t row_index_div,
+                            const int32_t* expert_offsets, const void* w_gate_up,
+                            const void* w_down, int32_t num_local_experts, int32_t hidden,
+                            int32_t inter, int32_t row_capacity, int32_t dtype, void* o_sorted,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const moe_status_t st = check_ffn_args(x, row_index, row_index_div, expert_offsets, w_gate_up,
+                                         w_down, num_local_experts, hidden, inter, row_capacity,
+                                         dtype, o_sorted);
+  if (st != MOE_OK) return st;
   const size_t need = moe::ffn_workspace_size(num_local_experts, hidden, inter, row_capacity,
                                               dtype == MOE_BF16);
   if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
   moe::FfnArgs a{x, row_index, row_index ? row_index_div : 1, expert_offsets, w_gate_up, w_down,
                  num_local_experts, hidden, inter, row_capacity, dtype == MOE_BF16, o_sorted,
                  workspace};
+  return from_hip(moe::launch_ffn(a, stream));
+}
+
+moe_status_t moe_expert_ffn_noalloc(const void* x, const int32_t* row_index, int32_t row_index_div,
+                                    const int32_t* expert_offsets, const void* w_gate_up,
+                                    const void* w_down, int32_t num_local_experts, int32_t hidden,
+                                    int32_t inter, int32_t row_capacity, int32_t dtype,
+                                    void* o_sorted, hipStream_t stream) {
+  const moe_status_t st = check_ffn_args(x, row_index, row_index_div, expert_offsets, w_gate_up,
+                                         w_down, num_local_experts, hidden, inter, row_capacity,
+                                         dtype, o_sorted);
+  if (st != MOE_OK) return st;
+  const size_t need = moe::ffn_workspace_size(num_local_experts, hidden, inter, row_capacity,
+                                              dtype == MOE_BF16);
+  if (need > MOE_FFN_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* ws = scratch_ptr();
+  if (!ws) return MOE_ERR_LAUNCH;
+  moe::FfnArgs a{x, row_index, row_index ? row_index_div : 1, expert_offsets, w_gate_up, w_down,
+                 num_local_experts, hidden, inter, row_capacity, dtype == MOE_BF16, o_sorted, ws};
   return from_hip(moe::launch_ffn(a, stream));
 }
 

@@ -36,6 +36,7 @@ _SIGNATURES = {
     "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "moe_expert_ffn": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P,
                                       ctypes.c_size_t, _P]),
+    "moe_expert_ffn_noalloc": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_quantize_e4m3": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_expert_ffn_fp8_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I]),
     "moe_expert_ffn_fp8": (ctypes.c_int, [_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P,
@@ -242,6 +243,40 @@ def moe_expert_ffn(x, expert_offsets, w_gate_up, w_down, row_index=None, row_ind
                                 _ptr(w_gate_up), _ptr(w_down), E_loc, hidden, inter, cap, _code(dt),
                                 _ptr(o_sorted), _ptr(workspace), workspace.numel(),
                                 _stream(stream)), "moe_expert_ffn")
+    return o_sorted
+
+
+MOE_ERR_SCRATCH = 5
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_expert_ffn_noalloc(x, expert_offsets, w_gate_up, w_down, o_sorted, row_index=None,
+                           row_index_div=1, row_capacity=None, stream=None):
+    """moe_expert_ffn with the library's fixed scratch instead of a workspace (no allocation:
+    o_sorted must be supplied). Raises MoeError for sizes whose workspace exceeds the scratch."""
+    dt = x.dtype
+    _dev(x, dt, "x")
+    _dev(expert_offsets, torch.int32, "expert_offsets")
+    _dev(w_gate_up, dt, "w_gate_up")
+    _dev(w_down, dt, "w_down")
+    _dev(o_sorted, dt, "o_sorted")
+    if row_index is not None:
+        _dev(row_index, torch.int32, "row_index")
+        cap = row_index.numel() if row_capacity is None else row_capacity
+        _at_least(row_index, cap, "row_index")
+    else:
+        cap = x.shape[0] if row_capacity is None else row_capacity
+    hidden = x.shape[1]
+    E_loc, two_i, d2 = w_gate_up.shape
+    inter = two_i // 2
+    _at_least(expert_offsets, E_loc + 1, "expert_offsets")
+    if d2 != hidden or tuple(w_down.shape) != (E_loc, hidden, inter):
+        raise MoeError("weight shapes do not match x")
+    if o_sorted.shape[0] < cap or o_sorted.shape[1] != hidden or (row_index is None and x.shape[0] < cap):
+        raise MoeError("row buffers are smaller than row_capacity")
+    _check(lib().moe_expert_ffn_noalloc(_ptr(x), _ptr(row_index), int(row_index_div), _ptr(expert_offsets),
+                                        _ptr(w_gate_up), _ptr(w_down), E_loc, hidden, inter, cap, _code(dt),
+                                        _ptr(o_sorted), _stream(stream)), "moe_expert_ffn_noalloc")
     return o_sorted
 
 

@@ -15,8 +15,10 @@
  * Conventions shared by every call
  * --------------------------------
  * - Every array argument is a DEVICE pointer owned by the caller (except
- *   those of moe_eplb_place, which are host pointers); the library
- *   keeps no pointer after a call returns and allocates no memory.
+ *   those of moe_eplb_place and moe_expert_capacity, which are host
+ *   pointers); the library keeps no pointer after a call returns and
+ *   allocates no memory (moe_expert_ffn_noalloc uses a fixed device array of
+ *   the library's own instead of a workspace argument).
  * - Calls are asynchronous on `stream` (0 = the default stream). They do not
  *   synchronise with the host, so a sequence of calls can be captured in a
  *   HIP graph.
@@ -63,7 +65,8 @@ typedef enum {
   MOE_ERR_INVALID = 1,      /* an argument is out of range or a required pointer is NULL */
   MOE_ERR_UNSUPPORTED = 2,  /* valid, but a shape this library does not implement */
   MOE_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than the *_workspace_size query */
-  MOE_ERR_LAUNCH = 4        /* a kernel launch failed */
+  MOE_ERR_LAUNCH = 4,       /* a kernel launch failed */
+  MOE_ERR_SCRATCH = 5       /* the sizes need more than the fixed scratch of moe_expert_ffn_noalloc */
 } moe_status_t;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
@@ -275,6 +278,33 @@ moe_status_t moe_expert_ffn(const void* x, const int32_t* row_index, int32_t row
                             const void* w_down, int32_t num_local_experts, int32_t hidden,
                             int32_t inter, int32_t row_capacity, int32_t dtype, void* o_sorted,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_ffn_noalloc -- moe_expert_ffn for callers that cannot allocate
+ * device memory at all (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation and kernels, with no
+ * workspace argument; h and the kernels' partial sums live in a fixed scratch
+ * array of MOE_FFN_NOALLOC_SCRATCH_BYTES (64 MiB) that the library holds on
+ * every GPU it runs on until the process ends. The call allocates nothing
+ * (no hipMalloc, no hipFree); its first call on a device looks up that
+ * device's copy of the array.
+ * Arguments, layouts, limits and errors: those of moe_expert_ffn, and
+ * MOE_ERR_SCRATCH (nothing enqueued) when moe_expert_ffn_workspace_size of
+ * the sizes exceeds the scratch; MOE_ERR_LAUNCH also when the device address
+ * of the scratch cannot be obtained (e.g. bf16 decode: 4096 rows x I = 2048 take 16 MiB; 512
+ * tokens x 8 slots over 256 experts with I = 64 take 36 MiB).
+ * Every call on one GPU shares that GPU's scratch, whatever the stream: two
+ * calls that may overlap in time on one GPU (different streams, different
+ * host threads) race and must be ordered by the caller. Nothing in the
+ * scratch needs clearing between calls (every byte a call reads, the same
+ * call wrote first).
+ */
+#define MOE_FFN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status_t moe_expert_ffn_noalloc(const void* x, const int32_t* row_index, int32_t row_index_div,
+                                    const int32_t* expert_offsets, const void* w_gate_up,
+                                    const void* w_down, int32_t num_local_experts, int32_t hidden,
+                                    int32_t inter, int32_t row_capacity, int32_t dtype,
+                                    void* o_sorted, hipStream_t stream);
 
 /*
  * FP8 operands (moe_quantize_e4m3, moe_expert_ffn_fp8). Values are OCP FP8

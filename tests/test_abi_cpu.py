@@ -38,10 +38,11 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = moe.lib()
-    assert lib.moe_abi_version() == 7
+    assert lib.moe_abi_version() == 8
     assert moe.status_string(0) == "ok"
     assert moe.status_string(1) == "invalid argument"
     assert moe.status_string(3).startswith("workspace")
+    assert moe.status_string(5).startswith("sizes exceed the fixed scratch")
     assert moe.status_string(99) == "unknown status"
 
 
@@ -129,6 +130,15 @@ def test_ffn_validation_and_workspace():
     assert l.moe_expert_ffn(p, None, 1, p, p, p, 8, 7168, 2048, 64, 1, p, p, 16, None) == 3   # small ws
     assert l.moe_expert_ffn(p, None, 1, p, p, p, 8, 7168, 2048, 64, 1, p, None, 1 << 30, None) == 3
     assert l.moe_expert_ffn(p, None, 1, p, p, p, 8000, 256, 64, 64, 0, p, p, 1 << 30, None) == 2
+    # the allocation-free variant validates the same way, and refuses sizes whose workspace
+    # exceeds its fixed 64 MiB scratch before it looks anything up on a device
+    assert l.moe_expert_ffn_noalloc(p, None, 1, p, p, p, 8, 7000, 2048, 64, 1, p, None) == 2
+    assert l.moe_expert_ffn_noalloc(p, None, 1, None, p, p, 8, 7168, 2048, 64, 1, p, None) == 1
+    assert l.moe_expert_ffn_noalloc(p, p, 0, p, p, p, 8, 7168, 2048, 64, 1, p, None) == 1
+    assert l.moe_expert_ffn_workspace_size(8, 7168, 2048, 65536, 1) > moe.NOALLOC_SCRATCH_BYTES
+    assert l.moe_expert_ffn_noalloc(p, p, 8, p, p, p, 32, 7168, 2048, 65536, 1, p, None) == 5
+    assert l.moe_expert_ffn_workspace_size(8, 7168, 2048, 4096, 1) <= moe.NOALLOC_SCRATCH_BYTES
+    assert l.moe_expert_ffn_workspace_size(256, 7168, 64, 4096, 1) <= moe.NOALLOC_SCRATCH_BYTES
 
 
 def test_fp8_validation_and_workspace():
