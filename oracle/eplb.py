@@ -26,14 +26,33 @@ one, else the replica on the lowest-numbered node.
 
 Readings where the page leaves a step open (ties): equal weights are taken
 in increasing index order, equal pack totals go to the lower pack, equal
-loads per replica to the lower expert index (the order the page's listing
-produces); floating point sums are float64, accumulated in placement order.
+loads per replica to the expert listed first; floating point sums are
+float64, accumulated in placement order. The functions below restate the
+page's description (a selection of the heaviest item, heaps of open packs
+and of loads per replica), not its listing.
 """
 from __future__ import annotations
+
+import heapq
 
 import numpy as np
 
 __all__ = ["balanced_pack", "replicate", "place", "gpu_loads", "remap", "nodes_per_token"]
+
+
+def _heaviest_first(weights: list[float]) -> list[int]:
+    """Item indices from heaviest to lightest, found by repeatedly taking the heaviest item
+    not yet taken (equal weights: the lower index first)."""
+    left = list(range(len(weights)))
+    order = []
+    while left:
+        best = left[0]
+        for i in left[1:]:
+            if weights[i] > weights[best]:
+                best = i
+        order.append(best)
+        left.remove(best)
+    return order
 
 
 def balanced_pack(weights, n_packs: int) -> list[list[int]]:
@@ -41,22 +60,22 @@ def balanced_pack(weights, n_packs: int) -> list[list[int]]:
 
     Every pack receives len(weights) // n_packs items (len(weights) must be a
     multiple of n_packs). Items go heaviest first (equal weights: lower index
-    first), each to the pack with the smallest running total among those not
-    yet full (equal totals: the lower pack).
+    first), each to the lightest pack that still has room (equal totals: the
+    lower pack). The packs with room are kept in a heap keyed by (total, pack
+    index); a pack leaves the heap when it is full.
     """
     w = [float(v) for v in weights]
     n = len(w)
     assert n % n_packs == 0
     room = n // n_packs
     packs: list[list[int]] = [[] for _ in range(n_packs)]
-    total = [0.0] * n_packs
-    for item in sorted(range(n), key=lambda i: (-w[i], i)):
-        target = -1
-        for p in range(n_packs):
-            if len(packs[p]) < room and (target < 0 or total[p] < total[target]):
-                target = p
-        packs[target].append(item)
-        total[target] += w[item]
+    open_packs = [(0.0, p) for p in range(n_packs)]
+    heapq.heapify(open_packs)
+    for item in _heaviest_first(w):
+        total, p = heapq.heappop(open_packs)
+        packs[p].append(item)
+        if len(packs[p]) < room:
+            heapq.heappush(open_packs, (total + w[item], p))
     return packs
 
 
@@ -65,16 +84,18 @@ def replicate(load, experts: list[int], n_physical: int) -> tuple[list[int], dic
 
     Starting from one replica each, a replica is added n_physical - len(experts)
     times to the expert with the highest load per replica (equal: the one that
-    comes first in `experts`). Returns the physical list (each expert repeated
-    by its count, in the order of `experts`) and the counts.
+    comes first in `experts`), taken from a heap keyed by (-load per replica,
+    position in `experts`). Returns the physical list (each expert repeated by
+    its count, in the order of `experts`) and the counts.
     """
     count = {e: 1 for e in experts}
+    heap = [(-float(load[e]), pos) for pos, e in enumerate(experts)]
+    heapq.heapify(heap)
     for _ in range(n_physical - len(experts)):
-        best = experts[0]
-        for e in experts[1:]:
-            if float(load[e]) / count[e] > float(load[best]) / count[best]:
-                best = e
-        count[best] += 1
+        _, pos = heapq.heappop(heap)
+        e = experts[pos]
+        count[e] += 1
+        heapq.heappush(heap, (-(float(load[e]) / count[e]), pos))
     physical = [e for e in experts for _ in range(count[e])]
     return physical, count
 

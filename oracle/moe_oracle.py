@@ -45,7 +45,7 @@ design notes of the repository):
    activation).
 2. The fused weight is [gate; up] stacked along N: rows [0, I) are the
    gate, rows [I, 2I) the up projection.
-3. Ties: the page's listing uses numpy's default argsort; here ties go
+3. Ties: the page does not say how equal scores are ordered; here ties go
    to the lower index (groups and experts), and -0 equals +0.
 4. Group scores are float32 sums of the two largest float32 scores (a
    duplicated maximum counts twice); the page sums in float64 -- the two
@@ -110,16 +110,27 @@ def route_softmax_topk(logits: np.ndarray, top_k: int, renormalize: bool = False
     return ids.astype(np.int32), w
 
 
+def _best_remaining(values: np.ndarray, allowed: np.ndarray) -> np.ndarray:
+    """Per row, the index of the highest value among the allowed columns; among equal values
+    the lowest index (np.argmax returns the first maximum). -0 and +0 compare equal."""
+    masked = np.where(allowed, values, -np.inf)
+    return np.argmax(masked, axis=1)
+
+
 def route_grouped(scores: np.ndarray, top_k: int, num_groups: int, topk_groups: int,
                   renormalize: bool = True):
     """Group-limited top-k routing [EPLB, section "EPLB 与路由约束"].
 
+    The page's statement, taken step by step:
     1. The E experts form ``num_groups`` contiguous groups of G = E / num_groups.
-    2. Group score = float32 sum of the group's two highest scores.
-    3. Keep the ``topk_groups`` groups with the highest group score
-       (ties: lower group index).
-    4. Among the experts of the kept groups, pick ``top_k`` by descending
-       score (ties: lower expert index); output slots are in that order.
+    2. A group's score is the sum of its two highest scores: the maximum, plus
+       the maximum of the members left after one member holding the maximum is
+       set aside (so a duplicated maximum counts twice); float32 sum.
+    3. The token keeps ``topk_groups`` groups: the best group, then the best of
+       the remaining ones, and so on (ties: lower group index).
+    4. It then picks ``top_k`` experts among the members of its kept groups the
+       same way, one at a time, best remaining first (ties: lower expert
+       index); the output slots are in that order.
     5. Weights are the selected raw scores, divided by their sum when
        ``renormalize`` (float64).
     With ``num_groups == 1`` steps 2-3 are skipped (plain top-k on scores).
@@ -132,22 +143,33 @@ def route_grouped(scores: np.ndarray, top_k: int, num_groups: int, topk_groups: 
     G = E // num_groups
     if not 1 <= topk_groups <= num_groups or not 1 <= top_k <= topk_groups * G:
         raise ValueError("top_k / topk_groups out of range")
+    rows = np.arange(T)
+    eligible = np.ones((T, E), dtype=bool)
     if num_groups > 1:
         if G < 2:
             raise ValueError("groups need at least two experts for a top-2 group score")
-        by_group = np.sort(s.reshape(T, num_groups, G), axis=-1)          # ascending
-        group_score = by_group[..., -1] + by_group[..., -2]                # float32 + float32 -> float32
-        kept_groups = np.argsort(-group_score, axis=1, kind="stable")[:, :topk_groups]
+        group_score = np.empty((T, num_groups), dtype=np.float32)
+        for g in range(num_groups):
+            members = s[:, g * G:(g + 1) * G]
+            first = np.argmax(members, axis=1)                      # one member holding the maximum
+            top1 = members[rows, first]
+            rest = np.ones(members.shape, dtype=bool)
+            rest[rows, first] = False
+            top2 = np.where(rest, members, -np.inf).max(axis=1).astype(np.float32)
+            group_score[:, g] = top1 + top2                         # float32 + float32 -> float32
         kept = np.zeros((T, num_groups), dtype=bool)
-        np.put_along_axis(kept, kept_groups, True, axis=1)
-        expert_kept = np.repeat(kept, G, axis=1)
-    else:
-        expert_kept = np.ones((T, E), dtype=bool)
-    # Sort key: kept experts first, then descending score; lexsort is stable,
-    # so equal keys stay in expert-index order.
-    order = np.lexsort((-s, ~expert_kept), axis=1)
-    ids = order[:, :top_k]
-    w = np.take_along_axis(s, ids, axis=1).astype(np.float64)
+        for _ in range(topk_groups):
+            best = _best_remaining(group_score, ~kept)
+            kept[rows, best] = True
+        eligible = np.zeros((T, E), dtype=bool)
+        for g in range(num_groups):
+            eligible[:, g * G:(g + 1) * G] = kept[:, g:g + 1]
+    ids = np.empty((T, top_k), dtype=np.int64)
+    for j in range(top_k):
+        best = _best_remaining(s, eligible)
+        ids[:, j] = best
+        eligible[rows, best] = False
+    w = s[rows[:, None], ids].astype(np.float64)
     if renormalize:
         w = w / w.sum(axis=1, keepdims=True)
     return ids.astype(np.int32), w
