@@ -167,7 +167,8 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
                          num_groups=wl.num_groups, topk_groups=wl.topk_groups, score_mode=mode,
                          renormalize=wl.renormalize, expert_begin=wl.expert_begin,
                          num_local_experts=wl.num_local, hidden=wl.hidden, inter=wl.inter,
-                         dtype=dt, device=dev, expert_capacity=cap, fp8=fp8)
+                         dtype=dt, device=dev, expert_capacity=None if wl.layout == "masked" else cap,
+                         fp8=fp8, masked_capacity=cap if wl.layout == "masked" else None)
     scores = to_device(inp.scores, dev)
     x = to_device(inp.x, dev) if wl.has_ffn else None
     weights = []
@@ -271,6 +272,10 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
         ai = acc["flops"] / acc["bytes"]
         res["mfma_peak_tflops"] = FP8_PEAK_TFLOPS if fp8 else BF16_PEAK_TFLOPS
         res["ffn_bound"] = "mfma" if ai > res["mfma_peak_tflops"] * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
+        if cap is not None:
+            demand = to_host(layer.buf["demand"])
+            res.update(capacity=cap, layout=wl.layout, dropped=int(demand.sum()) - acc["M"],
+                       experts_over_capacity=int((demand > cap).sum()))
     else:
         M = int(counts.sum())
         route_bytes = wl.T * wl.E * 4 + wl.T * wl.top_k * 8

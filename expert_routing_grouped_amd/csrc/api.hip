@@ -94,15 +94,18 @@ static moe_status_t dispatch_impl(const int32_t* topk_ids, int32_t num_tokens, i
                                   int32_t* expert_offsets, int32_t* sorted_assign,
                                   int32_t* assign_pos, void* x_sorted, void* workspace,
                                   size_t workspace_bytes, int32_t capacity, int32_t* demand,
-                                  hipStream_t stream) {
+                                  int fixed, hipStream_t stream) {
   if (num_tokens < 0 || top_k < 1 || expert_begin < 0 || num_local_experts < 1 || capacity < 0)
     return MOE_ERR_INVALID;
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
   if (num_local_experts > moe::kDispatchMaxLocal) return MOE_ERR_UNSUPPORTED;
   const int64_t n = (int64_t)num_tokens * top_k;
   if (n >= ((int64_t)1 << 31) - 65536) return MOE_ERR_UNSUPPORTED;
-  if (!expert_counts || !expert_offsets) return MOE_ERR_INVALID;
-  if (n > 0 && (!topk_ids || !sorted_assign || !assign_pos)) return MOE_ERR_INVALID;
+  // fixed slots: rows e * C + r are addressed with 32-bit ints
+  if (fixed && (int64_t)num_local_experts * capacity >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!expert_counts || (!fixed && !expert_offsets)) return MOE_ERR_INVALID;
+  if (n > 0 && (!topk_ids || !assign_pos)) return MOE_ERR_INVALID;
+  if (n > 0 && !sorted_assign && !(fixed && capacity == 0)) return MOE_ERR_INVALID;
   if ((x == nullptr) != (x_sorted == nullptr)) return MOE_ERR_INVALID;
   int row_bytes = 0;
   if (x) {
@@ -116,8 +119,8 @@ static moe_status_t dispatch_impl(const int32_t* topk_ids, int32_t num_tokens, i
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return MOE_ERR_WORKSPACE;
   moe::DispatchArgs a{topk_ids, (int)n, top_k, expert_begin, num_local_experts, expert_counts,
-                      expert_offsets, sorted_assign, assign_pos, x, x_sorted, row_bytes,
-                      workspace, capacity, demand};
+                      fixed ? nullptr : expert_offsets, sorted_assign, assign_pos, x, x_sorted,
+                      row_bytes, workspace, capacity, demand, fixed ? 1 : 0};
   return from_hip(moe::launch_dispatch(a, stream));
 }
 
@@ -129,7 +132,7 @@ moe_status_t moe_dispatch(const int32_t* topk_ids, int32_t num_tokens, int32_t t
                           hipStream_t stream) {
   return dispatch_impl(topk_ids, num_tokens, top_k, expert_begin, num_local_experts, x, hidden,
                        dtype, expert_counts, expert_offsets, sorted_assign, assign_pos, x_sorted,
-                       workspace, workspace_bytes, INT32_MAX, nullptr, stream);
+                       workspace, workspace_bytes, INT32_MAX, nullptr, 0, stream);
 }
 
 moe_status_t moe_dispatch_capacity(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
@@ -141,7 +144,18 @@ moe_status_t moe_dispatch_capacity(const int32_t* topk_ids, int32_t num_tokens, 
                                    size_t workspace_bytes, hipStream_t stream) {
   return dispatch_impl(topk_ids, num_tokens, top_k, expert_begin, num_local_experts, x, hidden,
                        dtype, expert_counts, expert_offsets, sorted_assign, assign_pos, x_sorted,
-                       workspace, workspace_bytes, expert_capacity, expert_demand, stream);
+                       workspace, workspace_bytes, expert_capacity, expert_demand, 0, stream);
+}
+
+moe_status_t moe_dispatch_masked(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
+                                 int32_t expert_begin, int32_t num_local_experts,
+                                 int32_t expert_capacity, const void* x, int32_t hidden,
+                                 int32_t dtype, int32_t* expert_counts, int32_t* expert_demand,
+                                 int32_t* slot_assign, int32_t* assign_pos, void* x_slots,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return dispatch_impl(topk_ids, num_tokens, top_k, expert_begin, num_local_experts, x, hidden,
+                       dtype, expert_counts, nullptr, slot_assign, assign_pos, x_slots, workspace,
+                       workspace_bytes, expert_capacity, expert_demand, 1, stream);
 }
 
 moe_status_t moe_expert_capacity(int32_t num_tokens, int32_t top_k, int32_t num_experts,
@@ -240,6 +254,37 @@ moe_status_t moe_expert_ffn_noalloc(const void* x, const int32_t* row_index, int
   moe::FfnArgs a{x, row_index, row_index ? row_index_div : 1, expert_offsets, w_gate_up, w_down,
                  num_local_experts, hidden, inter, row_capacity, dtype == MOE_BF16, o_sorted, ws};
   return from_hip(moe::launch_ffn(a, stream));
+}
+
+size_t moe_expert_ffn_masked_workspace_size(int32_t num_local_experts, int32_t hidden,
+                                            int32_t inter, int32_t expert_capacity, int32_t dtype) {
+  if (expert_capacity < 0 || num_local_experts < 1) return 0;
+  const int64_t rows = (int64_t)num_local_experts * expert_capacity;
+  if (rows >= ((int64_t)1 << 31)) return 0;
+  if (check_ffn_sizes(num_local_experts, hidden, inter, (int32_t)rows, dtype) != MOE_OK) return 0;
+  return moe::ffn_masked_workspace_size(num_local_experts, hidden, inter, expert_capacity,
+                                        dtype == MOE_BF16);
+}
+
+moe_status_t moe_expert_ffn_masked(const void* x_slots, const int32_t* expert_counts,
+                                   int32_t expert_capacity, const void* w_gate_up,
+                                   const void* w_down, int32_t num_local_experts, int32_t hidden,
+                                   int32_t inter, int32_t dtype, void* o_slots, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  if (expert_capacity < 0 || num_local_experts < 1) return MOE_ERR_INVALID;
+  const int64_t rows = (int64_t)num_local_experts * expert_capacity;
+  if (rows >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  const moe_status_t st = check_ffn_args(x_slots, nullptr, 1, expert_counts, w_gate_up, w_down,
+                                         num_local_experts, hidden, inter, (int32_t)rows, dtype,
+                                         o_slots);
+  if (st != MOE_OK) return st;
+  const size_t need = moe::ffn_masked_workspace_size(num_local_experts, hidden, inter,
+                                                     expert_capacity, dtype == MOE_BF16);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
+  if (rows == 0) return MOE_OK;
+  moe::FfnMaskedArgs a{x_slots, expert_counts, expert_capacity, w_gate_up, w_down,
+                       num_local_experts, hidden, inter, dtype == MOE_BF16, o_slots, workspace};
+  return from_hip(moe::launch_ffn_masked(a, stream));
 }
 
 moe_status_t moe_quantize_e4m3(const void* x, int32_t rows, int32_t cols, int32_t dtype, void* codes,

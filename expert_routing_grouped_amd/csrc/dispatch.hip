@@ -18,7 +18,9 @@
 // With a per-expert capacity C (the capacity factor of ch15 section 4.3,
 // drop policy) an expert keeps the assignments of rank < C, i.e. its first C
 // in assignment order; the offsets are the prefix sums of min(count, C) and a
-// dropped assignment gets assign_pos = -1, like a non-local one.
+// dropped assignment gets assign_pos = -1, like a non-local one. In the fixed
+// slot ("masked") layout expert e's rows start at e * C instead of at the
+// prefix sum, and no offsets are written.
 #include <algorithm>
 
 #include "device_common.h"
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(256) void block_count_kernel(const int* __restrict_
 // wavefronts, then scatters. Block 0 also writes counts and offsets.
 __global__ __launch_bounds__(256) void block_scatter_kernel(
     const int* __restrict__ ids, int n, int per_block, int begin, int nloc, int nbits,
-    const int* __restrict__ ws, int nblocks, int cap, int* __restrict__ counts,
+    const int* __restrict__ ws, int nblocks, int cap, int fixed, int* __restrict__ counts,
     int* __restrict__ offsets, int* __restrict__ demand, int* __restrict__ sorted_assign,
     int* __restrict__ assign_pos) {
   extern __shared__ int lds[];
@@ -225,10 +227,10 @@ __global__ __launch_bounds__(256) void block_scatter_kernel(
     if (e < nloc) {
       if (b == 0) {
         counts[e] = min(tot[q], cap);
-        offsets[e] = run;
+        if (offsets) offsets[e] = run;
         if (demand) demand[e] = tot[q];
       }
-      ebase[e] = run;
+      ebase[e] = fixed ? e * cap : run;
       // wave rank bases: the expert's assignments in earlier blocks and in
       // the block's earlier wavefronts
       int s = before[q];
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(256) void block_scatter_kernel(
     }
     run += min(tot[q], cap);
   }
-  if (b == 0 && tid == 0) offsets[nloc] = total;
+  if (b == 0 && tid == 0 && offsets) offsets[nloc] = total;
   __syncthreads();
   wave_scatter(ids, lo, hi, begin, nloc, nbits, cnt + w * nloc, ebase, cap, sorted_assign,
                assign_pos);
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(256) void block_scatter_kernel(
 constexpr int kSortGroups = kSingleBlockMax / kSortWaves / 64;   // 64-id groups per wavefront
 
 __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids, int n, int begin,
-                                                    int nloc, int nbits, int cap,
+                                                    int nloc, int nbits, int cap, int fixed,
                                                     int* __restrict__ counts,
                                                     int* __restrict__ offsets,
                                                     int* __restrict__ demand,
@@ -317,10 +319,10 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids,
     const int excl = incl - kept + wbase[w];
     if (e < nloc) {
       counts[e] = kept;
-      offsets[e] = excl;
-      ebase[e] = excl;
+      if (offsets) offsets[e] = excl;
+      ebase[e] = fixed ? e * cap : excl;
       if (demand) demand[e] = total;
-      if (e == nloc - 1) offsets[nloc] = excl + kept;
+      if (e == nloc - 1 && offsets) offsets[nloc] = excl + kept;
     }
   }
   __syncthreads();
@@ -351,7 +353,26 @@ __global__ void zero_counts_kernel(int nloc, int* counts, int* offsets, int* dem
       counts[e] = 0;
       if (demand) demand[e] = 0;
     }
-    offsets[e] = 0;
+    if (offsets) offsets[e] = 0;
+  }
+}
+
+// Fixed-slot layout: one wavefront per slot row r of the num_local x cap
+// block; rows past their expert's count are left untouched.
+__global__ __launch_bounds__(256) void gather_slots_kernel(const uint4* __restrict__ x,
+                                                           const int* __restrict__ slot_assign,
+                                                           const int* __restrict__ counts, int nloc,
+                                                           int cap, int k, int row_vec,
+                                                           uint4* __restrict__ x_slots) {
+  const int lane = threadIdx.x & 63;
+  const long rows = (long)nloc * cap;
+  for (long r = (long)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += (long)gridDim.x * 4) {
+    const int e = (int)(r / cap);
+    if ((int)(r - (long)e * cap) >= counts[e]) continue;
+    const int t = slot_assign[r] / k;
+    const uint4* src = x + (size_t)t * row_vec;
+    uint4* dst = x_slots + (size_t)r * row_vec;
+    for (int c = lane; c < row_vec; c += 64) dst[c] = src[c];
   }
 }
 
@@ -389,8 +410,8 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   if (a.n <= kSingleBlockMax) {
     const size_t lds = (size_t)((kSortWaves + 1) * a.num_local + kSortWaves) * sizeof(int);
     hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(kSortWaves * 64), lds, s, a.ids, a.n,
-                       a.expert_begin, a.num_local, nbits, a.capacity, a.counts, a.offsets,
-                       a.demand, a.sorted_assign, a.assign_pos);
+                       a.expert_begin, a.num_local, nbits, a.capacity, a.fixed_slots, a.counts,
+                       a.offsets, a.demand, a.sorted_assign, a.assign_pos);
   } else {
     const int blocks = sort_blocks(a.n), per_block = sort_per_block(a.n);
     const size_t lds = (size_t)(kBlkWaves * a.num_local + 4) * sizeof(int);
@@ -399,12 +420,21 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
     const size_t lds2 = lds + (size_t)a.num_local * sizeof(int);
     hipLaunchKernelGGL(block_scatter_kernel, dim3(blocks), dim3(256), lds2, s, a.ids, a.n,
                        per_block, a.expert_begin, a.num_local, nbits, (const int*)a.workspace,
-                       blocks, a.capacity, a.counts, a.offsets, a.demand, a.sorted_assign,
-                       a.assign_pos);
+                       blocks, a.capacity, a.fixed_slots, a.counts, a.offsets, a.demand,
+                       a.sorted_assign, a.assign_pos);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.row_bytes == 0) return err;
   const int row_vec = a.row_bytes / 16;
+  if (a.fixed_slots) {
+    const long rows = (long)a.num_local * a.capacity;
+    if (rows == 0) return hipSuccess;
+    const int blocks = (int)std::min<long>((rows + 3) / 4, 2048);
+    hipLaunchKernelGGL(gather_slots_kernel, dim3(blocks), dim3(256), 0, s, (const uint4*)a.x,
+                       a.sorted_assign, a.counts, a.num_local, a.capacity, a.k, row_vec,
+                       (uint4*)a.x_sorted);
+    return hipGetLastError();
+  }
   const int blocks = (int)std::min<long>((a.n + 3) / 4, 2048);
   hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(256), 0, s, (const uint4*)a.x,
                      a.sorted_assign, a.offsets, a.num_local, a.k, a.n, row_vec,

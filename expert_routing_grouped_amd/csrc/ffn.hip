@@ -1652,7 +1652,92 @@ hipError_t launch_gate_up_shared(const GemmArgs& g0, size_t h_bytes, void* works
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- masked layout
+
+// Fixed per-expert slots of `cap` rows with a valid count per expert: one
+// workgroup turns the counts into compact offsets (exclusive prefix sums of
+// min(max(count, 0), cap)) and, for compact row i of expert e, row_index[i] =
+// the slot row e * cap + (i - offsets[e]). nloc <= 1024: one expert per thread.
+__global__ __launch_bounds__(1024) void masked_plan_kernel(const int* __restrict__ counts, int nloc, int cap,
+                                                           int* __restrict__ offsets,
+                                                           int* __restrict__ row_index) {
+  __shared__ int s_off[kMaxLocal + 1];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int m = tid < nloc ? min(max(counts[tid], 0), cap) : 0;
+  int incl = m;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, MOE_WAVE);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += wsum[i];
+  const int excl = before + incl - m;
+  if (tid < nloc) {
+    s_off[tid] = excl;
+    offsets[tid] = excl;
+    if (tid == nloc - 1) {
+      s_off[nloc] = excl + m;
+      offsets[nloc] = excl + m;
+    }
+  }
+  __syncthreads();
+  for (int e = w; e < nloc; e += blockDim.x >> 6) {
+    const int o = s_off[e], n = s_off[e + 1] - o;
+    for (int r = lane; r < n; r += 64) row_index[o + r] = e * cap + r;
+  }
+}
+
+// o_slots[row_index[i]] = o_compact[i] for the compact rows i < offsets[nloc]:
+// one wavefront per row, 16-byte copies.
+__global__ __launch_bounds__(256) void masked_scatter_kernel(const uint4* __restrict__ o_compact,
+                                                             const int* __restrict__ row_index,
+                                                             const int* __restrict__ offsets, int nloc,
+                                                             int row_vec, uint4* __restrict__ o_slots) {
+  const int lane = threadIdx.x & 63;
+  const int M = offsets[nloc];
+  for (int r = blockIdx.x * 4 + (threadIdx.x >> 6); r < M; r += gridDim.x * 4) {
+    const uint4* src = o_compact + (size_t)r * row_vec;
+    uint4* dst = o_slots + (size_t)row_index[r] * row_vec;
+    for (int c = lane; c < row_vec; c += 64) dst[c] = src[c];
+  }
+}
+
 }  // namespace
+
+size_t ffn_masked_workspace_size(int num_local, int hidden, int inter, int cap, bool bf16) {
+  const size_t rows = (size_t)num_local * cap;
+  return align256((size_t)(num_local + 1) * sizeof(int)) + align256(rows * sizeof(int)) +
+         align256(rows * hidden * (bf16 ? 2 : 4)) + ffn_workspace_size(num_local, hidden, inter, (int)rows, bf16);
+}
+
+hipError_t launch_ffn_masked(const FfnMaskedArgs& a, hipStream_t s) {
+  const long rows = (long)a.num_local * a.cap;
+  if (rows == 0) return hipSuccess;
+  char* ws = (char*)a.workspace;
+  int* offsets = (int*)ws;
+  ws += align256((size_t)(a.num_local + 1) * sizeof(int));
+  int* row_index = (int*)ws;
+  ws += align256((size_t)rows * sizeof(int));
+  void* o_compact = ws;
+  const size_t row_bytes = (size_t)a.hidden * (a.bf16 ? 2 : 4);
+  ws += align256((size_t)rows * row_bytes);
+  hipLaunchKernelGGL(masked_plan_kernel, dim3(1), dim3(1024), 0, s, a.counts, a.num_local, a.cap, offsets,
+                     row_index);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  FfnArgs f{a.x_slots, row_index, 1, offsets, a.w_gate_up, a.w_down, a.num_local, a.hidden, a.inter, (int)rows,
+            a.bf16, o_compact, ws};
+  err = launch_ffn(f, s);
+  if (err != hipSuccess) return err;
+  const int blocks = (int)std::min<long>((rows + 3) / 4, 2048);
+  hipLaunchKernelGGL(masked_scatter_kernel, dim3(blocks), dim3(256), 0, s, (const uint4*)o_compact, row_index,
+                     offsets, a.num_local, (int)(row_bytes / 16), (uint4*)a.o_slots);
+  return hipGetLastError();
+}
 
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
   if (a.capacity == 0) return hipSuccess;

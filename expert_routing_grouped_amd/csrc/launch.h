@@ -30,6 +30,7 @@ struct DispatchArgs {
   void* workspace;
   int capacity;   // rows kept per expert (first come, first served); INT32_MAX = no limit
   int* demand;    // null, or [num_local] out: assignments per expert before the cap
+  int fixed_slots = 0;  // rows of expert e start at e * capacity (offsets may be null)
 };
 size_t dispatch_workspace_size(int n, int num_local);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
@@ -49,6 +50,23 @@ struct FfnArgs {
 };
 size_t ffn_workspace_size(int num_local, int hidden, int inter, int capacity, bool bf16);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
+
+// The expert FFN on fixed per-expert slots of `cap` rows with a valid count per
+// expert (the masked layout): a plan kernel, the grouped FFN through a row
+// index, and a scatter of the outputs back to the slot rows.
+struct FfnMaskedArgs {
+  const void* x_slots;   // [num_local * cap, hidden]
+  const int* counts;     // [num_local] valid rows per expert (clamped to [0, cap])
+  int cap;
+  const void* w_gate_up;
+  const void* w_down;
+  int num_local, hidden, inter;
+  bool bf16;
+  void* o_slots;         // [num_local * cap, hidden] out: valid rows written
+  void* workspace;
+};
+size_t ffn_masked_workspace_size(int num_local, int hidden, int inter, int cap, bool bf16);
+hipError_t launch_ffn_masked(const FfnMaskedArgs& a, hipStream_t s);
 
 // FP8 (e4m3 codes, float32 block scales) expert FFN and row quantiser.
 struct FfnFp8Args {

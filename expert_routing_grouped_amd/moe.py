@@ -32,7 +32,11 @@ _SIGNATURES = {
                                     ctypes.c_size_t, _P]),
     "moe_dispatch_capacity": (ctypes.c_int, [_P, _I, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P,
                                              _P, _P, ctypes.c_size_t, _P]),
+    "moe_dispatch_masked": (ctypes.c_int, [_P, _I, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P,
+                                           ctypes.c_size_t, _P]),
     "moe_expert_capacity": (ctypes.c_int, [_I, _I, _I, ctypes.c_int64, ctypes.c_int64, _P]),
+    "moe_expert_ffn_masked_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "moe_expert_ffn_masked": (ctypes.c_int, [_P, _P, _I, _P, _P, _I, _I, _I, _I, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "moe_expert_ffn": (ctypes.c_int, [_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P,
                                       ctypes.c_size_t, _P]),
@@ -189,6 +193,83 @@ def moe_dispatch(topk_ids, expert_begin, num_local_experts, x=None, out=None, st
                                        _ptr(o["x_sorted"]), ws_ptr, ws_bytes, _stream(stream)),
            "moe_dispatch_capacity")
     return o
+
+
+def moe_dispatch_masked(topk_ids, expert_begin, num_local_experts, capacity, x=None, out=None,
+                        stream=None):
+    """Capped dispatch into fixed per-expert slots of `capacity` rows (the masked layout).
+
+    Returns dict(counts, demand, slot_assign [E_loc * C], assign_pos [T * k], x_slots or None)."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    o = dict(out or {})
+    n = T * k
+    rows = num_local_experts * int(capacity)
+    o.setdefault("counts", torch.empty(num_local_experts, dtype=torch.int32, device=dev))
+    o.setdefault("demand", torch.empty(num_local_experts, dtype=torch.int32, device=dev))
+    o.setdefault("slot_assign", torch.empty(max(rows, 1), dtype=torch.int32, device=dev))
+    o.setdefault("assign_pos", torch.empty(max(n, 1), dtype=torch.int32, device=dev))
+    for name, need_n in (("counts", num_local_experts), ("demand", num_local_experts),
+                         ("slot_assign", rows), ("assign_pos", n)):
+        _at_least(_dev(o[name], torch.int32, name), need_n, name)
+    hidden, dtype = 0, MOE_BF16
+    if x is not None:
+        dtype = _code(x.dtype)
+        _dev(x, x.dtype, "x")
+        if x.dim() != 2 or x.shape[0] < T:
+            raise MoeError(f"x must be [>= {T}, hidden], got {tuple(x.shape)}")
+        hidden = x.shape[1]
+        o.setdefault("x_slots", torch.empty((max(rows, 1), hidden), dtype=x.dtype, device=dev))
+        xs = _dev(o["x_slots"], x.dtype, "x_slots")
+        if xs.dim() != 2 or xs.shape[1] != hidden or xs.shape[0] < rows:
+            raise MoeError(f"x_slots must be [>= {rows}, {hidden}], got {tuple(xs.shape)}")
+    else:
+        o["x_slots"] = None
+    need = int(lib().moe_dispatch_workspace_size(T, k, num_local_experts))
+    ws = o.get("workspace")
+    if need and (ws is None or ws.numel() < need):
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib().moe_dispatch_masked(_ptr(topk_ids), T, k, expert_begin, num_local_experts, int(capacity),
+                                     _ptr(x), hidden, dtype, _ptr(o["counts"]), _ptr(o["demand"]),
+                                     _ptr(o["slot_assign"]), _ptr(o["assign_pos"]), _ptr(o["x_slots"]),
+                                     _ptr(ws if need else None), ws.numel() if need else 0, _stream(stream)),
+           "moe_dispatch_masked")
+    return o
+
+
+def moe_expert_ffn_masked(x_slots, expert_counts, capacity, w_gate_up, w_down, o_slots=None,
+                          workspace=None, stream=None):
+    """Grouped SwiGLU FFN on the masked layout; returns o_slots [E_loc * C, d] (valid rows written)."""
+    dt = x_slots.dtype
+    _dev(x_slots, dt, "x_slots")
+    _dev(expert_counts, torch.int32, "expert_counts")
+    _dev(w_gate_up, dt, "w_gate_up")
+    _dev(w_down, dt, "w_down")
+    E_loc, two_i, d2 = w_gate_up.shape
+    inter = two_i // 2
+    hidden = x_slots.shape[1]
+    rows = E_loc * int(capacity)
+    _at_least(expert_counts, E_loc, "expert_counts")
+    if d2 != hidden or tuple(w_down.shape) != (E_loc, hidden, inter):
+        raise MoeError("weight shapes do not match x_slots")
+    if x_slots.shape[0] < rows:
+        raise MoeError(f"x_slots holds {x_slots.shape[0]} rows, {rows} needed")
+    if o_slots is None:
+        o_slots = torch.zeros((max(rows, 1), hidden), dtype=dt, device=x_slots.device)
+    _dev(o_slots, dt, "o_slots")
+    if o_slots.shape[0] < rows or o_slots.shape[1] != hidden:
+        raise MoeError(f"o_slots must be [>= {rows}, {hidden}]")
+    need = int(lib().moe_expert_ffn_masked_workspace_size(E_loc, hidden, inter, int(capacity), _code(dt)))
+    if need == 0:
+        raise MoeError("moe_expert_ffn_masked: unsupported sizes")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x_slots.device)
+    _check(lib().moe_expert_ffn_masked(_ptr(x_slots), _ptr(expert_counts), int(capacity), _ptr(w_gate_up),
+                                       _ptr(w_down), E_loc, hidden, inter, _code(dt), _ptr(o_slots),
+                                       _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_expert_ffn_masked")
+    return o_slots
 
 
 def moe_expert_capacity(num_tokens, top_k, num_experts, factor_num, factor_den=1) -> int:
@@ -411,7 +492,7 @@ class MoELayer:
 
     def __init__(self, *, num_tokens, num_experts, top_k, num_groups, topk_groups, score_mode,
                  renormalize, expert_begin, num_local_experts, hidden, inter, dtype, device,
-                 fuse_gather=True, expert_capacity=None, fp8=False):
+                 fuse_gather=True, expert_capacity=None, fp8=False, masked_capacity=None):
         self.T, self.E, self.k = num_tokens, num_experts, top_k
         self.num_groups, self.topk_groups = num_groups, topk_groups
         self.score_mode, self.renormalize = score_mode, renormalize
@@ -422,6 +503,10 @@ class MoELayer:
         self.fp8 = fp8   # e4m3 weights with block scales; x is quantised per row in forward()
         if fp8 and not fuse_gather:
             raise MoeError("the FP8 layer reads the token rows through sorted_assign (fuse_gather=True)")
+        # masked layout: fixed slots of masked_capacity rows per local expert
+        self.masked_capacity = masked_capacity
+        if masked_capacity is not None and (fp8 or expert_capacity is not None):
+            raise MoeError("the masked layout is a bf16 / float32 layer with its own capacity")
         cap = num_tokens * top_k
         self.cap = cap
         dev = torch.device(device)
@@ -437,7 +522,20 @@ class MoELayer:
         dneed = int(lib().moe_dispatch_workspace_size(num_tokens, top_k, num_local_experts))
         if dneed:
             self.buf["dispatch_ws"] = torch.empty(dneed, dtype=torch.uint8, device=dev)
-        if hidden and fp8:
+        if masked_capacity is not None:
+            rows = max(num_local_experts * int(masked_capacity), 1)
+            self.buf.update(demand=torch.empty(num_local_experts, **i32),
+                            slot_assign=torch.empty(rows, **i32))
+            if hidden:
+                self.buf["x_slots"] = torch.zeros((rows, hidden), dtype=dtype, device=dev)
+                self.buf["o_slots"] = torch.zeros((rows, hidden), dtype=dtype, device=dev)
+                self.buf["y"] = torch.empty((num_tokens, hidden), dtype=dtype, device=dev)
+                need = int(lib().moe_expert_ffn_masked_workspace_size(
+                    num_local_experts, hidden, inter, int(masked_capacity), _code(dtype)))
+                if need == 0:
+                    raise MoeError("unsupported FFN sizes")
+                self.buf["workspace"] = torch.empty(need, dtype=torch.uint8, device=dev)
+        elif hidden and fp8:
             self.buf["x_codes"] = torch.empty((num_tokens, hidden), dtype=torch.uint8, device=dev)
             self.buf["x_scales"] = torch.empty((num_tokens, hidden // 128), dtype=torch.float32, device=dev)
             self.buf["o_sorted"] = torch.empty((max(cap, 1), hidden), dtype=torch.bfloat16, device=dev)
@@ -463,6 +561,14 @@ class MoELayer:
     def dispatch(self, x=None, stream=None):
         """Counting sort; also gathers x into x_sorted unless the gather is fused into the FFN."""
         b = self.buf
+        if self.masked_capacity is not None:
+            out = {n: b[n] for n in ("counts", "demand", "slot_assign", "assign_pos")}
+            if "dispatch_ws" in b:
+                out["workspace"] = b["dispatch_ws"]
+            if x is not None:
+                out["x_slots"] = b["x_slots"]
+            return moe_dispatch_masked(b["topk_ids"], self.expert_begin, self.num_local,
+                                       self.masked_capacity, x, out, stream)
         out = {n: b[n] for n in ("counts", "offsets", "sorted_assign", "assign_pos")}
         if "dispatch_ws" in b:
             out["workspace"] = b["dispatch_ws"]
@@ -484,6 +590,9 @@ class MoELayer:
     def ffn(self, w_gate_up, w_down, x=None, stream=None, w_gate_up_scales=None, w_down_scales=None):
         """The expert FFN; the FP8 layer reads the codes that quantize() left in self.buf."""
         b = self.buf
+        if self.masked_capacity is not None:
+            return moe_expert_ffn_masked(b["x_slots"], b["counts"], self.masked_capacity, w_gate_up, w_down,
+                                         b["o_slots"], b["workspace"], stream)
         if self.fp8:
             return moe_expert_ffn_fp8(b["x_codes"], b["x_scales"], b["offsets"], w_gate_up, w_gate_up_scales, w_down,
                                       w_down_scales, row_index=b["sorted_assign"], row_index_div=self.k,
@@ -499,8 +608,8 @@ class MoELayer:
 
     def combine(self, stream=None):
         b = self.buf
-        return moe_combine(b["o_sorted"], b["assign_pos"], b["topk_weights"], b["y"].dtype, b["y"],
-                           stream)
+        o = b["o_slots"] if self.masked_capacity is not None else b["o_sorted"]
+        return moe_combine(o, b["assign_pos"], b["topk_weights"], b["y"].dtype, b["y"], stream)
 
     def forward(self, scores, x=None, w_gate_up=None, w_down=None, stream=None, w_gate_up_scales=None,
                 w_down_scales=None):

@@ -56,6 +56,7 @@ class Workload:
     seed: int = 0
     capacity_factor: str | None = None   # per-expert cap C = ceil(c T k / E), c as an exact decimal
     weight_format: str = "same"          # "fp8_e4m3_b128": x and expert weights as e4m3 with block scales
+    layout: str = "grouped"              # "masked": fixed slots of C rows per local expert
 
     @property
     def has_ffn(self) -> bool:
@@ -93,6 +94,13 @@ WORKLOADS = {
                               score_mode="raw", renormalize=True, bias_std=1.0,
                               hidden=7168, inter=2048, expert_begin=0, num_local=8, dtype="bf16",
                               weight_format="fp8_e4m3_b128"),
+    # decode_ep on the masked layout (fixed slots of C = ceil(2 T k / E) = 32 rows per local
+    # expert, the busiest expert's load at seed 0, so nothing is dropped): the layout of the
+    # grouped GEMM that the INFRA page measures on its EP32 shape (8 experts per card).
+    "decode_ep_masked": Workload("decode_ep_masked", T=512, E=256, top_k=8, num_groups=8, topk_groups=4,
+                                 score_mode="raw", renormalize=True, bias_std=1.0,
+                                 hidden=7168, inter=2048, expert_begin=0, num_local=8, dtype="bf16",
+                                 capacity_factor="2", layout="masked"),
     # The capacity-factor example of ch15 section 4.3 (T = 5600 tokens, k = 16
     # of E = 896 experts, c = 1.2: C = 120), routing and capped dispatch only:
     # no groups, scores drawn as above (the page gives no score distribution)

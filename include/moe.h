@@ -4,7 +4,8 @@
  *
  *   moe_route       group-limited top-k routing of each token
  *   moe_dispatch    counting-sort permutation of token rows to local experts
- *                   (moe_dispatch_capacity: the same with a per-expert capacity)
+ *                   (moe_dispatch_capacity: the same with a per-expert capacity;
+ *                   moe_dispatch_masked: into fixed per-expert slots)
  *   moe_expert_ffn  grouped SwiGLU expert FFN (fused gate_up GEMM, SiLU*up, down GEMM)
  *   moe_combine     router-weighted sum of the expert outputs, back in token order
  *
@@ -278,6 +279,56 @@ moe_status_t moe_expert_ffn(const void* x, const int32_t* row_index, int32_t row
                             const void* w_down, int32_t num_local_experts, int32_t hidden,
                             int32_t inter, int32_t row_capacity, int32_t dtype, void* o_sorted,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_dispatch_masked -- the capped dispatch of moe_dispatch_capacity into
+ * fixed per-expert slots: the "masked" layout of the grouped GEMM that the
+ * INFRA page measures (H20 paragraph, DeepGEMM masked). Local expert e owns
+ * slot rows [e * C, (e + 1) * C); its first C assignments in assignment order
+ * a = t * k + j take rows e * C, e * C + 1, ...; the others are dropped
+ * (ch15 section 4.3, capacity factor, drop policy). C = expert_capacity.
+ * expert_counts   [E_loc] out: rows used per expert, min(assignments, C).
+ * expert_demand   [E_loc] out, or NULL: assignments per expert before the cap.
+ * slot_assign     [E_loc * C] out: the assignment in each used slot row; rows
+ *                 at or past their expert's count are not written (may be
+ *                 NULL when C = 0).
+ * assign_pos      [T * k] out: slot row of each assignment, -1 when dropped or
+ *                 not local (moe_combine reads the slot-layout outputs with it).
+ * x, x_slots      as in moe_dispatch, x_slots [E_loc * C, hidden]: used rows
+ *                 are exact copies of their token's row, the others untouched.
+ * Workspace and other limits: those of moe_dispatch; E_loc * C < 2^31.
+ */
+moe_status_t moe_dispatch_masked(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
+                                 int32_t expert_begin, int32_t num_local_experts,
+                                 int32_t expert_capacity, const void* x, int32_t hidden,
+                                 int32_t dtype, int32_t* expert_counts, int32_t* expert_demand,
+                                 int32_t* slot_assign, int32_t* assign_pos, void* x_slots,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace moe_expert_ffn_masked needs; 0 when the sizes are invalid. */
+size_t moe_expert_ffn_masked_workspace_size(int32_t num_local_experts, int32_t hidden,
+                                            int32_t inter, int32_t expert_capacity, int32_t dtype);
+
+/*
+ * moe_expert_ffn_masked -- moe_expert_ffn on the masked layout: for each local
+ * expert e only its valid slot rows [e * C, e * C + min(counts[e], C)) of
+ * x_slots go through the expert, and their outputs go to the same rows of
+ * o_slots; every other row of o_slots is left untouched, and no expert does
+ * any work for its padding rows.
+ * x_slots         [E_loc * C, hidden] (dtype), e.g. from moe_dispatch_masked.
+ * expert_counts   [E_loc] int32, read on the device (negative counts count as 0).
+ * w_gate_up, w_down, dtype, hidden, inter: as in moe_expert_ffn.
+ * o_slots         [E_loc * C, hidden] (dtype) out.
+ * workspace       >= moe_expert_ffn_masked_workspace_size bytes (compact
+ *                 offsets, the row index, compact outputs and h); contents
+ *                 need not be initialised.
+ * Limits: those of moe_expert_ffn with row_capacity = E_loc * C.
+ */
+moe_status_t moe_expert_ffn_masked(const void* x_slots, const int32_t* expert_counts,
+                                   int32_t expert_capacity, const void* w_gate_up,
+                                   const void* w_down, int32_t num_local_experts, int32_t hidden,
+                                   int32_t inter, int32_t dtype, void* o_slots, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_expert_ffn_noalloc -- moe_expert_ffn for callers that cannot allocate

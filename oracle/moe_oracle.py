@@ -67,7 +67,8 @@ import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64", "route_softmax_topk", "route_grouped", "route",
-    "dispatch", "expert_capacity", "dispatch_capacity", "gather_rows", "expert_ffn",
+    "dispatch", "expert_capacity", "dispatch_capacity", "dispatch_masked", "gather_rows",
+    "expert_ffn", "expert_ffn_masked",
     "expert_ffn_rows", "combine", "layer",
 ]
 
@@ -246,6 +247,52 @@ def dispatch_capacity(topk_ids: np.ndarray, expert_begin: int, num_local: int, c
     assign_pos[sorted_assign] = np.arange(sorted_assign.shape[0])
     return (counts.astype(np.int32), offsets.astype(np.int32), sorted_assign.astype(np.int32),
             assign_pos.astype(np.int32), demand.astype(np.int32))
+
+
+def dispatch_masked(topk_ids: np.ndarray, expert_begin: int, num_local: int, capacity: int):
+    """Dispatch into fixed per-expert slots, the "masked" layout of the grouped GEMM that the
+    INFRA page measures ("推理 INFRA 方法论（2）", H20 paragraph: DeepGEMM masked), with the
+    capacity and drop policy of CH15 section 4.3.
+
+    Local expert e owns slot rows [e * C, (e + 1) * C) of a [num_local * C] buffer; its first C
+    assignments in assignment order a = t * k + j take rows e * C, e * C + 1, ...; later ones
+    are dropped. Written as one pass over the assignments with a running count per expert.
+    Returns (counts = rows used per expert, slot_assign [num_local * C] = assignment in each
+    slot row or -1 where empty, assign_pos [T * k] = slot row or -1, demand), int32.
+    """
+    flat = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    demand = np.zeros(num_local, dtype=np.int64)
+    slot_assign = np.full(num_local * capacity, -1, dtype=np.int64)
+    assign_pos = np.full(flat.shape[0], -1, dtype=np.int64)
+    for a, expert in enumerate(flat.tolist()):
+        e = expert - expert_begin
+        if 0 <= e < num_local:
+            if demand[e] < capacity:
+                row = e * capacity + int(demand[e])
+                slot_assign[row] = a
+                assign_pos[a] = row
+            demand[e] += 1
+    counts = np.minimum(demand, capacity)
+    return (counts.astype(np.int32), slot_assign.astype(np.int32), assign_pos.astype(np.int32),
+            demand.astype(np.int32))
+
+
+def expert_ffn_masked(x_slots: np.ndarray, counts: np.ndarray, capacity: int, w_gate_up: np.ndarray,
+                      w_down: np.ndarray) -> np.ndarray:
+    """The expert FFN on the masked layout: for local expert e only its first counts[e] slot rows,
+    [e * C, e * C + counts[e]), go through the expert (the rest of its slots are padding and have
+    no output). Returns o [num_local * C, d] float64 with zero rows where there is no output."""
+    counts = np.asarray(counts, dtype=np.int64)
+    E_loc = counts.shape[0]
+    I = w_gate_up.shape[1] // 2
+    out = np.zeros((E_loc * capacity, w_gate_up.shape[2]), dtype=np.float64)
+    for e in range(E_loc):
+        m = int(min(max(counts[e], 0), capacity))
+        if m == 0:
+            continue
+        lo = e * capacity
+        out[lo:lo + m] = _one_expert(_decode(x_slots[lo:lo + m]), w_gate_up[e], w_down[e], I)
+    return out
 
 
 def gather_rows(x: np.ndarray, sorted_assign: np.ndarray, top_k: int) -> np.ndarray:

@@ -117,6 +117,28 @@ def test_expert_capacity_is_exact():
     assert l.moe_expert_capacity(1 << 20, 1024, 1, 3, 1, ctypes.byref(out)) == 2  # C >= 2^31
 
 
+def test_masked_validation_and_workspace():
+    l = moe.lib()
+    p = ctypes.c_void_p(256)
+    W = (None, 0, None)
+    # (ids, T, k, begin, nloc, C, x, hidden, dtype, counts, demand, slot_assign, pos, x_slots, ws...)
+    assert l.moe_dispatch_masked(p, 4, 8, 0, 8, -1, None, 0, 1, p, None, p, p, None, *W) == 1   # C < 0
+    assert l.moe_dispatch_masked(p, 4, 8, 0, 8, 4, None, 0, 1, None, None, p, p, None, *W) == 1  # counts
+    assert l.moe_dispatch_masked(p, 4, 8, 0, 8, 4, None, 0, 1, p, None, None, p, None, *W) == 1  # slots
+    assert l.moe_dispatch_masked(p, 4, 8, 0, 1024, 1 << 21, None, 0, 1, p, None, p, p, None, *W) == 2
+    assert l.moe_dispatch_masked(p, 8192, 8, 0, 32, 4, None, 0, 1, p, None, p, p, None, *W) == 3
+    # FFN: workspace = compact offsets + row index + compact outputs + the FFN's own workspace
+    need = l.moe_expert_ffn_masked_workspace_size(8, 7168, 2048, 32, 1)
+    assert need >= 8 * 32 * 7168 * 2 + l.moe_expert_ffn_workspace_size(8, 7168, 2048, 8 * 32, 1)
+    assert l.moe_expert_ffn_masked_workspace_size(8, 7000, 2048, 32, 1) == 0
+    assert l.moe_expert_ffn_masked_workspace_size(8, 7168, 2048, -1, 1) == 0
+    args = [p, p, 32, p, p, 8, 7168, 2048, 1, p]
+    assert l.moe_expert_ffn_masked(*args, p, 16, None) == 3                      # small workspace
+    assert l.moe_expert_ffn_masked(p, None, 32, p, p, 8, 7168, 2048, 1, p, p, need, None) == 1   # counts
+    assert l.moe_expert_ffn_masked(p, p, -2, p, p, 8, 7168, 2048, 1, p, p, need, None) == 1
+    assert l.moe_expert_ffn_masked(p, p, 32, p, p, 8, 7000, 2048, 1, p, p, need, None) == 2
+
+
 def test_ffn_validation_and_workspace():
     l = moe.lib()
     p = ctypes.c_void_p(256)

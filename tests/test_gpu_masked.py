@@ -1,0 +1,150 @@
+"""GPU parity of the masked (fixed per-expert slot) layout against the oracle, through the C ABI:
+moe_dispatch_masked bit-exact (counts, demand, slot rows, assign_pos, gathered rows), and
+moe_expert_ffn_masked within the bf16 / float32 bars on every valid slot row, with every other
+row of the output left untouched; then the whole layer with the masked calls.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from expert_routing_grouped_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from expert_routing_grouped_amd import moe  # noqa: E402
+from expert_routing_grouped_amd.tensors import to_device, to_host  # noqa: E402
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(gpu):
+    moe.lib()
+    yield
+
+
+def rel_err(got, ref):
+    scale = np.abs(ref).max()
+    return float(np.abs(got - ref).max() / scale) if scale > 0 else float(np.abs(got).max())
+
+
+def check_dispatch_masked(ids, begin, nloc, C, x=None):
+    print(f"dispatch_masked T={ids.shape[0]} k={ids.shape[1]} local=[{begin},{begin + nloc}) C={C} "
+          f"x={x is not None}", flush=True)
+    d_ids = to_device(np.ascontiguousarray(ids, dtype=np.int32), DEV)
+    d_x = to_device(x, DEV) if x is not None else None
+    rows = nloc * C
+    out = {"slot_assign": torch.full((max(rows, 1),), -7, dtype=torch.int32, device=DEV)}
+    if x is not None:
+        out["x_slots"] = torch.zeros((max(rows, 1), x.shape[1]),
+                                     dtype=torch.bfloat16 if x.dtype == np.uint16 else torch.float32,
+                                     device=DEV)
+    o = moe.moe_dispatch_masked(d_ids, begin, nloc, C, d_x, out)
+    torch.cuda.synchronize()
+    counts, slot_assign, pos, demand = oracle.dispatch_masked(ids, begin, nloc, C)
+    assert np.array_equal(to_host(o["counts"]), counts)
+    assert np.array_equal(to_host(o["demand"]), demand)
+    assert np.array_equal(to_host(o["assign_pos"])[:ids.size], pos)
+    got_sa = to_host(o["slot_assign"])[:rows]
+    used = slot_assign >= 0
+    assert np.array_equal(got_sa[used], slot_assign[used])
+    assert (got_sa[~used] == -7).all()          # unused slot rows are not written
+    if x is not None:
+        xs = to_host(o["x_slots"])[:rows]
+        assert np.array_equal(xs[used], np.asarray(x)[slot_assign[used] // ids.shape[1]])
+        assert (xs[~used] == 0).all()
+    return o
+
+
+@pytest.mark.parametrize("T,k,E,begin,nloc,C", [
+    (37, 3, 16, 3, 5, 4), (512, 8, 256, 0, 8, 32), (512, 8, 256, 0, 8, 5), (100, 2, 8, 0, 8, 0),
+    (1000, 8, 64, 0, 64, 1000), (1100, 8, 1024, 0, 1024, 3), (9000, 4, 96, 0, 96, 300)])
+def test_dispatch_masked_ragged(T, k, E, begin, nloc, C):
+    rng = np.random.default_rng(T + 31 * C)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    x = rng.standard_normal((T, 64)).astype(np.float32)
+    check_dispatch_masked(ids, begin, nloc, C, x if nloc * C > 0 else None)
+
+
+def test_dispatch_masked_capacity_workload():
+    """The capacity-factor example's shape (T = 5600, k = 16 of E = 896, c = 1.2 -> C = 120):
+    multi-workgroup sort into 896 x 120 slots."""
+    wl = W.WORKLOADS["capacity_route"]
+    inp = W.generate(wl)
+    ids, _ = oracle.route_grouped(inp.scores, wl.top_k, 1, 1)
+    check_dispatch_masked(ids, 0, wl.num_local, oracle.expert_capacity(wl.T, wl.top_k, wl.E, "1.2"))
+
+
+def _ffn_masked_case(wl, C, dtype, seed):
+    inp = W.generate(wl)
+    ids, _ = oracle.route(inp.scores, wl.top_k, wl.num_groups, wl.topk_groups, wl.score_mode, wl.renormalize)
+    counts, slot_assign, pos, demand = oracle.dispatch_masked(ids, wl.expert_begin, wl.num_local, C)
+    rows = wl.num_local * C
+    used = slot_assign >= 0
+    x_slots = np.zeros((rows, wl.hidden), dtype=inp.x.dtype)
+    x_slots[used] = inp.x[slot_assign[used] // wl.top_k]
+    # padding rows hold large values: they must not reach any output
+    x_slots[~used] = inp.x[0] * 0 + (np.uint16(0x4780) if dtype == "bf16" else np.float32(65536.0))
+    print(f"ffn_masked {wl.name} C={C} rows used {int(used.sum())} of {rows}", flush=True)
+    d_x = to_device(x_slots, DEV)
+    sentinel = 12288.0          # exact in bf16
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    o_slots = torch.full((rows, wl.hidden), sentinel, dtype=tdt, device=DEV)
+    moe.moe_expert_ffn_masked(d_x, to_device(counts, DEV), C, to_device(inp.w_gate_up, DEV),
+                              to_device(inp.w_down, DEV), o_slots)
+    torch.cuda.synchronize()
+    got = to_host(o_slots)
+    got = oracle.bf16_bits_to_f64(got) if dtype == "bf16" else got.astype(np.float64)
+    ref = oracle.expert_ffn_masked(x_slots, counts, C, inp.w_gate_up, inp.w_down)
+    e = rel_err(got[used], ref[used])
+    print(f"  rel_err o={e:.2e}", flush=True)
+    assert e <= (2e-2 if dtype == "bf16" else 1e-4)
+    assert (got[~used] == sentinel).all()
+    return inp, ids, counts, pos
+
+
+@pytest.mark.parametrize("name,C", [("decode_ep", 32), ("decode_ep", 9), ("decode_tp", 12), ("toy_fp32", 40)])
+def test_ffn_masked_matches_oracle(name, C):
+    wl = W.WORKLOADS[name]
+    _ffn_masked_case(wl, C, wl.dtype, 0)
+
+
+def test_ffn_masked_random_small_shapes():
+    for seed in range(4):
+        rng = np.random.default_rng(500 + seed)
+        E = int(rng.choice([8, 16, 32]))
+        nloc = int(rng.integers(1, E + 1))
+        wl = W.Workload(f"masked{seed}", T=int(rng.integers(1, 300)), E=E, top_k=int(rng.integers(1, 5)),
+                        num_groups=1, topk_groups=1, score_mode="raw", renormalize=True, bias_std=1.0,
+                        hidden=256 * int(rng.integers(1, 4)), inter=64 * int(rng.integers(1, 4)),
+                        expert_begin=int(rng.integers(0, E - nloc + 1)), num_local=nloc, dtype="bf16",
+                        seed=seed)
+        _ffn_masked_case(wl, int(rng.integers(1, 80)), "bf16", seed)
+
+
+def test_masked_layer_matches_oracle():
+    """route -> moe_dispatch_masked (C = 16 of decode_ep's up to 32 rows per expert, so some
+    assignments are dropped) -> moe_expert_ffn_masked -> moe_combine over the slot rows."""
+    wl = W.WORKLOADS["decode_ep"]
+    C = 16
+    inp = W.generate(wl)
+    scores, x = to_device(inp.scores, DEV), to_device(inp.x, DEV)
+    ids, w = moe.moe_route(scores, wl.top_k, wl.num_groups, wl.topk_groups)
+    d = moe.moe_dispatch_masked(ids, wl.expert_begin, wl.num_local, C, x)
+    o = moe.moe_expert_ffn_masked(d["x_slots"], d["counts"], C, to_device(inp.w_gate_up, DEV),
+                                  to_device(inp.w_down, DEV))
+    y = moe.moe_combine(o, d["assign_pos"], w)
+    torch.cuda.synchronize()
+    rids, rw = oracle.route(inp.scores, wl.top_k, wl.num_groups, wl.topk_groups, "raw", True)
+    counts, slot_assign, pos, demand = oracle.dispatch_masked(rids, wl.expert_begin, wl.num_local, C)
+    assert int((demand - counts).sum()) > 0          # the cap drops some assignments
+    used = slot_assign >= 0
+    x_slots = np.zeros((wl.num_local * C, wl.hidden), dtype=np.uint16)
+    x_slots[used] = inp.x[slot_assign[used] // wl.top_k]
+    ref_o = oracle.expert_ffn_masked(x_slots, counts, C, inp.w_gate_up, inp.w_down)
+    ref_y = oracle.combine(ref_o, pos, rw)
+    assert np.array_equal(to_host(d["assign_pos"]), pos)
+    e = rel_err(oracle.bf16_bits_to_f64(to_host(y)), ref_y)
+    print(f"masked layer rel_err y={e:.2e}", flush=True)
+    assert e <= 2e-2
