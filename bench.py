@@ -138,7 +138,8 @@ def routing_stats(wl, topk_ids, counts):
     """Load statistics of the routed batch (ch15 page, section 4.3 "负载均衡"): the
     imbalance R = max_e n_e / mean_e n_e over all experts of the layer, and over
     this GPU's local experts; rows of the busiest local expert."""
-    n_all = np.bincount(np.asarray(topk_ids, dtype=np.int64).ravel(), minlength=wl.E)
+    ids = np.asarray(topk_ids, dtype=np.int64).ravel()
+    n_all = np.bincount(ids[ids >= 0], minlength=wl.E)      # dropped slots (-1) excluded
     counts = np.asarray(counts, dtype=np.int64)
     return dict(assignments=int(n_all.sum()), r_imbalance_all_experts=float(n_all.max() / n_all.mean()),
                 r_imbalance_local=float(counts.max() / counts.mean()) if counts.sum() else 0.0,
@@ -167,8 +168,10 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
                          num_groups=wl.num_groups, topk_groups=wl.topk_groups, score_mode=mode,
                          renormalize=wl.renormalize, expert_begin=wl.expert_begin,
                          num_local_experts=wl.num_local, hidden=wl.hidden, inter=wl.inter,
-                         dtype=dt, device=dev, expert_capacity=None if wl.layout == "masked" else cap,
-                         fp8=fp8, masked_capacity=cap if wl.layout == "masked" else None)
+                         dtype=dt, device=dev,
+                         expert_capacity=cap if (wl.layout != "masked" and wl.overflow == "drop") else None,
+                         fp8=fp8, masked_capacity=cap if wl.layout == "masked" else None,
+                         reroute_capacity=cap if wl.overflow == "reroute" else None)
     scores = to_device(inp.scores, dev)
     x = to_device(inp.x, dev) if wl.has_ffn else None
     weights = []
@@ -280,7 +283,11 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
         M = int(counts.sum())
         route_bytes = wl.T * wl.E * 4 + wl.T * wl.top_k * 8
         res.update(M=M, route_gbs=route_bytes / (parts_us[0] * 1e-6) / 1e9)
-        if cap is not None:
+        if cap is not None and wl.overflow == "reroute":
+            ids = to_host(layer.buf["topk_ids"])
+            res.update(capacity=cap, overflow="reroute", dropped=int((ids < 0).sum()),
+                       max_load=int(to_host(layer.buf["expert_load"]).max()))
+        elif cap is not None:
             demand = to_host(layer.buf["demand"])
             res.update(capacity=cap, assignments=int(demand.sum()), dropped=int(demand.sum()) - M,
                        experts_over_capacity=int((demand > cap).sum()))

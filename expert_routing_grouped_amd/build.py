@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
-SOURCES = ["api.hip", "route.hip", "dispatch.hip", "ffn.hip", "ffn_fp8.hip", "combine.hip", "eplb.hip"]
+SOURCES = ["api.hip", "route.hip", "dispatch.hip", "ffn.hip", "ffn_fp8.hip", "combine.hip", "eplb.hip",
+           "reroute.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",

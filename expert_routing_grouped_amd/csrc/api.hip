@@ -59,10 +59,8 @@ const char* moe_status_string(moe_status_t status) {
   return "unknown status";
 }
 
-moe_status_t moe_route(const float* scores, int32_t num_tokens, int32_t num_experts,
-                       int32_t top_k, int32_t num_groups, int32_t topk_groups,
-                       int32_t score_mode, int32_t renormalize, int32_t* topk_ids,
-                       float* topk_weights, hipStream_t stream) {
+static moe_status_t check_route_args(int32_t num_tokens, int32_t num_experts, int32_t top_k,
+                                     int32_t num_groups, int32_t topk_groups, int32_t score_mode) {
   if (num_tokens < 0 || num_experts < 1 || top_k < 1 || num_groups < 1 || topk_groups < 1)
     return MOE_ERR_INVALID;
   if (score_mode != MOE_SCORE_SOFTMAX && score_mode != MOE_SCORE_RAW) return MOE_ERR_INVALID;
@@ -73,12 +71,50 @@ moe_status_t moe_route(const float* scores, int32_t num_tokens, int32_t num_expe
   if (score_mode == MOE_SCORE_SOFTMAX && num_groups != 1) return MOE_ERR_INVALID;
   if (num_experts > 1024 || top_k > 64 || num_groups > 64) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)num_tokens * num_experts >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t moe_route(const float* scores, int32_t num_tokens, int32_t num_experts,
+                       int32_t top_k, int32_t num_groups, int32_t topk_groups,
+                       int32_t score_mode, int32_t renormalize, int32_t* topk_ids,
+                       float* topk_weights, hipStream_t stream) {
+  const moe_status_t st = check_route_args(num_tokens, num_experts, top_k, num_groups, topk_groups,
+                                           score_mode);
+  if (st != MOE_OK) return st;
   if (num_tokens == 0) return MOE_OK;
   if (!scores || !topk_ids || !topk_weights) return MOE_ERR_INVALID;
   moe::RouteArgs a{scores,      num_tokens,  num_experts, top_k,   num_groups, topk_groups,
                    score_mode == MOE_SCORE_SOFTMAX ? 1 : 0, renormalize ? 1 : 0, topk_ids,
                    topk_weights};
   return from_hip(moe::launch_route(a, stream));
+}
+
+size_t moe_route_reroute_workspace_size(int32_t num_tokens, int32_t num_experts, int32_t top_k,
+                                        int32_t num_groups, int32_t topk_groups) {
+  if (check_route_args(num_tokens, num_experts, top_k, num_groups, topk_groups, MOE_SCORE_RAW) != MOE_OK)
+    return 0;
+  if ((int64_t)num_tokens * 64 >= ((int64_t)1 << 31) - 65536) return 0;
+  return moe::reroute_workspace_size(num_tokens, num_experts, top_k, num_groups, topk_groups);
+}
+
+moe_status_t moe_route_reroute(const float* scores, int32_t num_tokens, int32_t num_experts,
+                               int32_t top_k, int32_t num_groups, int32_t topk_groups,
+                               int32_t renormalize, int32_t expert_capacity, int32_t* topk_ids,
+                               float* topk_weights, int32_t* expert_load, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  const moe_status_t st = check_route_args(num_tokens, num_experts, top_k, num_groups, topk_groups,
+                                           MOE_SCORE_RAW);
+  if (st != MOE_OK) return st;
+  if (expert_capacity < 0) return MOE_ERR_INVALID;
+  // the ranking and both counting sorts hold T * 2k assignments in 32-bit ints
+  if ((int64_t)num_tokens * 64 >= ((int64_t)1 << 31) - 65536) return MOE_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MOE_OK;
+  if (!scores || !topk_ids || !topk_weights) return MOE_ERR_INVALID;
+  const size_t need = moe::reroute_workspace_size(num_tokens, num_experts, top_k, num_groups, topk_groups);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
+  moe::RerouteArgs a{scores, num_tokens, num_experts, top_k, num_groups, topk_groups,
+                     renormalize ? 1 : 0, expert_capacity, topk_ids, topk_weights, expert_load, workspace};
+  return from_hip(moe::launch_route_reroute(a, stream));
 }
 
 size_t moe_dispatch_workspace_size(int32_t num_tokens, int32_t top_k, int32_t num_local_experts) {

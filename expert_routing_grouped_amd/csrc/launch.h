@@ -16,6 +16,19 @@ struct RouteArgs {
 };
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 
+// Routing with a per-expert capacity and the next-best expert overflow policy.
+struct RerouteArgs {
+  const float* scores;
+  int T, E, k, num_groups, topk_groups, renormalize, cap;
+  int* ids;        // [T, k] out
+  float* weights;  // [T, k] out
+  int* load;       // [E] out or null: assignments each expert ends with
+  void* workspace;
+};
+int reroute_ranks(int E, int k, int num_groups, int topk_groups);
+size_t reroute_workspace_size(int T, int E, int k, int num_groups, int topk_groups);
+hipError_t launch_route_reroute(const RerouteArgs& a, hipStream_t s);
+
 struct DispatchArgs {
   const int* ids;
   int n;  // T * k assignments

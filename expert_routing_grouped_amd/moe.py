@@ -27,6 +27,8 @@ _SIGNATURES = {
     "moe_abi_version": (ctypes.c_int32, []),
     "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_route": (ctypes.c_int, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "moe_route_reroute_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "moe_route_reroute": (ctypes.c_int, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_dispatch_workspace_size": (ctypes.c_size_t, [_I, _I, _I]),
     "moe_dispatch": (ctypes.c_int, [_P, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P,
                                     ctypes.c_size_t, _P]),
@@ -137,6 +139,33 @@ def moe_route(scores, top_k, num_groups=1, topk_groups=1, score_mode=MOE_SCORE_R
                            int(bool(renormalize)), _ptr(topk_ids), _ptr(topk_weights),
                            _stream(stream)), "moe_route")
     return topk_ids, topk_weights
+
+
+def moe_route_reroute(scores, top_k, capacity, num_groups=1, topk_groups=1, renormalize=True,
+                      topk_ids=None, topk_weights=None, expert_load=None, workspace=None, stream=None):
+    """Routing with a per-expert capacity and the next-best expert overflow policy (RAW scores).
+    Returns (topk_ids [T, k] int32 with -1 for dropped slots, topk_weights [T, k], expert_load [E])."""
+    _dev(scores, torch.float32, "scores")
+    T, E = scores.shape
+    dev = scores.device
+    if topk_ids is None:
+        topk_ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    if topk_weights is None:
+        topk_weights = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    if expert_load is None:
+        expert_load = torch.empty(E, dtype=torch.int32, device=dev)
+    _shape(_dev(topk_ids, torch.int32, "topk_ids"), (T, top_k), "topk_ids")
+    _shape(_dev(topk_weights, torch.float32, "topk_weights"), (T, top_k), "topk_weights")
+    _at_least(_dev(expert_load, torch.int32, "expert_load"), E, "expert_load")
+    need = int(lib().moe_route_reroute_workspace_size(T, E, top_k, num_groups, topk_groups))
+    if T and need == 0:
+        raise MoeError("moe_route_reroute: unsupported sizes")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(lib().moe_route_reroute(_ptr(scores), T, E, top_k, num_groups, topk_groups, int(bool(renormalize)),
+                                   int(capacity), _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_load),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)), "moe_route_reroute")
+    return topk_ids, topk_weights, expert_load
 
 
 def moe_dispatch(topk_ids, expert_begin, num_local_experts, x=None, out=None, stream=None,
@@ -492,7 +521,8 @@ class MoELayer:
 
     def __init__(self, *, num_tokens, num_experts, top_k, num_groups, topk_groups, score_mode,
                  renormalize, expert_begin, num_local_experts, hidden, inter, dtype, device,
-                 fuse_gather=True, expert_capacity=None, fp8=False, masked_capacity=None):
+                 fuse_gather=True, expert_capacity=None, fp8=False, masked_capacity=None,
+                 reroute_capacity=None):
         self.T, self.E, self.k = num_tokens, num_experts, top_k
         self.num_groups, self.topk_groups = num_groups, topk_groups
         self.score_mode, self.renormalize = score_mode, renormalize
@@ -505,6 +535,8 @@ class MoELayer:
             raise MoeError("the FP8 layer reads the token rows through sorted_assign (fuse_gather=True)")
         # masked layout: fixed slots of masked_capacity rows per local expert
         self.masked_capacity = masked_capacity
+        # capacity with the next-best expert overflow policy, applied by the router
+        self.reroute_capacity = reroute_capacity
         if masked_capacity is not None and (fp8 or expert_capacity is not None):
             raise MoeError("the masked layout is a bf16 / float32 layer with its own capacity")
         cap = num_tokens * top_k
@@ -519,6 +551,11 @@ class MoELayer:
             sorted_assign=torch.empty(max(cap, 1), **i32),
             assign_pos=torch.empty(max(cap, 1), **i32),
         )
+        if reroute_capacity is not None:
+            rneed = int(lib().moe_route_reroute_workspace_size(num_tokens, num_experts, top_k, num_groups,
+                                                               topk_groups))
+            self.buf["reroute_ws"] = torch.empty(max(rneed, 1), dtype=torch.uint8, device=dev)
+            self.buf["expert_load"] = torch.empty(num_experts, **i32)
         dneed = int(lib().moe_dispatch_workspace_size(num_tokens, top_k, num_local_experts))
         if dneed:
             self.buf["dispatch_ws"] = torch.empty(dneed, dtype=torch.uint8, device=dev)
@@ -555,8 +592,13 @@ class MoELayer:
             self.buf["workspace"] = torch.empty(need, dtype=torch.uint8, device=dev)
 
     def route(self, scores, stream=None):
+        b = self.buf
+        if self.reroute_capacity is not None:
+            return moe_route_reroute(scores, self.k, self.reroute_capacity, self.num_groups, self.topk_groups,
+                                     self.renormalize, b["topk_ids"], b["topk_weights"], b["expert_load"],
+                                     b["reroute_ws"], stream)[:2]
         return moe_route(scores, self.k, self.num_groups, self.topk_groups, self.score_mode,
-                         self.renormalize, self.buf["topk_ids"], self.buf["topk_weights"], stream)
+                         self.renormalize, b["topk_ids"], b["topk_weights"], stream)
 
     def dispatch(self, x=None, stream=None):
         """Counting sort; also gathers x into x_sorted unless the gather is fused into the FFN."""

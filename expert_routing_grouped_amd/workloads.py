@@ -57,6 +57,7 @@ class Workload:
     capacity_factor: str | None = None   # per-expert cap C = ceil(c T k / E), c as an exact decimal
     weight_format: str = "same"          # "fp8_e4m3_b128": x and expert weights as e4m3 with block scales
     layout: str = "grouped"              # "masked": fixed slots of C rows per local expert
+    overflow: str = "drop"               # "reroute": over-capacity slots go to the next-best expert
 
     @property
     def has_ffn(self) -> bool:
@@ -111,6 +112,8 @@ WORKLOADS = {
                                hidden=0, inter=0, expert_begin=0, num_local=896, dtype="f32",
                                capacity_factor="1.2"),
 }
+# The same example with the next-best expert overflow policy (routing with capacity).
+WORKLOADS["capacity_reroute"] = WORKLOADS["capacity_route"].replace(name="capacity_reroute", overflow="reroute")
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:

@@ -168,6 +168,40 @@ moe_status_t moe_route(const float* scores, int32_t num_tokens, int32_t num_expe
                        int32_t score_mode, int32_t renormalize,
                        int32_t* topk_ids, float* topk_weights, hipStream_t stream);
 
+/* Bytes of device workspace moe_route_reroute needs; 0 when the sizes are invalid. */
+size_t moe_route_reroute_workspace_size(int32_t num_tokens, int32_t num_experts, int32_t top_k,
+                                        int32_t num_groups, int32_t topk_groups);
+
+/*
+ * moe_route_reroute -- moe_route (RAW scores) with a per-expert capacity C and
+ * the first overflow policy of the table in ch15 section 4.3 ("负载均衡",
+ * capacity factor): an assignment over its expert's capacity goes to the
+ * token's next-highest-scoring expert instead.
+ * 1. Every token is ranked as in moe_route (kept groups, descending score,
+ *    lower index first); ranks 0 .. k-1 are its choices, ranks k, k+1, ...
+ *    (up to 2k in all, at most 64, within its kept groups) its spares.
+ * 2. Each expert keeps its first C original assignments in assignment order
+ *    a = t * k + j; the others overflow.
+ * 3. In assignment order, the i-th overflowing slot of a token (slot order)
+ *    takes the token's spare of rank k + i if that expert then holds fewer than
+ *    C assignments (the originals count first); otherwise, or without such a
+ *    spare, the slot is dropped: topk_ids = -1, weight 0 (moe_dispatch treats
+ *    -1 as not local).
+ * 4. Weight = the score of the slot's final expert, divided by the sum over
+ *    the token's slots that were not dropped when renormalize != 0.
+ * topk_ids, topk_weights [T, k] out; expert_load [E] int32 out or NULL:
+ * assignments each expert ends with (<= C).
+ * workspace  >= moe_route_reroute_workspace_size bytes; contents need not be
+ *            initialised.
+ * Limits: those of moe_route (RAW mode), C >= 0. T = 0 is a valid no-op
+ * (expert_load is then not written).
+ */
+moe_status_t moe_route_reroute(const float* scores, int32_t num_tokens, int32_t num_experts,
+                               int32_t top_k, int32_t num_groups, int32_t topk_groups,
+                               int32_t renormalize, int32_t expert_capacity, int32_t* topk_ids,
+                               float* topk_weights, int32_t* expert_load, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
 /*
  * Bytes of device workspace moe_dispatch needs for T * k assignments and
  * num_local_experts experts (0 when T * k <= 8192: then workspace may be NULL).

@@ -67,7 +67,8 @@ import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64", "route_softmax_topk", "route_grouped", "route",
-    "dispatch", "expert_capacity", "dispatch_capacity", "dispatch_masked", "gather_rows",
+    "route_reroute", "dispatch", "expert_capacity", "dispatch_capacity", "dispatch_masked",
+    "gather_rows",
     "expert_ffn", "expert_ffn_masked",
     "expert_ffn_rows", "combine", "layer",
 ]
@@ -293,6 +294,58 @@ def expert_ffn_masked(x_slots: np.ndarray, counts: np.ndarray, capacity: int, w_
         lo = e * capacity
         out[lo:lo + m] = _one_expert(_decode(x_slots[lo:lo + m]), w_gate_up[e], w_down[e], I)
     return out
+
+
+def route_reroute(scores: np.ndarray, top_k: int, num_groups: int, topk_groups: int, capacity: int,
+                  renormalize: bool = True):
+    """Group-limited routing with a per-expert capacity and the "next-best expert" overflow
+    policy [CH15 section 4.3, table of overflow policies: 转给次高分专家; EPLB page for the
+    routing itself].
+
+    Readings (the page names the policy only):
+    1. Every token is routed as ``route_grouped``; its spare candidates are the next experts of
+       the same ranking (its kept groups, descending score, lower index first), ranks k, k+1, ...
+    2. Capacity goes first to the original choices: in assignment order a = t * k + j, an expert
+       keeps its first C original assignments; the others overflow.
+    3. Then, in assignment order, the i-th overflowing slot of a token (in slot order) moves to
+       the token's spare candidate of rank k + i, which takes it if it holds fewer than C
+       assignments at that moment; otherwise (or when the token has no such candidate) the slot
+       is dropped: expert id -1, weight 0.
+    4. Weights are the scores of each slot's final expert, divided by the sum over the token's
+       slots that were not dropped when ``renormalize``.
+    Returns (topk_ids int32 [T, k], topk_weights float64 [T, k], load int64 [E] = assignments
+    each expert ends with). Written as plain loops over the assignments.
+    """
+    s = np.asarray(scores, dtype=np.float32)
+    T, E = s.shape
+    G = E // num_groups
+    n_ranked = min(2 * top_k, topk_groups * G)
+    ranked, _ = route_grouped(s, n_ranked, num_groups, topk_groups, renormalize=False)
+    ids = ranked[:, :top_k].astype(np.int64).copy()
+    load = np.zeros(E, dtype=np.int64)
+    overflow = []
+    for t in range(T):
+        for j in range(top_k):
+            e = int(ids[t, j])
+            if load[e] < capacity:
+                load[e] += 1
+            else:
+                overflow.append((t, j))
+    nth = {}
+    for t, j in overflow:
+        i = nth.get(t, 0)
+        nth[t] = i + 1
+        r = top_k + i
+        if r < n_ranked and load[int(ranked[t, r])] < capacity:
+            ids[t, j] = int(ranked[t, r])
+            load[int(ranked[t, r])] += 1
+        else:
+            ids[t, j] = -1
+    w = np.where(ids >= 0, s[np.arange(T)[:, None], np.maximum(ids, 0)].astype(np.float64), 0.0)
+    if renormalize:
+        tot = w.sum(axis=1, keepdims=True)
+        w = np.divide(w, tot, out=np.zeros_like(w), where=tot > 0)
+    return ids.astype(np.int32), w, load
 
 
 def gather_rows(x: np.ndarray, sorted_assign: np.ndarray, top_k: int) -> np.ndarray:

@@ -61,6 +61,21 @@ def test_route_validation():
     assert l.moe_route(None, 0, 256, 8, 8, 4, R, 1, None, None, None) == 0       # T = 0: no-op
 
 
+def test_route_reroute_validation():
+    l = moe.lib()
+    p = ctypes.c_void_p(256)
+    W = (p, 1 << 30, None)
+    # (scores, T, E, k, groups, topk_groups, renorm, C, ids, weights, load, ws, ws_bytes, stream)
+    assert l.moe_route_reroute(p, 4, 256, 8, 8, 4, 1, -1, p, p, None, *W) == 1    # C < 0
+    assert l.moe_route_reroute(p, 4, 250, 8, 8, 4, 1, 10, p, p, None, *W) == 1    # groups
+    assert l.moe_route_reroute(p, 4, 2048, 8, 1, 1, 1, 10, p, p, None, *W) == 2   # E > 1024
+    assert l.moe_route_reroute(None, 4, 256, 8, 8, 4, 1, 10, p, p, None, *W) == 1  # NULL scores
+    assert l.moe_route_reroute(p, 4, 256, 8, 8, 4, 1, 10, p, p, None, p, 16, None) == 3   # small ws
+    assert l.moe_route_reroute(None, 0, 256, 8, 8, 4, 1, 10, None, None, None, None, 0, None) == 0
+    assert l.moe_route_reroute_workspace_size(512, 256, 8, 8, 4) > 512 * 16 * 8
+    assert l.moe_route_reroute_workspace_size(512, 250, 8, 8, 4) == 0
+
+
 def test_dispatch_validation():
     l = moe.lib()
     p = ctypes.c_void_p(16)  # never dereferenced: validation fails first
