@@ -8,6 +8,7 @@
 #include <cmath>
 #include <mutex>
 
+#include "host_plan.h"
 #include "launch.h"
 
 namespace {
@@ -200,14 +201,10 @@ moe_status_t moe_expert_capacity(int32_t num_tokens, int32_t top_k, int32_t num_
     return MOE_ERR_INVALID;
   const int64_t lim = (int64_t)1 << 31;
   if (factor_num >= lim || factor_den >= lim) return MOE_ERR_UNSUPPORTED;
-  // ceil(num * T * k / (den * E)) in exact integer arithmetic (128-bit
-  // intermediates; every factor is below 2^31 once T * k is).
   const int64_t tk = (int64_t)num_tokens * top_k;
   if (tk >= lim) return MOE_ERR_UNSUPPORTED;
-  const __int128 q = (__int128)factor_num * tk;
-  const __int128 den = (__int128)factor_den * num_experts;
-  const __int128 c = (q + den - 1) / den;
-  if (c > (__int128)INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  const int64_t c = moe::expert_capacity(tk, factor_num, factor_den, num_experts);
+  if (c > (int64_t)INT32_MAX) return MOE_ERR_UNSUPPORTED;
   *capacity = (int32_t)c;
   return MOE_OK;
 }

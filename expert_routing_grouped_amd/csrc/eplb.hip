@@ -16,90 +16,12 @@
 // The replica choice follows the page's simulation: a token slot uses a
 // replica on a node the token already goes to when there is one (the lowest
 // such slot), else the lowest slot on the lowest-numbered node holding one.
+// The placement planner (host code) is in host_plan.cpp.
 #include <hip/hip_runtime.h>
-
-#include <algorithm>
-#include <cmath>
-#include <vector>
 
 #include "launch.h"
 
 namespace moe {
-
-namespace {
-
-std::vector<std::vector<int>> balanced_pack(const std::vector<double>& w, int n_packs) {
-  const int n = (int)w.size();
-  const int room = n / n_packs;
-  std::vector<int> order(n);
-  for (int i = 0; i < n; ++i) order[i] = i;
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return w[a] > w[b]; });
-  std::vector<std::vector<int>> packs(n_packs);
-  std::vector<double> total(n_packs, 0.0);
-  for (int item : order) {
-    int target = -1;
-    for (int p = 0; p < n_packs; ++p)
-      if ((int)packs[p].size() < room && (target < 0 || total[p] < total[target])) target = p;
-    packs[target].push_back(item);
-    total[target] += w[item];
-  }
-  return packs;
-}
-
-}  // namespace
-
-int eplb_place(const double* load, int E, int num_groups, int num_nodes, int num_gpus, int num_physical,
-               bool hierarchical, int* phys_to_logical, int* replica_offsets, int* replica_slots) {
-  const int G = E / num_groups;
-  std::vector<std::vector<int>> node_experts;
-  if (hierarchical) {
-    std::vector<double> group_load(num_groups, 0.0);
-    for (int g = 0; g < num_groups; ++g)
-      for (int e = g * G; e < (g + 1) * G; ++e) group_load[g] += load[e];
-    for (const auto& groups : balanced_pack(group_load, num_nodes)) {
-      std::vector<int> experts;
-      for (int g : groups)
-        for (int e = g * G; e < (g + 1) * G; ++e) experts.push_back(e);
-      node_experts.push_back(experts);
-    }
-  } else {
-    std::vector<int> all(E);
-    for (int e = 0; e < E; ++e) all[e] = e;
-    node_experts.push_back(all);
-  }
-  std::vector<int> count(E, 0);
-  int slot = 0;
-  for (const auto& experts : node_experts) {
-    const int n = (int)experts.size();
-    const int n_phys = (int)((long)num_physical * n / E);
-    const int n_gpus = (int)((long)num_gpus * n / E);
-    for (int e : experts) count[e] = 1;
-    for (int r = n; r < n_phys; ++r) {
-      int best = experts[0];
-      for (int i = 1; i < n; ++i) {
-        const int e = experts[i];
-        if (load[e] / count[e] > load[best] / count[best]) best = e;
-      }
-      ++count[best];
-    }
-    std::vector<int> physical;
-    std::vector<double> weight;
-    for (int e : experts)
-      for (int c = 0; c < count[e]; ++c) {
-        physical.push_back(e);
-        weight.push_back(load[e] / count[e]);
-      }
-    for (const auto& pack : balanced_pack(weight, n_gpus))
-      for (int i : pack) phys_to_logical[slot++] = physical[i];
-  }
-  // replica table: slots of each expert in ascending order (a counting sort)
-  for (int e = 0; e <= E; ++e) replica_offsets[e] = 0;
-  for (int s = 0; s < num_physical; ++s) ++replica_offsets[phys_to_logical[s] + 1];
-  for (int e = 0; e < E; ++e) replica_offsets[e + 1] += replica_offsets[e];
-  std::vector<int> fill(replica_offsets, replica_offsets + E);
-  for (int s = 0; s < num_physical; ++s) replica_slots[fill[phys_to_logical[s]]++] = s;
-  return slot;
-}
 
 namespace {
 

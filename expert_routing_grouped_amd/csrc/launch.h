@@ -111,10 +111,7 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
-// EPLB placement (host) and replica choice (device).
-int eplb_place(const double* load, int num_experts, int num_groups, int num_nodes, int num_gpus,
-               int num_physical, bool hierarchical, int* phys_to_logical, int* replica_offsets,
-               int* replica_slots);
+// EPLB replica choice (device); the placement planner is host code (host_plan.h).
 hipError_t launch_eplb_remap(const int* ids, int T, int k, const int* offsets, const int* slots,
                              int num_experts, int slots_per_gpu, int gpus_per_node, int* phys,
                              hipStream_t s);

@@ -343,6 +343,26 @@ def test_layer_prefill_sampled(name):
     assert e_o <= TOL_BF16 and e_y <= TOL_BF16
 
 
+def test_layer_prefill_straggler_every_row():
+    """The prefill_straggler share at full size (d = 7168, I = 2048, 14312 rows, both GEMMs on
+    the large-tile kernel for the 10 experts above 64 rows and the streaming kernel for the
+    other 6): every row of o and every token of y against the float64 oracle."""
+    name = "prefill_straggler"
+    wl = W.WORKLOADS[name]
+    inp = inputs(name)
+    g = run_layer(inp, wl)
+    ref = oracle_front(inp, wl)
+    M = check_front(g, ref)
+    ids, w, counts, offsets, sa, pos = ref
+    o_ref = oracle.expert_ffn(oracle.gather_rows(inp.x, sa, wl.top_k), offsets, inp.w_gate_up, inp.w_down)
+    e_o = rel_err(as_f64(g["o_sorted"][:M]), o_ref)
+    y_ref = oracle.combine(o_ref, pos, w)
+    del o_ref
+    e_y = rel_err(as_f64(g["y"]), y_ref)
+    print(f"  M={M} every row: rel_err o={e_o:.3e} y={e_y:.3e}", flush=True)
+    assert e_o <= TOL_BF16 and e_y <= TOL_BF16
+
+
 def test_layer_prefill_routing_every_row():
     """The prefill_straggler routing (experts of 2 .. 2659 rows) at d = 2048, I = 2048: the
     large-tile kernel runs both GEMMs and takes every expert above 64 rows (the ones with 97
