@@ -1174,10 +1174,40 @@ struct Big {
   static constexpr int LDS_BYTES = kBigStages * STAGE_BYTES;  // 128 KB
   static constexpr int BLOCKS = 8;                            // 8-row DMA blocks per operand per wavefront
 
+  // A wavefront multiplies its weight rows by token fragments 2j + wn (rows
+  // (2j + wn) * 32 .. + 31, j = 0..3): the two wavefront columns take every
+  // other 32-row fragment, so in an expert's last, partly filled tile they
+  // keep about the same number of fragments. Only the fragments that hold a
+  // valid row are multiplied (nj of them, a template argument so that the K
+  // loop stays fully unrolled); all 256 token rows are still loaded (skipping
+  // the blocks past the last row costs more scalar registers than the kernel
+  // has).
   __device__ static void run(const GemmArgs& a, int e, int row0, int rows, int nb, char* lds, int tid) {
+    const int wn = __builtin_amdgcn_readfirstlane(tid >> 6) & 1;
+    const int nj = __builtin_amdgcn_readfirstlane(min(4, (((rows + 31) >> 5) - wn + 1) >> 1));
+    switch (nj) {
+      case 4: body<4>(a, e, row0, rows, nb, lds, tid); break;
+      case 3: body<3>(a, e, row0, rows, nb, lds, tid); break;
+      case 2: body<2>(a, e, row0, rows, nb, lds, tid); break;
+      case 1: body<1>(a, e, row0, rows, nb, lds, tid); break;
+      default: body<0>(a, e, row0, rows, nb, lds, tid); break;
+    }
+  }
+
+  // MFMA of a stage after which DMA instruction d (0..15) of the next stage
+  // is issued: the 16 instructions are spread evenly over the first half of
+  // the stage's 16 NJ MFMAs.
+  template <int NJ>
+  __device__ static constexpr int dma_after(int d) {
+    const int m = (d + 1) * (8 * NJ) / 16 - 1;
+    return m < 0 ? 0 : m;
+  }
+
+  template <int NJ>
+  __device__ static void body(const GemmArgs& a, int e, int row0, int rows, int nb, char* lds, int tid) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;   // weight rows wm*128.., tokens wn*128..
+    const int wm = wave >> 1, wn = wave & 1;   // weight rows wm*128.., token fragments 2j + wn
     const uint32_t pitch = (uint32_t)a.K * 2;
     const int lrow = lane >> 3;                               // row within an 8-row DMA block
     const int lchunk = (lane & 7) ^ (lane >> 4);              // chunk fetched in even blocks
@@ -1213,16 +1243,8 @@ struct Big {
 #pragma unroll
     for (int i = 0; i < BLOCKS; ++i) xv[i] = xv[i] * pitch + (lchunk ^ ((i & 1) << 2)) * 16;
 
-    auto issue_all = [&](int kt) {   // this wavefront's share of stage kt
-      const uint32_t lw = lds_base + (kt & 1) * STAGE_BYTES;
-      const uint32_t lx = lw + OP_BYTES;
-      const uint32_t ko = (uint32_t)kt * kBigBK * 2;
-#pragma unroll
-      for (int i = 0; i < BLOCKS; ++i) lds_dma16(lw + (wave * BLOCKS + i) * 1024, wbuf, wv[i & 1], wso[i] + ko);
-#pragma unroll
-      for (int i = 0; i < BLOCKS; ++i) lds_dma16(lx + (wave * BLOCKS + i) * 1024, xbuf, xv[i], ko);
-    };
-    // DMA number d (0..15) of that share: weight blocks first, then token blocks.
+    // DMA number d (0..15) of this wavefront's share of stage kt: weight
+    // blocks first, then token blocks.
     auto issue_one = [&](int kt, int d) {
       const uint32_t lw = lds_base + (kt & 1) * STAGE_BYTES;
       const uint32_t ko = (uint32_t)kt * kBigBK * 2;
@@ -1230,58 +1252,70 @@ struct Big {
       else lds_dma16(lw + OP_BYTES + (wave * BLOCKS + d - BLOCKS) * 1024, xbuf, xv[d - BLOCKS], ko);
     };
 
-    f32x16_t acc[4][4];
+    f32x16_t acc[4][NJ > 0 ? NJ : 1];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16_t{};
 
     const int fr = lane & 31, fh = lane >> 5;  // fragment row, k half
     const int fsw = (fr >> 1) & 7;               // the swizzle of every row this lane reads
     // Multiplies stage `slot` and issues the DMA of stage knext (if >= 0) into
-    // the other buffer, one instruction after every second MFMA of the first
-    // half. A wavefront that issues a burst of vector-memory instructions
-    // stalls until the CU's address unit has taken them, and with one
-    // wavefront per SIMD nothing else keeps the SIMD's MFMA pipe busy
-    // meanwhile; spread out, they issue without stalls, and the last one still
-    // has half a stage to land. Fragments of the next 16 k are read while the
-    // current ones are multiplied.
+    // the other buffer, spread over the first half of the MFMAs. A wavefront
+    // that issues a burst of vector-memory instructions stalls until the CU's
+    // address unit has taken them, and with one wavefront per SIMD nothing
+    // else keeps the SIMD's MFMA pipe busy meanwhile; spread out, they issue
+    // without stalls, and the last one still has half a stage to land.
+    // Fragments of the next 16 k are read while the current ones are
+    // multiplied.
     auto compute = [&](int slot, int knext) {
+      if (NJ == 0) {
+        if (knext >= 0) {
+#pragma unroll
+          for (int d = 0; d < 2 * BLOCKS; ++d) issue_one(knext, d);
+        }
+        return;
+      }
       const char* lw = lds + slot * STAGE_BYTES + (wm * 128 + fr) * 128;
-      const char* lx = lds + slot * STAGE_BYTES + OP_BYTES + (wn * 128 + fr) * 128;
+      const char* lx = lds + slot * STAGE_BYTES + OP_BYTES + (wn * 32 + fr) * 128;
       constexpr int NQ = kBigBK / 16;
-      bf16x8_t av[4], bv[4];
+      bf16x8_t av[4], bv[NJ > 0 ? NJ : 1];
       {
         const int off = (fh ^ fsw) << 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) av[i] = *(const bf16x8_t*)(lw + i * 32 * 128 + off);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) bv[j] = *(const bf16x8_t*)(lx + j * 32 * 128 + off);
+        for (int j = 0; j < NJ; ++j) bv[j] = *(const bf16x8_t*)(lx + j * 64 * 128 + off);
       }
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
         const int offn = (((q + 1) * 2 + fh) ^ fsw) << 4;
-        bf16x8_t an[4], bn[4];
+        bf16x8_t an[4], bn[NJ > 0 ? NJ : 1];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (q + 1 < NQ) {
             an[i] = *(const bf16x8_t*)(lw + i * 32 * 128 + offn);
-            bn[i] = *(const bf16x8_t*)(lx + i * 32 * 128 + offn);
+            if (i < NJ) bn[i] = *(const bf16x8_t*)(lx + i * 64 * 128 + offn);
           }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int j = 0; j < NJ; ++j) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-            const int m = q * 16 + i * 4 + j;   // MFMA number within the stage
-            if (m % 2 == 1 && m / 2 < 2 * BLOCKS) {
-              __builtin_amdgcn_sched_barrier(0);
-              if (knext >= 0) issue_one(knext, m / 2);
-              __builtin_amdgcn_sched_barrier(0);
+            const int m = (q * 4 + i) * NJ + j;   // MFMA number within the stage
+#pragma unroll
+            for (int d = 0; d < 2 * BLOCKS; ++d) {
+              if (dma_after<NJ>(d) == m) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (knext >= 0) issue_one(knext, d);
+                __builtin_amdgcn_sched_barrier(0);
+              }
             }
           }
         }
         if (q + 1 < NQ) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) { av[i] = an[i]; bv[i] = bn[i]; }
+          for (int i = 0; i < 4; ++i) av[i] = an[i];
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) bv[j] = bn[j];
         }
       }
     };
@@ -1291,7 +1325,8 @@ struct Big {
     // wavefront has finished stage kt - 1, whose buffer stage kt + 1 reuses),
     // multiply stage kt while issuing stage kt + 1.
     const int nk = a.K / kBigBK;
-    issue_all(0);
+#pragma unroll
+    for (int d = 0; d < 2 * BLOCKS; ++d) issue_one(0, d);
     for (int kt = 0; kt < nk; ++kt) {
       wait_vmcnt<0>();
       __syncthreads();
@@ -1300,12 +1335,12 @@ struct Big {
 
     // One fragment column at a time (all lanes compute, only the store is
     // guarded), so the accumulators are read out piecewise.
-    // acc[i][j][r]: token wn*128 + j*32 + lane%32; wavefront weight row
+    // acc[i][j][r]: token (2j + wn)*32 + lane%32; wavefront weight row
     // i*32 + (r/4)*8 + (lane/32)*4 + r%4.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       __builtin_amdgcn_sched_barrier(0);
-      const int t = wn * 128 + j * 32 + fr;
+      const int t = (2 * j + wn) * 32 + fr;
       const bool ok = t < rows;
       uint16_t* crow = a.C + (size_t)(row0 + (ok ? t : 0)) * a.ldc;
       if (GATED) {
