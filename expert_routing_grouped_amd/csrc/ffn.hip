@@ -36,7 +36,6 @@ namespace {
 
 constexpr int kStreamMT = 4;                  // row tiles of 16 per streamed row chunk
 constexpr int kChunkRows = kStreamMT * 16;    // rows per streamed chunk
-constexpr int kStreamRows = 4 * kChunkRows;   // experts with more rows decide the large-tile path
 constexpr int kTileBM = 128;                  // tokens per tile in the tiled path
 constexpr int kBigBM = 256;                   // tokens per tile in the large-tile path
 constexpr int kStreamDW = 3;                  // weight register sets of the streaming path
@@ -97,9 +96,8 @@ constexpr int kNonTemporal = 2;
 
 // Splits the local experts by row count m, in expert order (and leaves the
 // clamped row bounds in s_lo: rows of expert e are [s_lo[e], s_lo[e] + m);
-// n_big = the tiles of kBigBM rows that the experts above kStreamRows rows
-// need, whatever stream_max is; with all_chunks every expert is cut into
-// chunks of chunk_rows rows):
+// n_big = the tiles of kBigBM rows that the tiled experts need; with
+// all_chunks every expert is cut into chunks of chunk_rows rows):
 //   1 <= m <= stream_max: streamed, in ceil(m / chunk_rows) row chunks;
 //                         s_first[e] = first chunk of expert e, s_first[nloc] = chunks
 //   m > stream_max:       tiled, in ceil(m / bm) row tiles;
@@ -108,7 +106,7 @@ constexpr int kNonTemporal = 2;
 __device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_first, int* s_lo,
                             int* wsum, int& n_chunks, int& n_tiles, int& n_big,
                             bool all_chunks = false, int chunk_rows = kChunkRows,
-                            int stream_max = kStreamRows) {
+                            int stream_max = kChunkRows) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int cc[4], tc[4], cs = 0, ct = 0, cb = 0;
 #pragma unroll
@@ -127,7 +125,7 @@ __device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_firs
     tc[q] = (m > 0 && !chunked) ? (m + bm - 1) / bm : 0;
     cs += cc[q];
     ct += tc[q];
-    cb += (m > kStreamRows) ? (m + kBigBM - 1) / kBigBM : 0;
+    cb += (m > 0 && !chunked) ? (m + kBigBM - 1) / kBigBM : 0;
   }
   cb = wave_sum_i32(cb);
   int is = cs, it = ct;
@@ -1101,9 +1099,8 @@ struct Tiled {
 
 // ---------------------------------------------------------------- large-tile path
 
-// Experts with more than kChunkRows rows when the experts above kStreamRows
-// rows fill the GPU with these tiles (prefill), instead of the 128 x 128
-// tiles above: 256 weight rows x 256 tokens per tile, one workgroup
+// Experts with more than kChunkRows rows when their tiles fill the GPU
+// (prefill; big_takes below), instead of the 128 x 128 tiles above: 256 weight rows x 256 tokens per tile, one workgroup
 // of 4 wavefronts per CU, each wavefront 128 x 128 on v_mfma_f32_32x32x16_bf16
 // (4 x 4 fragments, 256 float32 accumulators per lane). Per k16 step a
 // wavefront reads 8 KB of fragments from LDS for 16 MFMAs, which leaves the
@@ -1371,6 +1368,16 @@ struct Big {
   }
 };
 
+// The large-tile kernel takes every expert with more than kChunkRows rows
+// when its items (256-row tiles x N blocks) fill at least 3/4 of the CUs in
+// their first round; else the persistent kernel's 128 x 128 tiles do (two
+// workgroups per CU). The 256 x 256 tiles move half the bytes through L2, but
+// a workgroup keeps only one 64 KB stage in flight, so on fewer CUs the
+// aggregate L2 -> LDS rate of the smaller tiles wins. For an expert with 65
+// .. 256 rows a row of (partly filled) 256 x 256 tiles costs less than
+// streaming its weights once per 64-row chunk.
+__device__ __forceinline__ bool big_takes(int items, int cus) { return 4 * items >= 3 * cus; }
+
 // Tiles of the experts with more than kChunkRows rows, 256 tokens each; a
 // persistent loop over them, one workgroup per CU.
 template <bool GATED>
@@ -1382,15 +1389,10 @@ __global__ __launch_bounds__(256, 1) void ffn_big_kernel(GemmArgs a) {
   __shared__ int s_lo[kMaxLocal + 1];
   __shared__ int wsum[12];
   int n_chunks, n_tiles, n_big;
-  build_lists(a, kBigBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big);
-  const int nblk = (GATED ? a.inter : a.N) / B::COLS;
-  if (n_big * nblk < a.big_min_items) return;  // the persistent kernel does these experts
-  // This kernel takes every expert with more than kChunkRows rows: for one
-  // with 65 .. kStreamRows rows a row of (partly filled) 256 x 256 tiles
-  // costs less than streaming its weights once per 64-row chunk, and the
-  // extra items land in the partly idle last round.
   build_lists(a, kBigBM, s_first, t_first, s_lo, wsum, n_chunks, n_tiles, n_big, false, kChunkRows,
               kChunkRows);
+  const int nblk = (GATED ? a.inter : a.N) / B::COLS;
+  if (!big_takes(n_tiles * nblk, a.big_min_items)) return;  // the persistent kernel does these experts
   const int total = n_tiles * nblk;
   // Items are (token tile, N block) with N blocks fastest, taken round-robin
   // by a grid that is a multiple of 8: workgroup b runs on XCD b % 8 and its
@@ -1438,10 +1440,10 @@ __global__ __launch_bounds__(256, 2) void ffn_gemm_kernel(GemmArgs a) {
   const int ncols = GATED ? a.inter : a.N;
   const int slabs = ncols / S::COLS;
   const int nblk = ncols / T::COLS;
-  // Same decision as ffn_big_kernel: when the experts above kStreamRows rows
-  // fill the GPU with its tiles, it takes every tiled expert and only the
-  // streamed ones are done here; else the tiles are done here, 128 x 128.
-  const bool big = a.big_ok && n_big * (ncols / Big<GATED>::COLS) >= a.big_min_items;
+  // Same decision as ffn_big_kernel (big_takes over the same tiles): when it
+  // takes every tiled expert only the streamed ones are done here; else the
+  // tiles are done here, 128 x 128.
+  const bool big = a.big_ok && big_takes(n_big * (ncols / Big<GATED>::COLS), a.big_min_items);
   const int n_stream = n_chunks * slabs;
   const int total = n_stream + (big ? 0 : n_tiles * nblk);
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
@@ -1590,9 +1592,9 @@ int stream_ks(int K) {
 }
 
 // Tiled experts go to ffn_big_kernel when the output width allows its tiles,
-// the row capacity is prefill-sized and (on the device) the experts above
-// kStreamRows rows make at least one tile per CU; else to the 128 x 128 tiles
-// of the persistent kernel. Both paths are complete; the capacity test keeps
+// the row capacity is prefill-sized and (on the device) its tiles fill at
+// least 3/4 of the CUs (big_takes); else to the 128 x 128 tiles of the
+// persistent kernel. Both paths are complete; the capacity test keeps
 // decode-sized calls from paying for a second launch that finds no work.
 template <bool GATED>
 bool use_big(const GemmArgs& g) {
@@ -1611,17 +1613,16 @@ hipError_t launch_gemm_t(const GemmArgs& g0, hipStream_t s) {
   auto kernel = ffn_gemm_kernel<NTW, KS, GATED>;
   static const int occ = occupancy(kernel, 256);
   const int ncols = GATED ? g.inter : g.N;
-  const long max_chunks = std::min<long>((long)g.nloc * (kStreamRows / kChunkRows),
-                                         (long)(g.capacity + kChunkRows - 1) / kChunkRows + g.nloc);
+  const long max_chunks = g.nloc;   // streamed experts have at most kChunkRows rows: one chunk each
   const long max_tiles = (long)(g.capacity + kTileBM - 1) / kTileBM + g.nloc;
   const long per_chunk = ncols / S::COLS;
   const long max_work = max_chunks * per_chunk + max_tiles * (ncols / T::COLS);
   const int grid = (int)std::max<long>(1, std::min<long>(max_work, (long)cu_count() * occ));
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, g);
   if (!g.big_ok) return hipGetLastError();
-  // tiles <= ceil(capacity / 256) + (number of experts above kStreamRows rows)
+  // tiles <= ceil(capacity / 256) + (number of experts above kChunkRows rows)
   const long max_big = ((long)(g.capacity + kBigBM - 1) / kBigBM +
-                        std::min<long>(g.nloc, (long)g.capacity / (kStreamRows + 1))) *
+                        std::min<long>(g.nloc, (long)g.capacity / (kChunkRows + 1))) *
                        (ncols / Big<GATED>::COLS);
   // persistent: one workgroup per CU (a multiple of 8, so each keeps its XCD's range)
   const long cus8 = std::max(8, cu_count() / 8 * 8);

@@ -282,9 +282,10 @@ def test_layer_toy_fp32(fuse):
     (700, 8, 2, 1, 1, 256, 256, 0, 8),      # > 64 rows per expert
     (1200, 4, 2, 1, 1, 512, 128, 0, 4),     # > 256 rows per expert: 128 x 128 tiles, ragged
     (1500, 4, 2, 1, 1, 2048, 1024, 0, 4),   # 128 x 128 tiles, K = 2048
-    (2100, 16, 8, 2, 1, 512, 256, 0, 16),   # row capacity >= 16384 but too few large tiles: 128 x 128
+    (2100, 16, 8, 2, 1, 512, 256, 0, 16),   # row capacity >= 16384 but 160 large tiles (< 3/4 of the CUs): 128 x 128
     (2100, 16, 8, 2, 1, 512, 192, 2, 12),   # same capacity, I % 128 != 0: 128 x 128 tiles
     (2060, 16, 8, 4, 2, 4096, 512, 0, 16),  # >= one 256 x 256 tile per CU in both GEMMs, ragged
+    (2048, 64, 8, 1, 1, 2048, 1024, 0, 4),  # experts of 589, 69, 70, 376 rows, row capacity 16384
     # narrow experts: shared activation tiles, K split in 2 / 1 / 4 parts + finalize
     (300, 32, 8, 8, 4, 2048, 64, 4, 12),
     (200, 16, 4, 4, 2, 1024, 128, 0, 16),
@@ -370,6 +371,20 @@ def test_layer_prefill_routing_every_row():
     o and y is checked against the oracle."""
     wl = W.WORKLOADS["prefill_straggler"].replace(name="prefill_straggler_d2048", hidden=2048)
     check_full(wl, W.generate(wl), TOL_BF16)
+
+
+def test_layer_prefill_literal_routing_every_row():
+    """The prefill_literal routing (5 experts of 87 .. 506 rows above 64, two below) at d = 2048,
+    I = 2048: 7 large tiles per column block, 112 items per GEMM, too few for the large-tile
+    kernel, so both GEMMs take 128 x 128 tiles (at d = 7168 the down GEMM's 196 items take the
+    large tiles: test_layer_prefill_sampled); every row of o and y against the oracle, and a
+    second run bit-identical to the first."""
+    wl = W.WORKLOADS["prefill_literal"].replace(name="prefill_literal_d2048", hidden=2048)
+    inp = W.generate(wl)
+    g1 = check_full(wl, inp, TOL_BF16)
+    g2 = run_layer(inp, wl)
+    for key in ("o_sorted", "y"):
+        assert np.array_equal(g1[key], g2[key]), key
 
 
 # ------------------------------------------------------------------ capacity-limited dispatch
