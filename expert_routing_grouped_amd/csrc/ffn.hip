@@ -1393,20 +1393,26 @@ __global__ __launch_bounds__(256, 1) void ffn_big_kernel(GemmArgs a) {
               kChunkRows);
   const int nblk = (GATED ? a.inter : a.N) / B::COLS;
   if (!big_takes(n_tiles * nblk, a.big_min_items)) return;  // the persistent kernel does these experts
-  const int total = n_tiles * nblk;
   // Items are (token tile, N block) with N blocks fastest, taken round-robin
-  // by a grid that is a multiple of 8: workgroup b runs on XCD b % 8 and its
-  // items keep the same N block whenever nblk divides the grid, so its weight
-  // block stays in that XCD's L2 from one token tile to the next, while the
-  // XCDs read the same token tiles at about the same time (shared through the
-  // last-level cache).
+  // by a grid that is a multiple of 8: workgroup b runs on XCD b % 8, so the
+  // items of one N block -- the same weight block for every token tile of an
+  // expert -- share that XCD's L2 when the N blocks per tile are a multiple
+  // of 8, while the XCDs read the same token tiles at about the same time
+  // (shared through the last-level cache). When all items fit in one round,
+  // the N blocks per tile are padded to a multiple of 8 (the padding items
+  // are skipped; the workgroups they would take are idle anyway), so that
+  // holds for any nblk; with more rounds padding would leave whole
+  // workgroups idle, so the numbering stays dense.
   // (The loop runs over a multiple of 8 items and skips the ones past the
   // end; this form compiles without register spills.)
+  const int nblk8 = (nblk + 7) & ~7;
+  const int nbp = __builtin_amdgcn_readfirstlane(n_tiles * nblk8 <= (int)gridDim.x ? nblk8 : nblk);
+  const int total = n_tiles * nbp;
   const int per = (total + 7) / 8;
   for (int w = blockIdx.x; w < 8 * per; w += gridDim.x) {
-    if (w >= total) continue;
-    const int tile = __builtin_amdgcn_readfirstlane(w / nblk);
-    const int nb = __builtin_amdgcn_readfirstlane(w % nblk);
+    if (w >= total || w % nbp >= nblk) continue;
+    const int tile = __builtin_amdgcn_readfirstlane(w / nbp);
+    const int nb = __builtin_amdgcn_readfirstlane(w % nbp);
     const int e = __builtin_amdgcn_readfirstlane(find_expert(t_first, a.nloc, tile));
     const int row0 = __builtin_amdgcn_readfirstlane(s_lo[e] + (tile - t_first[e]) * kBigBM);
     const int rows = __builtin_amdgcn_readfirstlane(min(kBigBM, s_lo[e + 1] - row0));
