@@ -89,6 +89,10 @@ TRAFFIC_RECORDS = {
                   os.path.join(ROOT, "profiles", "decode_tp_ffn_traffic.md")),
     "decode_ep_fp8": ([_CSRC + "ffn_fp8.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
                       os.path.join(ROOT, "profiles", "decode_ep_fp8_ffn_traffic.md")),
+    "prefill_literal": ([_CSRC + "ffn.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
+                        os.path.join(ROOT, "profiles", "prefill_literal_ffn_traffic.md")),
+    "prefill_straggler": ([_CSRC + "ffn.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
+                          os.path.join(ROOT, "profiles", "prefill_straggler_ffn_traffic.md")),
 }
 
 
@@ -243,9 +247,14 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
     ffn_us = None
     if x is not None:
         # moe_expert_ffn alone, back to back on the launch stream (the routing of
-        # the last step stays in place): the per-launch duration of the roofline
+        # the last step stays in place): the per-launch duration of the roofline.
+        # After the host-side pause above the chip's power management needs about
+        # 15 calls of the prefill FFN (some 20 ms) to settle -- the first large-tile
+        # calls after an idle gap run up to 45% slower -- so the calls are warmed up
+        # for about 25 ms of GPU time (at least 2 calls) before they are timed.
         n_ffn = max(steps, 10)
-        for i in range(2):
+        n_warm = int(min(max(2, 25e3 / max(parts_us[2], 1.0)), 2000))
+        for i in range(n_warm):
             ffn(i)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -266,6 +275,7 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
     if wl.has_ffn:
         acc = ffn_accounting(wl, counts)
         res["ffn_us_per_launch"] = ffn_us
+        res["ffn_warmup_calls"] = n_warm
         t_ffn = ffn_us * 1e-6
         res.update(M=acc["M"], hit_experts=acc["hit"], ffn_gflop=acc["flops"] / 1e9,
                    ffn_bytes_mb=acc["bytes"] / 1e6,
