@@ -37,7 +37,7 @@ __device__ __forceinline__ void top2_merge(float& a1, float& a2, float b1, float
 template <int V, bool ALIGNED>
 __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ scores, int T, int E,
                                                     int k, int num_groups, int topk_groups,
-                                                    int softmax, int renormalize,
+                                                    int softmax, int renormalize, int vec4,
                                                     int* __restrict__ topk_ids,
                                                     float* __restrict__ topk_weights) {
   const int lane = threadIdx.x & 63;
@@ -47,11 +47,29 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ sc
 
   float val[V];
   bool valid[V];
+  if (V >= 4 && vec4) {
+    // rows 16-byte aligned and E % 4 == 0: a lane's scores are V / 4 whole
+    // 16-byte loads, each all valid or all past E
 #pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int idx = lane * V + v;
-    valid[v] = idx < E;
-    val[v] = valid[v] ? row[idx] : 0.0f;
+    for (int j = 0; j < (V >= 4 ? V / 4 : 1); ++j) {
+      const int idx = lane * V + 4 * j;
+      const float4 q = idx < E ? *(const float4*)(row + idx) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float qv[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (4 * j + i < V) {
+          val[4 * j + i] = qv[i];
+          valid[4 * j + i] = idx < E;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int idx = lane * V + v;
+      valid[v] = idx < E;
+      val[v] = valid[v] ? row[idx] : 0.0f;
+    }
   }
 
   float lmax = 0.0f, lsum = 1.0f;
@@ -177,12 +195,13 @@ hipError_t launch_v(const RouteArgs& a, hipStream_t s) {
   const int G = a.num_groups > 1 ? a.E / a.num_groups : a.E;
   const int lpg = G / V;
   const bool aligned = a.num_groups > 1 && G % V == 0 && lpg >= 1 && lpg <= 64 && (lpg & (lpg - 1)) == 0;
+  const int vec4 = (reinterpret_cast<uintptr_t>(a.scores) % 16 == 0 && a.E % 4 == 0) ? 1 : 0;
   if (aligned)
     hipLaunchKernelGGL((route_kernel<V, true>), grid, block, 0, s, a.scores, a.T, a.E, a.k,
-                       a.num_groups, a.topk_groups, a.softmax, a.renormalize, a.ids, a.weights);
+                       a.num_groups, a.topk_groups, a.softmax, a.renormalize, vec4, a.ids, a.weights);
   else
     hipLaunchKernelGGL((route_kernel<V, false>), grid, block, 0, s, a.scores, a.T, a.E, a.k,
-                       a.num_groups, a.topk_groups, a.softmax, a.renormalize, a.ids, a.weights);
+                       a.num_groups, a.topk_groups, a.softmax, a.renormalize, vec4, a.ids, a.weights);
   return hipGetLastError();
 }
 
