@@ -68,7 +68,7 @@ import numpy as np
 __all__ = [
     "bf16_bits_to_f64", "route_softmax_topk", "route_grouped", "route",
     "route_reroute", "dispatch", "expert_capacity", "dispatch_capacity", "dispatch_masked",
-    "gather_rows",
+    "dispatch_deferred", "remap_capacity", "gather_rows",
     "expert_ffn", "expert_ffn_masked",
     "expert_ffn_rows", "combine", "layer",
 ]
@@ -248,6 +248,79 @@ def dispatch_capacity(topk_ids: np.ndarray, expert_begin: int, num_local: int, c
     assign_pos[sorted_assign] = np.arange(sorted_assign.shape[0])
     return (counts.astype(np.int32), offsets.astype(np.int32), sorted_assign.astype(np.int32),
             assign_pos.astype(np.int32), demand.astype(np.int32))
+
+
+def dispatch_deferred(topk_ids: np.ndarray, expert_begin: int, num_local: int, capacity: int,
+                      rounds: int):
+    """Dispatch with a per-expert capacity and the "defer to a second round" overflow policy
+    [CH15 section 4.3, table of overflow policies: the assignment keeps its expert and is
+    processed later].
+
+    The assignments of local expert e, in assignment order a = t * k + j, fill round 0 up to
+    `capacity`, then round 1, and so on: the i-th of them (from 0) goes to round i // C. Ones
+    past `rounds` rounds are dropped (no row, assign_pos = -1); with C = 0 all are. Rows are
+    laid out round after round, and inside a round expert after expert, each expert's rows in
+    assignment order. Returns (round_counts [rounds, num_local], round_offsets [rounds,
+    num_local + 1] (absolute rows: round r starts where round r - 1 ends), sorted_assign [M],
+    assign_pos [T * k], demand [num_local] = assignments per expert), int32.
+    Written as one pass over the assignments with a running count per expert.
+    """
+    flat = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    demand = [0] * num_local
+    rows = [[[] for _ in range(num_local)] for _ in range(rounds)]
+    for a, expert in enumerate(flat.tolist()):
+        e = expert - expert_begin
+        if 0 <= e < num_local:
+            r = demand[e] // capacity if capacity > 0 else rounds
+            if r < rounds:
+                rows[r][e].append(a)
+            demand[e] += 1
+    counts = np.zeros((rounds, num_local), dtype=np.int64)
+    offsets = np.zeros((rounds, num_local + 1), dtype=np.int64)
+    order = []
+    row = 0
+    for r in range(rounds):
+        for e in range(num_local):
+            offsets[r, e] = row
+            counts[r, e] = len(rows[r][e])
+            order.extend(rows[r][e])
+            row += len(rows[r][e])
+        offsets[r, num_local] = row
+    sorted_assign = np.array(order, dtype=np.int64)
+    assign_pos = np.full(flat.shape[0], -1, dtype=np.int64)
+    assign_pos[sorted_assign] = np.arange(sorted_assign.shape[0])
+    return (counts.astype(np.int32), offsets.astype(np.int32), sorted_assign.astype(np.int32),
+            assign_pos.astype(np.int32), np.array(demand, dtype=np.int32))
+
+
+def remap_capacity(topk_ids: np.ndarray, replica_offsets: np.ndarray, replica_slots: np.ndarray,
+                   capacity: int) -> np.ndarray:
+    """Logical to physical expert with a per-replica capacity and the "send to a same-weight
+    replica" overflow policy [CH15 section 4.3, table of overflow policies; section 4.4: the
+    gating picks the logical expert, the system maps it to one of its identical replicas].
+
+    Logical expert e's replicas are replica_slots[replica_offsets[e] : replica_offsets[e + 1]],
+    in that order, each with room for `capacity` assignments. The assignments of e, in
+    assignment order a = t * k + j, fill its first replica, then the next one: the i-th (from 0)
+    goes to replica i // C. Past the room of all its replicas, for ids outside [0, E) and for
+    experts without a replica the result is -1 (dropped). Written as one pass over the
+    assignments with a running count per logical expert. Returns phys [T, k] int32.
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    off = np.asarray(replica_offsets, dtype=np.int64)
+    slots = np.asarray(replica_slots, dtype=np.int64)
+    E = off.shape[0] - 1
+    seen = [0] * E
+    out = np.full(ids.shape, -1, dtype=np.int64)
+    flat_out = out.reshape(-1)
+    for a, e in enumerate(ids.reshape(-1).tolist()):
+        if not 0 <= e < E:
+            continue
+        rep = seen[e] // capacity if capacity > 0 else off[e + 1] - off[e]
+        if rep < off[e + 1] - off[e]:
+            flat_out[a] = slots[off[e] + rep]
+        seen[e] += 1
+    return out.astype(np.int32)
 
 
 def dispatch_masked(topk_ids: np.ndarray, expert_begin: int, num_local: int, capacity: int):
