@@ -175,7 +175,8 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
                          dtype=dt, device=dev,
                          expert_capacity=cap if (wl.layout != "masked" and wl.overflow == "drop") else None,
                          fp8=fp8, masked_capacity=cap if wl.layout == "masked" else None,
-                         reroute_capacity=cap if wl.overflow == "reroute" else None)
+                         reroute_capacity=cap if wl.overflow == "reroute" else None,
+                         deferred=(cap, wl.rounds) if wl.overflow == "defer" else None)
     scores = to_device(inp.scores, dev)
     x = to_device(inp.x, dev) if wl.has_ffn else None
     weights = []
@@ -264,6 +265,10 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
         torch.cuda.synchronize()
         ffn_us = e0.elapsed_time(e1) / n_ffn * 1e3
     counts = to_host(layer.buf["counts"])
+    round_counts = None
+    if wl.overflow == "defer":   # rows per (round, expert); the FFN runs once per round
+        round_counts = to_host(layer.buf["round_counts"])
+        counts = round_counts.sum(0)
     res = dict(workload=wl.name, T=wl.T, ms_per_step=ms_per_step, wall_ms_per_step=wall / steps * 1e3,
                median_ms_per_step=float(np.median(step_ms)), median_over_steps=n_med,
                tokens_per_s=wl.T / (ms_per_step * 1e-3), gen_s=gen_s, weight_copies=len(weights),
@@ -274,6 +279,10 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
     res["local_rows_per_s"] = int(counts.sum()) / (ms_per_step * 1e-3)
     if wl.has_ffn:
         acc = ffn_accounting(wl, counts)
+        if round_counts is not None:   # each round's call streams its hit experts' weights again
+            per = [ffn_accounting(wl, rc) for rc in round_counts]
+            acc = dict(acc, hit=sum(a["hit"] for a in per), bytes=sum(a["bytes"] for a in per),
+                       weight_bytes=sum(a["weight_bytes"] for a in per))
         res["ffn_us_per_launch"] = ffn_us
         res["ffn_warmup_calls"] = n_warm
         t_ffn = ffn_us * 1e-6
@@ -289,6 +298,8 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
             demand = to_host(layer.buf["demand"])
             res.update(capacity=cap, layout=wl.layout, dropped=int(demand.sum()) - acc["M"],
                        experts_over_capacity=int((demand > cap).sum()))
+            if round_counts is not None:
+                res.update(overflow="defer", rounds=wl.rounds, rows_per_round=round_counts.sum(1).tolist())
     else:
         M = int(counts.sum())
         route_bytes = wl.T * wl.E * 4 + wl.T * wl.top_k * 8
@@ -297,6 +308,10 @@ def run_workload(wl, steps, warmup, copies, torch, moe, to_device, to_host, oper
             ids = to_host(layer.buf["topk_ids"])
             res.update(capacity=cap, overflow="reroute", dropped=int((ids < 0).sum()),
                        max_load=int(to_host(layer.buf["expert_load"]).max()))
+        elif cap is not None and round_counts is not None:
+            demand = to_host(layer.buf["demand"])
+            res.update(capacity=cap, overflow="defer", rounds=wl.rounds, assignments=int(demand.sum()),
+                       rows_per_round=round_counts.sum(1).tolist(), dropped=int(demand.sum()) - M)
         elif cap is not None:
             demand = to_host(layer.buf["demand"])
             res.update(capacity=cap, assignments=int(demand.sum()), dropped=int(demand.sum()) - M,
@@ -331,9 +346,26 @@ def run_eplb(torch, moe, to_device, to_host):
             torch.cuda.synchronize()
             per = phys // gpus
             gpu_load = np.bincount(to_host(phys_ids).ravel() // per, minlength=gpus)
+            # the same table with a per-replica capacity of 1.2 x the even share per slot and
+            # the overflow sent on to the expert's next replica (ch15 section 4.3 table)
+            C = int(-(-6 * ids_h.size // (5 * phys)))
+            ws = torch.empty(moe.lib().moe_eplb_remap_capacity_workspace_size(ids.shape[0], 8, 256),
+                             dtype=torch.uint8, device="cuda:0")
+            cap_ids = moe.moe_eplb_remap_capacity(ids, d_offs, d_slots, C, workspace=ws)
+            e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e2.record(stream)
+            for _ in range(20):
+                moe.moe_eplb_remap_capacity(ids, d_offs, d_slots, C, cap_ids, ws)
+            e3.record(stream)
+            torch.cuda.synchronize()
+            cap_h = to_host(cap_ids).ravel()
+            cap_load = np.bincount(cap_h[cap_h >= 0] // per, minlength=gpus)
             out[f"{nodes}n_{gpus}g_{'hier' if hier else 'global'}"] = dict(
                 plan_us=plan_us, remap_us=e0.elapsed_time(e1) / 20 * 1e3,
-                busiest_gpu_over_mean_after_remap=float(gpu_load.max() / gpu_load.mean()))
+                busiest_gpu_over_mean_after_remap=float(gpu_load.max() / gpu_load.mean()),
+                replica_capacity=C, remap_capacity_us=e2.elapsed_time(e3) / 20 * 1e3,
+                dropped_with_capacity=int((cap_h < 0).sum()),
+                busiest_gpu_over_mean_with_capacity=float(cap_load.max() / cap_load.mean()))
     return out
 
 

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 SOURCES = ["api.hip", "route.hip", "dispatch.hip", "ffn.hip", "ffn_fp8.hip", "combine.hip", "eplb.hip",
-           "reroute.hip", "host_plan.cpp"]
+           "reroute.hip", "policies.hip", "host_plan.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 
 // The fixed scratch of moe_expert_ffn_noalloc (h and partial sums). In host
 // code `scratch` names a host-side stand-in, not device memory: kernels get
@@ -422,6 +422,71 @@ moe_status_t moe_eplb_remap(const int32_t* topk_ids, int32_t num_tokens, int32_t
   return from_hip(moe::launch_eplb_remap(topk_ids, num_tokens, top_k, replica_offsets, replica_slots,
                                          num_experts, num_physical / num_gpus, num_gpus / num_nodes,
                                          physical_ids, stream));
+}
+
+size_t moe_dispatch_deferred_workspace_size(int32_t num_tokens, int32_t top_k, int32_t num_local_experts) {
+  if (num_tokens < 0 || top_k < 1 || num_local_experts < 1 || num_local_experts > moe::kDispatchMaxLocal)
+    return 0;
+  const int64_t n = (int64_t)num_tokens * top_k;
+  if (n >= ((int64_t)1 << 31) - 65536) return 0;
+  return moe::deferred_workspace_size((int)n, num_local_experts);
+}
+
+moe_status_t moe_dispatch_deferred(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
+                                   int32_t expert_begin, int32_t num_local_experts, int32_t expert_capacity,
+                                   int32_t rounds, const void* x, int32_t hidden, int32_t dtype,
+                                   int32_t* round_counts, int32_t* round_offsets, int32_t* expert_demand,
+                                   int32_t* sorted_assign, int32_t* assign_pos, void* x_sorted,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (num_tokens < 0 || top_k < 1 || expert_begin < 0 || num_local_experts < 1 || expert_capacity < 0 ||
+      rounds < 1)
+    return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (num_local_experts > moe::kDispatchMaxLocal) return MOE_ERR_UNSUPPORTED;
+  const int64_t n = (int64_t)num_tokens * top_k;
+  if (n >= ((int64_t)1 << 31) - 65536) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)rounds * (num_local_experts + 1) >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!round_counts || !round_offsets) return MOE_ERR_INVALID;
+  if (n > 0 && (!topk_ids || !assign_pos || !sorted_assign)) return MOE_ERR_INVALID;
+  if ((x == nullptr) != (x_sorted == nullptr)) return MOE_ERR_INVALID;
+  int row_bytes = 0;
+  if (x) {
+    if (hidden < 8 || hidden % 8 != 0) return MOE_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(x_sorted)) return MOE_ERR_INVALID;
+    const int64_t rb = (int64_t)hidden * (dtype == MOE_BF16 ? 2 : 4);
+    if (rb > (1 << 30)) return MOE_ERR_UNSUPPORTED;
+    row_bytes = (int)rb;
+  }
+  const size_t need = moe::deferred_workspace_size((int)n, num_local_experts);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
+  moe::DeferredArgs a{topk_ids, (int)n, top_k, expert_begin, num_local_experts, expert_capacity, rounds,
+                      x, x_sorted, row_bytes, round_counts, round_offsets, expert_demand, sorted_assign,
+                      assign_pos, workspace};
+  return from_hip(moe::launch_dispatch_deferred(a, stream));
+}
+
+size_t moe_eplb_remap_capacity_workspace_size(int32_t num_tokens, int32_t top_k, int32_t num_experts) {
+  if (num_tokens < 0 || top_k < 1 || num_experts < 1 || num_experts > moe::kDispatchMaxLocal) return 0;
+  const int64_t n = (int64_t)num_tokens * top_k;
+  if (n >= ((int64_t)1 << 31) - 65536) return 0;
+  return moe::remap_capacity_workspace_size((int)n, num_experts);
+}
+
+moe_status_t moe_eplb_remap_capacity(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
+                                     const int32_t* replica_offsets, const int32_t* replica_slots,
+                                     int32_t num_experts, int32_t replica_capacity, int32_t* physical_ids,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (num_tokens < 0 || top_k < 1 || num_experts < 1 || replica_capacity < 0) return MOE_ERR_INVALID;
+  if (num_experts > moe::kDispatchMaxLocal) return MOE_ERR_UNSUPPORTED;
+  const int64_t n = (int64_t)num_tokens * top_k;
+  if (n >= ((int64_t)1 << 31) - 65536) return MOE_ERR_UNSUPPORTED;
+  if (n == 0) return MOE_OK;
+  if (!topk_ids || !replica_offsets || !replica_slots || !physical_ids) return MOE_ERR_INVALID;
+  const size_t need = moe::remap_capacity_workspace_size((int)n, num_experts);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return MOE_ERR_WORKSPACE;
+  moe::RemapCapacityArgs a{topk_ids, (int)n, num_experts, replica_capacity, replica_offsets, replica_slots,
+                           physical_ids, workspace};
+  return from_hip(moe::launch_remap_capacity(a, stream));
 }
 
 }  // extern "C"

@@ -442,4 +442,15 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Row gather for rows laid out by another pass (the deferred dispatch): rows
+// [0, end[num_local]) of x_sorted from sorted_assign.
+hipError_t launch_gather_rows(const void* x, const int* sorted_assign, const int* end, int num_local, int k,
+                              int n, int row_bytes, void* x_sorted, hipStream_t s) {
+  if (n == 0 || row_bytes == 0) return hipSuccess;
+  const int blocks = (int)std::min<long>(((long)n + 3) / 4, 2048);
+  hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(256), 0, s, (const uint4*)x, sorted_assign, end,
+                     num_local, k, n, row_bytes / 16, (uint4*)x_sorted);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -48,6 +48,42 @@ struct DispatchArgs {
 size_t dispatch_workspace_size(int n, int num_local);
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
 constexpr int kDispatchMaxLocal = 1024;  // per-(wave, expert) counters and offsets: 68 KiB of LDS at most
+// Rows [0, end[num_local]) of x_sorted gathered from x through sorted_assign (row i = x[sorted_assign[i] / k]).
+hipError_t launch_gather_rows(const void* x, const int* sorted_assign, const int* end, int num_local, int k,
+                              int n, int row_bytes, void* x_sorted, hipStream_t s);
+
+// Dispatch with the "defer to a later round" overflow policy (policies.hip):
+// the i-th assignment of local expert e (assignment order) goes to round
+// i / capacity; rounds are laid out one after another.
+struct DeferredArgs {
+  const int* ids;
+  int n, k, expert_begin, num_local, capacity, rounds;
+  const void* x;
+  void* x_sorted;
+  int row_bytes;       // 0 = no gather
+  int* round_counts;   // [rounds][num_local]
+  int* round_offsets;  // [rounds][num_local + 1], absolute rows
+  int* demand;         // null, or [num_local]
+  int* sorted_assign;
+  int* assign_pos;
+  void* workspace;
+};
+size_t deferred_workspace_size(int n, int num_local);
+hipError_t launch_dispatch_deferred(const DeferredArgs& a, hipStream_t s);
+
+// Logical -> physical expert with the "send to a same-weight replica" overflow
+// policy (policies.hip): the i-th assignment of logical expert e goes to its
+// replica i / capacity, or -1 past them.
+struct RemapCapacityArgs {
+  const int* ids;
+  int n, num_experts, capacity;
+  const int* rep_offsets;  // [num_experts + 1]
+  const int* rep_slots;
+  int* phys;
+  void* workspace;
+};
+size_t remap_capacity_workspace_size(int n, int num_experts);
+hipError_t launch_remap_capacity(const RemapCapacityArgs& a, hipStream_t s);
 
 struct FfnArgs {
   const void* x;         // permuted rows, or token rows read through row_index

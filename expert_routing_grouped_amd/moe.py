@@ -50,6 +50,11 @@ _SIGNATURES = {
     "moe_combine": (ctypes.c_int, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
     "moe_eplb_place": (ctypes.c_int, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P]),
     "moe_eplb_remap": (ctypes.c_int, [_P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P]),
+    "moe_dispatch_deferred_workspace_size": (ctypes.c_size_t, [_I, _I, _I]),
+    "moe_dispatch_deferred": (ctypes.c_int, [_P, _I, _I, _I, _I, _I, _I, _P, _I, _I, _P, _P, _P, _P, _P, _P,
+                                             _P, ctypes.c_size_t, _P]),
+    "moe_eplb_remap_capacity_workspace_size": (ctypes.c_size_t, [_I, _I, _I]),
+    "moe_eplb_remap_capacity": (ctypes.c_int, [_P, _I, _I, _P, _P, _I, _I, _P, _P, ctypes.c_size_t, _P]),
 }
 
 _lib = None
@@ -512,6 +517,78 @@ def moe_eplb_remap(topk_ids, replica_offsets, replica_slots, num_gpus, num_nodes
     return physical_ids
 
 
+def moe_dispatch_deferred(topk_ids, expert_begin, num_local_experts, capacity, rounds, x=None, out=None,
+                          stream=None):
+    """Dispatch with the "defer to a later round" overflow policy: the i-th assignment of an
+    expert goes to round i // capacity (dropped past `rounds` rounds). Returns dict(round_counts
+    [rounds, E_loc], round_offsets [rounds, E_loc + 1] (absolute rows), demand, sorted_assign,
+    assign_pos, x_sorted)."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    o = dict(out or {})
+    n = T * k
+    o.setdefault("round_counts", torch.empty((rounds, num_local_experts), dtype=torch.int32, device=dev))
+    o.setdefault("round_offsets", torch.empty((rounds, num_local_experts + 1), dtype=torch.int32, device=dev))
+    o.setdefault("demand", torch.empty(num_local_experts, dtype=torch.int32, device=dev))
+    o.setdefault("sorted_assign", torch.empty(max(n, 1), dtype=torch.int32, device=dev))
+    o.setdefault("assign_pos", torch.empty(max(n, 1), dtype=torch.int32, device=dev))
+    hidden, dtype = 0, MOE_BF16
+    if x is not None:
+        dtype = _code(x.dtype)
+        _dev(x, x.dtype, "x")
+        if x.dim() != 2 or x.shape[0] < T:
+            raise MoeError(f"x must be [>= {T}, hidden], got {tuple(x.shape)}")
+        hidden = x.shape[1]
+        o.setdefault("x_sorted", torch.empty((max(n, 1), hidden), dtype=x.dtype, device=dev))
+        _dev(o["x_sorted"], x.dtype, "x_sorted")
+        if o["x_sorted"].dim() != 2 or o["x_sorted"].shape[1] != hidden or o["x_sorted"].shape[0] < n:
+            raise MoeError(f"x_sorted must be [>= {n}, {hidden}], got {tuple(o['x_sorted'].shape)}")
+    else:
+        o["x_sorted"] = None
+    for name, need_n in (("round_counts", rounds * num_local_experts),
+                         ("round_offsets", rounds * (num_local_experts + 1)),
+                         ("demand", num_local_experts), ("sorted_assign", n), ("assign_pos", n)):
+        _at_least(_dev(o[name], torch.int32, name), need_n, name)
+    need = int(lib().moe_dispatch_deferred_workspace_size(T, k, num_local_experts))
+    if need == 0:
+        raise MoeError("moe_dispatch_deferred: unsupported sizes")
+    ws = o.get("workspace")
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib().moe_dispatch_deferred(_ptr(topk_ids), T, k, expert_begin, num_local_experts, int(capacity),
+                                       int(rounds), _ptr(x), hidden, dtype, _ptr(o["round_counts"]),
+                                       _ptr(o["round_offsets"]), _ptr(o["demand"]), _ptr(o["sorted_assign"]),
+                                       _ptr(o["assign_pos"]), _ptr(o["x_sorted"]), _ptr(ws), ws.numel(),
+                                       _stream(stream)), "moe_dispatch_deferred")
+    return o
+
+
+def moe_eplb_remap_capacity(topk_ids, replica_offsets, replica_slots, capacity, physical_ids=None,
+                            workspace=None, stream=None):
+    """Physical slot per routed (token, slot) with a per-replica capacity: the i-th assignment of
+    logical expert e goes to its replica i // capacity (in table order), or -1 past them."""
+    _dev(topk_ids, torch.int32, "topk_ids")
+    _dev(replica_offsets, torch.int32, "replica_offsets")
+    _dev(replica_slots, torch.int32, "replica_slots")
+    T, k = topk_ids.shape
+    E = replica_offsets.numel() - 1
+    if E < 1:
+        raise MoeError("the replica table is empty")
+    if physical_ids is None:
+        physical_ids = torch.empty_like(topk_ids)
+    _shape(_dev(physical_ids, torch.int32, "physical_ids"), (T, k), "physical_ids")
+    need = int(lib().moe_eplb_remap_capacity_workspace_size(T, k, E))
+    if need == 0:
+        raise MoeError("moe_eplb_remap_capacity: unsupported sizes")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=topk_ids.device)
+    _check(lib().moe_eplb_remap_capacity(_ptr(topk_ids), T, k, _ptr(replica_offsets), _ptr(replica_slots), E,
+                                         int(capacity), _ptr(physical_ids), _ptr(workspace), workspace.numel(),
+                                         _stream(stream)), "moe_eplb_remap_capacity")
+    return physical_ids
+
+
 class MoELayer:
     """One GPU's share of the MoE layer with its buffers allocated once.
 
@@ -522,7 +599,7 @@ class MoELayer:
     def __init__(self, *, num_tokens, num_experts, top_k, num_groups, topk_groups, score_mode,
                  renormalize, expert_begin, num_local_experts, hidden, inter, dtype, device,
                  fuse_gather=True, expert_capacity=None, fp8=False, masked_capacity=None,
-                 reroute_capacity=None):
+                 reroute_capacity=None, deferred=None):
         self.T, self.E, self.k = num_tokens, num_experts, top_k
         self.num_groups, self.topk_groups = num_groups, topk_groups
         self.score_mode, self.renormalize = score_mode, renormalize
@@ -537,6 +614,10 @@ class MoELayer:
         self.masked_capacity = masked_capacity
         # capacity with the next-best expert overflow policy, applied by the router
         self.reroute_capacity = reroute_capacity
+        # (C, rounds): capacity with the overflow deferred to later rounds, one FFN call per round
+        self.deferred = deferred
+        if deferred is not None and (fp8 or masked_capacity is not None or expert_capacity is not None):
+            raise MoeError("the deferred policy is a bf16 / float32 grouped layer with its own capacity")
         if masked_capacity is not None and (fp8 or expert_capacity is not None):
             raise MoeError("the masked layout is a bf16 / float32 layer with its own capacity")
         cap = num_tokens * top_k
@@ -557,6 +638,12 @@ class MoELayer:
             self.buf["reroute_ws"] = torch.empty(max(rneed, 1), dtype=torch.uint8, device=dev)
             self.buf["expert_load"] = torch.empty(num_experts, **i32)
         dneed = int(lib().moe_dispatch_workspace_size(num_tokens, top_k, num_local_experts))
+        if deferred is not None:
+            C, R = deferred
+            dneed = int(lib().moe_dispatch_deferred_workspace_size(num_tokens, top_k, num_local_experts))
+            self.buf.update(round_counts=torch.empty((R, num_local_experts), **i32),
+                            round_offsets=torch.empty((R, num_local_experts + 1), **i32),
+                            demand=torch.empty(num_local_experts, **i32))
         if dneed:
             self.buf["dispatch_ws"] = torch.empty(dneed, dtype=torch.uint8, device=dev)
         if masked_capacity is not None:
@@ -611,6 +698,14 @@ class MoELayer:
                 out["x_slots"] = b["x_slots"]
             return moe_dispatch_masked(b["topk_ids"], self.expert_begin, self.num_local,
                                        self.masked_capacity, x, out, stream)
+        if self.deferred is not None:
+            out = {n: b[n] for n in ("round_counts", "round_offsets", "demand", "sorted_assign", "assign_pos")}
+            out["workspace"] = b["dispatch_ws"]
+            xg = None
+            if x is not None and not self.fuse_gather:
+                out["x_sorted"], xg = b["x_sorted"], x
+            return moe_dispatch_deferred(b["topk_ids"], self.expert_begin, self.num_local, self.deferred[0],
+                                         self.deferred[1], xg, out, stream)
         out = {n: b[n] for n in ("counts", "offsets", "sorted_assign", "assign_pos")}
         if "dispatch_ws" in b:
             out["workspace"] = b["dispatch_ws"]
@@ -640,6 +735,16 @@ class MoELayer:
                                       w_down_scales, row_index=b["sorted_assign"], row_index_div=self.k,
                                       row_capacity=self.cap, o_sorted=b["o_sorted"],
                                       workspace=b["workspace"], stream=stream)
+        if self.deferred is not None:   # one grouped FFN call per round, over that round's offsets
+            for r in range(self.deferred[1]):
+                if self.fuse_gather:
+                    moe_expert_ffn(x, b["round_offsets"][r], w_gate_up, w_down, row_index=b["sorted_assign"],
+                                   row_index_div=self.k, row_capacity=self.cap, o_sorted=b["o_sorted"],
+                                   workspace=b["workspace"], stream=stream)
+                else:
+                    moe_expert_ffn(b["x_sorted"], b["round_offsets"][r], w_gate_up, w_down, row_capacity=self.cap,
+                                   o_sorted=b["o_sorted"], workspace=b["workspace"], stream=stream)
+            return b["o_sorted"]
         if self.fuse_gather:
             return moe_expert_ffn(x, b["offsets"], w_gate_up, w_down, row_index=b["sorted_assign"],
                                   row_index_div=self.k, row_capacity=self.cap,

@@ -57,7 +57,9 @@ class Workload:
     capacity_factor: str | None = None   # per-expert cap C = ceil(c T k / E), c as an exact decimal
     weight_format: str = "same"          # "fp8_e4m3_b128": x and expert weights as e4m3 with block scales
     layout: str = "grouped"              # "masked": fixed slots of C rows per local expert
-    overflow: str = "drop"               # "reroute": over-capacity slots go to the next-best expert
+    overflow: str = "drop"               # "reroute": over-capacity slots go to the next-best expert;
+                                         # "defer": they wait for a later round (of `rounds`)
+    rounds: int = 1
 
     @property
     def has_ffn(self) -> bool:
@@ -114,6 +116,14 @@ WORKLOADS = {
 }
 # The same example with the next-best expert overflow policy (routing with capacity).
 WORKLOADS["capacity_reroute"] = WORKLOADS["capacity_route"].replace(name="capacity_reroute", overflow="reroute")
+# ... and with the overflow deferred to a second round (dispatch into two rounds of C rows).
+WORKLOADS["capacity_deferred"] = WORKLOADS["capacity_route"].replace(name="capacity_deferred", overflow="defer",
+                                                                     rounds=2)
+# decode_ep with C = ceil(T k / E) = 16 and the overflow deferred to a second round: the two
+# grouped FFN calls together compute every row of the dropless layer (the busiest local expert
+# has 32 rows at seed 0).
+WORKLOADS["decode_ep_deferred"] = WORKLOADS["decode_ep"].replace(name="decode_ep_deferred", capacity_factor="1",
+                                                                 overflow="defer", rounds=2)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:

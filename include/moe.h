@@ -5,13 +5,15 @@
  *   moe_route       group-limited top-k routing of each token
  *   moe_dispatch    counting-sort permutation of token rows to local experts
  *                   (moe_dispatch_capacity: the same with a per-expert capacity;
- *                   moe_dispatch_masked: into fixed per-expert slots)
+ *                   moe_dispatch_masked: into fixed per-expert slots;
+ *                   moe_dispatch_deferred: overflow deferred to later rounds)
  *   moe_expert_ffn  grouped SwiGLU expert FFN (fused gate_up GEMM, SiLU*up, down GEMM)
  *   moe_combine     router-weighted sum of the expert outputs, back in token order
  *
  * the FP8 variant of the expert FFN (moe_quantize_e4m3 for the token rows,
  * moe_expert_ffn_fp8), and, for placement across GPUs, moe_eplb_place (host
- * planner) and moe_eplb_remap (logical to physical replica per routed slot).
+ * planner), moe_eplb_remap (logical to physical replica per routed slot) and
+ * moe_eplb_remap_capacity (the same with a per-replica capacity).
  *
  * Conventions shared by every call
  * --------------------------------
@@ -136,6 +138,69 @@ moe_status_t moe_eplb_remap(const int32_t* topk_ids, int32_t num_tokens, int32_t
                             const int32_t* replica_offsets, const int32_t* replica_slots,
                             int32_t num_experts, int32_t num_physical, int32_t num_gpus,
                             int32_t num_nodes, int32_t* physical_ids, hipStream_t stream);
+
+/*
+ * moe_dispatch_deferred -- dispatch with a per-expert capacity and the "defer
+ * to a later round" overflow policy of ch15 section 4.3 (table of overflow
+ * policies): an assignment past its expert's capacity keeps its expert and is
+ * processed in a later round. The assignments of local expert e, in
+ * assignment order a = t * k + j, fill round 0 up to expert_capacity = C, then
+ * round 1, ...: the i-th (from 0) goes to round i / C; those past `rounds`
+ * rounds (all, with C = 0) are dropped (assign_pos = -1). Rows are laid out
+ * round after round and, inside a round, expert after expert in assignment
+ * order, so round r is one moe_expert_ffn call with expert_offsets =
+ * round_offsets + r * (E_loc + 1) (absolute rows), and one moe_combine over
+ * assign_pos covers every round.
+ *
+ * round_counts   [rounds, E_loc] out: rows of expert e in round r.
+ * round_offsets  [rounds, E_loc + 1] out: first row of expert e in round r;
+ *                entry E_loc is the end of round r (= the start of round r + 1).
+ * expert_demand  [E_loc] out, or NULL: assignments per local expert.
+ * sorted_assign  [T * k] out: rows [0, end of the last round) written.
+ * assign_pos     [T * k] out: row, or -1 (dropped or not local).
+ * x, x_sorted    as moe_dispatch (both NULL, or the gather of the kept rows).
+ * workspace      moe_dispatch_deferred_workspace_size bytes, 16-byte aligned;
+ *                contents need not be initialised.
+ * Limits: those of moe_dispatch; rounds >= 1. Errors as moe_dispatch;
+ * MOE_ERR_INVALID also for C < 0 or rounds < 1.
+ */
+size_t moe_dispatch_deferred_workspace_size(int32_t num_tokens, int32_t top_k, int32_t num_local_experts);
+moe_status_t moe_dispatch_deferred(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
+                                   int32_t expert_begin, int32_t num_local_experts, int32_t expert_capacity,
+                                   int32_t rounds, const void* x, int32_t hidden, int32_t dtype,
+                                   int32_t* round_counts, int32_t* round_offsets, int32_t* expert_demand,
+                                   int32_t* sorted_assign, int32_t* assign_pos, void* x_sorted,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_eplb_remap_capacity -- logical to physical expert per routed (token,
+ * slot) with a per-replica capacity and the "send to a same-weight replica"
+ * overflow policy of ch15 section 4.3 (table of overflow policies; section
+ * 4.4: the gating picks a logical expert, the system one of its identical
+ * replicas). Logical expert e's replicas are replica_slots[replica_offsets[e]
+ * .. replica_offsets[e + 1]) in that order, each with room for
+ * replica_capacity = C assignments; e's assignments, in assignment order
+ * a = t * k + j, fill its first replica, then the next: the i-th (from 0)
+ * goes to replica i / C.
+ *
+ * topk_ids         [T, k] int32 logical experts (moe_route).
+ * replica_offsets  [num_experts + 1], replica_slots int32, device memory (the
+ *                  table moe_eplb_place writes, or any other replica list).
+ * physical_ids     [T, k] int32 out: the physical slot, or -1 past the room
+ *                  of all e's replicas, for ids outside [0, num_experts) and
+ *                  for experts without a replica.
+ * workspace        moe_eplb_remap_capacity_workspace_size bytes, 16-byte
+ *                  aligned; contents need not be initialised.
+ * Limits: num_experts <= 1024 (the counting sort of moe_dispatch over all of
+ * them gives the ranks). T = 0 is a valid no-op. Errors: MOE_ERR_INVALID for
+ * negative sizes or C, or a NULL pointer; MOE_ERR_WORKSPACE; MOE_ERR_UNSUPPORTED
+ * past the limits.
+ */
+size_t moe_eplb_remap_capacity_workspace_size(int32_t num_tokens, int32_t top_k, int32_t num_experts);
+moe_status_t moe_eplb_remap_capacity(const int32_t* topk_ids, int32_t num_tokens, int32_t top_k,
+                                     const int32_t* replica_offsets, const int32_t* replica_slots,
+                                     int32_t num_experts, int32_t replica_capacity, int32_t* physical_ids,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status; host only, never NULL. */
 const char* moe_status_string(moe_status_t status);

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     lib = moe.lib()
-    assert lib.moe_abi_version() == 8
+    assert lib.moe_abi_version() == 9
     assert moe.status_string(0) == "ok"
     assert moe.status_string(1) == "invalid argument"
     assert moe.status_string(3).startswith("workspace")
@@ -224,3 +224,35 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(moe.MoeError):
         moe.lib()
+
+
+def test_deferred_and_replica_capacity_validation():
+    """The deferred dispatch and the capacity-aware replica choice: workspace sizes and argument
+    checks (every call below fails validation before anything is enqueued)."""
+    l = moe.lib()
+    p = ctypes.c_void_p(256)
+    ws = l.moe_dispatch_deferred_workspace_size(512, 8, 8)
+    assert ws >= (8 + 9 + 4096) * 4
+    assert l.moe_dispatch_deferred_workspace_size(70001, 8, 256) > l.moe_dispatch_workspace_size(70001, 8, 256)
+    assert l.moe_dispatch_deferred_workspace_size(512, 8, 1025) == 0
+    assert l.moe_dispatch_deferred_workspace_size(-1, 8, 8) == 0
+    args = lambda **kw: [kw.get("ids", p), 512, 8, 0, 8, kw.get("C", 20), kw.get("R", 2), None, 0, 1,
+                         kw.get("rc", p), kw.get("ro", p), None, p, p, None, kw.get("ws", p),
+                         kw.get("wsb", ws), None]
+    assert l.moe_dispatch_deferred(*args(C=-1)) == 1
+    assert l.moe_dispatch_deferred(*args(R=0)) == 1
+    assert l.moe_dispatch_deferred(*args(rc=None)) == 1
+    assert l.moe_dispatch_deferred(*args(ids=None)) == 1
+    assert l.moe_dispatch_deferred(*args(wsb=ws - 1)) == 3
+    assert l.moe_dispatch_deferred(*args(ws=None)) == 3
+    bad_ids = args()
+    bad_ids[4] = 1025                                                     # local experts past the limit
+    assert l.moe_dispatch_deferred(*bad_ids) == 2
+    rws = l.moe_eplb_remap_capacity_workspace_size(512, 8, 256)
+    assert rws >= (256 + 257 + 2 * 4096) * 4
+    assert l.moe_eplb_remap_capacity_workspace_size(512, 8, 1025) == 0
+    assert l.moe_eplb_remap_capacity(p, 512, 8, p, p, 256, -1, p, p, rws, None) == 1
+    assert l.moe_eplb_remap_capacity(p, 512, 8, None, p, 256, 4, p, p, rws, None) == 1
+    assert l.moe_eplb_remap_capacity(p, 512, 8, p, p, 256, 4, p, p, rws - 1, None) == 3
+    assert l.moe_eplb_remap_capacity(p, 512, 8, p, p, 1025, 4, p, p, rws, None) == 2
+    assert l.moe_eplb_remap_capacity(None, 0, 8, None, None, 256, 4, None, None, 0, None) == 0   # T = 0: no-op
