@@ -19,14 +19,22 @@
 // block), code = the e4m3 value nearest to v / scale, ties to the even code,
 // magnitudes above 448 saturate; both divisions are correctly rounded float32.
 //
-// The GEMMs stream the weights: every expert is cut into row chunks of up to
-// 64 rows, and a work item is one chunk and one slab of output columns. A K
+// Experts with at most 64 rows (decode) stream the weights: a work item is
+// the expert's rows and one slab of output columns. A K
 // step is 128 k, one 128-byte line of each row, loaded coalesced (8 rows per
 // instruction) into a wavefront-private XOR-swizzled LDS tile and read back
 // as MFMA fragments for v_mfma_scale_f32_16x16x128_f8f6f4 (block scales of
 // the instruction left at 1): one instruction covers exactly one scale block
 // of k, so its float32 result is multiplied by (row scale x weight block
 // scale) and added to the accumulator. Loads run two K steps ahead.
+//
+// Experts with more than 64 rows (prefill) are tiled instead: 128 weight rows
+// x 128 tokens per work item, so the weights are read once per 128 rows and
+// each loaded byte feeds 128 multiply-adds. A K step (128 k, one scale block)
+// of both operands is staged through a double-buffered XOR-swizzled LDS tile;
+// each wavefront multiplies 64 x 64 of the tile on
+// v_mfma_scale_f32_32x32x64_f8f6f4 (two per K step and fragment pair, into a
+// zeroed float32 partial that is then added with its scale factor).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -45,6 +53,7 @@ constexpr int kF8Depth = 3;       // register sets: loads run kF8Depth - 1 steps
 constexpr int kF8MaxLocal = 1024;
 constexpr int kF8Config = 0x00020000;   // buffer resource word 3 (raw buffer loads)
 constexpr int kF8NonTemporal = 2;
+constexpr int kT8Rows = 128;      // tokens per tile (experts with more than kF8Rows rows)
 
 typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 
@@ -144,13 +153,17 @@ struct F8Args {
   int ldc;
 };
 
-// Chunks of every expert with rows, in expert order: c_first[e] = first chunk
-// of expert e, c_first[nloc] = chunks; c_lo[e] = first row (clamped to the
-// capacity), c_lo[nloc] = end of the last expert. 4 experts per thread of the
-// 256-thread workgroup; returns the chunk count.
-__device__ int f8_chunk_lists(const F8Args& a, int* c_first, int* c_lo, int* wsum) {
+// Work lists, in expert order, of the experts with rows: those with at most
+// kF8Rows rows are one chunk each (c_first[e] = the chunk of expert e,
+// c_first[nloc] = chunks), the others are cut into tiles of kT8Rows rows
+// (t_first[e] = first tile of expert e, t_first[nloc] = tiles). c_lo[e] =
+// first row of expert e (clamped to the capacity), c_lo[nloc] = end of the
+// last expert. 4 experts per thread of the 256-thread workgroup; returns the
+// chunk and tile counts.
+__device__ void f8_lists(const F8Args& a, int* c_first, int* t_first, int* c_lo, int* wsum, int& n_chunks,
+                         int& n_tiles) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int cnt[4], sum = 0;
+  int cc[4], tc[4], cs = 0, ct = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = tid * 4 + q;
@@ -162,35 +175,44 @@ __device__ int f8_chunk_lists(const F8Args& a, int* c_first, int* c_lo, int* wsu
       c_lo[e] = lo;
       if (e == a.nloc - 1) c_lo[a.nloc] = max(lo, hi);
     }
-    cnt[q] = (m + kF8Rows - 1) / kF8Rows;
-    sum += cnt[q];
+    cc[q] = (m > 0 && m <= kF8Rows) ? 1 : 0;
+    tc[q] = m > kF8Rows ? (m + kT8Rows - 1) / kT8Rows : 0;
+    cs += cc[q];
+    ct += tc[q];
   }
-  int incl = sum;
+  int is = cs, it = ct;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, MOE_WAVE);
-    if (lane >= d) incl += o;
+    const int os = __shfl_up(is, d, MOE_WAVE), ot = __shfl_up(it, d, MOE_WAVE);
+    if (lane >= d) { is += os; it += ot; }
   }
-  if (lane == 63) wsum[w] = incl;
+  if (lane == 63) { wsum[w] = is; wsum[4 + w] = it; }
   __syncthreads();
-  int before = 0, total = 0;
+  int bs = 0, bt = 0, ts = 0, tt = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    if (i < w) before += wsum[i];
-    total += wsum[i];
+    if (i < w) { bs += wsum[i]; bt += wsum[4 + i]; }
+    ts += wsum[i];
+    tt += wsum[4 + i];
   }
-  int p = before + incl - sum;
+  int ps = bs + is - cs, pt = bt + it - ct;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = tid * 4 + q;
     if (e < a.nloc) {
-      c_first[e] = p;
-      p += cnt[q];
+      c_first[e] = ps;
+      t_first[e] = pt;
+      ps += cc[q];
+      pt += tc[q];
     }
   }
-  if (tid == 0) c_first[a.nloc] = total;
+  if (tid == 0) {
+    c_first[a.nloc] = ts;
+    t_first[a.nloc] = tt;
+  }
   __syncthreads();
-  return __builtin_amdgcn_readfirstlane(total);
+  n_chunks = __builtin_amdgcn_readfirstlane(ts);
+  n_tiles = __builtin_amdgcn_readfirstlane(tt);
 }
 
 __device__ __forceinline__ int f8_find_expert(const int* first, int nloc, int idx) {
@@ -434,23 +456,207 @@ struct Stream8 {
     }
   }
 
-  // Chunk `chunk` of expert e, output slab `slab`. The weights of an expert
-  // with a single chunk are read once per GEMM, non-temporally.
-  __device__ static void run(const F8Args& a, const int* c_lo, int e, int chunk, int slab, char* smem) {
+  // The rows of expert e (at most kF8Rows), output slab `slab`. The expert's
+  // weights are read once per GEMM, non-temporally.
+  __device__ static void run(const F8Args& a, const int* c_lo, int e, int slab, char* smem) {
     e = __builtin_amdgcn_readfirstlane(e);
-    const int lo = __builtin_amdgcn_readfirstlane(c_lo[e] + chunk * kF8Rows);
+    const int lo = __builtin_amdgcn_readfirstlane(c_lo[e]);
     const int m = __builtin_amdgcn_readfirstlane(min(kF8Rows, c_lo[e + 1] - lo));
-    const bool nt = __builtin_amdgcn_readfirstlane(c_lo[e + 1] - c_lo[e]) <= kF8Rows;
     slab = __builtin_amdgcn_readfirstlane(slab);
-    switch (((m + 15) >> 4) * 2 + (nt ? 1 : 0)) {
-      case 2: run_mt<1, false>(a, e, lo, m, slab, smem); break;
-      case 3: run_mt<1, true>(a, e, lo, m, slab, smem); break;
-      case 4: run_mt<2, false>(a, e, lo, m, slab, smem); break;
-      case 5: run_mt<2, true>(a, e, lo, m, slab, smem); break;
-      case 6: run_mt<3, false>(a, e, lo, m, slab, smem); break;
-      case 7: run_mt<3, true>(a, e, lo, m, slab, smem); break;
-      case 9: run_mt<4, true>(a, e, lo, m, slab, smem); break;
-      default: run_mt<4, false>(a, e, lo, m, slab, smem); break;
+    switch ((m + 15) >> 4) {
+      case 1: run_mt<1, true>(a, e, lo, m, slab, smem); break;
+      case 2: run_mt<2, true>(a, e, lo, m, slab, smem); break;
+      case 3: run_mt<3, true>(a, e, lo, m, slab, smem); break;
+      default: run_mt<4, true>(a, e, lo, m, slab, smem); break;
+    }
+  }
+};
+
+// Tile of kT8Rows tokens x 128 weight rows (experts with more than kF8Rows
+// rows). Thread (rbase = tid / 8, kc = tid % 8) loads the 16-byte chunk kc
+// of tile rows rbase + 32 i (i = 0..3) of both operands per K step; chunk c
+// of LDS row r sits at slot c ^ (r % 8), so 8 threads store one row's 128
+// bytes and the 32 rows a fragment read touches per chunk spread over the
+// banks. Wavefront (wm, wn) multiplies weight rows wm*64.. by tokens wn*64..:
+// 2 x 2 fragments of 32 x 32. MFMA u (0, 1) of a fragment pair takes chunks
+// 4u + 2 fh and 4u + 2 fh + 1 of its row for lane half fh, the same bytes for
+// weights and tokens, so the two instructions sum each k of the step once.
+//
+// A gated tile holds 64 output columns: tile rows [gate 32 | up 32] for
+// wavefront row 0, then for row 1, so fragment 0 (gate) and fragment 1 (up)
+// of a wavefront cover the same columns and SiLU(gate) * up is formed from
+// its own accumulators. Weight rows of a fragment lie in one 128-row scale
+// block (32 | 128), so a lane's partial of a step takes one factor: its
+// token's row scale x the fragment's weight block scale.
+template <bool GATED>
+struct Tiled8 {
+  static constexpr int COLS = GATED ? 64 : 128;     // output columns per tile
+  static constexpr int OP = 128 * 128;               // bytes of one operand tile (128 rows x 128 k)
+  static constexpr int LDS_BYTES = 2 * 2 * OP;       // [buffer][W | X]
+
+  __device__ static __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+  __device__ static void run(const F8Args& a, int e, int row0, int rows, int nb, char* lds) {
+    // the thread index passes through an empty asm statement, so the
+    // compiler derives this item's lane offsets here instead of keeping them
+    // in registers across the persistent loop (where the streaming path
+    // needs them)
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int kc = tid & 7, rbase = tid >> 3;
+    const int fr = lane & 31, fh = lane >> 5;
+    const uint32_t pitch = (uint32_t)a.K;
+    const int KB = a.K / kQBlock;
+
+    const __amdgpu_buffer_rsrc_t wbuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.W + (size_t)e * a.N * a.K), 0, (int)(a.N * pitch), kF8Config);
+    const __amdgpu_buffer_rsrc_t wsbuf = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.Ws + (size_t)e * (a.N / kQBlock) * KB), 0, (a.N / kQBlock) * KB * 4, kF8Config);
+    const __amdgpu_buffer_rsrc_t abuf = __builtin_amdgcn_make_buffer_rsrc((void*)a.A, 0, -1, kF8Config);
+    const __amdgpu_buffer_rsrc_t asbuf = __builtin_amdgcn_make_buffer_rsrc((void*)a.As, 0, -1, kF8Config);
+
+    // This thread's weight rows (loads) and token rows (rows past the tile's
+    // end read its first row; their outputs are not stored).
+    uint32_t wv[4], xv[4], sv[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int wr = GATED ? nb * COLS + rbase + ((i & 1) ? a.inter : 0) + (i >> 1) * 32
+                           : nb * COLS + rbase + 32 * i;
+      wv[i] = (uint32_t)wr * pitch + kc * 16;
+      const int r = rbase + 32 * i;
+      xv[i] = (uint32_t)(row0 + (r < rows ? r : 0));
+    }
+    // the rows of the lane's two MFMA columns, for their scales
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = wn * 64 + j * 32 + fr;
+      sv[j] = (uint32_t)(row0 + (t < rows ? t : 0));
+    }
+    f8_rows<4>(a, xv);
+    f8_rows<2>(a, sv);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[i] = xv[i] * pitch + kc * 16;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sv[j] = sv[j] * (uint32_t)KB * 4;
+    // weight scale block of the wavefront's fragments (gated: gate, up)
+    int wsb[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int n0 = GATED ? nb * COLS + wm * 32 + (i ? a.inter : 0) : nb * COLS + wm * 64 + i * 32;
+      wsb[i] = __builtin_amdgcn_readfirstlane((n0 / kQBlock) * KB * 4);
+    }
+
+    u32x4_t gw[4], gx[4];
+    float gsa[2], gsw[2];
+    auto gload = [&](int kt) {
+      const int k0 = kt * 128;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gw[i] = __builtin_amdgcn_raw_buffer_load_b128(wbuf, wv[i], k0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gx[i] = __builtin_amdgcn_raw_buffer_load_b128(abuf, xv[i], k0, 0);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        gsa[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(asbuf, sv[j], kt * 4, 0));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        gsw[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(wsbuf, 0, wsb[i] + kt * 4, 0));
+    };
+    auto sstore = [&](int buf) {
+      char* lw = lds + buf * 2 * OP;
+      char* lx = lw + OP;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(u32x4_t*)(lw + swz(rbase + 32 * i, kc)) = gw[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(u32x4_t*)(lx + swz(rbase + 32 * i, kc)) = gx[i];
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+
+    const int nk = a.K / 128;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      float sc[2][2];   // this step's factors, taken before the next step's loads replace them
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) sc[i][j] = gsw[i] * gsa[j];
+      if (kt + 1 < nk) gload(kt + 1);
+      const char* lw = lds + buf * 2 * OP;
+      const char* lx = lw + OP;
+      f32x16_t p[2][2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c0 = 4 * u + 2 * fh;
+        i32x8_t af[2], bfr[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int r = wm * 64 + i * 32 + fr;
+          const i32x4_t lo4 = *(const i32x4_t*)(lw + swz(r, c0));
+          const i32x4_t hi4 = *(const i32x4_t*)(lw + swz(r, c0 + 1));
+          af[i] = i32x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int r = wn * 64 + j * 32 + fr;
+          const i32x4_t lo4 = *(const i32x4_t*)(lx + swz(r, c0));
+          const i32x4_t hi4 = *(const i32x4_t*)(lx + swz(r, c0 + 1));
+          bfr[j] = i32x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            p[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bfr[j], u ? p[i][j] : f32x16_t{}, 0,
+                                                                      0, 0, 127, 0, 127);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = fmaf(p[i][j][r], sc[i][j], acc[i][j][r]);
+      if (kt + 1 < nk) sstore(buf ^ 1);
+      __syncthreads();
+    }
+
+    // acc[i][j][r]: token wn*64 + j*32 + lane%32; tile row wm*64 + i*32 +
+    // (r/4)*8 + (lane/32)*4 + r%4.
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int t = wn * 64 + j * 32 + fr;
+      if (t >= rows) continue;
+      if (GATED) {
+        float* crow = (float*)a.C + (size_t)(row0 + t) * a.ldc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = nb * COLS + wm * 32 + q * 8 + fh * 4;
+          f32x4_t v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = silu_f(acc[0][j][q * 4 + r]) * acc[1][j][q * 4 + r];
+          *(f32x4_t*)(crow + col) = v;
+        }
+      } else {
+        uint16_t* crow = (uint16_t*)a.C + (size_t)(row0 + t) * a.ldc;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = nb * COLS + wm * 64 + i * 32 + q * 8 + fh * 4;
+            const f32x16_t& c = acc[i][j];
+            *(uint2*)(crow + col) = make_uint2(pack_bf16x2(c[q * 4], c[q * 4 + 1]),
+                                               pack_bf16x2(c[q * 4 + 2], c[q * 4 + 3]));
+          }
+      }
     }
   }
 };
@@ -458,17 +664,33 @@ struct Stream8 {
 template <int NTW, int KS, bool GATED>
 __global__ __launch_bounds__(256, 2) void ffn_fp8_kernel(F8Args a) {
   using S = Stream8<NTW, KS, GATED>;
-  __shared__ __attribute__((aligned(16))) char smem[S::LDS_BYTES];
+  using T = Tiled8<GATED>;
+  constexpr int SMEM = S::LDS_BYTES > T::LDS_BYTES ? S::LDS_BYTES : T::LDS_BYTES;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ int c_first[kF8MaxLocal + 1];
+  __shared__ int t_first[kF8MaxLocal + 1];
   __shared__ int c_lo[kF8MaxLocal + 1];
-  __shared__ int wsum[4];
-  const int chunks = f8_chunk_lists(a, c_first, c_lo, wsum);
-  const int slabs = (GATED ? a.inter : a.N) / S::COLS;
-  const int total = chunks * slabs;
+  __shared__ int wsum[8];
+  int chunks, tiles;
+  f8_lists(a, c_first, t_first, c_lo, wsum, chunks, tiles);
+  const int ncols = GATED ? a.inter : a.N;
+  const int slabs = ncols / S::COLS;
+  const int nblk = ncols / T::COLS;
+  const int n_stream = chunks * slabs;
+  const int total = n_stream + tiles * nblk;
+  // streamed chunks first, then the tiles with their N blocks fastest
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    const int c = w / slabs;
-    const int e = f8_find_expert(c_first, a.nloc, c);
-    S::run(a, c_lo, e, c - c_first[e], w % slabs, smem);
+    if (w < n_stream) {
+      const int c = w / slabs;
+      const int e = f8_find_expert(c_first, a.nloc, c);
+      S::run(a, c_lo, e, w % slabs, smem);
+    } else {
+      const int tile = (w - n_stream) / nblk, nb = (w - n_stream) % nblk;
+      const int e = __builtin_amdgcn_readfirstlane(f8_find_expert(t_first, a.nloc, tile));
+      const int row0 = __builtin_amdgcn_readfirstlane(c_lo[e] + (tile - t_first[e]) * kT8Rows);
+      const int rows = __builtin_amdgcn_readfirstlane(min(kT8Rows, c_lo[e + 1] - row0));
+      T::run(a, e, row0, rows, __builtin_amdgcn_readfirstlane(nb), smem);
+    }
     __syncthreads();  // the LDS buffer is reused by the next work item
   }
 }
@@ -497,8 +719,10 @@ hipError_t launch_fp8_gemm(const F8Args& g, hipStream_t s) {
       n = 1;
     return n;
   }();
-  const long max_chunks = (long)(g.capacity + kF8Rows - 1) / kF8Rows + g.nloc;
-  const long max_work = max_chunks * ((GATED ? g.inter : g.N) / S::COLS);
+  const int ncols = GATED ? g.inter : g.N;
+  // at most min(nloc, capacity) streamed experts, or capacity / kT8Rows + nloc tiles
+  const long max_work = std::max<long>(std::min<long>(g.nloc, g.capacity) * (ncols / S::COLS),
+                                       ((long)g.capacity / kT8Rows + g.nloc) * (ncols / Tiled8<GATED>::COLS));
   const int grid = (int)std::max<long>(1, std::min<long>(max_work, (long)f8_cu_count() * occ));
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, g);
   return hipGetLastError();

@@ -124,6 +124,11 @@ WORKLOADS["capacity_deferred"] = WORKLOADS["capacity_route"].replace(name="capac
 # has 32 rows at seed 0).
 WORKLOADS["decode_ep_deferred"] = WORKLOADS["decode_ep"].replace(name="decode_ep_deferred", capacity_factor="1",
                                                                  overflow="defer", rounds=2)
+# prefill_straggler on FP8 operands (decode_ep_fp8's format: e4m3 weights with 128 x 128 block
+# scales, x quantised per row in the step): the prefill-sized FP8 call, whose experts of more
+# than 64 rows take the tiled path.
+WORKLOADS["prefill_straggler_fp8"] = WORKLOADS["prefill_straggler"].replace(name="prefill_straggler_fp8",
+                                                                           weight_format="fp8_e4m3_b128")
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:

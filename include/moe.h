@@ -512,9 +512,10 @@ size_t moe_expert_ffn_fp8_workspace_size(int32_t num_local_experts, int32_t hidd
  *                 float32 and in FP8); contents need not be initialised.
  * Limits: hidden % 512 == 0, inter % 256 == 0; E_loc <= 1024;
  * row_capacity * inter * 4 < 2^31; the caller keeps x_codes below 2^32
- * bytes. M = offsets[E_loc] must not exceed row_capacity. Every expert's rows
- * are streamed in chunks of 64 (the weights are read once per chunk): the
- * path is built for decode-sized calls.
+ * bytes. M = offsets[E_loc] must not exceed row_capacity. Experts with at
+ * most 64 rows stream their weights once per call (decode); larger ones are
+ * multiplied in tiles of 128 rows x 128 weight rows (prefill), so their
+ * weights are read once per 128 rows.
  */
 moe_status_t moe_expert_ffn_fp8(const void* x_codes, const float* x_scales, const int32_t* row_index,
                                 int32_t row_index_div, const int32_t* expert_offsets,

@@ -180,6 +180,29 @@ def test_ffn_fp8_ragged(counts, d, I, k):
     check_ffn(counts, d, I, k, seed=sum(counts) + d + I)
 
 
+# Experts with more than 64 rows take 128-row tiles (128 weight rows x 128 tokens per item).
+@pytest.mark.parametrize("counts,d,I,k", [
+    ([129, 0, 65, 64, 300, 1], 1024, 512, 4),   # 64 streamed / 65 tiled, a one-row last tile
+    ([1000], 2048, 256, 8),                     # 8 tiles, the last with 104 rows
+    ([128, 256, 200], 512, 768, 2),             # whole tiles; inter = 768: 12 gated N blocks
+    ([70, 3, 190, 0, 0, 2500], 1536, 256, 8),   # a 20-tile expert beside streamed ones
+])
+def test_ffn_fp8_tiled(counts, d, I, k):
+    check_ffn(counts, d, I, k, seed=sum(counts) * 3 + d + I)
+
+
+def test_ffn_fp8_tiled_permuted_and_spare_rows():
+    check_ffn([90, 0, 300], 1024, 512, 2, seed=13, permuted=True)
+    check_ffn([90, 0, 300], 1024, 512, 2, seed=14, spare_rows=200)
+
+
+def test_ffn_fp8_tiled_1024_local_experts():
+    rng = np.random.default_rng(15)
+    counts = rng.integers(0, 4, 1024) * (rng.random(1024) < 0.3)
+    counts[[5, 400, 1023]] = [70, 300, 129]
+    check_ffn(counts.tolist(), 512, 256, 8, seed=16, distinct=7)
+
+
 def test_ffn_fp8_permuted_rows():
     check_ffn([40, 0, 90], 1024, 512, 2, seed=3, permuted=True)
 
@@ -201,10 +224,12 @@ def test_ffn_fp8_1024_local_experts():
 
 # ------------------------------------------------------------------ layer at the decode_ep_fp8 size
 
-def test_layer_decode_ep_fp8_sampled():
-    """Full-size FP8 decode share through MoELayer: routing and permutation exact, x's codes
-    exact, o and y checked on sampled rows and tokens."""
-    wl = W.WORKLOADS["decode_ep_fp8"]
+@pytest.mark.parametrize("name", ["decode_ep_fp8", "prefill_straggler_fp8"])
+def test_layer_fp8_sampled(name):
+    """Full-size FP8 shares through MoELayer (decode: every expert streamed; prefill: the
+    straggler GPU's experts on 128-row tiles): routing and permutation exact, x's codes exact,
+    o and y checked on sampled rows and tokens."""
+    wl = W.WORKLOADS[name]
     inp = W.generate(wl)
     layer = moe.MoELayer(num_tokens=wl.T, num_experts=wl.E, top_k=wl.top_k, num_groups=wl.num_groups,
                          topk_groups=wl.topk_groups, score_mode=moe.MOE_SCORE_RAW,
