@@ -104,4 +104,57 @@ __device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
   return max(max(readlane_u32(v, 0), readlane_u32(v, 16)), max(readlane_u32(v, 32), readlane_u32(v, 48)));
 }
 
+// Buffer resource word 3 for raw (unformatted, unswizzled) buffer loads on gfx9.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// A buffer resource over [base, base + bytes) as four scalar words.
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane((int)bytes);
+  r.w = kRawBufferWord3;
+  return r;
+}
+
+// Memory -> LDS copy of 16 bytes per lane (LDS DMA): LDS byte address lds +
+// 16 * lane, memory offset voff + soff in buffer rsrc. m0 is saved and
+// restored. The copy is counted by vmcnt; the compiler does not track it, so
+// callers wait for it with wait_vmcnt.
+__device__ __forceinline__ void lds_dma16(uint32_t lds, const i32x4_t& rsrc, uint32_t voff, uint32_t soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"  // one wait state between an SALU write of m0 and an LDS DMA
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+// The same with 4 bytes per lane: LDS byte address lds + 4 * lane.
+__device__ __forceinline__ void lds_dma4(uint32_t lds, const i32x4_t& rsrc, uint32_t voff, uint32_t soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt bits [3:0] and [15:14], the other
+// counters left at their maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 }  // namespace moe

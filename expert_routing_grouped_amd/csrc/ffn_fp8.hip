@@ -54,6 +54,8 @@ constexpr int kF8MaxLocal = 1024;
 constexpr int kF8Config = 0x00020000;   // buffer resource word 3 (raw buffer loads)
 constexpr int kF8NonTemporal = 2;
 constexpr int kT8Rows = 128;      // tokens per tile (experts with more than kF8Rows rows)
+constexpr int kB8Rows = 256;      // tokens per large tile
+constexpr int kB8MinCapacity = 16384;   // row capacity from which the large-tile kernel is launched
 
 typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 
@@ -78,10 +80,14 @@ __device__ __forceinline__ uint32_t e4m3_code(float q) {
 
 // ---------------------------------------------------------------- quantiser
 
-// A wavefront takes 4 consecutive blocks of one row (512 values): lane l
+// A wavefront item is 4 consecutive blocks of one row (512 values): lane l
 // holds 8 values of block l / 16, and the block's maximum is reduced over its
-// 16 lanes. Lanes past the row's last block do nothing. The row count is
-// rows, or min(rows, *rows_dev) when rows_dev is given.
+// 16 lanes. Lanes past the row's last block do nothing. A wavefront takes
+// kQItems items per pass (items w, w + stride, ...), all loads issued before
+// the first is used. The row count is rows, or min(rows, *rows_dev) when
+// rows_dev is given.
+constexpr int kQItems = 4;
+
 template <bool BF16_IN>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* in, int rows, const int* rows_dev,
                                                            int cols, uint8_t* codes, float* scales) {
@@ -92,48 +98,59 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* in, int 
   const long total = (long)n * groups;
   const int lane = threadIdx.x & 63;
   const long stride = (long)gridDim.x * 4;
-  for (long w = (long)blockIdx.x * 4 + (threadIdx.x >> 6); w < total; w += stride) {
-    const int r = (int)(w / groups);
-    const int b = (int)(w - (long)r * groups) * 4 + (lane >> 4);
-    const bool active = b < nb;
-    const size_t first = (size_t)r * cols + (size_t)b * kQBlock + (lane & 15) * 8;   // of 8 values
-    float v[8];
-    if (active) {
-      if (BF16_IN) {
-        const u32x4_t p = *(const u32x4_t*)((const uint16_t*)in + first);
+  for (long w0 = (long)blockIdx.x * 4 + (threadIdx.x >> 6); w0 < total; w0 += stride * kQItems) {
+    float v[kQItems][8];
+    size_t first[kQItems];
+    int row[kQItems], blk[kQItems];
+    bool active[kQItems];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[2 * j] = bf16_lo(p[j]);
-          v[2 * j + 1] = bf16_hi(p[j]);
+    for (int u = 0; u < kQItems; ++u) {
+      const long w = w0 + u * stride;
+      const int r = (int)(w / groups);
+      row[u] = r;
+      blk[u] = (int)(w - (long)r * groups) * 4 + (lane >> 4);
+      active[u] = w < total && blk[u] < nb;
+      first[u] = (size_t)r * cols + (size_t)blk[u] * kQBlock + (lane & 15) * 8;   // of 8 values
+      if (active[u]) {
+        if (BF16_IN) {
+          const u32x4_t p = *(const u32x4_t*)((const uint16_t*)in + first[u]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[u][2 * j] = bf16_lo(p[j]);
+            v[u][2 * j + 1] = bf16_hi(p[j]);
+          }
+        } else {
+          const f32x4_t p0 = *(const f32x4_t*)((const float*)in + first[u]);
+          const f32x4_t p1 = *(const f32x4_t*)((const float*)in + first[u] + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[u][j] = p0[j];
+            v[u][4 + j] = p1[j];
+          }
         }
       } else {
-        const f32x4_t p0 = *(const f32x4_t*)((const float*)in + first);
-        const f32x4_t p1 = *(const f32x4_t*)((const float*)in + first + 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[j] = p0[j];
-          v[4 + j] = p1[j];
-        }
+        for (int j = 0; j < 8; ++j) v[u][j] = 0.0f;
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
     }
-    float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    for (int u = 0; u < kQItems; ++u) {
+      float amax = 0.0f;
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, MOE_WAVE));
-    if (!active) continue;
-    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-    uint32_t lo = 0, hi = 0;
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[u][j]));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      lo |= e4m3_code(v[j] / s) << (8 * j);
-      hi |= e4m3_code(v[4 + j] / s) << (8 * j);
+      for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, MOE_WAVE));
+      if (!active[u]) continue;
+      const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo |= e4m3_code(v[u][j] / s) << (8 * j);
+        hi |= e4m3_code(v[u][4 + j] / s) << (8 * j);
+      }
+      *(uint2*)(codes + first[u]) = make_uint2(lo, hi);
+      if ((lane & 15) == 0) scales[(size_t)row[u] * nb + blk[u]] = s;
     }
-    *(uint2*)(codes + first) = make_uint2(lo, hi);
-    if ((lane & 15) == 0) scales[(size_t)r * nb + b] = s;
   }
 }
 
@@ -151,19 +168,23 @@ struct F8Args {
   int N, K, inter;        // gated GEMMs pair weight row n with row inter + n
   void* C;                // gated: float h [capacity, ldc]; plain: bf16 [capacity, ldc]
   int ldc;
+  int big_ok;             // the large-tile kernel is launched too ...
+  int big_min_items;      // ... and takes the tiled experts when it has at least this many items
 };
 
 // Work lists, in expert order, of the experts with rows: those with at most
 // kF8Rows rows are one chunk each (c_first[e] = the chunk of expert e,
-// c_first[nloc] = chunks), the others are cut into tiles of kT8Rows rows
+// c_first[nloc] = chunks), the others are cut into tiles of tile_rows rows
 // (t_first[e] = first tile of expert e, t_first[nloc] = tiles). c_lo[e] =
 // first row of expert e (clamped to the capacity), c_lo[nloc] = end of the
-// last expert. 4 experts per thread of the 256-thread workgroup; returns the
-// chunk and tile counts.
-__device__ void f8_lists(const F8Args& a, int* c_first, int* t_first, int* c_lo, int* wsum, int& n_chunks,
-                         int& n_tiles) {
+// last expert. n_big = the tiles of kB8Rows rows that the tiled experts
+// need. Every thread of a workgroup of 256 calls this (4 experts per
+// thread; a larger workgroup's other threads only take part in the
+// barriers).
+__device__ void f8_lists(const F8Args& a, int tile_rows, int* c_first, int* t_first, int* c_lo, int* wsum,
+                         int& n_chunks, int& n_tiles, int& n_big) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int cc[4], tc[4], cs = 0, ct = 0;
+  int cc[4], tc[4], cs = 0, ct = 0, cb = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = tid * 4 + q;
@@ -176,24 +197,27 @@ __device__ void f8_lists(const F8Args& a, int* c_first, int* t_first, int* c_lo,
       if (e == a.nloc - 1) c_lo[a.nloc] = max(lo, hi);
     }
     cc[q] = (m > 0 && m <= kF8Rows) ? 1 : 0;
-    tc[q] = m > kF8Rows ? (m + kT8Rows - 1) / kT8Rows : 0;
+    tc[q] = m > kF8Rows ? (m + tile_rows - 1) / tile_rows : 0;
     cs += cc[q];
     ct += tc[q];
+    cb += m > kF8Rows ? (m + kB8Rows - 1) / kB8Rows : 0;
   }
+  cb = wave_sum_i32(cb);
   int is = cs, it = ct;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const int os = __shfl_up(is, d, MOE_WAVE), ot = __shfl_up(it, d, MOE_WAVE);
     if (lane >= d) { is += os; it += ot; }
   }
-  if (lane == 63) { wsum[w] = is; wsum[4 + w] = it; }
+  if (lane == 63 && w < 4) { wsum[w] = is; wsum[4 + w] = it; wsum[8 + w] = cb; }
   __syncthreads();
-  int bs = 0, bt = 0, ts = 0, tt = 0;
+  int bs = 0, bt = 0, ts = 0, tt = 0, tb = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (i < w) { bs += wsum[i]; bt += wsum[4 + i]; }
     ts += wsum[i];
     tt += wsum[4 + i];
+    tb += wsum[8 + i];
   }
   int ps = bs + is - cs, pt = bt + it - ct;
 #pragma unroll
@@ -213,6 +237,7 @@ __device__ void f8_lists(const F8Args& a, int* c_first, int* t_first, int* c_lo,
   __syncthreads();
   n_chunks = __builtin_amdgcn_readfirstlane(ts);
   n_tiles = __builtin_amdgcn_readfirstlane(tt);
+  n_big = __builtin_amdgcn_readfirstlane(tb);
 }
 
 __device__ __forceinline__ int f8_find_expert(const int* first, int nloc, int idx) {
@@ -472,6 +497,258 @@ struct Stream8 {
   }
 };
 
+// ---------------------------------------------------------------- large-tile path
+
+// Experts with more than kF8Rows rows when their 256-row tiles fill the GPU
+// (prefill; f8_big_takes): 256 weight rows x 256 tokens per tile, one
+// workgroup of 8 wavefronts per CU, two per SIMD, so that one wavefront's
+// scale arithmetic runs while the other's MFMAs do. Wavefront w = 2 wm + wn
+// multiplies tile weight rows wm*64 .. +63 (fragments i = 0..3 of 16 rows)
+// by the token fragments 2j + wn (16 rows each, j = 0..7) on
+// v_mfma_scale_f32_16x16x128_f8f6f4: one instruction per fragment pair and K
+// step, i.e. per scale block, so its float32 result is added at once with
+// the factor row scale x weight block scale (4 accumulators per pair, 128
+// per lane). Only the token fragments that hold a valid row are multiplied
+// (NJ of them, rounded up to even; a template argument so that the stage
+// stays fully unrolled).
+//
+// K is staged 128 at a time (128 bytes of every row) in two 64 KB LDS
+// buffers filled by LDS DMA: per stage each wavefront copies 4 blocks of 8
+// weight rows and 4 blocks of 8 token rows (one instruction each, whole
+// 128-byte lines), and wavefronts 0..3 copy the stage's 256 token scales
+// (one dword instruction each), issued one per few MFMAs over the first half
+// of the previous stage. Chunk c (16 bytes) of LDS row r sits at slot
+// c ^ ((r >> 1) & 7): the 16 rows of a fragment read fall on 16 distinct
+// 16-byte bank groups; the DMA writes 8 rows in lane order (lane l: row
+// l / 8, slot l % 8), so in block b lane l fetches chunk
+// (l % 8) ^ (4 (b % 2) + l / 16). A fragment read gives lane (r = l % 16,
+// g = l / 16) chunks g and 4 + g of its row, the same bytes for weights and
+// tokens.
+//
+// Gated tiles hold 128 output columns: wavefront row wm has the 32 gate rows
+// of columns wm*32 .. +31 (fragments 0, 1) and then the 32 matching up rows
+// (fragments 2, 3), so SiLU(gate) * up is formed from its own accumulators.
+// Weight rows of a fragment lie in one 128-row scale block.
+template <bool GATED>
+struct Big8 {
+  static constexpr int COLS = GATED ? 128 : 256;           // output columns per tile
+  static constexpr int OP_BYTES = 256 * 128;                // one operand of one stage
+  static constexpr int STAGE_BYTES = 2 * OP_BYTES;
+  static constexpr int SCALE_OFF = 2 * STAGE_BYTES;         // token scales: [buffer][256] float
+  static constexpr int LDS_BYTES = SCALE_OFF + 2 * 1024;    // 130 KB
+  static constexpr int DMA = 9;   // DMA instructions per wavefront per stage (wavefronts 4..7: 8)
+
+  __device__ static void run(const F8Args& a, int e, int row0, int rows, int nb, char* lds, int tid) {
+    const int wn = __builtin_amdgcn_readfirstlane(tid >> 6) & 1;
+    const int nf = (rows + 15) >> 4;   // token fragments holding a valid row
+    const int nj = __builtin_amdgcn_readfirstlane(min(8, (((nf - wn + 1) >> 1) + 1) & ~1));
+    switch (nj) {
+      case 8: body<8>(a, e, row0, rows, nb, lds, tid); break;
+      case 6: body<6>(a, e, row0, rows, nb, lds, tid); break;
+      case 4: body<4>(a, e, row0, rows, nb, lds, tid); break;
+      case 2: body<2>(a, e, row0, rows, nb, lds, tid); break;
+      default: body<0>(a, e, row0, rows, nb, lds, tid); break;
+    }
+  }
+
+  // MFMA of a stage after which DMA instruction d of the next stage is
+  // issued: spread evenly over the first half of the stage's 4 NJ MFMAs.
+  template <int NJ>
+  __device__ static constexpr int dma_after(int d) {
+    const int m = (d + 1) * (2 * NJ) / DMA - 1;
+    return m < 0 ? 0 : m;
+  }
+
+  template <int NJ>
+  __device__ static void body(const F8Args& a, int e, int row0, int rows, int nb, char* lds, int tid) {
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const uint32_t pitch = (uint32_t)a.K;
+    const int KB = a.K / kQBlock;
+    const int lrow = lane >> 3;                            // row within an 8-row DMA block
+    const int lchunk = (lane & 7) ^ (lane >> 4);           // chunk fetched in even blocks
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);
+
+    // DMA blocks b = 4 wave + d (d = 0..3) of both operands; odd blocks
+    // fetch chunk lchunk ^ 4. Weights: the wavefront's 4 blocks are the 32
+    // tile rows of group `wave` (gated: wavefront row wave / 2, gate rows for
+    // even groups, up rows for odd ones), consecutive weight rows from the
+    // first one: block d starts 8 d rows further.
+    const i32x4_t wbuf = buffer_rsrc(a.W + (size_t)e * a.N * a.K, (uint32_t)(a.N * pitch));
+    const int wfirst = GATED ? ((wave & 1) ? a.inter : 0) + nb * COLS + (wave >> 1) * 32 : nb * COLS + wave * 32;
+    const int wso0 = __builtin_amdgcn_readfirstlane(wfirst * (int)pitch);
+    const int wstep = __builtin_amdgcn_readfirstlane(8 * (int)pitch);
+    const uint32_t wv[2] = {(uint32_t)lrow * pitch + lchunk * 16, (uint32_t)lrow * pitch + (lchunk ^ 4) * 16};
+    // Tokens: rows past the tile's end read its first row (not stored).
+    const i32x4_t xbuf = buffer_rsrc(a.A, 0xFFFFFFFFu);
+    uint32_t xv[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int r = (wave * 4 + d) * 8 + lrow;
+      xv[d] = row0 + (r < rows ? r : 0);
+    }
+    f8_rows<4>(a, xv);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) xv[d] = xv[d] * pitch + (lchunk ^ ((d & 1) << 2)) * 16;
+
+    // Scales. The stage's 256 token scales go to LDS with the operands:
+    // wavefronts 0..3 copy them with one dword DMA each (lane l: token
+    // 64 wave + l). Weight blocks of the wavefront's fragments (uniform):
+    // gated gate and up, plain one block for all four; loaded a stage ahead
+    // through per-lane addresses (the kernel has no scalar registers left
+    // for another buffer resource).
+    const int fr = lane & 15, fg = lane >> 4;
+    uint32_t svoff = 0;
+    if (wave < 4) {
+      const int t = wave * 64 + lane;
+      uint32_t r[1] = {(uint32_t)(row0 + (t < rows ? t : 0))};
+      f8_rows<1>(a, r);
+      svoff = r[0] * (uint32_t)KB * 4;
+    }
+    const i32x4_t asbuf = buffer_rsrc(a.As, 0xFFFFFFFFu);
+    constexpr int NW = GATED ? 2 : 1;   // weight scale blocks per wavefront
+    const float* wsp[NW];
+    {
+      const float* we = a.Ws + (size_t)e * (a.N / kQBlock) * KB;
+      int blk0 = GATED ? (nb * COLS) / kQBlock : (nb * COLS + wm * 64) / kQBlock;
+      asm volatile("" : "+v"(blk0));
+      wsp[0] = we + (size_t)blk0 * KB;
+      if (GATED) wsp[NW - 1] = wsp[0] + (size_t)(a.inter / kQBlock) * KB;
+    }
+
+    // DMA number d of this wavefront's share of stage kt: weight blocks
+    // first, then token blocks, then (wavefronts 0..3) the token scales.
+    auto issue_one = [&](int kt, int d) {
+      // (opaque, so that the 9 LDS addresses of each buffer are formed at
+      // their instructions rather than held in scalar registers)
+      uint32_t ls = lds_base + (kt & 1) * STAGE_BYTES;
+      asm volatile("" : "+s"(ls));
+      const uint32_t ko = (uint32_t)kt * 128;
+      if (d < 4) lds_dma16(ls + (wave * 4 + d) * 1024, wbuf, wv[d & 1], wso0 + d * wstep + ko);
+      else if (d < 8) lds_dma16(ls + OP_BYTES + (wave * 4 + d - 4) * 1024, xbuf, xv[d - 4], ko);
+      else if (wave < 4) lds_dma4(ls - (kt & 1) * STAGE_BYTES + SCALE_OFF + (kt & 1) * 1024 + wave * 256, asbuf, svoff,
+                                  kt * 4);
+    };
+    float sw[NW];
+    auto load_scales = [&](int kt) {
+#pragma unroll
+      for (int i = 0; i < NW; ++i) sw[i] = wsp[i][kt];
+    };
+
+    f32x4_t acc[4][NJ > 0 ? NJ : 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int fsw = (fr >> 1) & 7;
+    const int off0 = (fg ^ fsw) << 4, off1 = ((4 + fg) ^ fsw) << 4;
+    // Multiplies stage `slot` (its weight scales in sw, token scales in LDS):
+    // takes the weight scales, loads stage knext's (if knext >= 0) in their
+    // place, and issues the DMA of stage knext into the other buffers over
+    // the MFMAs.
+    auto compute = [&](int slot, int knext) {
+      if (NJ == 0) {
+        if (knext >= 0) {
+#pragma unroll
+          for (int d = 0; d < DMA; ++d) issue_one(knext, d);
+        }
+        return;
+      }
+      float swc[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) swc[w] = sw[w];
+      if (knext >= 0) load_scales(knext);
+      const float* ssa = (const float*)(lds + SCALE_OFF + slot * 1024) + wn * 16 + fr;
+      const char* lw = lds + slot * STAGE_BYTES + (wm * 64 + fr) * 128;
+      const char* lx = lds + slot * STAGE_BYTES + OP_BYTES + (wn * 16 + fr) * 128;
+      i32x8_t af[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const i32x4_t lo4 = *(const i32x4_t*)(lw + i * 16 * 128 + off0);
+        const i32x4_t hi4 = *(const i32x4_t*)(lw + i * 16 * 128 + off1);
+        af[i] = i32x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const float sa = ssa[j * 32];   // token (2j + wn)*16 + lane%16
+        float sc[NW];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sc[w] = swc[w] * sa;
+        i32x8_t bcur;
+        {
+          const i32x4_t lo4 = *(const i32x4_t*)(lx + j * 32 * 128 + off0);
+          const i32x4_t hi4 = *(const i32x4_t*)(lx + j * 32 * 128 + off1);
+          bcur = i32x8_t{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              af[i], bcur, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+          const float c = sc[GATED ? (i >> 1) : 0];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(p[r], c, acc[i][j][r]);
+          const int m = j * 4 + i;   // MFMA number within the stage
+#pragma unroll
+          for (int d = 0; d < DMA; ++d) {
+            if (dma_after<NJ>(d) == m) {
+              __builtin_amdgcn_sched_barrier(0);
+              if (knext >= 0) issue_one(knext, d);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+        }
+      }
+    };
+
+    // Iteration kt: wait until this wavefront's DMA and scale loads of stage
+    // kt have landed, barrier (every wavefront's share of stage kt is in LDS,
+    // and every wavefront has finished stage kt - 1, whose buffers stage
+    // kt + 1 reuses), multiply stage kt while loading stage kt + 1.
+    const int nk = a.K / 128;
+#pragma unroll
+    for (int d = 0; d < DMA; ++d) issue_one(0, d);
+    load_scales(0);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      compute(kt & 1, kt + 1 < nk ? kt + 1 : -1);
+    }
+
+    // acc[i][j][q]: token (2j + wn)*16 + lane%16; wavefront weight row
+    // i*16 + 4*(lane/16) + q. C's rows are dense (ldc = inter for h, N for
+    // o), which saves the kernel a scalar register.
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int t = (2 * j + wn) * 16 + fr;
+      if (t >= rows) continue;
+      if (GATED) {
+        float* crow = (float*)a.C + (size_t)(row0 + t) * a.inter + nb * COLS + wm * 32 + fg * 4;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          f32x4_t v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = silu_f(acc[i][j][q]) * acc[i + 2][j][q];
+          *(f32x4_t*)(crow + i * 16) = v;
+        }
+      } else {
+        uint16_t* crow = (uint16_t*)a.C + (size_t)(row0 + t) * a.N + nb * COLS + wm * 64 + fg * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4_t& c = acc[i][j];
+          *(uint2*)(crow + i * 16) = make_uint2(pack_bf16x2(c[0], c[1]), pack_bf16x2(c[2], c[3]));
+        }
+      }
+    }
+  }
+};
+
+// The large tiles take every expert with more than kF8Rows rows when their
+// items (256-row tiles x N blocks) fill at least 3/4 of the CUs in the first
+// round; else the 128 x 128 tiles of ffn_fp8_kernel do.
+__device__ __forceinline__ bool f8_big_takes(int items, int cus) { return 4 * items >= 3 * cus; }
+
 // Tile of kT8Rows tokens x 128 weight rows (experts with more than kF8Rows
 // rows). Thread (rbase = tid / 8, kc = tid % 8) loads the 16-byte chunk kc
 // of tile rows rbase + 32 i (i = 0..3) of both operands per K step; chunk c
@@ -670,14 +947,17 @@ __global__ __launch_bounds__(256, 2) void ffn_fp8_kernel(F8Args a) {
   __shared__ int c_first[kF8MaxLocal + 1];
   __shared__ int t_first[kF8MaxLocal + 1];
   __shared__ int c_lo[kF8MaxLocal + 1];
-  __shared__ int wsum[8];
-  int chunks, tiles;
-  f8_lists(a, c_first, t_first, c_lo, wsum, chunks, tiles);
+  __shared__ int wsum[12];
+  int chunks, tiles, n_big;
+  f8_lists(a, kT8Rows, c_first, t_first, c_lo, wsum, chunks, tiles, n_big);
   const int ncols = GATED ? a.inter : a.N;
   const int slabs = ncols / S::COLS;
   const int nblk = ncols / T::COLS;
   const int n_stream = chunks * slabs;
-  const int total = n_stream + tiles * nblk;
+  // the same decision as ffn_fp8_big_kernel's: when it takes the tiled
+  // experts only the streamed ones are done here
+  const bool big = a.big_ok && f8_big_takes(n_big * (ncols / Big8<GATED>::COLS), a.big_min_items);
+  const int total = n_stream + (big ? 0 : tiles * nblk);
   // streamed chunks first, then the tiles with their N blocks fastest
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
     if (w < n_stream) {
@@ -695,6 +975,50 @@ __global__ __launch_bounds__(256, 2) void ffn_fp8_kernel(F8Args a) {
   }
 }
 
+// Tiles of the experts with more than kF8Rows rows, 256 tokens each; a
+// persistent loop over them, one workgroup of 8 wavefronts per CU. Items are
+// (token tile, N block) with N blocks fastest, taken round-robin by a grid
+// that is a multiple of 8 (workgroup b runs on XCD b % 8), so the items of
+// one N block -- the same weight rows for every tile of an expert -- share
+// an XCD's L2 when the N blocks per tile are a multiple of 8; when all items
+// fit in one round the N blocks are numbered up to a multiple of 8 (the
+// padding items are skipped).
+template <bool GATED>
+__global__ __launch_bounds__(512, 1) void ffn_fp8_big_kernel(F8Args a) {
+  using B = Big8<GATED>;
+  __shared__ __attribute__((aligned(16))) char smem[B::LDS_BYTES];
+  __shared__ int c_first[kF8MaxLocal + 1];
+  __shared__ int t_first[kF8MaxLocal + 1];
+  __shared__ int c_lo[kF8MaxLocal + 1];
+  __shared__ int wsum[12];
+  int chunks, tiles, n_big;
+  f8_lists(a, kB8Rows, c_first, t_first, c_lo, wsum, chunks, tiles, n_big);
+  const int nblk = (GATED ? a.inter : a.N) / B::COLS;
+  if (!f8_big_takes(n_big * nblk, a.big_min_items)) return;   // ffn_fp8_kernel does these experts
+  const int nblk8 = (nblk + 7) & ~7;
+  const int nbp = __builtin_amdgcn_readfirstlane(n_big * nblk8 <= (int)gridDim.x ? nblk8 : nblk);
+  const int total = n_big * nbp;
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    if (w % nbp >= nblk) continue;
+    const int tile = __builtin_amdgcn_readfirstlane(w / nbp);
+    const int nb = __builtin_amdgcn_readfirstlane(w % nbp);
+    int nloc = a.nloc;
+    asm volatile("" : "+s"(nloc));
+    const int e = __builtin_amdgcn_readfirstlane(f8_find_expert(t_first, nloc, tile));
+    const int row0 = __builtin_amdgcn_readfirstlane(c_lo[e] + (tile - t_first[e]) * kB8Rows);
+    const int rows = __builtin_amdgcn_readfirstlane(min(kB8Rows, c_lo[e + 1] - row0));
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));  // keeps per-thread setup inside the tile loop
+    // likewise the sizes and pointers: what is derived from them is computed
+    // per tile instead of occupying scalar registers across the loop
+    F8Args at = a;
+    asm volatile("" : "+s"(at.K), "+s"(at.N), "+s"(at.inter), "+s"(at.row_div));
+    asm volatile("" : "+s"(at.A), "+s"(at.As), "+s"(at.W), "+s"(at.Ws), "+s"(at.C), "+s"(at.row_index));
+    B::run(at, e, row0, rows, nb, smem, tid);
+    __syncthreads();  // the LDS buffers are reused by the next tile
+  }
+}
+
 int f8_cu_count() {
   static int cus[64] = {0};
   int dev = 0;
@@ -708,9 +1032,17 @@ int f8_cu_count() {
   return cus[dev];
 }
 
+// Tiled experts go to ffn_fp8_big_kernel when the row capacity is
+// prefill-sized and (on the device) its tiles fill at least 3/4 of the CUs
+// (f8_big_takes); else to the 128 x 128 tiles of ffn_fp8_kernel. Both paths
+// are complete; the capacity test keeps decode-sized calls from paying for a
+// second launch that finds no work.
 template <int NTW, int KS, bool GATED>
-hipError_t launch_fp8_gemm(const F8Args& g, hipStream_t s) {
+hipError_t launch_fp8_gemm(const F8Args& g0, hipStream_t s) {
   using S = Stream8<NTW, KS, GATED>;
+  F8Args g = g0;
+  g.big_ok = (g.capacity >= kB8MinCapacity && (GATED ? g.inter % 128 == 0 : g.N % 256 == 0)) ? 1 : 0;
+  g.big_min_items = f8_cu_count();
   auto kernel = ffn_fp8_kernel<NTW, KS, GATED>;
   static const int occ = [] {
     int n = 0;
@@ -725,13 +1057,23 @@ hipError_t launch_fp8_gemm(const F8Args& g, hipStream_t s) {
                                        ((long)g.capacity / kT8Rows + g.nloc) * (ncols / Tiled8<GATED>::COLS));
   const int grid = (int)std::max<long>(1, std::min<long>(max_work, (long)f8_cu_count() * occ));
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(256), 0, s, g);
+  if (!g.big_ok) return hipGetLastError();
+  // tiles <= ceil(capacity / 256) + (number of experts above kF8Rows rows)
+  const long max_big = ((long)(g.capacity + kB8Rows - 1) / kB8Rows +
+                        std::min<long>(g.nloc, (long)g.capacity / (kF8Rows + 1))) *
+                       (ncols / Big8<GATED>::COLS);
+  // persistent: one workgroup per CU (a multiple of 8, so each keeps its XCD)
+  const long cus8 = std::max(8, f8_cu_count() / 8 * 8);
+  const int grid_big = (int)std::max<long>(8, std::min<long>((max_big + 7) / 8 * 8, cus8));
+  hipLaunchKernelGGL(ffn_fp8_big_kernel<GATED>, dim3(grid_big), dim3(512), 0, s, g);
   return hipGetLastError();
 }
 
 inline size_t f8_align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Workgroups of 4 wavefronts for rows x ceil(cols / 512) wavefront items, at
-// most max_per_cu per CU (the rest loop).
+// Workgroups of 4 wavefronts for rows x ceil(cols / 512) wavefront items: one
+// item per wavefront while they fit in max_per_cu workgroups per CU (the
+// passes of kQItems items then start at once), else that many workgroups.
 int quantize_grid(long rows, int cols, int max_per_cu) {
   const long items = rows * ((cols / kQBlock + 3) / 4);
   return (int)std::max<long>(1, std::min<long>((items + 3) / 4, (long)f8_cu_count() * max_per_cu));

@@ -203,6 +203,24 @@ def test_ffn_fp8_tiled_1024_local_experts():
     check_ffn(counts.tolist(), 512, 256, 8, seed=16, distinct=7)
 
 
+# A prefill-sized row capacity (>= 16384) launches the 256 x 256 tile kernel too, which takes
+# the experts above 64 rows when their tiles x N blocks fill 3/4 of the CUs (here 30 tiles x 8
+# N blocks in both GEMMs); with fewer the 128-row tiles keep them.
+BIG_CAP = 16384
+
+
+@pytest.mark.parametrize("permuted", [False, True])
+def test_ffn_fp8_large_tiles(permuted):
+    counts = [1000, 0, 2600, 65, 300, 2050, 64, 1, 700]      # 30 tiles of 256, ragged last tiles
+    M = sum(counts)
+    check_ffn(counts, 2048, 1024, 8, seed=21 + permuted, spare_rows=BIG_CAP - M, permuted=permuted)
+
+
+def test_ffn_fp8_large_capacity_few_tiles():
+    counts = [300, 0, 200, 40]                                 # 3 tiles of 256 x 8 N blocks: too few
+    check_ffn(counts, 2048, 1024, 8, seed=23, spare_rows=BIG_CAP - sum(counts))
+
+
 def test_ffn_fp8_permuted_rows():
     check_ffn([40, 0, 90], 1024, 512, 2, seed=3, permuted=True)
 
