@@ -431,9 +431,10 @@ def roofline_block(res, fp8):
             "algorithmic_flops": res["ffn_gflop"] * 1e9}
 
 
-# The shapes whose FFN fractions are graded beside the headline decode_ep:
-# prefill (MFMA-bound) and the TP-sliced decode (HBM-bound).
-GRADED = ("prefill_straggler", "decode_tp")
+# The shapes whose FFN fractions are reported beside the headline decode_ep:
+# prefill (MFMA-bound), the TP-sliced decode (HBM-bound) and prefill on FP8
+# operands (MFMA-bound against the fp8 peak).
+GRADED = ("prefill_straggler", "decode_tp", "prefill_straggler_fp8")
 
 
 def main():
@@ -489,10 +490,12 @@ def main():
             r = run_workload(g, args.steps, args.warmup, args.copies, torch, moe, to_device, to_host,
                              args.operands, args.median_steps)
             r.pop("_inputs")
+            g_fp8 = g.weight_format == "fp8_e4m3_b128"
             entry = {"workload": name, "tokens": g.T, "local_experts": f"[{g.expert_begin}, "
                      f"{g.expert_begin + g.num_local})", "inter": g.inter,
+                     "dtype": "fp8_e4m3" if g_fp8 else "bf16",
                      "ms_per_step": r["ms_per_step"], "tokens_per_s": r["tokens_per_s"],
-                     "roofline": roofline_block(r, False),
+                     "roofline": roofline_block(r, g_fp8),
                      "detail": {k: v for k, v in r.items() if k not in ("tokens_per_s", "ms_per_step")}}
             graded[name] = entry
             print(f"bench: {name} {r['ms_per_step'] * 1e3:.1f} us/step, FFN {r['ffn_us_per_launch']:.1f} us "
