@@ -93,6 +93,8 @@ TRAFFIC_RECORDS = {
                         os.path.join(ROOT, "profiles", "prefill_literal_ffn_traffic.md")),
     "prefill_straggler": ([_CSRC + "ffn.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
                           os.path.join(ROOT, "profiles", "prefill_straggler_ffn_traffic.md")),
+    "prefill_straggler_fp8": ([_CSRC + "ffn_fp8.hip", _CSRC + "device_common.h", _CSRC + "launch.h"],
+                              os.path.join(ROOT, "profiles", "prefill_straggler_fp8_ffn_traffic.md")),
 }
 
 

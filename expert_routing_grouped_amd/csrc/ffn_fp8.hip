@@ -83,12 +83,13 @@ __device__ __forceinline__ uint32_t e4m3_code(float q) {
 // A wavefront item is 4 consecutive blocks of one row (512 values): lane l
 // holds 8 values of block l / 16, and the block's maximum is reduced over its
 // 16 lanes. Lanes past the row's last block do nothing. A wavefront takes
-// kQItems items per pass (items w, w + stride, ...), all loads issued before
-// the first is used. The row count is rows, or min(rows, *rows_dev) when
-// rows_dev is given.
+// ITEMS items per pass (items w, w + stride, ...), all loads issued before
+// the first is used: ITEMS = 1 when the grid has a wavefront for every item,
+// else kQItems. The row count is rows, or min(rows, *rows_dev) when rows_dev
+// is given.
 constexpr int kQItems = 4;
 
-template <bool BF16_IN>
+template <bool BF16_IN, int ITEMS>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* in, int rows, const int* rows_dev,
                                                            int cols, uint8_t* codes, float* scales) {
   int n = rows;
@@ -98,19 +99,28 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* in, int 
   const long total = (long)n * groups;
   const int lane = threadIdx.x & 63;
   const long stride = (long)gridDim.x * 4;
-  for (long w0 = (long)blockIdx.x * 4 + (threadIdx.x >> 6); w0 < total; w0 += stride * kQItems) {
-    float v[kQItems][8];
-    size_t first[kQItems];
-    int row[kQItems], blk[kQItems];
-    bool active[kQItems];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (long w0 = (long)blockIdx.x * 4 + wave; w0 < total; w0 += stride * ITEMS) {
+    // items of this pass (the same for the whole wavefront): the others are
+    // skipped, index arithmetic included
+    const int cnt = ITEMS == 1 ? 1 : (int)min((long)ITEMS, (total - w0 + stride - 1) / stride);
+    float v[ITEMS][8];
+    size_t first[ITEMS];
+    int row[ITEMS], blk[ITEMS];
+    bool active[ITEMS];
 #pragma unroll
-    for (int u = 0; u < kQItems; ++u) {
-      const long w = w0 + u * stride;
-      const int r = (int)(w / groups);
-      row[u] = r;
-      blk[u] = (int)(w - (long)r * groups) * 4 + (lane >> 4);
-      active[u] = w < total && blk[u] < nb;
-      first[u] = (size_t)r * cols + (size_t)blk[u] * kQBlock + (lane & 15) * 8;   // of 8 values
+    for (int u = 0; u < ITEMS; ++u) {
+      active[u] = false;
+      row[u] = blk[u] = 0;
+      first[u] = 0;
+      if (u < cnt) {
+        const long w = w0 + u * stride;
+        const int r = (int)(w / groups);
+        row[u] = r;
+        blk[u] = (int)(w - (long)r * groups) * 4 + (lane >> 4);
+        active[u] = blk[u] < nb;
+        first[u] = (size_t)r * cols + (size_t)blk[u] * kQBlock + (lane & 15) * 8;   // of 8 values
+      }
       if (active[u]) {
         if (BF16_IN) {
           const u32x4_t p = *(const u32x4_t*)((const uint16_t*)in + first[u]);
@@ -134,7 +144,8 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* in, int 
       }
     }
 #pragma unroll
-    for (int u = 0; u < kQItems; ++u) {
+    for (int u = 0; u < ITEMS; ++u) {
+      if (u >= cnt) break;
       float amax = 0.0f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[u][j]));
@@ -1072,11 +1083,26 @@ hipError_t launch_fp8_gemm(const F8Args& g0, hipStream_t s) {
 inline size_t f8_align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workgroups of 4 wavefronts for rows x ceil(cols / 512) wavefront items: one
-// item per wavefront while they fit in max_per_cu workgroups per CU (the
-// passes of kQItems items then start at once), else that many workgroups.
+// item per wavefront while they fit in max_per_cu workgroups per CU, else
+// that many workgroups.
 int quantize_grid(long rows, int cols, int max_per_cu) {
   const long items = rows * ((cols / kQBlock + 3) / 4);
   return (int)std::max<long>(1, std::min<long>((items + 3) / 4, (long)f8_cu_count() * max_per_cu));
+}
+
+// Launches the quantiser on `grid` workgroups: kQItems items per wavefront
+// pass when rows (an upper bound with rows_dev) has more items than the grid
+// has wavefronts, else one.
+template <bool BF16_IN>
+void launch_quantize(int grid, const void* in, int rows, const int* rows_dev, int cols, uint8_t* codes,
+                     float* scales, hipStream_t s) {
+  const long items = (long)rows * ((cols / kQBlock + 3) / 4);
+  if (items > (long)grid * 4)
+    hipLaunchKernelGGL((quantize_rows_kernel<BF16_IN, kQItems>), dim3(grid), dim3(256), 0, s, in, rows, rows_dev,
+                       cols, codes, scales);
+  else
+    hipLaunchKernelGGL((quantize_rows_kernel<BF16_IN, 1>), dim3(grid), dim3(256), 0, s, in, rows, rows_dev, cols,
+                       codes, scales);
 }
 
 }  // namespace
@@ -1085,11 +1111,8 @@ hipError_t launch_quantize_rows(const void* x, int rows, int cols, bool bf16_in,
                                 hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const int grid = quantize_grid(rows, cols, 16);
-  if (bf16_in)
-    hipLaunchKernelGGL(quantize_rows_kernel<true>, dim3(grid), dim3(256), 0, s, x, rows, nullptr, cols, codes, scales);
-  else
-    hipLaunchKernelGGL(quantize_rows_kernel<false>, dim3(grid), dim3(256), 0, s, x, rows, nullptr, cols, codes,
-                       scales);
+  if (bf16_in) launch_quantize<true>(grid, x, rows, nullptr, cols, codes, scales, s);
+  else launch_quantize<false>(grid, x, rows, nullptr, cols, codes, scales, s);
   return hipGetLastError();
 }
 
@@ -1113,10 +1136,15 @@ hipError_t launch_ffn_fp8(const FfnFp8Args& a, hipStream_t s) {
   hipError_t err = launch_fp8_gemm<2, 4, true>(g1, s);
   if (err != hipSuccess) return err;
   // h has offsets[E_loc] rows, known on the device only: one workgroup per CU
-  // covers a decode batch in one pass and loops over larger ones.
+  // covers a decode batch in one pass and loops over larger ones (several
+  // items per pass from a prefill-sized capacity on).
   const int grid = quantize_grid(a.capacity, I, 1);
-  hipLaunchKernelGGL(quantize_rows_kernel<false>, dim3(grid), dim3(256), 0, s, (const void*)h, a.capacity,
-                     a.offsets + a.num_local, I, hq, hs);
+  if (a.capacity >= kB8MinCapacity)
+    hipLaunchKernelGGL((quantize_rows_kernel<false, kQItems>), dim3(grid), dim3(256), 0, s, (const void*)h,
+                       a.capacity, a.offsets + a.num_local, I, hq, hs);
+  else
+    hipLaunchKernelGGL((quantize_rows_kernel<false, 1>), dim3(grid), dim3(256), 0, s, (const void*)h, a.capacity,
+                       a.offsets + a.num_local, I, hq, hs);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_fp8_gemm<2, 2, false>(g2, s);
