@@ -17,7 +17,8 @@
 //
 // Quantising a block of 128 values: scale = amax / 448 (1 for an all-zero
 // block), code = the e4m3 value nearest to v / scale, ties to the even code,
-// magnitudes above 448 saturate; both divisions are correctly rounded float32.
+// magnitudes above 448 saturate; both divisions are correctly rounded float32
+// (the one by the scale computed as in div_by_scale).
 //
 // Experts with at most 64 rows (decode) stream the weights: a work item is
 // the expert's rows and one slab of output columns. A K
@@ -34,7 +35,11 @@
 // of both operands is staged through a double-buffered XOR-swizzled LDS tile;
 // each wavefront multiplies 64 x 64 of the tile on
 // v_mfma_scale_f32_32x32x64_f8f6f4 (two per K step and fragment pair, into a
-// zeroed float32 partial that is then added with its scale factor).
+// zeroed float32 partial that is then added with its scale factor). When
+// their tiles fill the GPU (prefill) they take 256 x 256 tiles in
+// ffn_fp8_big_kernel instead, whose gate_up also quantises its rows of h
+// (128 output columns = one scale block per row), leaving the other rows to
+// quantize_h_kernel.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -77,6 +82,17 @@ __device__ __forceinline__ uint32_t e4m3_code(float q) {
   }
   return c | sign;
 }
+
+// v / s rounded to float32 -- the correctly rounded float32 quotient --
+// from rs = 1 / s rounded to float64, as RN32(RN64(v * rs)). For float32 v
+// and s the float64 product is within 2^-51.9 (relative) of v / s, while a
+// quotient of two 24-bit significands that is not itself a float32 lies at
+// least 2^-49 (relative) away from every float32 rounding midpoint (write
+// v / s = (a / b) 2^e and a midpoint as M 2^f with a, b < 2^24 and M < 2^25
+// odd: a 2^e - b M 2^f is a nonzero multiple of 2^f, and e > f), so both
+// round to the same float32. One float64 multiply per value instead of a
+// float32 division.
+__device__ __forceinline__ float div_by_scale(float v, double rs) { return (float)((double)v * rs); }
 
 // ---------------------------------------------------------------- quantiser
 
@@ -153,11 +169,12 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* in, int 
       for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, MOE_WAVE));
       if (!active[u]) continue;
       const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+      const double rs = 1.0 / (double)s;
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        lo |= e4m3_code(v[u][j] / s) << (8 * j);
-        hi |= e4m3_code(v[u][4 + j] / s) << (8 * j);
+        lo |= e4m3_code(div_by_scale(v[u][j], rs)) << (8 * j);
+        hi |= e4m3_code(div_by_scale(v[u][4 + j], rs)) << (8 * j);
       }
       *(uint2*)(codes + first[u]) = make_uint2(lo, hi);
       if ((lane & 15) == 0) scales[(size_t)row[u] * nb + blk[u]] = s;
@@ -181,7 +198,40 @@ struct F8Args {
   int ldc;
   int big_ok;             // the large-tile kernel is launched too ...
   int big_min_items;      // ... and takes the tiled experts when it has at least this many items
+  uint8_t* Cq;            // gated, large tiles: also h's e4m3 codes [capacity, ldc] ...
+  float* Cs;              // ... and scales [capacity, ldc / 128]
 };
+
+struct F8QOut {
+  uint8_t* q;
+  float* s;
+};
+
+// F8Args in the kernel argument segment (constant memory: scalar loads).
+typedef const __attribute__((address_space(4))) F8Args KernargF8Args;
+
+__device__ __forceinline__ F8Args f8_args_copy(KernargF8Args* p) {
+  F8Args r;
+  r.A = p->A;
+  r.As = p->As;
+  r.row_index = p->row_index;
+  r.row_div = p->row_div;
+  r.offsets = p->offsets;
+  r.nloc = p->nloc;
+  r.capacity = p->capacity;
+  r.W = p->W;
+  r.Ws = p->Ws;
+  r.N = p->N;
+  r.K = p->K;
+  r.inter = p->inter;
+  r.C = p->C;
+  r.ldc = p->ldc;
+  r.big_ok = p->big_ok;
+  r.big_min_items = p->big_min_items;
+  r.Cq = p->Cq;
+  r.Cs = p->Cs;
+  return r;
+}
 
 // Work lists, in expert order, of the experts with rows: those with at most
 // kF8Rows rows are one chunk each (c_first[e] = the chunk of expert e,
@@ -546,19 +596,21 @@ struct Big8 {
   static constexpr int OP_BYTES = 256 * 128;                // one operand of one stage
   static constexpr int STAGE_BYTES = 2 * OP_BYTES;
   static constexpr int SCALE_OFF = 2 * STAGE_BYTES;         // token scales: [buffer][256] float
-  static constexpr int LDS_BYTES = SCALE_OFF + 2 * 1024;    // 130 KB
+  static constexpr int AMAX_OFF = SCALE_OFF + 2 * 1024;     // gated: h's row maxima [wm][256] float
+  static constexpr int LDS_BYTES = AMAX_OFF + (GATED ? 4 * 1024 : 0);
   static constexpr int DMA = 9;   // DMA instructions per wavefront per stage (wavefronts 4..7: 8)
 
-  __device__ static void run(const F8Args& a, int e, int row0, int rows, int nb, char* lds, int tid) {
+  __device__ static void run(const F8Args& a, int e, int row0, int rows, int nb, char* lds, const F8QOut* qo,
+                             int tid) {
     const int wn = __builtin_amdgcn_readfirstlane(tid >> 6) & 1;
     const int nf = (rows + 15) >> 4;   // token fragments holding a valid row
     const int nj = __builtin_amdgcn_readfirstlane(min(8, (((nf - wn + 1) >> 1) + 1) & ~1));
     switch (nj) {
-      case 8: body<8>(a, e, row0, rows, nb, lds, tid); break;
-      case 6: body<6>(a, e, row0, rows, nb, lds, tid); break;
-      case 4: body<4>(a, e, row0, rows, nb, lds, tid); break;
-      case 2: body<2>(a, e, row0, rows, nb, lds, tid); break;
-      default: body<0>(a, e, row0, rows, nb, lds, tid); break;
+      case 8: body<8>(a, e, row0, rows, nb, lds, qo, tid); break;
+      case 6: body<6>(a, e, row0, rows, nb, lds, qo, tid); break;
+      case 4: body<4>(a, e, row0, rows, nb, lds, qo, tid); break;
+      case 2: body<2>(a, e, row0, rows, nb, lds, qo, tid); break;
+      default: body<0>(a, e, row0, rows, nb, lds, qo, tid); break;
     }
   }
 
@@ -571,7 +623,8 @@ struct Big8 {
   }
 
   template <int NJ>
-  __device__ static void body(const F8Args& a, int e, int row0, int rows, int nb, char* lds, int tid) {
+  __device__ static void body(const F8Args& a, int e, int row0, int rows, int nb, char* lds, const F8QOut* qo,
+                              int tid) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -730,20 +783,63 @@ struct Big8 {
     // acc[i][j][q]: token (2j + wn)*16 + lane%16; wavefront weight row
     // i*16 + 4*(lane/16) + q. C's rows are dense (ldc = inter for h, N for
     // o), which saves the kernel a scalar register.
+    if (GATED) {
+      // h = SiLU(gate) * up in float32, and its e4m3 codes: the tile's 128
+      // output columns are one scale block of every token row, the four
+      // wavefront rows (wm) each hold 32 of them, so the row maxima are
+      // combined through LDS. The arithmetic is that of quantize_rows_kernel.
+      float h[NJ > 0 ? NJ : 1][8];
+      float* amax_part = (float*)(lds + AMAX_OFF);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int t = (2 * j + wn) * 16 + fr;
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            h[j][i * 4 + q] = silu_f(acc[i][j][q]) * acc[i + 2][j][q];
+            m = fmaxf(m, fabsf(h[j][i * 4 + q]));
+          }
+        if (t < rows) {
+          float* crow = (float*)a.C + (size_t)(row0 + t) * a.inter + nb * COLS + wm * 32 + fg * 4;
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            *(f32x4_t*)(crow + i * 16) = f32x4_t{h[j][i * 4], h[j][i * 4 + 1], h[j][i * 4 + 2], h[j][i * 4 + 3]};
+        }
+        m = fmaxf(m, __shfl_xor(m, 16, MOE_WAVE));
+        m = fmaxf(m, __shfl_xor(m, 32, MOE_WAVE));
+        if (fg == 0) amax_part[wm * 256 + t] = m;
+      }
+      {
+        __syncthreads();   // every wavefront reaches it once (also with NJ = 0)
+        uint8_t* const cq = qo->q;
+        float* const cs = qo->s;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int t = (2 * j + wn) * 16 + fr;
+          if (t >= rows) continue;
+          const float amax = fmaxf(fmaxf(amax_part[t], amax_part[256 + t]),
+                                   fmaxf(amax_part[512 + t], amax_part[768 + t]));
+          const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+          const double rs = 1.0 / (double)sc;
+          uint8_t* qrow = cq + (size_t)(row0 + t) * a.inter + nb * COLS + wm * 32 + fg * 4;
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) c |= e4m3_code(div_by_scale(h[j][i * 4 + q], rs)) << (8 * q);
+            *(uint32_t*)(qrow + i * 16) = c;
+          }
+          if (wm == 0 && fg == 0) cs[(size_t)(row0 + t) * (a.inter / kQBlock) + nb] = sc;
+        }
+      }
+    } else {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int t = (2 * j + wn) * 16 + fr;
       if (t >= rows) continue;
-      if (GATED) {
-        float* crow = (float*)a.C + (size_t)(row0 + t) * a.inter + nb * COLS + wm * 32 + fg * 4;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          f32x4_t v;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = silu_f(acc[i][j][q]) * acc[i + 2][j][q];
-          *(f32x4_t*)(crow + i * 16) = v;
-        }
-      } else {
+      {
         uint16_t* crow = (uint16_t*)a.C + (size_t)(row0 + t) * a.N + nb * COLS + wm * 64 + fg * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -752,6 +848,7 @@ struct Big8 {
         }
       }
     }
+    }
   }
 };
 
@@ -759,6 +856,133 @@ struct Big8 {
 // items (256-row tiles x N blocks) fill at least 3/4 of the CUs in the first
 // round; else the 128 x 128 tiles of ffn_fp8_kernel do.
 __device__ __forceinline__ bool f8_big_takes(int items, int cus) { return 4 * items >= 3 * cus; }
+
+// The FFN's h quantiser at prefill sizes: when ffn_fp8_big_kernel takes the
+// experts above kF8Rows rows (the same decision, from the same offsets) it
+// has written their codes itself, so only the other experts' rows are
+// quantised here; else every row. The rows to quantise are numbered
+// expert after expert (q_first[e] = those before expert e); a wavefront item
+// is 4 blocks of one of them (kQItems items per pass), as in
+// quantize_rows_kernel.
+__global__ __launch_bounds__(256) void quantize_h_kernel(const float* __restrict__ h, const int* __restrict__ offsets,
+                                                         int nloc, int capacity, int cols, int cus,
+                                                         uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  __shared__ int s_lo[kF8MaxLocal + 1];
+  __shared__ int q_first[kF8MaxLocal + 1];
+  __shared__ int wsum[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int m4[4], cb = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    m4[q] = 0;
+    if (e < nloc) {
+      const int lo = min(offsets[e], capacity);
+      const int hi = min(offsets[e + 1], capacity);
+      m4[q] = max(0, hi - lo);
+      s_lo[e] = lo;
+      if (e == nloc - 1) s_lo[nloc] = max(lo, hi);
+      cb += m4[q] > kF8Rows ? (m4[q] + kB8Rows - 1) / kB8Rows : 0;
+    }
+  }
+  cb = wave_sum_i32(cb);
+  if (lane == 0) wsum[wave] = cb;
+  __syncthreads();
+  const bool big = f8_big_takes((wsum[0] + wsum[1] + wsum[2] + wsum[3]) * (cols / Big8<true>::COLS), cus);
+  int qc[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    qc[q] = (big && m4[q] > kF8Rows) ? 0 : m4[q];
+    sum += qc[q];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, MOE_WAVE);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wsum[4 + wave] = incl;
+  __syncthreads();
+  int before = 0, n_q = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < wave) before += wsum[4 + i];
+    n_q += wsum[4 + i];
+  }
+  int p = before + incl - sum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    if (e < nloc) q_first[e] = p;
+    p += qc[q];
+  }
+  if (tid == 0) q_first[nloc] = n_q;
+  __syncthreads();
+
+  const int nb = cols / kQBlock;
+  const int groups = (nb + 3) / 4;
+  const long total = (long)n_q * groups;
+  const long stride = (long)gridDim.x * 4;
+  for (long w0 = (long)blockIdx.x * 4 + wave; w0 < total; w0 += stride * kQItems) {
+    const int cnt = (int)min((long)kQItems, (total - w0 + stride - 1) / stride);
+    float v[kQItems][8];
+    size_t first[kQItems];
+    int row[kQItems], blk[kQItems];
+    bool active[kQItems];
+#pragma unroll
+    for (int u = 0; u < kQItems; ++u) {
+      active[u] = false;
+      row[u] = blk[u] = 0;
+      first[u] = 0;
+      if (u < cnt) {
+        const long w = w0 + u * stride;
+        const int qi = (int)(w / groups);
+        int e = 0, hi = nloc - 1;   // the expert whose rows to quantise hold number qi
+        while (e < hi) {
+          const int mid = (e + hi + 1) >> 1;
+          if (q_first[mid] <= qi) e = mid; else hi = mid - 1;
+        }
+        const int r = s_lo[e] + (qi - q_first[e]);
+        row[u] = r;
+        blk[u] = (int)(w - (long)qi * groups) * 4 + (lane >> 4);
+        active[u] = blk[u] < nb;
+        first[u] = (size_t)r * cols + (size_t)blk[u] * kQBlock + (lane & 15) * 8;
+      }
+      if (active[u]) {
+        const f32x4_t p0 = *(const f32x4_t*)(h + first[u]);
+        const f32x4_t p1 = *(const f32x4_t*)(h + first[u] + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[u][j] = p0[j];
+          v[u][4 + j] = p1[j];
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[u][j] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kQItems; ++u) {
+      if (u >= cnt) break;
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[u][j]));
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, MOE_WAVE));
+      if (!active[u]) continue;
+      const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+      const double rs = 1.0 / (double)s;
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        lo |= e4m3_code(div_by_scale(v[u][j], rs)) << (8 * j);
+        hi |= e4m3_code(div_by_scale(v[u][4 + j], rs)) << (8 * j);
+      }
+      *(uint2*)(codes + first[u]) = make_uint2(lo, hi);
+      if ((lane & 15) == 0) scales[(size_t)row[u] * nb + blk[u]] = s;
+    }
+  }
+}
 
 // Tile of kT8Rows tokens x 128 weight rows (experts with more than kF8Rows
 // rows). Thread (rbase = tid / 8, kc = tid % 8) loads the 16-byte chunk kc
@@ -1002,8 +1226,12 @@ __global__ __launch_bounds__(512, 1) void ffn_fp8_big_kernel(F8Args a) {
   __shared__ int t_first[kF8MaxLocal + 1];
   __shared__ int c_lo[kF8MaxLocal + 1];
   __shared__ int wsum[12];
+  // the codes and scales outputs, read back from LDS in the epilogue only
+  // (held in scalar registers they would not fit beside the K loop's)
+  __shared__ F8QOut s_qout;
+  if (threadIdx.x == 0) s_qout = F8QOut{a.Cq, a.Cs};
   int chunks, tiles, n_big;
-  f8_lists(a, kB8Rows, c_first, t_first, c_lo, wsum, chunks, tiles, n_big);
+  f8_lists(a, kB8Rows, c_first, t_first, c_lo, wsum, chunks, tiles, n_big);   // (its barriers publish s_qout)
   const int nblk = (GATED ? a.inter : a.N) / B::COLS;
   if (!f8_big_takes(n_big * nblk, a.big_min_items)) return;   // ffn_fp8_kernel does these experts
   const int nblk8 = (nblk + 7) & ~7;
@@ -1020,12 +1248,14 @@ __global__ __launch_bounds__(512, 1) void ffn_fp8_big_kernel(F8Args a) {
     const int rows = __builtin_amdgcn_readfirstlane(min(kB8Rows, c_lo[e + 1] - row0));
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));  // keeps per-thread setup inside the tile loop
-    // likewise the sizes and pointers: what is derived from them is computed
-    // per tile instead of occupying scalar registers across the loop
-    F8Args at = a;
-    asm volatile("" : "+s"(at.K), "+s"(at.N), "+s"(at.inter), "+s"(at.row_div));
-    asm volatile("" : "+s"(at.A), "+s"(at.As), "+s"(at.W), "+s"(at.Ws), "+s"(at.C), "+s"(at.row_index));
-    B::run(at, e, row0, rows, nb, smem, tid);
+    // likewise the arguments: read again per tile from the kernel argument
+    // segment (the only argument is `a`, at its start) through an opaque
+    // pointer, so that they and what is derived from them are not held in
+    // scalar registers across the loop
+    KernargF8Args* ka = (KernargF8Args*)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(ka));
+    const F8Args at = f8_args_copy(ka);
+    B::run(at, e, row0, rows, nb, smem, &s_qout, tid);
     __syncthreads();  // the LDS buffers are reused by the next tile
   }
 }
@@ -1131,17 +1361,22 @@ hipError_t launch_ffn_fp8(const FfnFp8Args& a, hipStream_t s) {
   float* hs = (float*)((char*)hq + f8_align256((size_t)a.capacity * I));
   F8Args g1{(const uint8_t*)a.x_codes, a.x_scales, a.row_index, a.row_div, a.offsets, a.num_local, a.capacity,
             (const uint8_t*)a.w_gate_up, a.w_gate_up_scales, 2 * I, d, I, h, I};
+  if (a.capacity >= kB8MinCapacity) {   // the large-tile gate_up quantises its rows of h (quantize_h_kernel)
+    g1.Cq = hq;
+    g1.Cs = hs;
+  }
   F8Args g2{hq, hs, nullptr, 1, a.offsets, a.num_local, a.capacity,
             (const uint8_t*)a.w_down, a.w_down_scales, d, I, I, a.o_sorted, d};
   hipError_t err = launch_fp8_gemm<2, 4, true>(g1, s);
   if (err != hipSuccess) return err;
   // h has offsets[E_loc] rows, known on the device only: one workgroup per CU
-  // covers a decode batch in one pass and loops over larger ones (several
-  // items per pass from a prefill-sized capacity on).
+  // covers a decode batch in one pass and loops over larger ones. From a
+  // prefill-sized capacity on, the large-tile gate_up writes the codes of the
+  // experts it takes, and the quantiser does the others.
   const int grid = quantize_grid(a.capacity, I, 1);
   if (a.capacity >= kB8MinCapacity)
-    hipLaunchKernelGGL((quantize_rows_kernel<false, kQItems>), dim3(grid), dim3(256), 0, s, (const void*)h,
-                       a.capacity, a.offsets + a.num_local, I, hq, hs);
+    hipLaunchKernelGGL(quantize_h_kernel, dim3(grid), dim3(256), 0, s, (const float*)h, a.offsets, a.num_local,
+                       a.capacity, I, f8_cu_count(), hq, hs);
   else
     hipLaunchKernelGGL((quantize_rows_kernel<false, 1>), dim3(grid), dim3(256), 0, s, (const void*)h, a.capacity,
                        a.offsets + a.num_local, I, hq, hs);

@@ -216,6 +216,21 @@ def test_ffn_fp8_large_tiles(permuted):
     check_ffn(counts, 2048, 1024, 8, seed=21 + permuted, spare_rows=BIG_CAP - M, permuted=permuted)
 
 
+def test_ffn_fp8_large_capacity_no_rows():
+    check_ffn([0, 0, 0, 0], 2048, 1024, 8, seed=24, spare_rows=BIG_CAP)   # both kernels find no work
+
+
+def test_ffn_fp8_large_tiles_1024_local_experts():
+    """1024 local experts at a prefill-sized capacity: the lists of both kernels span every
+    expert, 30 of them large enough for 256-row tiles (4 tiles each is 120 x 8 N blocks)."""
+    rng = np.random.default_rng(25)
+    counts = rng.integers(0, 4, 1024) * (rng.random(1024) < 0.3)
+    big = rng.choice(1024, 30, replace=False)
+    counts[big] = rng.integers(769, 1025, 30)
+    M = int(counts.sum())
+    check_ffn(counts.tolist(), 512, 1024, 8, seed=26, distinct=5, spare_rows=max(0, BIG_CAP - M))
+
+
 def test_ffn_fp8_large_capacity_few_tiles():
     counts = [300, 0, 200, 40]                                 # 3 tiles of 256 x 8 N blocks: too few
     check_ffn(counts, 2048, 1024, 8, seed=23, spare_rows=BIG_CAP - sum(counts))
