@@ -865,7 +865,7 @@ __device__ __forceinline__ bool f8_big_takes(int items, int cus) { return 4 * it
 // is 4 blocks of one of them (kQItems items per pass), as in
 // quantize_rows_kernel.
 __global__ __launch_bounds__(256) void quantize_h_kernel(const float* __restrict__ h, const int* __restrict__ offsets,
-                                                         int nloc, int capacity, int cols, int cus,
+                                                         int nloc, int capacity, int cols, int big_ok, int cus,
                                                          uint8_t* __restrict__ codes, float* __restrict__ scales) {
   __shared__ int s_lo[kF8MaxLocal + 1];
   __shared__ int q_first[kF8MaxLocal + 1];
@@ -888,7 +888,7 @@ __global__ __launch_bounds__(256) void quantize_h_kernel(const float* __restrict
   cb = wave_sum_i32(cb);
   if (lane == 0) wsum[wave] = cb;
   __syncthreads();
-  const bool big = f8_big_takes((wsum[0] + wsum[1] + wsum[2] + wsum[3]) * (cols / Big8<true>::COLS), cus);
+  const bool big = big_ok && f8_big_takes((wsum[0] + wsum[1] + wsum[2] + wsum[3]) * (cols / Big8<true>::COLS), cus);
   int qc[4], sum = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -1278,11 +1278,16 @@ int f8_cu_count() {
 // (f8_big_takes); else to the 128 x 128 tiles of ffn_fp8_kernel. Both paths
 // are complete; the capacity test keeps decode-sized calls from paying for a
 // second launch that finds no work.
+template <bool GATED>
+bool fp8_big_ok(const F8Args& g) {
+  return g.capacity >= kB8MinCapacity && (GATED ? g.inter % 128 == 0 : g.N % 256 == 0);
+}
+
 template <int NTW, int KS, bool GATED>
 hipError_t launch_fp8_gemm(const F8Args& g0, hipStream_t s) {
   using S = Stream8<NTW, KS, GATED>;
   F8Args g = g0;
-  g.big_ok = (g.capacity >= kB8MinCapacity && (GATED ? g.inter % 128 == 0 : g.N % 256 == 0)) ? 1 : 0;
+  g.big_ok = fp8_big_ok<GATED>(g) ? 1 : 0;
   g.big_min_items = f8_cu_count();
   auto kernel = ffn_fp8_kernel<NTW, KS, GATED>;
   static const int occ = [] {
@@ -1361,7 +1366,8 @@ hipError_t launch_ffn_fp8(const FfnFp8Args& a, hipStream_t s) {
   float* hs = (float*)((char*)hq + f8_align256((size_t)a.capacity * I));
   F8Args g1{(const uint8_t*)a.x_codes, a.x_scales, a.row_index, a.row_div, a.offsets, a.num_local, a.capacity,
             (const uint8_t*)a.w_gate_up, a.w_gate_up_scales, 2 * I, d, I, h, I};
-  if (a.capacity >= kB8MinCapacity) {   // the large-tile gate_up quantises its rows of h (quantize_h_kernel)
+  const bool big_gu = fp8_big_ok<true>(g1);
+  if (big_gu) {   // the large-tile gate_up quantises its rows of h (quantize_h_kernel the others)
     g1.Cq = hq;
     g1.Cs = hs;
   }
@@ -1374,9 +1380,9 @@ hipError_t launch_ffn_fp8(const FfnFp8Args& a, hipStream_t s) {
   // prefill-sized capacity on, the large-tile gate_up writes the codes of the
   // experts it takes, and the quantiser does the others.
   const int grid = quantize_grid(a.capacity, I, 1);
-  if (a.capacity >= kB8MinCapacity)
+  if (big_gu)
     hipLaunchKernelGGL(quantize_h_kernel, dim3(grid), dim3(256), 0, s, (const float*)h, a.offsets, a.num_local,
-                       a.capacity, I, f8_cu_count(), hq, hs);
+                       a.capacity, I, 1, f8_cu_count(), hq, hs);
   else
     hipLaunchKernelGGL((quantize_rows_kernel<false, 1>), dim3(grid), dim3(256), 0, s, (const void*)h, a.capacity,
                        a.offsets + a.num_local, I, hq, hs);
