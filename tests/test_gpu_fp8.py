@@ -231,6 +231,19 @@ def test_ffn_fp8_large_tiles_1024_local_experts():
     check_ffn(counts.tolist(), 512, 1024, 8, seed=26, distinct=5, spare_rows=max(0, BIG_CAP - M))
 
 
+@pytest.mark.parametrize("seed", [31, 32, 33])
+def test_ffn_fp8_large_tiles_random(seed):
+    """Random expert sizes at a prefill-sized capacity: a skewed mix of empty, streamed (<= 64
+    rows) and tiled experts, the 256-row tiles filling the GPU or not depending on the draw."""
+    rng = np.random.default_rng(seed)
+    nloc = int(rng.integers(8, 40))
+    counts = (rng.pareto(1.2, nloc) * rng.uniform(40, 400)).astype(np.int64)
+    counts[rng.random(nloc) < 0.2] = 0
+    d, I = int(rng.choice([1024, 2048])), int(rng.choice([512, 1024]))
+    M = int(counts.sum())
+    check_ffn(counts.tolist(), d, I, 8, seed=seed + 100, spare_rows=max(0, BIG_CAP - M) + int(rng.integers(0, 50)))
+
+
 def test_ffn_fp8_large_capacity_few_tiles():
     counts = [300, 0, 200, 40]                                 # 3 tiles of 256 x 8 N blocks: too few
     check_ffn(counts, 2048, 1024, 8, seed=23, spare_rows=BIG_CAP - sum(counts))

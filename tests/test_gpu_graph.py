@@ -34,13 +34,17 @@ def _layer(wl, fp8=False):
                         dtype=torch.bfloat16, device=DEV, fp8=fp8)
 
 
+# decode: streamed experts only; prefill: a row capacity of 65536 and about 24 k local rows, so the
+# large-tile kernels take the experts above 64 rows (and, on FP8, quantise their rows of h).
+@pytest.mark.parametrize("size", ["decode", "prefill"])
 @pytest.mark.parametrize("fp8", [False, True])
-def test_layer_graph_replays_match_eager(fp8):
-    wl = W.Workload("graph", T=96, E=64, top_k=6, num_groups=8, topk_groups=4, score_mode="raw",
-                    renormalize=True, bias_std=1.0, hidden=1024, inter=256, expert_begin=8,
+def test_layer_graph_replays_match_eager(fp8, size):
+    T, k, I = (96, 6, 256) if size == "decode" else (8192, 8, 512)
+    wl = W.Workload("graph", T=T, E=64, top_k=k, num_groups=8, topk_groups=4, score_mode="raw",
+                    renormalize=True, bias_std=1.0, hidden=1024, inter=I, expert_begin=8,
                     num_local=24, dtype="bf16", seed=11,
                     weight_format="fp8_e4m3_b128" if fp8 else "same")
-    print(f"graph capture fp8={fp8}: T={wl.T} E={wl.E} local={wl.num_local} d={wl.hidden} I={wl.inter}",
+    print(f"graph capture fp8={fp8} {size}: T={wl.T} E={wl.E} local={wl.num_local} d={wl.hidden} I={wl.inter}",
           flush=True)
     inp = W.generate(wl)
     inp2 = W.generate(wl.replace(seed=12))
