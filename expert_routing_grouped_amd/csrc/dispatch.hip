@@ -7,13 +7,16 @@
 // equals a stable sort by expert.
 //
 // Sort kernel: one workgroup of 16 wavefronts. Wave w owns a contiguous chunk
-// of assignments and walks it 64 at a time. Lanes holding the same expert are
-// found with one ballot per key bit (a wave-wide "match"), which gives each
-// lane its rank among equal keys in the step without atomics. Pass 1 counts
-// per (wave, expert) in LDS; a scan turns the counts into per-(wave, expert)
-// rank bases (assignments of the expert in earlier waves) and per-expert
-// offsets; pass 2 re-walks the chunk and writes each assignment at offset +
-// rank. All integer, no atomics: bit-for-bit deterministic.
+// of assignments and walks it 64 at a time. Pass 1 counts per (wave, expert)
+// in LDS (an integer atomic add per assignment); a scan turns the counts into
+// per-(wave, expert) rank bases (assignments of the expert in earlier waves)
+// and per-expert offsets; pass 2 re-walks the chunk: lanes holding the same
+// expert are found with ballots (a wave-wide "match": one ballot per distinct
+// expert present when few lanes hold a local one, else one per key bit), which
+// gives each lane its rank among equal keys in the step, and the lowest lane
+// of each key group advances the wave's base for the next step. Each
+// assignment goes to offset + rank. Integer arithmetic only, and the ranks
+// follow assignment order: bit-for-bit deterministic.
 //
 // With a per-expert capacity C (the capacity factor of ch15 section 4.3,
 // drop policy) an expert keeps the assignments of rank < C, i.e. its first C
@@ -44,13 +47,39 @@ __device__ __forceinline__ uint64_t match_key(int key, bool active, int nbits) {
   return active ? m : 0ull;
 }
 
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(v, d, MOE_WAVE);
-    if (lane >= d) v += o;
+// The same masks for the lanes of `act` (non-negative keys), one ballot per
+// distinct key present: cheaper than a ballot per key bit when few lanes
+// hold a local expert (expert parallelism: about T*k / E * E_loc of T*k).
+__device__ __forceinline__ uint64_t match_few(int key, uint64_t act) {
+  uint64_t m = 0ull;
+  while (act) {
+    const int k = __builtin_amdgcn_readlane(key, __ffsll((unsigned long long)act) - 1);
+    const uint64_t mk = __ballot(key == k) & act;
+    if (key == k) m = mk;
+    act &= ~mk;
   }
+  return m;
+}
+
+constexpr int kFewKeys = 8;   // lanes with a local expert up to which match_few is used
+
+// Masks of equal local experts (e >= 0) in one 64-id group.
+__device__ __forceinline__ uint64_t match_local(int e, int nbits) {
+  const uint64_t act = __ballot(e >= 0);
+  return __popcll(act) <= kFewKeys ? match_few(e, act) : match_key(e, e >= 0, nbits);
+}
+
+// Inclusive prefix sum over the 64 lanes with DPP: row_shr 1, 2, 4, 8 inside
+// each row of 16 lanes (lanes whose source lies before the row start add 0),
+// then row_bcast:15 adds the last lane of rows 0 and 2 to rows 1 and 3, and
+// row_bcast:31 adds lane 31 to rows 2 and 3 (gfx9 DPP controls).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);
   return v;
 }
 
@@ -74,27 +103,28 @@ __device__ __forceinline__ void load_batch(const int* __restrict__ ids, int base
 }
 
 // Counts one wavefront's assignments [lo, hi) per local expert into my_cnt
-// (this wavefront's LDS row). The lowest lane of each group of equal keys adds
-// the group's size, so no two lanes write the same counter.
+// (this wavefront's LDS row): each lane with a local expert adds 1 with an
+// LDS atomic (integer sums: the result does not depend on their order).
 __device__ __forceinline__ void wave_count(const int* __restrict__ ids, int lo, int hi, int begin,
-                                           int nloc, int nbits, int* my_cnt) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
+                                           int nloc, int* my_cnt) {
   for (int base = lo; base < hi; base += 64 * kBatch) {
     int ev[kBatch];
     load_batch(ids, base, hi, begin, nloc, ev);
 #pragma unroll
-    for (int g = 0; g < kBatch; ++g) {
-      const uint64_t peers = match_key(ev[g], ev[g] >= 0, nbits);
-      if (ev[g] >= 0 && (peers & lt_mask) == 0ull) my_cnt[ev[g]] += __popcll(peers);
-    }
+    for (int g = 0; g < kBatch; ++g)
+      if (ev[g] >= 0) atomicAdd(&my_cnt[ev[g]], 1);
   }
 }
 
 // Writes one wavefront's assignments [lo, hi) in order: assignment a with
 // local expert e has rank r = my_base[e] + (earlier assignments of e in this
 // wavefront's range) and goes to ebase[e] + r when r < cap. Non-local and
-// dropped assignments get assign_pos = -1.
+// dropped assignments get assign_pos = -1. Per 64-id group the lowest lane of
+// each key group advances my_base[e] by the group's size with an LDS atomic
+// that returns the old value, and the other lanes of the key group read it
+// from that lane. A wavefront's LDS operations execute in issue order, so the
+// ranks follow assignment order; the batch's atomics are all issued before
+// the first result is used.
 __device__ __forceinline__ void wave_scatter(const int* __restrict__ ids, int lo, int hi, int begin,
                                              int nloc, int nbits, int* my_base, const int* ebase,
                                              int cap, int* __restrict__ sorted_assign,
@@ -104,13 +134,22 @@ __device__ __forceinline__ void wave_scatter(const int* __restrict__ ids, int lo
   for (int base = lo; base < hi; base += 64 * kBatch) {
     int ev[kBatch];
     load_batch(ids, base, hi, begin, nloc, ev);
+    uint64_t peers[kBatch];
+    int old[kBatch];
+#pragma unroll
+    for (int g = 0; g < kBatch; ++g) {
+      peers[g] = match_local(ev[g], nbits);
+      old[g] = 0;
+      if (ev[g] >= 0 && (peers[g] & lt_mask) == 0ull) old[g] = atomicAdd(&my_base[ev[g]], __popcll(peers[g]));
+    }
 #pragma unroll
     for (int g = 0; g < kBatch; ++g) {
       const int a = base + g * 64 + lane;
       const int e = ev[g];
-      const uint64_t peers = match_key(e, e >= 0, nbits);
+      const int first = e >= 0 ? __ffsll((unsigned long long)peers[g]) - 1 : lane;
+      const int b0 = __shfl(old[g], first, MOE_WAVE);
       if (a < hi) {
-        const int r = e >= 0 ? my_base[e] + __popcll(peers & lt_mask) : cap;
+        const int r = e >= 0 ? b0 + __popcll(peers[g] & lt_mask) : cap;
         if (r < cap) {
           const int p = ebase[e] + r;
           sorted_assign[p] = a;
@@ -119,9 +158,6 @@ __device__ __forceinline__ void wave_scatter(const int* __restrict__ ids, int lo
           assign_pos[a] = -1;
         }
       }
-      // LDS operations of one wave execute in order: every lane has read the
-      // running base above before the leader advances it here.
-      if (e >= 0 && (peers & lt_mask) == 0ull) my_base[e] += __popcll(peers);
     }
   }
 }
@@ -158,7 +194,7 @@ __global__ __launch_bounds__(256) void block_count_kernel(const int* __restrict_
   const int per_wave = per_block / kBlkWaves;
   const int lo = (int)min((long)n, (long)b * per_block + (long)w * per_wave);
   const int hi = (int)min((long)n, (long)lo + per_wave);
-  wave_count(ids, lo, hi, begin, nloc, nbits, cnt + w * nloc);
+  wave_count(ids, lo, hi, begin, nloc, cnt + w * nloc);
   __syncthreads();
   for (int e = threadIdx.x; e < nloc; e += blockDim.x) {
     int c = 0;
@@ -185,7 +221,7 @@ __global__ __launch_bounds__(256) void block_scatter_kernel(
   const int per_wave = per_block / kBlkWaves;
   const int lo = (int)min((long)n, (long)b * per_block + (long)w * per_wave);
   const int hi = (int)min((long)n, (long)lo + per_wave);
-  wave_count(ids, lo, hi, begin, nloc, nbits, cnt + w * nloc);
+  wave_count(ids, lo, hi, begin, nloc, cnt + w * nloc);
 
   // totals and this block's preceding counts for experts tid*4 .. tid*4+3;
   // the per-block counts are loaded eight blocks at a time (all eight loads
@@ -233,11 +269,13 @@ __global__ __launch_bounds__(256) void block_scatter_kernel(
       ebase[e] = fixed ? e * cap : run;
       // wave rank bases: the expert's assignments in earlier blocks and in
       // the block's earlier wavefronts
-      int s = before[q];
+      int c[kBlkWaves], s = before[q];
+#pragma unroll
+      for (int ww = 0; ww < kBlkWaves; ++ww) c[ww] = cnt[ww * nloc + e];
+#pragma unroll
       for (int ww = 0; ww < kBlkWaves; ++ww) {
-        const int c = cnt[ww * nloc + e];
         cnt[ww * nloc + e] = s;
-        s += c;
+        s += c[ww];
       }
     }
     run += min(tot[q], cap);
@@ -270,6 +308,7 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids,
 
   const int per_wave = (((n + kSortWaves - 1) / kSortWaves) + 63) & ~63;   // <= 64 * kSortGroups
   const int lo = min(n, w * per_wave), hi = min(n, lo + per_wave);
+  const int ng = (hi - lo + 63) >> 6;   // 64-id groups holding this wavefront's chunk (uniform)
   int* my_cnt = cnt + w * nloc;
 
   // load the chunk: one id per lane and group
@@ -280,28 +319,31 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids,
     raw[g] = a < hi ? ids[a] - begin : -1;
   }
   int ev[kSortGroups];
-  uint64_t peers[kSortGroups];
 #pragma unroll
-  for (int g = 0; g < kSortGroups; ++g) {
-    ev[g] = (unsigned)raw[g] < (unsigned)nloc ? raw[g] : -1;
-    peers[g] = match_key(ev[g], ev[g] >= 0, nbits);
-  }
+  for (int g = 0; g < kSortGroups; ++g) ev[g] = (unsigned)raw[g] < (unsigned)nloc ? raw[g] : -1;
   __syncthreads();  // counters cleared
 
-  // pass 1: counts per (wave, expert); the lowest lane of each key group adds
+  // pass 1: counts per (wave, expert), one LDS atomic add of 1 per lane with a
+  // local expert (integer sums: the result does not depend on their order)
 #pragma unroll
-  for (int g = 0; g < kSortGroups; ++g)
-    if (ev[g] >= 0 && (peers[g] & lt_mask) == 0ull) my_cnt[ev[g]] += __popcll(peers[g]);
+  for (int g = 0; g < kSortGroups; ++g) {
+    if (g >= ng) break;
+    if (ev[g] >= 0) atomicAdd(&my_cnt[ev[g]], 1);
+  }
   __syncthreads();
 
-  // scan: per-expert column prefix over waves (the wave rank bases), then an
-  // exclusive scan over experts of the rows kept
+  // scan: per-expert column prefix over waves (the wave rank bases; the
+  // column is read into registers first), then an exclusive scan over
+  // experts of the rows kept
   int total = 0;
   for (int e = threadIdx.x; e < nloc; e += blockDim.x) {  // nloc <= blockDim.x: one expert per thread
+    int c[kSortWaves];
+#pragma unroll
+    for (int ww = 0; ww < kSortWaves; ++ww) c[ww] = cnt[ww * nloc + e];
+#pragma unroll
     for (int ww = 0; ww < kSortWaves; ++ww) {
-      const int c = cnt[ww * nloc + e];
       cnt[ww * nloc + e] = total;
-      total += c;
+      total += c[ww];
     }
   }
   const int kept = min(total, cap);
@@ -327,23 +369,37 @@ __global__ __launch_bounds__(1024) void sort_kernel(const int* __restrict__ ids,
   }
   __syncthreads();
 
-  // pass 2: scatter in chunk order; LDS operations of one wave execute in
-  // order, so every lane reads the running base before its group's leader
-  // advances it
+  // pass 2: scatter in chunk order. Per group the lowest lane of each key
+  // group advances the wave's rank base with an LDS atomic that returns the
+  // old value, which the key group's other lanes read from it; a wavefront's
+  // LDS operations execute in issue order, so the ranks follow assignment
+  // order. All groups' atomics go out before the first result is used.
+  uint64_t peers[kSortGroups];
+  int old[kSortGroups];
 #pragma unroll
   for (int g = 0; g < kSortGroups; ++g) {
+    if (g >= ng) break;
+    peers[g] = match_local(ev[g], nbits);
+    old[g] = 0;
+    if (ev[g] >= 0 && (peers[g] & lt_mask) == 0ull) old[g] = atomicAdd(&my_cnt[ev[g]], __popcll(peers[g]));
+  }
+#pragma unroll
+  for (int g = 0; g < kSortGroups; ++g) {
+    if (g >= ng) break;
     const int a = lo + g * 64 + lane;
+    const int e = ev[g];
+    const int first = e >= 0 ? __ffsll((unsigned long long)peers[g]) - 1 : lane;
+    const int b0 = __shfl(old[g], first, MOE_WAVE);
     if (a < hi) {
-      const int r = ev[g] >= 0 ? my_cnt[ev[g]] + __popcll(peers[g] & lt_mask) : cap;
+      const int r = e >= 0 ? b0 + __popcll(peers[g] & lt_mask) : cap;
       if (r < cap) {
-        const int p = ebase[ev[g]] + r;
+        const int p = ebase[e] + r;
         sorted_assign[p] = a;
         assign_pos[a] = p;
       } else {
         assign_pos[a] = -1;
       }
     }
-    if (ev[g] >= 0 && (peers[g] & lt_mask) == 0ull) my_cnt[ev[g]] += __popcll(peers[g]);
   }
 }
 
