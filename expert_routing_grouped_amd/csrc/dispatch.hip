@@ -162,12 +162,18 @@ __device__ __forceinline__ void wave_scatter(const int* __restrict__ ids, int lo
   }
 }
 
-// ---- multi-workgroup sort (large T*k): block b owns assignments
-// [b*per_block, (b+1)*per_block), wavefront w a quarter of that. per_block is
-// 2048 until the block count reaches kMaxBlocks, then grows, so every block's
-// pass over the per-block counts stays short.
+// ---- multi-workgroup sort (large T*k), three passes: block b owns
+// assignments [b*per_block, (b+1)*per_block), wavefront w a quarter of that.
+// per_block is 1024 until the block count reaches kMaxBlocks, then grows.
+// ws holds [nblocks][nloc] ints, then the experts' totals [nloc].
+// 1. block_count_kernel: per-block counts per local expert -> ws[b][e].
+// 2. block_scan_kernel (a workgroup per 64 experts): ws[b][e] becomes the
+//    expert's assignments in blocks before b; the totals are written.
+// 3. block_scatter_kernel: each block reads its row of ws and the totals,
+//    scans the kept rows over the experts (block 0 writes counts, offsets and
+//    demand), recounts its wavefronts and scatters.
 constexpr int kBlkWaves = 4;
-constexpr int kBlkElems = kBlkWaves * 512;
+constexpr int kBlkElems = kBlkWaves * 256;
 constexpr int kMaxBlocks = 256;
 
 __host__ __device__ inline int sort_blocks(int n) {
@@ -182,10 +188,9 @@ __host__ __device__ inline int sort_per_block(int n) {
   return (int)((per + 255) & ~255L);
 }
 
-// Pass 1: per-block counts per local expert -> ws[b * nloc + e].
 __global__ __launch_bounds__(256) void block_count_kernel(const int* __restrict__ ids, int n,
                                                           int per_block, int begin, int nloc,
-                                                          int nbits, int* __restrict__ ws) {
+                                                          int* __restrict__ ws) {
   extern __shared__ int lds[];
   int* cnt = lds;  // [kBlkWaves][nloc]
   const int w = threadIdx.x >> 6, b = blockIdx.x;
@@ -199,13 +204,56 @@ __global__ __launch_bounds__(256) void block_count_kernel(const int* __restrict_
   for (int e = threadIdx.x; e < nloc; e += blockDim.x) {
     int c = 0;
     for (int ww = 0; ww < kBlkWaves; ++ww) c += cnt[ww * nloc + e];
-    ws[b * nloc + e] = c;
+    ws[(size_t)b * nloc + e] = c;
   }
 }
 
-// Pass 2: every block derives the expert offsets and its own start per expert
-// from the per-block counts (same sums in every block), recounts its
-// wavefronts, then scatters. Block 0 also writes counts and offsets.
+// Workgroup j takes experts [64 j, 64 j + 64), lane = expert; wavefront q takes
+// the q-th quarter of the blocks, so each load reads 64 consecutive experts of
+// one block. Pass 1 sums a quarter (kScanBatch loads in flight), the quarter
+// sums give each quarter's start, pass 2 re-reads the quarter and writes the
+// exclusive prefix over the blocks in place.
+constexpr int kScanBatch = 16;
+
+__global__ __launch_bounds__(256) void block_scan_kernel(int* __restrict__ ws, int nblocks, int nloc) {
+  __shared__ int qsum[kBlkWaves][64];
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const int nq = (nblocks + kBlkWaves - 1) / kBlkWaves;
+  const int b_lo = min(nblocks, q * nq), b_hi = min(nblocks, b_lo + nq);
+  int sum = 0;
+  if (e < nloc) {
+    for (int b0 = b_lo; b0 < b_hi; b0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) c[i] = b0 + i < b_hi ? ws[(size_t)(b0 + i) * nloc + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) sum += c[i];
+    }
+  }
+  qsum[q][lane] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int qq = 0; qq < q; ++qq) run += qsum[qq][lane];
+  if (e < nloc) {
+    for (int b0 = b_lo; b0 < b_hi; b0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) c[i] = b0 + i < b_hi ? ws[(size_t)(b0 + i) * nloc + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) {
+        if (b0 + i < b_hi) ws[(size_t)(b0 + i) * nloc + e] = run;
+        run += c[i];
+      }
+    }
+    if (q == kBlkWaves - 1) ws[(size_t)nblocks * nloc + e] = run;   // the expert's total
+  }
+}
+
+// Rank bases per (wave, expert): the expert's assignments in earlier blocks
+// (the scan) plus those in this block's earlier wavefronts (the recount). The
+// expert offsets come from an exclusive scan of min(total, cap) over the
+// experts, four per thread (the same sums in every block).
 __global__ __launch_bounds__(256) void block_scatter_kernel(
     const int* __restrict__ ids, int n, int per_block, int begin, int nloc, int nbits,
     const int* __restrict__ ws, int nblocks, int cap, int fixed, int* __restrict__ counts,
@@ -214,40 +262,22 @@ __global__ __launch_bounds__(256) void block_scatter_kernel(
   extern __shared__ int lds[];
   int* cnt = lds;                          // [kBlkWaves][nloc]
   int* wsum = lds + kBlkWaves * nloc;      // [4]
-  int* ebase = wsum + 4;                   // [nloc] expert offsets
+  int* ebase = wsum + 4;                   // [nloc] expert first rows
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, b = blockIdx.x;
   for (int i = tid; i < kBlkWaves * nloc; i += blockDim.x) cnt[i] = 0;
+  // this block's row of bases and the totals of experts tid*4 .. tid*4+3
+  int tot[4], before[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    tot[q] = e < nloc ? ws[(size_t)nblocks * nloc + e] : 0;
+    before[q] = e < nloc ? ws[(size_t)b * nloc + e] : 0;
+  }
   __syncthreads();
   const int per_wave = per_block / kBlkWaves;
   const int lo = (int)min((long)n, (long)b * per_block + (long)w * per_wave);
   const int hi = (int)min((long)n, (long)lo + per_wave);
   wave_count(ids, lo, hi, begin, nloc, cnt + w * nloc);
-
-  // totals and this block's preceding counts for experts tid*4 .. tid*4+3;
-  // the per-block counts are loaded eight blocks at a time (all eight loads
-  // in flight before the first is added)
-  int tot[4], before[4], sum = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    tot[q] = 0;
-    before[q] = 0;
-  }
-  for (int bb = 0; bb < nblocks; bb += 8) {
-    int c[4][8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid * 4 + q;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) c[q][i] = (e < nloc && bb + i < nblocks) ? ws[(bb + i) * nloc + e] : 0;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        tot[q] += c[q][i];
-        if (bb + i < b) before[q] += c[q][i];
-      }
-  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) sum += min(tot[q], cap);   // rows kept
   const int incl = wave_inclusive_scan(sum);
@@ -267,8 +297,6 @@ __global__ __launch_bounds__(256) void block_scatter_kernel(
         if (demand) demand[e] = tot[q];
       }
       ebase[e] = fixed ? e * cap : run;
-      // wave rank bases: the expert's assignments in earlier blocks and in
-      // the block's earlier wavefronts
       int c[kBlkWaves], s = before[q];
 #pragma unroll
       for (int ww = 0; ww < kBlkWaves; ++ww) c[ww] = cnt[ww * nloc + e];
@@ -452,7 +480,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
 
 size_t dispatch_workspace_size(int n, int num_local) {
   if (n <= kSingleBlockMax) return 0;
-  return (size_t)sort_blocks(n) * num_local * sizeof(int);
+  return ((size_t)sort_blocks(n) + 1) * num_local * sizeof(int);
 }
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
@@ -470,10 +498,12 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
                        a.offsets, a.demand, a.sorted_assign, a.assign_pos);
   } else {
     const int blocks = sort_blocks(a.n), per_block = sort_per_block(a.n);
-    const size_t lds = (size_t)(kBlkWaves * a.num_local + 4) * sizeof(int);
+    const size_t lds = (size_t)kBlkWaves * a.num_local * sizeof(int);
     hipLaunchKernelGGL(block_count_kernel, dim3(blocks), dim3(256), lds, s, a.ids, a.n, per_block,
-                       a.expert_begin, a.num_local, nbits, (int*)a.workspace);
-    const size_t lds2 = lds + (size_t)a.num_local * sizeof(int);
+                       a.expert_begin, a.num_local, (int*)a.workspace);
+    hipLaunchKernelGGL(block_scan_kernel, dim3((a.num_local + 63) / 64), dim3(256), 0, s, (int*)a.workspace,
+                       blocks, a.num_local);
+    const size_t lds2 = lds + (size_t)(a.num_local + 4) * sizeof(int);
     hipLaunchKernelGGL(block_scatter_kernel, dim3(blocks), dim3(256), lds2, s, a.ids, a.n,
                        per_block, a.expert_begin, a.num_local, nbits, (const int*)a.workspace,
                        blocks, a.capacity, a.fixed_slots, a.counts, a.offsets, a.demand,

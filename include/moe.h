@@ -289,8 +289,9 @@ size_t moe_dispatch_workspace_size(int32_t num_tokens, int32_t top_k, int32_t nu
  * x               [T, hidden] (dtype) or NULL: token rows to gather.
  * x_sorted        [T * k, hidden] (dtype) out, or NULL (only with x == NULL):
  *                 row i = x[sorted_assign[i] / k] for i < M (exact copy).
- * workspace       device buffer of moe_dispatch_workspace_size bytes (per-block
- *                 counts of the multi-workgroup sort); contents need not be set.
+ * workspace       device buffer of moe_dispatch_workspace_size bytes, 16-byte
+ *                 aligned (the multi-workgroup sort's per-(expert, block)
+ *                 counts and rank bases); contents need not be set.
  * Limits: 1 <= num_local_experts <= 1024 (as moe_expert_ffn); T * k < 2^31;
  * hidden % 8 == 0 when x is given. T = 0 writes zero counts and offsets.
  */

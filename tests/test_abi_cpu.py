@@ -90,7 +90,8 @@ def test_dispatch_validation():
     assert l.moe_dispatch(None, 4, 8, 0, 8, None, 0, 1, p, p, p, p, None, *W) == 1 # NULL ids
     # large T*k needs a workspace of one int per (2048-assignment block, local expert)
     assert l.moe_dispatch_workspace_size(1024, 8, 32) == 0
-    assert l.moe_dispatch_workspace_size(8192, 8, 32) == 32 * 32 * 4
+    # 65536 assignments: 64 blocks of 1024, a [blocks][experts] table plus one row of totals
+    assert l.moe_dispatch_workspace_size(8192, 8, 32) == (64 + 1) * 32 * 4
     assert l.moe_dispatch(p, 8192, 8, 0, 32, None, 0, 1, p, p, p, p, None, None, 0, None) == 3
     assert l.moe_dispatch(p, 8192, 8, 0, 32, None, 0, 1, p, p, p, p, None, p, 100, None) == 3
 
