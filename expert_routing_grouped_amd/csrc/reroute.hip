@@ -40,56 +40,53 @@ __global__ __launch_bounds__(256) void reroute_originals_kernel(const int* __res
   }
 }
 
-// One thread per token: the i-th overflowing slot (pos1 < 0) takes spare rank
-// k + i, or -1 when the token has no such candidate; kept slots get -1 (not
-// rerouted).
+// One wavefront per token, lane j = slot j (k <= 64): the i-th overflowing slot
+// (pos1 < 0; i = overflowing slots before it, a ballot prefix) takes spare
+// rank k + i, or -1 when the token has no such candidate; kept slots get -1
+// (not rerouted).
 __global__ __launch_bounds__(256) void reroute_candidates_kernel(const int* __restrict__ ids2,
                                                                  const int* __restrict__ pos1, int T, int k,
                                                                  int k2, int* __restrict__ rid) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
-  int i = 0;
-  for (int j = 0; j < k; ++j) {
-    const long a = (long)t * k + j;
-    int r = -1;
-    if (pos1[a] < 0) {
-      if (k + i < k2) r = ids2[(long)t * k2 + k + i];
-      ++i;
-    }
-    rid[a] = r;
-  }
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;   // uniform per wave
+  const long a = (long)t * k + lane;
+  const bool over = lane < k && pos1[a] < 0;
+  const int i = __popcll(__ballot(over) & ((1ull << lane) - 1ull));
+  if (lane < k) rid[a] = (over && k + i < k2) ? ids2[(long)t * k2 + k + i] : -1;
 }
 
-// One thread per token: final experts and weights. A rerouted slot is kept
-// when its rank among its expert's rerouted slots is below C - counts1[e].
-// Threads t < E also write the final load of expert t.
+// One wavefront per token, lane j = slot j: final experts and weights. A
+// rerouted slot is kept when its rank among its expert's rerouted slots is
+// below C - counts1[e]. The scores of the final experts are summed in slot
+// order (the weights' normaliser). Threads of the grid also write the final
+// load of every expert.
 __global__ __launch_bounds__(256) void reroute_finalize_kernel(
     const float* __restrict__ scores, const int* __restrict__ ids2, const int* __restrict__ pos1,
     const int* __restrict__ counts1, const int* __restrict__ rid, const int* __restrict__ pos2,
     const int* __restrict__ offsets2, const int* __restrict__ counts2, int T, int E, int k, int k2, int cap,
     int renormalize, int* __restrict__ ids, float* __restrict__ weights, int* __restrict__ load) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (load && t < E) load[t] = counts1[t] + min(counts2[t], cap - counts1[t]);
-  if (t >= T) return;
-  float sum = 0.0f;
-  for (int j = 0; j < k; ++j) {   // final experts, and the sum of their scores in slot order
-    const long a = (long)t * k + j;
-    int e = -1;
+  if (load)
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < E; e += gridDim.x * blockDim.x)
+      load[e] = counts1[e] + min(counts2[e], cap - counts1[e]);
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;   // uniform per wave
+  const long a = (long)t * k + lane;
+  int e = -1;
+  if (lane < k) {
     if (pos1[a] >= 0) {
-      e = ids2[(long)t * k2 + j];
+      e = ids2[(long)t * k2 + lane];
     } else {
       const int r = rid[a];
       if (r >= 0 && pos2[a] - offsets2[r] < cap - counts1[r]) e = r;
     }
     ids[a] = e;
-    if (e >= 0) sum += scores[(long)t * E + e];
   }
-  for (int j = 0; j < k; ++j) {   // weights (the thread re-reads its own ids)
-    const long a = (long)t * k + j;
-    const int e = ids[a];
-    const float w = e >= 0 ? scores[(long)t * E + e] : 0.0f;
-    weights[a] = renormalize ? (sum > 0.0f ? w / sum : 0.0f) : w;
-  }
+  const float w = e >= 0 ? scores[(long)t * E + e] : 0.0f;
+  float sum = 0.0f;
+  for (int j = 0; j < k; ++j) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
+  if (lane < k) weights[a] = renormalize ? (sum > 0.0f ? w / sum : 0.0f) : w;
 }
 
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -136,15 +133,14 @@ hipError_t launch_route_reroute(const RerouteArgs& a, hipStream_t s) {
   err = launch_dispatch(d1, s);
   if (err != hipSuccess) return err;
   // 3. each overflowing slot's candidate, then its rank among its expert's rerouted slots
-  const int tb = (a.T + 255) / 256;
+  const int tb = (a.T + 3) / 4;   // a wavefront per token
   hipLaunchKernelGGL(reroute_candidates_kernel, dim3(tb), dim3(256), 0, s, ids2, pos1, a.T, a.k, k2, rid);
   DispatchArgs d2{rid, (int)n, a.k, 0, a.E, counts2, offsets2, sa2, pos2, nullptr, nullptr, 0, dws, INT32_MAX,
                   nullptr};
   err = launch_dispatch(d2, s);
   if (err != hipSuccess) return err;
   // 4. final experts, weights and loads
-  const int fb = (std::max(a.T, a.E) + 255) / 256;
-  hipLaunchKernelGGL(reroute_finalize_kernel, dim3(fb), dim3(256), 0, s, a.scores, ids2, pos1, counts1, rid, pos2,
+  hipLaunchKernelGGL(reroute_finalize_kernel, dim3(tb), dim3(256), 0, s, a.scores, ids2, pos1, counts1, rid, pos2,
                      offsets2, counts2, a.T, a.E, a.k, k2, a.cap, a.renormalize, a.ids, a.weights, a.load);
   return hipGetLastError();
 }
