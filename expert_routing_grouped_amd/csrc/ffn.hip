@@ -64,6 +64,7 @@ struct GemmArgs {
   int sk_grid;            // shared-activation path: workgroups that share out the K steps
   int sk_items;           // shared-activation path: finalize items (largest pair count x row blocks)
   int* chunk_desc;        // shared-activation path: [0] = pairs, then (lo, m, v0, v1) per (chunk, slab) pair
+  const int* out_index = nullptr;   // streaming path, plain GEMM: output row i goes to C row out_index[i]
 };
 
 // Replaces each permuted row number by the row of A that holds it. All index
@@ -254,6 +255,16 @@ struct Stream {
 #pragma unroll
       for (int h = 0; h < 2; ++h) av[i][h] = av[i][h] * pitch + lc * 16;
 
+    // Output rows of the lane's MFMA columns (rows i*16 + lane % 16), loaded
+    // now so that the epilogue does not wait for them.
+    int orow[MTA];
+#pragma unroll
+    for (int i = 0; i < MTA; ++i) {
+      const int r = i * 16 + fr;
+      orow[i] = lo + r;
+      if (!GATED && a.out_index && r < m) orow[i] = a.out_index[lo + r];
+    }
+
     char* xs = smem + wave * WAVE_LDS;  // NTW weight tiles, then MT activation tiles
     const int woff[2] = {lr * 128 + ((lc ^ lr) << 4), (8 + lr) * 128 + ((lc ^ lr) << 4)};
     const int roff[2] = {fr * 128 + ((g ^ (fr & 7)) << 4), fr * 128 + (((4 + g) ^ (fr & 7)) << 4)};
@@ -365,7 +376,7 @@ struct Stream {
       if (KS > 1 && i % KS != ks) continue;
       const int row = i * 16 + fr;
       if (row >= m) continue;
-      uint16_t* crow = a.C + (size_t)(lo + row) * a.ldc + col0 + g * 4;
+      uint16_t* crow = a.C + (size_t)orow[i] * a.ldc + col0 + g * 4;
 #pragma unroll
       for (int t = 0; t < HT; ++t) {
         float v[4];
@@ -1738,10 +1749,15 @@ hipError_t launch_ffn_masked(const FfnMaskedArgs& a, hipStream_t s) {
                      row_index);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  // With at most kChunkRows rows per expert every expert is streamed, and
+  // (inter outside the walk path's 64 and 128) the down GEMM's streaming
+  // epilogue writes each output row straight to its slot row.
+  const bool direct = a.bf16 && a.cap <= kChunkRows && a.inter != 64 && a.inter != 128;
   FfnArgs f{a.x_slots, row_index, 1, offsets, a.w_gate_up, a.w_down, a.num_local, a.hidden, a.inter, (int)rows,
-            a.bf16, o_compact, ws};
+            a.bf16, direct ? a.o_slots : o_compact, ws};
+  if (direct) f.out_index = row_index;
   err = launch_ffn(f, s);
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || direct) return err;
   const int blocks = (int)std::min<long>((rows + 3) / 4, 2048);
   hipLaunchKernelGGL(masked_scatter_kernel, dim3(blocks), dim3(256), 0, s, (const uint4*)o_compact, row_index,
                      offsets, a.num_local, (int)(row_bytes / 16), (uint4*)a.o_slots);
@@ -1757,6 +1773,7 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
                 (uint16_t*)a.workspace, I};
     GemmArgs g2{(const uint16_t*)a.workspace, nullptr, 1, a.offsets, a.num_local, a.capacity,
                 (const uint16_t*)a.w_down, d, I, I, (uint16_t*)a.o_sorted, d};
+    g2.out_index = a.out_index;
     const hipError_t err = use_shared(d, I)
         ? launch_gate_up_shared(g1, (size_t)a.capacity * I * 2, a.workspace, s)
         : launch_gemm<true>(g1, s);
