@@ -158,6 +158,58 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ sc
   for (int v = 0; v < V; ++v) key[v] = cand[v] ? ordered_key(val[v]) : 0u;
   int my_id = 0;
   float my_val = 0.0f;
+  if constexpr (V >= 8) {
+    // Many values per lane: each lane sorts its (key, v) pairs once (bitonic
+    // network on key << 32 | (V - 1 - v): larger key first, then lower v), parks
+    // the sorted list and its values in its wavefront's LDS, and a round pops
+    // only the winner's head -- O(1) instructions per round instead of a pass
+    // over the V values. Same winners, same order, same values.
+    __shared__ uint64_t s_pk[4][V][64];
+    __shared__ float s_val[4][V][64];
+    const int wv = threadIdx.x >> 6;
+    uint64_t pk[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      pk[v] = ((uint64_t)key[v] << 32) | (uint32_t)(V - 1 - v);
+      s_val[wv][v][lane] = val[v];
+    }
+#pragma unroll
+    for (int size = 2; size <= V; size <<= 1)
+#pragma unroll
+      for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          const int j = i ^ stride;
+          if (j > i) {
+            const uint64_t x = pk[i], y = pk[j];
+            const bool sw = (i & size) == 0 ? x < y : x > y;   // descending runs first
+            pk[i] = sw ? y : x;
+            pk[j] = sw ? x : y;
+          }
+        }
+#pragma unroll
+    for (int v = 0; v < V; ++v) s_pk[wv][v][lane] = pk[v];
+    uint64_t cur = pk[0], nxt = pk[1];
+    int head = 1;   // position of nxt
+    for (int r = 0; r < k; ++r) {
+      const uint32_t ck = (uint32_t)(cur >> 32);
+      const uint32_t win = wave_max_u32_dpp(ck);
+      const uint64_t holders = __ballot(ck == win);
+      const int owner = __ffsll((unsigned long long)holders) - 1;
+      int vsel = 0;
+      float sv = 0.0f;   // no candidate left anywhere: expert 0, value 0, as the plain pass gives
+      if (win != 0u) {
+        vsel = V - 1 - __builtin_amdgcn_readlane((int)(uint32_t)cur, owner);
+        sv = s_val[wv][vsel][owner];
+        if (lane == owner) {
+          cur = nxt;
+          ++head;
+          nxt = head < V ? s_pk[wv][head][lane] : 0ull;
+        }
+      }
+      if (lane == r) { my_id = owner * V + vsel; my_val = sv; }
+    }
+  } else {
   for (int r = 0; r < k; ++r) {
     uint32_t best = 0u;
     int bv = 0;
@@ -176,6 +228,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ sc
         if (v == vsel) key[v] = 0u;
     }
     if (lane == r) { my_id = owner * V + vsel; my_val = sv; }
+  }
   }
 
   float w = softmax ? expf(my_val - lmax) / lsum : my_val;
