@@ -64,7 +64,11 @@ struct GemmArgs {
   int sk_grid;            // shared-activation path: workgroups that share out the K steps
   int sk_items;           // shared-activation path: finalize items (largest pair count x row blocks)
   int* chunk_desc;        // shared-activation path: [0] = pairs, then (lo, m, v0, v1) per (chunk, slab) pair
-  const int* out_index = nullptr;   // streaming path, plain GEMM: output row i goes to C row out_index[i]
+  // Masked layout (streaming path only): the rows per expert are min(max(count, 0), slot_cap)
+  // from slot_counts instead of offsets, and expert e's r-th row is row e * slot_cap + r of A
+  // (slot_a) or of C (slot_c) instead of its compact row.
+  const int* slot_counts = nullptr;
+  int slot_cap = 0, slot_a = 0, slot_c = 0;
 };
 
 // Replaces each permuted row number by the row of A that holds it. All index
@@ -110,11 +114,43 @@ __device__ void build_lists(const GemmArgs& a, int bm, int* s_first, int* t_firs
                             int stream_max = kChunkRows) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int cc[4], tc[4], cs = 0, ct = 0, cb = 0;
+  int ms[4] = {0, 0, 0, 0};
+  if (a.slot_counts) {   // compact row bounds: the prefix sums of the clamped counts
+    int rs = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid * 4 + q;
+      ms[q] = e < a.nloc ? min(max(a.slot_counts[e], 0), a.slot_cap) : 0;
+      rs += ms[q];
+    }
+    int ir = rs;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(ir, d, MOE_WAVE);
+      if (lane >= d) ir += o;
+    }
+    if (lane == 63) wsum[w] = ir;
+    __syncthreads();
+    int pr = ir - rs, tr = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < w) pr += wsum[i];
+      tr += wsum[i];
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid * 4 + q;
+      if (e < a.nloc) s_lo[e] = pr;
+      pr += ms[q];
+    }
+    if (tid == 0) s_lo[a.nloc] = tr;
+    __syncthreads();   // wsum is reused below
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = tid * 4 + q;
-    int m = 0;
-    if (e < a.nloc) {
+    int m = ms[q];
+    if (e < a.nloc && !a.slot_counts) {
       const int lo = min(a.offsets[e], a.capacity);
       const int hi = min(a.offsets[e + 1], a.capacity);
       m = max(0, hi - lo);
@@ -217,7 +253,7 @@ struct Stream {
   // MTA = active row tiles of the chunk (1..MT): the K loop has no branches,
   // so the only waits are on the registers an MFMA reads.
   template <int MTA, bool NT>
-  __device__ static void run_mt(const GemmArgs& a, int e, int lo, int m, int slab, char* smem) {
+  __device__ static void run_mt(const GemmArgs& a, int e, int lo, int m, int slab, int shift, char* smem) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int ks = wave % KS, wn = wave / KS;
@@ -247,23 +283,14 @@ struct Stream {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int r = i * 16 + h * 8 + lr;
-        av[i][h] = lo + (r < m ? r : 0);
+        av[i][h] = lo + (r < m ? r : 0) + (a.slot_a ? shift : 0);
       }
     a_rows<MTA * 2>(a, &av[0][0]);
 #pragma unroll
     for (int i = 0; i < MTA; ++i)
 #pragma unroll
       for (int h = 0; h < 2; ++h) av[i][h] = av[i][h] * pitch + lc * 16;
-
-    // Output rows of the lane's MFMA columns (rows i*16 + lane % 16), loaded
-    // now so that the epilogue does not wait for them.
-    int orow[MTA];
-#pragma unroll
-    for (int i = 0; i < MTA; ++i) {
-      const int r = i * 16 + fr;
-      orow[i] = lo + r;
-      if (!GATED && a.out_index && r < m) orow[i] = a.out_index[lo + r];
-    }
+    const int cshift = a.slot_c ? shift : 0;   // output rows: compact, or slot rows
 
     char* xs = smem + wave * WAVE_LDS;  // NTW weight tiles, then MT activation tiles
     const int woff[2] = {lr * 128 + ((lc ^ lr) << 4), (8 + lr) * 128 + ((lc ^ lr) << 4)};
@@ -376,7 +403,7 @@ struct Stream {
       if (KS > 1 && i % KS != ks) continue;
       const int row = i * 16 + fr;
       if (row >= m) continue;
-      uint16_t* crow = a.C + (size_t)orow[i] * a.ldc + col0 + g * 4;
+      uint16_t* crow = a.C + (size_t)(lo + row + cshift) * a.ldc + col0 + g * 4;
 #pragma unroll
       for (int t = 0; t < HT; ++t) {
         float v[4];
@@ -398,15 +425,17 @@ struct Stream {
     const int m = __builtin_amdgcn_readfirstlane(min(kChunkRows, s_lo[e + 1] - lo));
     const bool nt = __builtin_amdgcn_readfirstlane(s_lo[e + 1] - s_lo[e]) <= kChunkRows && a.K >= 512;
     slab = __builtin_amdgcn_readfirstlane(slab);
+    // masked layout: slot row = e * slot_cap + (compact row - s_lo[e])
+    const int shift = a.slot_counts ? __builtin_amdgcn_readfirstlane(e * a.slot_cap - s_lo[e]) : 0;
     switch (((m + 15) >> 4) * 2 + (nt ? 1 : 0)) {
-      case 2: run_mt<1, false>(a, e, lo, m, slab, smem); break;
-      case 3: run_mt<1, true>(a, e, lo, m, slab, smem); break;
-      case 4: run_mt<2, false>(a, e, lo, m, slab, smem); break;
-      case 5: run_mt<2, true>(a, e, lo, m, slab, smem); break;
-      case 6: run_mt<3, false>(a, e, lo, m, slab, smem); break;
-      case 7: run_mt<3, true>(a, e, lo, m, slab, smem); break;
-      case 9: run_mt<4, true>(a, e, lo, m, slab, smem); break;
-      default: run_mt<4, false>(a, e, lo, m, slab, smem); break;
+      case 2: run_mt<1, false>(a, e, lo, m, slab, shift, smem); break;
+      case 3: run_mt<1, true>(a, e, lo, m, slab, shift, smem); break;
+      case 4: run_mt<2, false>(a, e, lo, m, slab, shift, smem); break;
+      case 5: run_mt<2, true>(a, e, lo, m, slab, shift, smem); break;
+      case 6: run_mt<3, false>(a, e, lo, m, slab, shift, smem); break;
+      case 7: run_mt<3, true>(a, e, lo, m, slab, shift, smem); break;
+      case 9: run_mt<4, true>(a, e, lo, m, slab, shift, smem); break;
+      default: run_mt<4, false>(a, e, lo, m, slab, shift, smem); break;
     }
   }
 };
@@ -1738,6 +1767,19 @@ hipError_t launch_ffn_masked(const FfnMaskedArgs& a, hipStream_t s) {
   const long rows = (long)a.num_local * a.cap;
   if (rows == 0) return hipSuccess;
   char* ws = (char*)a.workspace;
+  // With at most kChunkRows rows per expert (and inter outside the shared and
+  // walk paths' 64 and 128) every expert is streamed: the GEMMs take the counts
+  // and read x and write o in slot rows themselves, so no plan, row index or
+  // copy back is needed.
+  if (a.bf16 && a.cap <= kChunkRows && a.inter != 64 && a.inter != 128) {
+    ws += align256((size_t)(a.num_local + 1) * sizeof(int)) + align256((size_t)rows * sizeof(int)) +
+          align256((size_t)rows * a.hidden * 2);
+    FfnArgs f{a.x_slots, nullptr, 1, nullptr, a.w_gate_up, a.w_down, a.num_local, a.hidden, a.inter, (int)rows,
+              true, a.o_slots, ws};
+    f.slot_counts = a.counts;
+    f.slot_cap = a.cap;
+    return launch_ffn(f, s);
+  }
   int* offsets = (int*)ws;
   ws += align256((size_t)(a.num_local + 1) * sizeof(int));
   int* row_index = (int*)ws;
@@ -1749,15 +1791,10 @@ hipError_t launch_ffn_masked(const FfnMaskedArgs& a, hipStream_t s) {
                      row_index);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // With at most kChunkRows rows per expert every expert is streamed, and
-  // (inter outside the walk path's 64 and 128) the down GEMM's streaming
-  // epilogue writes each output row straight to its slot row.
-  const bool direct = a.bf16 && a.cap <= kChunkRows && a.inter != 64 && a.inter != 128;
   FfnArgs f{a.x_slots, row_index, 1, offsets, a.w_gate_up, a.w_down, a.num_local, a.hidden, a.inter, (int)rows,
-            a.bf16, direct ? a.o_slots : o_compact, ws};
-  if (direct) f.out_index = row_index;
+            a.bf16, o_compact, ws};
   err = launch_ffn(f, s);
-  if (err != hipSuccess || direct) return err;
+  if (err != hipSuccess) return err;
   const int blocks = (int)std::min<long>((rows + 3) / 4, 2048);
   hipLaunchKernelGGL(masked_scatter_kernel, dim3(blocks), dim3(256), 0, s, (const uint4*)o_compact, row_index,
                      offsets, a.num_local, (int)(row_bytes / 16), (uint4*)a.o_slots);
@@ -1773,7 +1810,12 @@ hipError_t launch_ffn(const FfnArgs& a, hipStream_t s) {
                 (uint16_t*)a.workspace, I};
     GemmArgs g2{(const uint16_t*)a.workspace, nullptr, 1, a.offsets, a.num_local, a.capacity,
                 (const uint16_t*)a.w_down, d, I, I, (uint16_t*)a.o_sorted, d};
-    g2.out_index = a.out_index;
+    if (a.slot_counts) {   // masked layout: x and o in slot rows, h compact
+      g1.slot_counts = g2.slot_counts = a.slot_counts;
+      g1.slot_cap = g2.slot_cap = a.slot_cap;
+      g1.slot_a = 1;
+      g2.slot_c = 1;
+    }
     const hipError_t err = use_shared(d, I)
         ? launch_gate_up_shared(g1, (size_t)a.capacity * I * 2, a.workspace, s)
         : launch_gemm<true>(g1, s);

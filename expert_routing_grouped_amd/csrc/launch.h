@@ -96,15 +96,20 @@ struct FfnArgs {
   bool bf16;
   void* o_sorted;
   void* workspace;
-  const int* out_index = nullptr;  // null, or (bf16, streamed experts only) o row i is o_sorted row out_index[i]
+  // Masked layout (bf16, every expert streamed): rows per expert from these
+  // counts (clamped to [0, slot_cap]) instead of offsets; x and o_sorted hold
+  // expert e's r-th row at row e * slot_cap + r.
+  const int* slot_counts = nullptr;
+  int slot_cap = 0;
 };
 size_t ffn_workspace_size(int num_local, int hidden, int inter, int capacity, bool bf16);
 hipError_t launch_ffn(const FfnArgs& a, hipStream_t s);
 
 // The expert FFN on fixed per-expert slots of `cap` rows with a valid count per
-// expert (the masked layout): a plan kernel, the grouped FFN through a row
-// index, and the outputs back to the slot rows (written there directly by the
-// down GEMM when every expert is streamed, else by a scatter kernel).
+// expert (the masked layout): when every expert is streamed the grouped FFN
+// takes the counts and works on the slot rows directly; else a plan kernel, the
+// grouped FFN through a row index, and a scatter of the outputs back to the
+// slot rows.
 struct FfnMaskedArgs {
   const void* x_slots;   // [num_local * cap, hidden]
   const int* counts;     // [num_local] valid rows per expert (clamped to [0, cap])
