@@ -148,3 +148,33 @@ def test_masked_layer_matches_oracle():
     e = rel_err(oracle.bf16_bits_to_f64(to_host(y)), ref_y)
     print(f"masked layer rel_err y={e:.2e}", flush=True)
     assert e <= 2e-2
+
+
+@pytest.mark.parametrize("C,inter", [(24, 256), (24, 64), (96, 256)])
+def test_ffn_masked_counts_out_of_range(C, inter):
+    """Counts below 0 or above C are clamped to [0, C] by every FFN path: the GEMMs that take the
+    counts themselves (C <= 64, inter 256) and the plan / scatter path (inter 64: the narrow-expert
+    kernels; C = 96: experts above 64 rows). Slot rows past an expert's clamped count, here filled
+    with large values, reach no output, and their output rows keep the sentinel."""
+    rng = np.random.default_rng(900 + C + inter)
+    E_loc, d = 6, 512
+    counts = np.array([-3, C + 5, 0, C, 1, C // 2 + 1], dtype=np.int32)
+    x_slots = rng.standard_normal((E_loc * C, d)).astype(np.float32)
+    wgu = (rng.standard_normal((E_loc, 2 * inter, d)) * 0.05).astype(np.float32)
+    wd = (rng.standard_normal((E_loc, d, inter)) * 0.05).astype(np.float32)
+    xb, gub, db = W.f32_to_bf16_bits(x_slots), W.f32_to_bf16_bits(wgu), W.f32_to_bf16_bits(wd)
+    valid = np.zeros(E_loc * C, dtype=bool)
+    for e in range(E_loc):
+        valid[e * C:e * C + min(max(int(counts[e]), 0), C)] = True
+    xb[~valid] = np.uint16(0x4780)             # 65536: must reach no output
+    sentinel = 12288.0
+    o_slots = torch.full((E_loc * C, d), sentinel, dtype=torch.bfloat16, device=DEV)
+    moe.moe_expert_ffn_masked(to_device(xb, DEV), to_device(counts, DEV), C, to_device(gub, DEV),
+                              to_device(db, DEV), o_slots)
+    torch.cuda.synchronize()
+    got = oracle.bf16_bits_to_f64(to_host(o_slots))
+    ref = oracle.expert_ffn_masked(xb, counts, C, gub, db)
+    e = rel_err(got[valid], ref[valid])
+    print(f"masked counts out of range C={C} inter={inter}: rel_err {e:.2e}", flush=True)
+    assert e <= 2e-2
+    assert (got[~valid] == sentinel).all()
