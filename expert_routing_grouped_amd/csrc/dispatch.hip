@@ -49,7 +49,8 @@ __device__ __forceinline__ uint64_t match_key(int key, bool active, int nbits) {
 
 // The same masks for the lanes of `act` (non-negative keys), one ballot per
 // distinct key present: cheaper than a ballot per key bit when few lanes
-// hold a local expert (expert parallelism: about T*k / E * E_loc of T*k).
+// hold a local expert (under expert parallelism about E_loc / E of the
+// assignments are local).
 __device__ __forceinline__ uint64_t match_few(int key, uint64_t act) {
   uint64_t m = 0ull;
   while (act) {

@@ -178,3 +178,30 @@ def test_ffn_masked_counts_out_of_range(C, inter):
     print(f"masked counts out of range C={C} inter={inter}: rel_err {e:.2e}", flush=True)
     assert e <= 2e-2
     assert (got[~valid] == sentinel).all()
+
+
+def test_ffn_masked_1024_experts_direct():
+    """1024 local experts x C = 16 slots: the GEMMs take the counts themselves (C <= 64), and with
+    16384 slot rows the large-tile kernel is launched as well and must find no work in the same
+    counts; counts from -2 to 20 (clamped), against the oracle."""
+    rng = np.random.default_rng(977)
+    E_loc, C, d, inter = 1024, 16, 256, 256
+    counts = rng.integers(-2, 21, size=E_loc).astype(np.int32)
+    x_slots = W.f32_to_bf16_bits(rng.standard_normal((E_loc * C, d)).astype(np.float32))
+    gub = W.f32_to_bf16_bits((rng.standard_normal((E_loc, 2 * inter, d)) * 0.06).astype(np.float32))
+    db = W.f32_to_bf16_bits((rng.standard_normal((E_loc, d, inter)) * 0.06).astype(np.float32))
+    valid = np.zeros(E_loc * C, dtype=bool)
+    for e in range(E_loc):
+        valid[e * C:e * C + min(max(int(counts[e]), 0), C)] = True
+    x_slots[~valid] = np.uint16(0x4780)
+    sentinel = 12288.0
+    o_slots = torch.full((E_loc * C, d), sentinel, dtype=torch.bfloat16, device=DEV)
+    moe.moe_expert_ffn_masked(to_device(x_slots, DEV), to_device(counts, DEV), C, to_device(gub, DEV),
+                              to_device(db, DEV), o_slots)
+    torch.cuda.synchronize()
+    got = oracle.bf16_bits_to_f64(to_host(o_slots))
+    ref = oracle.expert_ffn_masked(x_slots, counts, C, gub, db)
+    e = rel_err(got[valid], ref[valid])
+    print(f"masked 1024 experts: {int(valid.sum())} valid rows, rel_err {e:.2e}", flush=True)
+    assert e <= 2e-2
+    assert (got[~valid] == sentinel).all()
