@@ -66,21 +66,21 @@ typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.0f + expf(-z)); }
 
-// Nearest e4m3 code of a float32 value, ties to the even code, saturating.
-// From 2^-6 up the code is the float32 pattern with its mantissa rounded to
-// 3 bits (a carry moves into the exponent) and the exponent rebiased from
-// 127 to 7; below 2^-6 it is the integer nearest to |q| * 2^9.
-__device__ __forceinline__ uint32_t e4m3_code(float q) {
-  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
-  const float a = fminf(fabsf(q), 448.0f);
-  uint32_t c;
-  if (a >= 0x1p-6f) {
-    const uint32_t u = __float_as_uint(a);
-    c = ((u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20) - (120u << 3);
-  } else {
-    c = (uint32_t)__builtin_rintf(a * 512.0f);
-  }
-  return c | sign;
+// e4m3 codes of four float32 values (value j in byte j): the nearest code,
+// ties to the even code, saturating at +-448. The rounding is gfx950's packed
+// float32 -> fp8 conversion (OCP e4m3): ties to even, subnormals below 2^-6
+// as integers times 2^-9, the sign kept for -0; between 448 and 464 it rounds
+// to 448 by itself, and the clamp keeps larger magnitudes there too. (Checked
+// equal, on every float32 of magnitude up to 464 and both signs, to the code
+// built from the bit pattern: the float32 mantissa rounded to 3 bits with a
+// carry into the exponent, rebiased from 127 to 7, and below 2^-6 the integer
+// nearest to |q| * 2^9.)
+__device__ __forceinline__ float e4m3_clamp(float q) { return fmaxf(fminf(q, 448.0f), -448.0f); }
+
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), w, true);
+  return (uint32_t)w;
 }
 
 // v / s rounded to float32 -- the correctly rounded float32 quotient --
@@ -170,12 +170,10 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* in, int 
       if (!active[u]) continue;
       const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
       const double rs = 1.0 / (double)s;
-      uint32_t lo = 0, hi = 0;
+      float q[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lo |= e4m3_code(div_by_scale(v[u][j], rs)) << (8 * j);
-        hi |= e4m3_code(div_by_scale(v[u][4 + j], rs)) << (8 * j);
-      }
+      for (int j = 0; j < 8; ++j) q[j] = div_by_scale(v[u][j], rs);
+      const uint32_t lo = e4m3_pack4(q[0], q[1], q[2], q[3]), hi = e4m3_pack4(q[4], q[5], q[6], q[7]);
       *(uint2*)(codes + first[u]) = make_uint2(lo, hi);
       if ((lane & 15) == 0) scales[(size_t)row[u] * nb + blk[u]] = s;
     }
@@ -826,9 +824,8 @@ struct Big8 {
           uint8_t* qrow = cq + (size_t)(row0 + t) * a.inter + nb * COLS + wm * 32 + fg * 4;
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
-            uint32_t c = 0;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) c |= e4m3_code(div_by_scale(h[j][i * 4 + q], rs)) << (8 * q);
+            const uint32_t c = e4m3_pack4(div_by_scale(h[j][i * 4], rs), div_by_scale(h[j][i * 4 + 1], rs),
+                                          div_by_scale(h[j][i * 4 + 2], rs), div_by_scale(h[j][i * 4 + 3], rs));
             *(uint32_t*)(qrow + i * 16) = c;
           }
           if (wm == 0 && fg == 0) cs[(size_t)(row0 + t) * (a.inter / kQBlock) + nb] = sc;
@@ -972,12 +969,10 @@ __global__ __launch_bounds__(256) void quantize_h_kernel(const float* __restrict
       if (!active[u]) continue;
       const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
       const double rs = 1.0 / (double)s;
-      uint32_t lo = 0, hi = 0;
+      float q[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        lo |= e4m3_code(div_by_scale(v[u][j], rs)) << (8 * j);
-        hi |= e4m3_code(div_by_scale(v[u][4 + j], rs)) << (8 * j);
-      }
+      for (int j = 0; j < 8; ++j) q[j] = div_by_scale(v[u][j], rs);
+      const uint32_t lo = e4m3_pack4(q[0], q[1], q[2], q[3]), hi = e4m3_pack4(q[4], q[5], q[6], q[7]);
       *(uint2*)(codes + first[u]) = make_uint2(lo, hi);
       if ((lane & 15) == 0) scales[(size_t)row[u] * nb + blk[u]] = s;
     }
