@@ -75,6 +75,39 @@ def test_quantize_bit_exact(R, C, dtype):
     assert np.array_equal(to_host(scales).view(np.uint32), rs.view(np.uint32))
 
 
+def test_quantize_e4m3_rounding_dense():
+    """Every 128-value block holds +-448, so its scale is exactly 1 and the codes are the plain e4m3
+    rounding of the other 127 values: for each interval between neighbouring e4m3 values its ends,
+    the midpoint (a tie), the float32 values one ulp either side of those, and random interior
+    values; also values below the smallest subnormal, both signs. Codes and scales bit-exact
+    against the oracle's table-based encoder."""
+    rng = np.random.default_rng(4481)
+    pos = F.e4m3_positive_values().astype(np.float32)
+    vals = [np.float32(0.0), np.float32(2.0 ** -11), np.float32(2.0 ** -10), np.float32(3 * 2.0 ** -11)]
+    for lo, hi in zip(pos[:-1], pos[1:]):
+        mid = np.float32((np.float64(lo) + np.float64(hi)) / 2)
+        for v in (lo, hi, mid):
+            vals += [v, np.nextafter(v, np.float32(np.inf)), np.nextafter(v, np.float32(-np.inf))]
+        vals += list(rng.uniform(lo, hi, 4).astype(np.float32))
+    v = np.abs(np.array(vals, dtype=np.float32))
+    v = v[v <= 448.0]
+    v = np.concatenate([v, -v])
+    rng.shuffle(v)
+    nb = (v.size + 126) // 127
+    v = np.concatenate([v, np.zeros(nb * 127 - v.size, np.float32)]).reshape(nb, 127)
+    blocks = np.concatenate([np.where(np.arange(nb)[:, None] % 2, -448.0, 448.0).astype(np.float32), v], axis=1)
+    x = blocks.reshape(-1, 8 * 128) if nb % 8 == 0 else \
+        np.concatenate([blocks, np.tile(blocks[:1], (8 - nb % 8, 1))]).reshape(-1, 8 * 128)
+    print(f"dense e4m3 rounding: {x.size} values in {x.shape[0]} rows", flush=True)
+    codes, scales = moe.moe_quantize_e4m3(to_device(x, DEV))
+    torch.cuda.synchronize()
+    rc, rs = F.quantize_rows(x)
+    assert (rs == 1.0).all()
+    assert np.array_equal(to_host(codes), rc)
+    assert np.array_equal(to_host(codes).reshape(-1), F.e4m3_encode(x.reshape(-1)))
+    assert np.array_equal(to_host(scales).view(np.uint32), rs.view(np.uint32))
+
+
 def test_quantize_no_rows():
     x = torch.zeros((0, 256), dtype=torch.float32, device=DEV)
     c, s = moe.moe_quantize_e4m3(x)
